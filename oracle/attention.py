@@ -1,0 +1,334 @@
+"""Plain float64 definition of sink attention, its GA sibling, decode and sparse form.
+
+TEST INFRASTRUCTURE ONLY: used by tests, the smoke check and the CPU-baseline
+leg of the benchmark; never by the product path.
+
+Notation follows "MiMo-V2-Flash: Hybrid Sliding Window Attention Architecture"
+(rslog.cc).  Indices here are 0-based; the page counts from 1.  For query row
+i of head h with key set J_i:
+
+    a_ij = q~_i . k~_j * scale                       (section 1.2 / 2.3)
+    m_i  = max(max_{j in J_i} a_ij, sink_h)          (section 4.4)
+    s_ij = exp(a_ij - m_i) / (exp(sink_h - m_i) + sum_{j' in J_i} exp(a_ij' - m_i))
+    o_i  = sum_{j in J_i} s_ij v_j                   (section 4.4, final output)
+
+sink_h = -inf means "no sink" (section 4.3 table: the -inf limit is the
+ordinary softmax; section 5: GA layers have no sink term).  q~ and k~ carry
+partial RoPE (pwwt.cn article, section 5); V is never rotated.
+
+Each query row is evaluated on its own with a two-pass sum: first the max,
+then the exponentials, the denominator and the weighted sum of values.  No
+online rescaling, no tiling: library matrix products are the only steps
+borrowed.
+"""
+
+import math
+
+import numpy as np
+
+NEG_INF = float("-inf")
+
+
+# ----------------------------------------------------------------------------
+# Partial rotary position embedding
+# ----------------------------------------------------------------------------
+
+def rotary_dims(d_qk, rotary_fraction):
+    """Number of rotated dims R: the largest even integer <= fraction * d_qk.
+
+    The pwwt.cn article (section 5) gives partial_rotary_factor 0.334 and
+    head_dim 192: 0.334 * 192 = 64.13, so R = 64, i.e. about a third of the
+    dims rotate.  Reading: the rotated dims are the first R.
+    """
+    if not (0.0 <= rotary_fraction <= 1.0):
+        raise ValueError("rotary_fraction must lie in [0, 1]")
+    return 2 * int(math.floor(rotary_fraction * d_qk / 2.0))
+
+
+def rope(x, pos, theta, rotary_fraction):
+    """Rotate the first R dims of x by position.
+
+    x: float64 array [..., n, H, d]; pos: n integer positions.
+    Pairing reading (the pages are silent): dim r pairs with dim r + R/2 for
+    r < R/2, angle pos * theta^(-2r/R).  Written here as one complex product
+    per pair: (x_r + i x_{r+R/2}) * exp(i * angle).  Dims >= R are untouched.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    rot = rotary_dims(d, rotary_fraction)
+    out = x.copy()
+    if rot == 0:
+        return out
+    half = rot // 2
+    r = np.arange(half, dtype=np.float64)
+    inv_freq = np.power(float(theta), -(2.0 * r) / rot)
+    angle = np.asarray(pos, dtype=np.float64)[:, None] * inv_freq[None, :]  # [n, half]
+    turn = np.exp(1j * angle)[:, None, :]                                    # [n, 1, half]
+    z = (x[..., :half] + 1j * x[..., half:rot]) * turn
+    out[..., :half] = z.real
+    out[..., half:rot] = z.imag
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Key sets J_i
+# ----------------------------------------------------------------------------
+
+def window_keys(i, window):
+    """Causal window of query i (0-based): keys max(0, i-W+1) .. i inclusive.
+
+    rslog.cc section 2.1 defines W(i) = {j : max(1, i-W+1) <= j <= i} on
+    1-based indices: W tokens including the query itself.  window None or
+    <= 0 means the full causal set 0 .. i (section 1, the GA layer).
+    """
+    lo = 0 if (window is None or window <= 0) else max(0, i - window + 1)
+    return np.arange(lo, i + 1, dtype=np.int64)
+
+
+def ring_slot_positions(p, window):
+    """Positions held by the W slots of a ring cache when the newest token is p.
+
+    Slot s holds the token at position p - ((p - s) mod W), i.e. the cache
+    writes token t into slot t mod W (youngju.dev article: the SWA pool is
+    bounded by the window).  A negative entry marks a slot that has not been
+    written yet (p < W - 1).
+    """
+    s = np.arange(window, dtype=np.int64)
+    return p - np.mod(p - s, window)
+
+
+def sparse_keys(i, selected, count, recent):
+    """Key set of token-level sparse attention for query i.
+
+    aideepthink.cn article, section 4: the most recent `recent` tokens
+    (including i) plus the selected tokens outside that window, merged into
+    one attention.  Set union of the two parts.
+    """
+    lo = max(0, i - recent + 1)
+    rec = np.arange(lo, i + 1, dtype=np.int64)
+    sel = np.asarray(selected[:count], dtype=np.int64)
+    return np.union1d(sel, rec)
+
+
+# ----------------------------------------------------------------------------
+# One query row
+# ----------------------------------------------------------------------------
+
+def attend_row(qg, kj, vj, sink, scale):
+    """Sink softmax attention of G query heads against one key set.
+
+    qg: [G, d] (already rotated), kj: [m, d] (rotated), vj: [m, dv],
+    sink: [G] (use -inf for no sink).  Returns [G, dv].
+    Two passes, as rslog.cc section 4.4 writes it: m first, then the sums.
+    """
+    qg = np.asarray(qg, dtype=np.float64)
+    kj = np.asarray(kj, dtype=np.float64)
+    vj = np.asarray(vj, dtype=np.float64)
+    sink = np.asarray(sink, dtype=np.float64).reshape(-1)
+    G = qg.shape[0]
+    dv = vj.shape[-1]
+    if kj.shape[0] == 0:
+        # No key at all: only the sink is in the denominator, nothing in the
+        # numerator.  With no sink either the row is undefined; return 0.
+        return np.zeros((G, dv), dtype=np.float64)
+    a = (qg @ kj.T) * scale                       # [G, m]   a_ij
+    m = np.maximum(a.max(axis=1), sink)           # m_i
+    out = np.zeros((G, dv), dtype=np.float64)
+    for g in range(G):
+        if m[g] == NEG_INF:
+            continue
+        e = np.exp(a[g] - m[g])                   # exp(a_ij - m_i)
+        den = math.exp(sink[g] - m[g]) if sink[g] != NEG_INF else 0.0
+        den += e.sum()
+        out[g] = (e @ vj) / den                   # sum_j s_ij v_j
+    return out
+
+
+def _sink_vector(sink, hq):
+    if sink is None:
+        return np.full(hq, NEG_INF)
+    s = np.asarray(sink, dtype=np.float64).reshape(-1)
+    if s.shape[0] != hq:
+        raise ValueError("sink must hold one value per query head")
+    return s
+
+
+def _check_heads(hq, hkv):
+    if hkv <= 0 or hq % hkv != 0:
+        raise ValueError("query heads must be a multiple of kv heads")
+    return hq // hkv
+
+
+# ----------------------------------------------------------------------------
+# Prefill (SWA with sink, and the GA sibling)
+# ----------------------------------------------------------------------------
+
+def prefill_rows(q, k, v, rows, sink=None, window=128, scale=None,
+                 rope_theta=10000.0, rotary_fraction=0.0, pos_offset=0):
+    """Prefill outputs for the query rows listed in `rows` only.
+
+    q: [B, n, Hq, d_qk], k: [B, n, Hkv, d_qk], v: [B, n, Hkv, d_v].
+    Token i sits at RoPE position pos_offset + i.  Query head h reads kv head
+    h // (Hq/Hkv) (reading: contiguous GQA groups).  Returns [B, len(rows), Hq, d_v].
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, n, hq, d = q.shape
+    hkv = k.shape[2]
+    G = _check_heads(hq, hkv)
+    rows = np.asarray(rows, dtype=np.int64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s_all = _sink_vector(sink, hq)
+    qr = rope(q[:, rows], pos_offset + rows, rope_theta, rotary_fraction)
+    kr = rope(k, pos_offset + np.arange(n), rope_theta, rotary_fraction)
+    vv = np.asarray(v, dtype=np.float64)
+    out = np.zeros((B, len(rows), hq, v.shape[-1]), dtype=np.float64)
+    for b in range(B):
+        for t, i in enumerate(rows):
+            J = window_keys(int(i), window)
+            for g in range(hkv):
+                hs = slice(g * G, (g + 1) * G)
+                out[b, t, hs] = attend_row(qr[b, t, hs], kr[b, J, g], vv[b, J, g],
+                                           s_all[hs], scale)
+    return out
+
+
+def swa_sink_prefill(q, k, v, sink, window=128, scale=None, rope_theta=10000.0,
+                     rotary_fraction=0.0, pos_offset=0):
+    """SWA layer with a learnable sink (rslog.cc section 4.4): every row."""
+    n = np.asarray(q).shape[1]
+    return prefill_rows(q, k, v, np.arange(n), sink=sink, window=window, scale=scale,
+                        rope_theta=rope_theta, rotary_fraction=rotary_fraction,
+                        pos_offset=pos_offset)
+
+
+def ga_prefill(q, k, v, scale=None, rope_theta=1.0e7, rotary_fraction=0.0, pos_offset=0):
+    """GA layer (rslog.cc section 1 and section 5): full causal set, no sink."""
+    n = np.asarray(q).shape[1]
+    return prefill_rows(q, k, v, np.arange(n), sink=None, window=None, scale=scale,
+                        rope_theta=rope_theta, rotary_fraction=rotary_fraction,
+                        pos_offset=pos_offset)
+
+
+# ----------------------------------------------------------------------------
+# Decode: one new token per sequence
+# ----------------------------------------------------------------------------
+
+def swa_sink_decode_ring(q, k_ring, v_ring, pos, sink, scale=None, rope_theta=10000.0,
+                         rotary_fraction=0.0, seqs=None):
+    """Decode against a W-slot ring cache.
+
+    q: [B, Hq, d_qk] (RoPE at position pos[b] is applied here; the cache is
+    taken to hold keys already rotated when they were written);
+    k_ring: [B, W, Hkv, d_qk], v_ring: [B, W, Hkv, d_v], pos: [B] >= 0.
+    The key set is every written slot (ring_slot_positions >= 0); the token
+    at pos[b] itself is in the cache (the window includes the query).
+    `seqs` restricts the evaluation to some sequences; returns [len(seqs), Hq, d_v].
+    """
+    q = np.asarray(q)
+    B, hq, d = q.shape
+    W = k_ring.shape[1]
+    hkv = k_ring.shape[2]
+    G = _check_heads(hq, hkv)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s_all = _sink_vector(sink, hq)
+    seqs = np.arange(B) if seqs is None else np.asarray(seqs, dtype=np.int64)
+    out = np.zeros((len(seqs), hq, v_ring.shape[-1]), dtype=np.float64)
+    for t, b in enumerate(seqs):
+        p = int(pos[b])
+        qb = rope(q[b][None], np.array([p]), rope_theta, rotary_fraction)[0]
+        slots = np.nonzero(ring_slot_positions(p, W) >= 0)[0]
+        kb = np.asarray(k_ring[b], dtype=np.float64)
+        vb = np.asarray(v_ring[b], dtype=np.float64)
+        for g in range(hkv):
+            hs = slice(g * G, (g + 1) * G)
+            out[t, hs] = attend_row(qb[hs], kb[slots, g], vb[slots, g], s_all[hs], scale)
+    return out
+
+
+def swa_sink_decode_contiguous(q, k, v, seq_offsets, pos, sink=None, window=None,
+                               scale=None, rope_theta=1.0e7, rotary_fraction=0.0,
+                               seqs=None, kv_loader=None):
+    """Decode against a contiguous per-sequence cache (the O(N) pool).
+
+    k: [sum_b len_b, Hkv, d_qk], v: [sum_b len_b, Hkv, d_v]; sequence b owns
+    rows seq_offsets[b] .. seq_offsets[b+1]-1 and its query sits at pos[b].
+    Keys are rows seq_offsets[b] + window_keys(pos[b], window): the full
+    prefix when window is None (GA layer, no sink), the last W otherwise.
+    `kv_loader(b)` may supply (k_b, v_b) for one sequence instead of k, v, so
+    that a cache too large for host memory is read one sequence at a time.
+    """
+    q = np.asarray(q)
+    B, hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s_all = _sink_vector(sink, hq)
+    seqs = np.arange(B) if seqs is None else np.asarray(seqs, dtype=np.int64)
+    out = None
+    for t, b in enumerate(seqs):
+        p = int(pos[b])
+        if kv_loader is not None:
+            kb, vb = kv_loader(int(b))
+        else:
+            lo, hi = int(seq_offsets[b]), int(seq_offsets[b + 1])
+            kb, vb = k[lo:hi], v[lo:hi]
+        if p >= kb.shape[0]:
+            raise ValueError("pos[b] must index a row inside sequence b's cache")
+        hkv = kb.shape[1]
+        G = _check_heads(hq, hkv)
+        if out is None:
+            out = np.zeros((len(seqs), hq, vb.shape[-1]), dtype=np.float64)
+        qb = rope(q[b][None], np.array([p]), rope_theta, rotary_fraction)[0]
+        J = window_keys(p, window)
+        kJ = np.asarray(kb[J], dtype=np.float64)
+        vJ = np.asarray(vb[J], dtype=np.float64)
+        for g in range(hkv):
+            hs = slice(g * G, (g + 1) * G)
+            out[t, hs] = attend_row(qb[hs], kJ[:, g], vJ[:, g], s_all[hs], scale)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Token-level sparse attention on one shared cache
+# ----------------------------------------------------------------------------
+
+def sparse_rows(q, k, v, sel_idx, sel_count, rows, sink, recent=128, scale=None,
+                rope_theta=10000.0, rotary_fraction=0.0, pos_offset=0):
+    """Sparse attention outputs for the query rows listed in `rows`.
+
+    q: [B, n, Hq, d_qk]; k: [B, n, Hkv, d_qk]; v: [B, n, Hkv, d_v];
+    sel_idx: [B, n, Hkv, max_sel] int; sel_count: [B, n, Hkv] int.
+    Query i of kv group g attends to sparse_keys(i, sel_idx[b,i,g], count, recent).
+    """
+    q = np.asarray(q)
+    B, n, hq, d = q.shape
+    hkv = k.shape[2]
+    G = _check_heads(hq, hkv)
+    rows = np.asarray(rows, dtype=np.int64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s_all = _sink_vector(sink, hq)
+    qr = rope(q[:, rows], pos_offset + rows, rope_theta, rotary_fraction)
+    kr = rope(k, pos_offset + np.arange(n), rope_theta, rotary_fraction)
+    vv = np.asarray(v, dtype=np.float64)
+    out = np.zeros((B, len(rows), hq, v.shape[-1]), dtype=np.float64)
+    for b in range(B):
+        for t, i in enumerate(rows):
+            for g in range(hkv):
+                J = sparse_keys(int(i), sel_idx[b, i, g], int(sel_count[b, i, g]), recent)
+                hs = slice(g * G, (g + 1) * G)
+                out[b, t, hs] = attend_row(qr[b, t, hs], kr[b, J, g], vv[b, J, g],
+                                           s_all[hs], scale)
+    return out
+
+
+def sparse_sink_attn(q, k, v, sel_idx, sel_count, sink, recent=128, scale=None,
+                     rope_theta=10000.0, rotary_fraction=0.0, pos_offset=0):
+    """Every row of token-level sparse attention with a sink."""
+    n = np.asarray(q).shape[1]
+    return sparse_rows(q, k, v, sel_idx, sel_count, np.arange(n), sink, recent=recent,
+                       scale=scale, rope_theta=rope_theta, rotary_fraction=rotary_fraction,
+                       pos_offset=pos_offset)

@@ -1,0 +1,19 @@
+"""Seeded synthetic inputs for the attention hot path.
+
+This module only draws random numbers and lays them out; it holds none of
+the attention arithmetic.  Both the oracle-side tests and the GPU-side tests
+and benchmark take their inputs from here.
+"""
+
+from .workloads import (  # noqa: F401
+    WORKLOADS,
+    tensor_seed,
+    normal,
+    uniform,
+    prefill_inputs,
+    ring_decode_inputs,
+    contiguous_decode_inputs,
+    decode_positions,
+    sparse_selection,
+    sparse_inputs,
+)

@@ -1,0 +1,197 @@
+"""Workload shapes and seeded generators.
+
+Recipe (the same for every workload):
+  * every tensor draws from its own torch.Generator seeded with
+    tensor_seed(base, tensor_id[, part]) so that any tensor can be rebuilt
+    alone;
+  * q, k, v ~ N(0, 1) drawn in float32 and, for bf16 workloads, cast to
+    bfloat16 with round-to-nearest-even;
+  * per-head sinks ~ U(lo, hi) in float32;
+  * decode positions ~ U{lo .. hi} drawn on the host;
+  * sparse selections: for query i and kv head g, `avail = max(0, i - recent)`
+    candidates [0, avail); all of them when avail <= max_sel, otherwise
+    max_sel distinct ones drawn uniformly (Floyd's sampling), sorted
+    ascending and padded with -1.
+
+Shapes follow the pages: window 128, 64 query heads with 8 (SWA) or 4 (GA)
+kv heads, head dims 192 / 128, RoPE bases 1e4 (SWA) / 1e7 (GA) on the first
+64 dims ("39 SWA + 9 GA layers: MiMo-V2.6-Flash hybrid SWA", pwwt.cn,
+sections 3-5), 128 recent + 1024 selected tokens ("MiMo-V3 HySparse2",
+aideepthink.cn, section 4).
+"""
+
+import torch
+
+# Tensor ids inside one workload seed space.
+TID_Q, TID_K, TID_V, TID_SINK, TID_POS, TID_SEL = 1, 2, 3, 4, 5, 6
+TID_K_GA, TID_V_GA, TID_Q_GA = 12, 13, 11
+
+WORKLOADS = {
+    # Tiny fp32 SWA+sink prefill, no RoPE; also run with sink = -inf and W = 512.
+    "tiny_fp32_swa_n512": dict(kind="prefill", seed=1, B=1, n=512, hq=2, hkv=1, d_qk=192,
+                               d_v=128, window=128, dtype="f32", sink_range=(-3.0, 3.0),
+                               rope_theta=10000.0, rotary_fraction=0.0),
+    # SWA layer prefill: n = 32768, 64 q / 8 kv heads, W = 128, RoPE 1e4 on 64 dims, sink.
+    "swa_prefill_n32768": dict(kind="prefill", seed=2, B=1, n=32768, hq=64, hkv=8, d_qk=192,
+                               d_v=128, window=128, dtype="bf16", sink_range=(-2.0, 2.0),
+                               rope_theta=1.0e4, rotary_fraction=0.334),
+    # GA layer prefill: n = 32768, 64 q / 4 kv heads, full causal, no sink, RoPE 1e7.
+    "ga_prefill_n32768": dict(kind="prefill", seed=3, B=1, n=32768, hq=64, hkv=4, d_qk=192,
+                              d_v=128, window=0, dtype="bf16", sink_range=None,
+                              rope_theta=1.0e7, rotary_fraction=0.334),
+    # Hybrid decode step: 64 sequences, one token each at p in [131072, 262143].
+    "hybrid_decode_b64": dict(kind="decode", seed=4, B=64, pos_range=(131072, 262143),
+                              d_qk=192, d_v=128, dtype="bf16",
+                              swa=dict(hq=64, hkv=8, window=128, sink_range=(-2.0, 2.0)),
+                              ga=dict(hq=64, hkv=4, window=0, sink_range=None)),
+    # Token-level sparse prefill: n = 65536, 64 q / 4 kv heads, 128 recent + <= 1024 selected.
+    "sparse_prefill_n65536": dict(kind="sparse", seed=5, B=1, n=65536, hq=64, hkv=4, d_qk=192,
+                                  d_v=128, recent=128, max_sel=1024, dtype="bf16",
+                                  sink_range=(-2.0, 2.0), rope_theta=1.0e4, rotary_fraction=0.0),
+}
+
+
+def tensor_seed(base, tensor_id, part=0):
+    """Seed of one tensor (or one part of it, e.g. one sequence of a cache)."""
+    return (int(base) * 1000 + int(tensor_id)) * 100003 + int(part)
+
+
+def _gen(seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _torch_dtype(dtype):
+    if dtype in ("f32", torch.float32):
+        return torch.float32
+    if dtype in ("bf16", torch.bfloat16):
+        return torch.bfloat16
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def normal(shape, seed, device="cpu", dtype="f32", out=None):
+    """N(0,1) drawn in float32, then cast (round-to-nearest-even) to `dtype`."""
+    x = torch.randn(shape, generator=_gen(seed, device), device=device, dtype=torch.float32)
+    if out is not None:
+        out.copy_(x)
+        return out
+    return x.to(_torch_dtype(dtype))
+
+
+def uniform(shape, lo, hi, seed, device="cpu"):
+    g = _gen(seed, device)
+    return torch.rand(shape, generator=g, device=device, dtype=torch.float32) * (hi - lo) + lo
+
+
+def prefill_inputs(B, n, hq, hkv, d_qk, d_v, dtype, seed, device="cpu", sink_range=(-2.0, 2.0)):
+    """q [B,n,Hq,d_qk], k [B,n,Hkv,d_qk], v [B,n,Hkv,d_v] and sink [Hq] (or None)."""
+    q = normal((B, n, hq, d_qk), tensor_seed(seed, TID_Q), device, dtype)
+    k = normal((B, n, hkv, d_qk), tensor_seed(seed, TID_K), device, dtype)
+    v = normal((B, n, hkv, d_v), tensor_seed(seed, TID_V), device, dtype)
+    sink = None
+    if sink_range is not None:
+        sink = uniform((hq,), sink_range[0], sink_range[1], tensor_seed(seed, TID_SINK), device)
+    return dict(q=q, k=k, v=v, sink=sink)
+
+
+def decode_positions(B, lo, hi, seed):
+    """Host int64 positions p ~ U{lo .. hi}."""
+    g = _gen(tensor_seed(seed, TID_POS), "cpu")
+    return torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64)
+
+
+def ring_decode_inputs(B, hq, hkv, window, d_qk, d_v, dtype, seed, pos, device="cpu",
+                       sink_range=(-2.0, 2.0)):
+    """q [B,Hq,d_qk] and a W-slot ring cache k [B,W,Hkv,d_qk], v [B,W,Hkv,d_v]."""
+    q = normal((B, hq, d_qk), tensor_seed(seed, TID_Q), device, dtype)
+    k = normal((B, window, hkv, d_qk), tensor_seed(seed, TID_K), device, dtype)
+    v = normal((B, window, hkv, d_v), tensor_seed(seed, TID_V), device, dtype)
+    sink = None
+    if sink_range is not None:
+        sink = uniform((hq,), sink_range[0], sink_range[1], tensor_seed(seed, TID_SINK), device)
+    return dict(q=q, k=k, v=v, sink=sink, pos=pos.to(device))
+
+
+def contiguous_decode_inputs(B, hq, hkv, d_qk, d_v, dtype, seed, pos, device="cpu",
+                             sink_range=None, extra_rows=0):
+    """q [B,Hq,d_qk] and a packed cache: sequence b owns pos[b] + 1 + extra_rows rows.
+
+    k [sum len, Hkv, d_qk], v [sum len, Hkv, d_v], seq_offsets [B+1] int64.
+    Each sequence's rows come from their own seeds, so one sequence can be
+    drawn again on its own.
+    """
+    lens = pos.to(torch.int64).cpu() + 1 + int(extra_rows)
+    offs = torch.zeros(B + 1, dtype=torch.int64)
+    offs[1:] = torch.cumsum(lens, 0)
+    total = int(offs[-1])
+    tdt = _torch_dtype(dtype)
+    q = normal((B, hq, d_qk), tensor_seed(seed, TID_Q_GA), device, dtype)
+    k = torch.empty((total, hkv, d_qk), dtype=tdt, device=device)
+    v = torch.empty((total, hkv, d_v), dtype=tdt, device=device)
+    for b in range(B):
+        lo, hi = int(offs[b]), int(offs[b + 1])
+        k[lo:hi] = normal((hi - lo, hkv, d_qk), tensor_seed(seed, TID_K_GA, b), device, "f32")
+        v[lo:hi] = normal((hi - lo, hkv, d_v), tensor_seed(seed, TID_V_GA, b), device, "f32")
+    sink = None
+    if sink_range is not None:
+        sink = uniform((hq,), sink_range[0], sink_range[1], tensor_seed(seed, TID_SINK), device)
+    return dict(q=q, k=k, v=v, sink=sink, pos=pos.to(device), seq_offsets=offs.to(device))
+
+
+def sparse_selection(B, n, hkv, recent, max_sel, seed, device="cpu", chunk_rows=8192):
+    """Selected-token lists idx [B,n,Hkv,max_sel] int32 (-1 padded) and counts [B,n,Hkv].
+
+    Candidates for query i are [0, max(0, i - recent)).  When there are more
+    than max_sel, Floyd's algorithm draws max_sel distinct ones uniformly:
+    for j = avail - max_sel .. avail - 1 draw t ~ U{0..j}; keep t unless it
+    was already taken, in which case keep j.  A per-row bitmap records the
+    set, so reading it back in index order gives the sorted list.
+    """
+    avail = torch.clamp(torch.arange(n, dtype=torch.int64) - recent, min=0)   # [n]
+    count = torch.clamp(avail, max=max_sel)
+    idx = torch.full((B, n, hkv, max_sel), -1, dtype=torch.int32, device=device)
+    cols = torch.arange(max_sel, dtype=torch.int64)
+    small = avail <= max_sel
+    # Rows with few candidates take all of them.
+    small_rows = torch.nonzero(small).flatten()
+    if small_rows.numel():
+        fill = torch.where(cols[None, :] < avail[small_rows][:, None],
+                           cols[None, :], torch.full_like(cols[None, :], -1)).to(torch.int32)
+        idx[:, small_rows] = fill[None, :, None, :].to(device)
+    big_rows = torch.nonzero(~small).flatten()
+    if big_rows.numel():
+        g = _gen(tensor_seed(seed, TID_SEL), device)
+        # Flatten (b, i, head) over the rows that need sampling.
+        A = avail[big_rows].to(device)                                        # [R]
+        R = big_rows.numel()
+        flatA = A[None, :, None].expand(B, R, hkv).reshape(-1)
+        total = flatA.numel()
+        out = torch.empty((total, max_sel), dtype=torch.int32, device=device)
+        amax = int(avail.max())
+        for c0 in range(0, total, chunk_rows):
+            c1 = min(total, c0 + chunk_rows)
+            Ac = flatA[c0:c1]
+            m = c1 - c0
+            bitmap = torch.zeros((m, amax), dtype=torch.bool, device=device)
+            ar = torch.arange(m, device=device)
+            for step in range(max_sel):
+                j = Ac - max_sel + step                                        # [m]
+                u = torch.rand(m, generator=g, device=device, dtype=torch.float64)
+                t = torch.minimum(torch.floor(u * (j + 1).to(torch.float64)).to(torch.int64), j)
+                taken = bitmap[ar, t]
+                pick = torch.where(taken, j, t)
+                bitmap[ar, pick] = True
+            nz = torch.nonzero(bitmap)                                         # row-major: sorted
+            out[c0:c1] = nz[:, 1].reshape(m, max_sel).to(torch.int32)
+        idx[:, big_rows] = out.reshape(B, R, hkv, max_sel)
+    cnt = count[None, :, None].expand(B, n, hkv).to(torch.int32).contiguous().to(device)
+    return idx, cnt
+
+
+def sparse_inputs(B, n, hq, hkv, d_qk, d_v, dtype, seed, recent=128, max_sel=1024,
+                  device="cpu", sink_range=(-2.0, 2.0)):
+    d = prefill_inputs(B, n, hq, hkv, d_qk, d_v, dtype, seed, device, sink_range)
+    idx, cnt = sparse_selection(B, n, hkv, recent, max_sel, seed, device)
+    d.update(sel_idx=idx, sel_count=cnt)
+    return d

@@ -1,0 +1,481 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each pin checks the oracle against something other than itself: library
+routines (torch SDPA in float64, scipy), closed forms, a scalar brute force
+with a different RoPE formulation, and invariants the pages state.  The
+mutant tests plant plausible mistakes in a copy of the oracle and require
+that at least one pin catches each of them.
+
+Pages: "MiMo-V2-Flash: Hybrid Sliding Window Attention Architecture"
+(rslog.cc), "MiMo-V2.6-Flash hybrid SWA" (pwwt.cn), "MiMo-V3 HySparse2"
+(aideepthink.cn), "MiMo v2.5 inference optimisation" (youngju.dev).
+"""
+
+import inspect
+import json
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from scipy.special import expit, logsumexp
+
+import oracle.attention as OA
+import synthetic
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLD = json.load(open(os.path.join(HERE, "golden", "page_constants.json")))
+NEG_INF = float("-inf")
+
+
+def _inputs(B, n, hq, hkv, d=192, dv=128, seed=0, sink=(-2.0, 2.0)):
+    x = synthetic.prefill_inputs(B, n, hq, hkv, d, dv, "f32", seed, sink_range=sink)
+    q, k, v = (x[t].double().numpy() for t in "qkv")
+    s = None if x["sink"] is None else x["sink"].double().numpy()
+    return q, k, v, s
+
+
+# ---------------------------------------------------------------------------
+# Independent references
+# ---------------------------------------------------------------------------
+
+def _sdpa(q, k, v, allowed, sink, scale):
+    """torch SDPA (float64) with a boolean key mask and the sink as an extra key.
+
+    The sink becomes one appended key with zero vector and zero value whose
+    additive mask is sink_h: its score is 0 + sink_h and it adds nothing to
+    the output, which is exactly the extra denominator term of the sink
+    softmax (rslog.cc section 4.2).  allowed: [B or 1, n_q, n_k] bool.
+    """
+    B, n, hq, d = q.shape
+    G = hq // k.shape[2]
+    Q = torch.from_numpy(q).permute(0, 2, 1, 3)
+    K = torch.from_numpy(np.repeat(k, G, axis=2)).permute(0, 2, 1, 3)
+    V = torch.from_numpy(np.repeat(v, G, axis=2)).permute(0, 2, 1, 3)
+    mask = torch.where(torch.from_numpy(allowed), 0.0, NEG_INF).double()[:, None]  # [B,1,nq,nk]
+    mask = mask.expand(B, hq, *mask.shape[2:])
+    if sink is not None:
+        K = torch.cat([K, torch.zeros(B, hq, 1, d, dtype=torch.float64)], dim=2)
+        V = torch.cat([V, torch.zeros(B, hq, 1, V.shape[-1], dtype=torch.float64)], dim=2)
+        col = torch.from_numpy(np.asarray(sink, dtype=np.float64))[None, :, None, None]
+        col = col.expand(B, hq, mask.shape[2], 1)
+        mask = torch.cat([mask, col], dim=3)
+    o = F.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=scale)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def _window_mask(n, W):
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    ok = j <= i
+    if W is not None:
+        ok &= j >= i - W + 1
+    return ok[None]
+
+
+def _brute_rope(x, p, theta, R):
+    """Real-arithmetic statement of the RoPE reading: pair (r, r+R/2)."""
+    out = list(x)
+    half = R // 2
+    for r in range(half):
+        ang = p * theta ** (-2.0 * r / R)
+        c, s = math.cos(ang), math.sin(ang)
+        out[r] = x[r] * c - x[r + half] * s
+        out[r + half] = x[r + half] * c + x[r] * s
+    return out
+
+
+def _brute_prefill(q, k, v, sink, W, theta, frac):
+    """Scalar loops with math.fsum: a third formulation of the definition."""
+    B, n, hq, d = q.shape
+    hkv = k.shape[2]
+    G = hq // hkv
+    R = 2 * int(math.floor(frac * d / 2))
+    out = np.zeros((B, n, hq, v.shape[-1]))
+    for b in range(B):
+        kr = [[_brute_rope(list(k[b, j, g]), j, theta, R) for g in range(hkv)] for j in range(n)]
+        for i in range(n):
+            keys = [j for j in range(i + 1) if W is None or j >= i - W + 1]
+            for h in range(hq):
+                g = h // G
+                qi = _brute_rope(list(q[b, i, h]), i, theta, R)
+                a = {j: math.fsum(qi[t] * kr[j][g][t] for t in range(d)) / math.sqrt(d) for j in keys}
+                sh = NEG_INF if sink is None else float(sink[h])
+                m = max(max(a.values()), sh)
+                terms = [math.exp(a[j] - m) for j in keys]
+                den = math.fsum(terms + ([math.exp(sh - m)] if sh != NEG_INF else []))
+                for c in range(v.shape[-1]):
+                    out[b, i, h, c] = math.fsum(terms[t] * v[b, j, g, c] for t, j in enumerate(keys)) / den
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Pins.  Each takes the oracle module so that mutants can be run through them.
+# ---------------------------------------------------------------------------
+
+def pin_p1_no_sink_is_masked_softmax(O):
+    """sink -> -inf gives the ordinary softmax over the window (rslog.cc 4.3)."""
+    q, k, v, _ = _inputs(1, 40, 4, 2, seed=11)
+    for W in (1, 5, 16):
+        got = O.swa_sink_prefill(q, k, v, None, window=W)
+        ref = _sdpa(q, k, v, _window_mask(40, W), None, 1 / math.sqrt(192))
+        assert np.abs(got - ref).max() < 1e-12, W
+
+
+def pin_p2_wide_window_is_causal(O):
+    """W >= n with no sink is full causal attention (rslog.cc section 5, GA row)."""
+    q, k, v, _ = _inputs(2, 24, 4, 1, seed=12)
+    Q = torch.from_numpy(q).permute(0, 2, 1, 3)
+    K = torch.from_numpy(np.repeat(k, 4, axis=2)).permute(0, 2, 1, 3)
+    V = torch.from_numpy(np.repeat(v, 4, axis=2)).permute(0, 2, 1, 3)
+    ref = F.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=1 / math.sqrt(192))
+    ref = ref.permute(0, 2, 1, 3).numpy()
+    for got in (O.swa_sink_prefill(q, k, v, None, window=24),
+                O.swa_sink_prefill(q, k, v, None, window=1000),
+                O.ga_prefill(q, k, v)):
+        assert np.abs(got - ref).max() < 1e-12
+
+
+def pin_p3_sink_as_extra_key(O):
+    """The sink term equals one extra zero-valued key scored sink_h (rslog.cc 4.2, 4.4)."""
+    q, k, v, s = _inputs(1, 36, 8, 2, seed=13)
+    for W in (1, 3, 16, 36):
+        got = O.swa_sink_prefill(q, k, v, s, window=W)
+        ref = _sdpa(q, k, v, _window_mask(36, W), s, 1 / math.sqrt(192))
+        assert np.abs(got - ref).max() < 1e-12, W
+
+
+def pin_p4_weights_sum(O):
+    """With V = 1 every output is the weight sum, exp(LSE)/(exp(sink)+exp(LSE)) < 1.
+
+    rslog.cc section 4.2 (weights sum below one) and section 6 table (sum is
+    exactly one without the sink).
+    """
+    q, k, v, s = _inputs(1, 30, 2, 1, seed=14)
+    ones = np.ones_like(v)
+    W = 7
+    got = O.swa_sink_prefill(q, k, ones, s, window=W)
+    got0 = O.swa_sink_prefill(q, k, ones, None, window=W)
+    a = np.einsum("nhd,mhd->hnm", q[0], np.repeat(k[0], 2, axis=1)) / math.sqrt(192)
+    for i in range(30):
+        lo = max(0, i - W + 1)
+        lse = logsumexp(a[:, i, lo:i + 1], axis=1)
+        expect = expit(lse - s)       # = 1 / (1 + exp(sink - LSE))
+        assert np.abs(got[0, i, :, :] - expect[:, None]).max() < 1e-13
+        assert (got[0, i] < 1.0).all()
+    assert np.abs(got0 - 1.0).max() < 1e-13
+
+
+def pin_p5_unit_window(O):
+    """W = 1: o_i = sigmoid(a_ii - sink) v_i, the logistic closed form."""
+    q, k, v, s = _inputs(1, 12, 2, 2, seed=15)
+    got = O.swa_sink_prefill(q, k, v, s, window=1)
+    a = np.einsum("nhd,nhd->nh", q[0], k[0]) / math.sqrt(192)
+    expect = expit(a - s[None, :])[:, :, None] * v[0]
+    assert np.abs(got[0] - expect).max() < 1e-13
+
+
+def pin_p6_zero_query(O):
+    """q = 0: all scores vanish, o_i = sum_J v_j / (exp(sink) + |J_i|)."""
+    _, k, v, s = _inputs(1, 20, 4, 2, seed=16)
+    q = np.zeros((1, 20, 4, 192))
+    for W in (4, 9):
+        got = O.swa_sink_prefill(q, k, v, s, window=W, rope_theta=1e4, rotary_fraction=0.334)
+        for i in range(20):
+            lo = max(0, i - W + 1)
+            cnt = i + 1 - lo
+            for h in range(4):
+                expect = v[0, lo:i + 1, h // 2].sum(axis=0) / (math.exp(s[h]) + cnt)
+                assert np.abs(got[0, i, h] - expect).max() < 1e-13
+
+
+def pin_p7_brute_force(O):
+    """Every W <= n, G in {1, 2}, sinks {-inf, -1, 0, 2}, with and without RoPE."""
+    rng = np.random.default_rng(17)
+    n, d, dv = 6, 8, 4
+    for G in (1, 2):
+        q = rng.standard_normal((1, n, 2 * G, d)) * 1.5
+        k = rng.standard_normal((1, n, 2, d)) * 1.5
+        v = rng.standard_normal((1, n, 2, dv))
+        for sv in (NEG_INF, -1.0, 0.0, 2.0):
+            sink = None if sv == NEG_INF else np.full(2 * G, sv) + np.arange(2 * G) * 0.25
+            for W in list(range(1, n + 1)) + [None]:
+                for frac, theta in ((0.0, 1.0e4), (0.5, 3.0)):
+                    got = (O.ga_prefill(q, k, v, rope_theta=theta, rotary_fraction=frac)
+                           if (W is None and sink is None) else
+                           O.swa_sink_prefill(q, k, v, sink, window=0 if W is None else W,
+                                              rope_theta=theta, rotary_fraction=frac))
+                    ref = _brute_prefill(q, k, v, sink, W, theta, frac)
+                    assert np.abs(got - ref).max() < 1e-12, (G, sv, W, frac)
+
+
+def pin_p8_rope(O):
+    """RoPE reading: closed form on basis vectors, relative-position property,
+    norm preservation, identity at fraction 0, R = 64 at 192 dims and 0.334."""
+    assert O.rotary_dims(GOLD["d_qk"]["value"], GOLD["partial_rotary_factor"]["value"]) == \
+        GOLD["rotated_dims_at_192"]["value"]
+    d, frac, theta = 192, 0.334, 1.0e4
+    R = 64
+    half = R // 2
+    pos = np.array([0, 1, 7, 1000, 262143])
+    for r in (0, 1, 13, half - 1):
+        e = np.zeros((len(pos), 1, d))
+        e[:, 0, r] = 1.0
+        out = O.rope(e, pos, theta, frac)
+        ang = pos * theta ** (-2.0 * r / R)
+        # the angle is pos * inv_freq; two pow() routines may differ by an ulp
+        tol = 1e-12 + pos * 4e-16
+        assert (np.abs(out[:, 0, r] - np.cos(ang)) < tol).all()
+        assert (np.abs(out[:, 0, r + half] - np.sin(ang)) < tol).all()
+        e2 = np.zeros((len(pos), 1, d))
+        e2[:, 0, r + half] = 1.0
+        out2 = O.rope(e2, pos, theta, frac)
+        assert (np.abs(out2[:, 0, r] + np.sin(ang)) < tol).all()
+        assert (np.abs(out2[:, 0, r + half] - np.cos(ang)) < tol).all()
+        mask = np.ones(d, bool)
+        mask[[r, r + half]] = False
+        assert np.abs(out[:, 0, mask]).max() == 0.0
+    rng = np.random.default_rng(18)
+    x = rng.standard_normal((5, 3, d))
+    y = rng.standard_normal((5, 3, d))
+    p = np.array([3, 10, 50, 99, 4000])
+    for delta in (1, 17, 100000):
+        s0 = np.einsum("nhd,nhd->nh", O.rope(x, p, theta, frac), O.rope(y, p[::-1], theta, frac))
+        s1 = np.einsum("nhd,nhd->nh", O.rope(x, p + delta, theta, frac),
+                       O.rope(y, p[::-1] + delta, theta, frac))
+        assert np.abs(s0 - s1).max() < 1e-9
+    xr = O.rope(x, p, theta, frac)
+    assert np.abs(np.linalg.norm(xr, axis=-1) - np.linalg.norm(x, axis=-1)).max() < 1e-12
+    assert np.array_equal(xr[..., R:], x[..., R:])
+    assert np.array_equal(O.rope(x, p, theta, 0.0), x)
+
+
+def pin_p9_gqa(O):
+    """Grouped heads equal multi-head attention with each kv head repeated G times."""
+    q, k, v, s = _inputs(1, 20, 8, 2, seed=19)
+    got = O.swa_sink_prefill(q, k, v, s, window=6, rope_theta=1e4, rotary_fraction=0.334)
+    ref = O.swa_sink_prefill(q, np.repeat(k, 4, axis=2), np.repeat(v, 4, axis=2), s, window=6,
+                             rope_theta=1e4, rotary_fraction=0.334)
+    assert np.abs(got - ref).max() < 1e-13
+    # and the grouping is contiguous: head h reads kv head h // G
+    got1 = O.swa_sink_prefill(q[:, :, :4], k[:, :, :1], v[:, :, :1], s[:4], window=6,
+                              rope_theta=1e4, rotary_fraction=0.334)
+    assert np.abs(got[:, :, :4] - got1).max() < 1e-13
+
+
+def pin_p10_decode_equals_prefill_row(O):
+    """Decode at p over a cache filled from a sequence equals prefill row p.
+
+    Ring cache: token t sits in slot t mod W (youngju.dev dual-pool cache);
+    contiguous cache: rows 0..p.  Keys in the cache carry RoPE already.
+    """
+    rng = np.random.default_rng(20)
+    W, hq, hkv, d, dv = 16, 4, 2, 192, 128
+    theta, frac = 1.0e4, 0.334
+    sink = rng.uniform(-2, 2, hq)
+    for L in (40, 9):                                   # 9 < W - 1: ring warm-up
+        q = rng.standard_normal((1, L, hq, d))
+        k = rng.standard_normal((1, L, hkv, d))
+        v = rng.standard_normal((1, L, hkv, dv))
+        p = L - 1
+        swa = O.swa_sink_prefill(q, k, v, sink, window=W, rope_theta=theta, rotary_fraction=frac)
+        ga = O.ga_prefill(q, k, v, rope_theta=theta, rotary_fraction=frac)
+        kr = O.rope(k[0], np.arange(L), theta, frac)
+        ring_k = rng.standard_normal((1, W, hkv, d)) * 50.0     # stale junk in unwritten slots
+        ring_v = rng.standard_normal((1, W, hkv, dv)) * 50.0
+        for t in range(max(0, p - W + 1), p + 1):
+            ring_k[0, t % W] = kr[t]
+            ring_v[0, t % W] = v[0, t]
+        got = O.swa_sink_decode_ring(q[:, p], ring_k, ring_v, np.array([p]), sink,
+                                     rope_theta=theta, rotary_fraction=frac)
+        assert np.abs(got[0] - swa[0, p]).max() < 1e-12
+        offs = np.array([0, L + 3])
+        kc = np.concatenate([kr, rng.standard_normal((3, hkv, d))])
+        vc = np.concatenate([v[0], rng.standard_normal((3, hkv, dv))])
+        got_ga = O.swa_sink_decode_contiguous(q[:, p], kc, vc, offs, np.array([p]), None, None,
+                                              rope_theta=theta, rotary_fraction=frac)
+        assert np.abs(got_ga[0] - ga[0, p]).max() < 1e-12
+        got_sw = O.swa_sink_decode_contiguous(q[:, p], kc, vc, offs, np.array([p]), sink, W,
+                                              rope_theta=theta, rotary_fraction=frac)
+        assert np.abs(got_sw[0] - swa[0, p]).max() < 1e-12
+        got_ld = O.swa_sink_decode_contiguous(q[:, p], None, None, offs, np.array([p]), None,
+                                              None, rope_theta=theta, rotary_fraction=frac,
+                                              kv_loader=lambda b: (kc, vc))
+        assert np.abs(got_ld - got_ga).max() == 0.0
+
+
+def pin_p11_sparse(O):
+    """Sparse attention reductions (aideepthink.cn section 4).
+
+    No selection: SWA with W = recent.  Complete selection: causal over
+    [0, i] without i - recent.  General lists: SDPA with the lists as a mask.
+    """
+    recent, n, hq, hkv = 8, 40, 4, 2
+    q, k, v, s = _inputs(1, n, hq, hkv, seed=21)
+    idx, cnt = synthetic.sparse_selection(1, n, hkv, recent, 1024, 21)
+    idx, cnt = idx.numpy(), cnt.numpy()
+    got = O.sparse_sink_attn(q, k, v, idx, cnt, s, recent=recent)
+    swa = O.swa_sink_prefill(q, k, v, s, window=recent)
+    assert np.abs(got[:, :recent + 1] - swa[:, :recent + 1]).max() < 1e-12
+    allowed = np.tril(np.ones((n, n), bool))
+    for i in range(recent, n):
+        allowed[i, i - recent] = False
+    ref = _sdpa(q, k, v, allowed[None], s, 1 / math.sqrt(192))
+    assert np.abs(got - ref).max() < 1e-12
+    # sampled lists (max_sel < available)
+    idx2, cnt2 = synthetic.sparse_selection(1, n, hkv, recent, 5, 22)
+    idx2, cnt2 = idx2.numpy(), cnt2.numpy()
+    got2 = O.sparse_sink_attn(q, k, v, idx2, cnt2, s, recent=recent)
+    for g in range(hkv):
+        al = np.zeros((n, n), bool)
+        for i in range(n):
+            al[i, max(0, i - recent + 1):i + 1] = True
+            al[i, idx2[0, i, g, :cnt2[0, i, g]]] = True
+        ref2 = _sdpa(q[:, :, g * 2:(g + 1) * 2], k[:, :, g:g + 1], v[:, :, g:g + 1], al[None],
+                     s[g * 2:(g + 1) * 2], 1 / math.sqrt(192))
+        assert np.abs(got2[:, :, g * 2:(g + 1) * 2] - ref2).max() < 1e-12
+
+
+def pin_p12_large_sink_is_stable(O):
+    """The max includes the sink (rslog.cc 4.4): huge sinks give finite, tiny outputs."""
+    q, k, v, _ = _inputs(1, 10, 2, 1, seed=23)
+    s = np.array([800.0, -800.0])
+    got = O.swa_sink_prefill(q, k, v, s, window=4)
+    assert np.isfinite(got).all()
+    assert np.abs(got[0, :, 0]).max() < 1e-300
+    ref = O.swa_sink_prefill(q, k, v, None, window=4)
+    assert np.abs(got[0, :, 1] - ref[0, :, 1]).max() < 1e-12
+
+
+PINS = [pin_p1_no_sink_is_masked_softmax, pin_p2_wide_window_is_causal, pin_p3_sink_as_extra_key,
+        pin_p4_weights_sum, pin_p5_unit_window, pin_p6_zero_query, pin_p7_brute_force,
+        pin_p8_rope, pin_p9_gqa, pin_p10_decode_equals_prefill_row, pin_p11_sparse,
+        pin_p12_large_sink_is_stable]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
+def test_pin_holds(pin):
+    pin(OA)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each must be caught by at least one pin.
+# ---------------------------------------------------------------------------
+
+MUTANTS = {
+    "drop_sink_from_denominator": ("den = math.exp(sink[g] - m[g]) if sink[g] != NEG_INF else 0.0",
+                                   "den = 0.0"),
+    "window_one_too_wide": ("max(0, i - window + 1)", "max(0, i - window)"),
+    "window_one_too_narrow": ("max(0, i - window + 1)", "max(0, i - window + 2)"),
+    "rope_wrong_sign": ("np.exp(1j * angle)", "np.exp(-1j * angle)"),
+    "rope_freq_over_d": ("-(2.0 * r) / rot)", "-(2.0 * r) / d)"),
+    "rope_adjacent_pairs": ("z = (x[..., :half] + 1j * x[..., half:rot]) * turn",
+                            "z = (x[..., 0:rot:2] + 1j * x[..., 1:rot:2]) * turn"),
+    "gqa_interleaved_heads": ("hs = slice(g * G, (g + 1) * G)", "hs = slice(g, None, hkv)"),
+    "scale_by_dv": ("scale = 1.0 / math.sqrt(d)\n    s_all = _sink_vector(sink, hq)\n    qr",
+                    "scale = 1.0 / math.sqrt(v.shape[-1])\n    s_all = _sink_vector(sink, hq)\n    qr"),
+    "values_misaligned": ("out[g] = (e @ vj) / den", "out[g] = (e @ vj[::-1]) / den"),
+    "max_ignores_sink": ("m = np.maximum(a.max(axis=1), sink)", "m = a.max(axis=1)"),
+    "ring_slot_reversed": ("return p - np.mod(p - s, window)", "return p - np.mod(s - p, window)"),
+    "sparse_drops_selection": ("return np.union1d(sel, rec)", "return rec"),
+    "sparse_recent_too_wide": ("lo = max(0, i - recent + 1)", "lo = max(0, i - recent)"),
+    "sink_in_numerator": ("out[g] = (e @ vj) / den", "out[g] = (e @ vj + math.exp(min(sink[g] - m[g], 0.0))) / den"),
+    "decode_query_not_rotated": ("qb = rope(q[b][None], np.array([p]), rope_theta, rotary_fraction)[0]\n        slots",
+                                 "qb = np.asarray(q[b], dtype=np.float64)\n        slots"),
+}
+
+
+def _mutant(name):
+    old, new = MUTANTS[name]
+    src = inspect.getsource(OA)
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mod = types.ModuleType("oracle_mutant_" + name)
+    exec(compile(src.replace(old, new), "<mutant " + name + ">", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    mod = _mutant(name)
+    caught = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod)
+        except Exception as exc:  # noqa: BLE001 - any failure counts as caught
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"no pin catches the planted mistake {name}"
+
+
+# ---------------------------------------------------------------------------
+# Input generator checks and the page constants
+# ---------------------------------------------------------------------------
+
+def test_sparse_selection_lists_are_valid():
+    n, hkv, recent, max_sel = 300, 3, 16, 40
+    idx, cnt = synthetic.sparse_selection(2, n, hkv, recent, max_sel, 31)
+    idx, cnt = idx.numpy(), cnt.numpy()
+    for b in range(2):
+        for i in range(n):
+            avail = max(0, i - recent)
+            for g in range(hkv):
+                c = cnt[b, i, g]
+                assert c == min(max_sel, avail)
+                row = idx[b, i, g]
+                sel = row[:c]
+                assert (row[c:] == -1).all()
+                if c:
+                    assert (np.diff(sel) > 0).all()
+                    assert sel[0] >= 0 and sel[-1] < avail
+                if avail <= max_sel:
+                    assert np.array_equal(sel, np.arange(avail))
+    # different (i, g) rows draw different sets
+    assert not np.array_equal(idx[0, n - 1, 0], idx[0, n - 1, 1])
+
+
+def test_sparse_selection_is_uniform():
+    # Floyd's sampling: every candidate equally likely (chi-square style bound).
+    n, recent, max_sel = 64, 4, 10
+    idx, cnt = synthetic.sparse_selection(1, n, 400, recent, max_sel, 32)
+    i = n - 1
+    vals = idx[0, i, :, :max_sel].numpy().ravel()
+    hist = np.bincount(vals, minlength=i - recent)
+    expect = 400 * max_sel / (i - recent)
+    assert hist.min() > 0.4 * expect and hist.max() < 1.8 * expect
+
+
+def test_workloads_use_page_constants():
+    wl = synthetic.WORKLOADS
+    W = GOLD["window"]["value"]
+    assert wl["swa_prefill_n32768"]["window"] == W
+    assert (wl["swa_prefill_n32768"]["hq"], wl["swa_prefill_n32768"]["hkv"]) == \
+        tuple(GOLD["swa_heads_q_kv"]["value"])
+    assert (wl["ga_prefill_n32768"]["hq"], wl["ga_prefill_n32768"]["hkv"]) == \
+        tuple(GOLD["ga_heads_q_kv"]["value"])
+    for name in ("swa_prefill_n32768", "ga_prefill_n32768", "sparse_prefill_n65536"):
+        assert wl[name]["d_qk"] == GOLD["d_qk"]["value"]
+        assert wl[name]["d_v"] == GOLD["d_v"]["value"]
+    assert wl["swa_prefill_n32768"]["rope_theta"] == GOLD["swa_rope_theta"]["value"]
+    assert wl["ga_prefill_n32768"]["rope_theta"] == GOLD["ga_rope_theta"]["value"]
+    assert wl["swa_prefill_n32768"]["rotary_fraction"] == GOLD["partial_rotary_factor"]["value"]
+    assert wl["sparse_prefill_n65536"]["recent"] == GOLD["sparse_recent"]["value"]
+    assert wl["sparse_prefill_n65536"]["max_sel"] == GOLD["sparse_selected"]["value"]
+    dec = wl["hybrid_decode_b64"]
+    assert dec["swa"]["window"] == W
+    assert (dec["swa"]["hq"], dec["swa"]["hkv"]) == tuple(GOLD["swa_heads_q_kv"]["value"])
+    assert (dec["ga"]["hq"], dec["ga"]["hkv"]) == tuple(GOLD["ga_heads_q_kv"]["value"])
+
+
+def test_generator_is_seeded_and_rne():
+    a = synthetic.normal((1000,), 5, "cpu", "bf16")
+    b = synthetic.normal((1000,), 5, "cpu", "bf16")
+    assert torch.equal(a, b)
+    f = synthetic.normal((1000,), 5, "cpu", "f32")
+    # bf16 cast is round-to-nearest-even of the same float32 draw
+    bits = f.view(torch.int32).to(torch.int64)
+    lsb = (bits >> 16) & 1
+    rne = ((bits + 0x7FFF + lsb) >> 16) & 0xFFFF
+    assert torch.equal(rne.to(torch.int32), a.view(torch.int16).to(torch.int32) & 0xFFFF)
