@@ -1,0 +1,283 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu]
+
+A step is one sliding-window+sink prefill of the SWA-layer workload
+(n = 32768 tokens, 64 query / 8 kv heads, d_qk 192, d_v 128, W = 128,
+partial RoPE base 1e4 on 64 dims, per-head sinks): the rows A1-A7 of the
+hot path in one library call.  `value` is useful TFLOP/s: 640 FLOP per
+unmasked (query head, key) pair, 171.47 GFLOP per step.
+
+Printed as one JSON line, with
+  * roofline: the prefill kernel against HBM bandwidth (algorithmic bytes
+    Q + K + V + O per launch over its average event-timed duration);
+  * cpu_baseline: the fp64 oracle timed on a bounded row sample of the same
+    workload on the host cores;
+  * secondary: the siblings measured the same way (GA prefill TFLOP/s,
+    hybrid decode HBM GB/s for the ring and contiguous caches, sparse
+    prefill TFLOP/s).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import hybrid_sliding_window_amd as hswa  # noqa: E402
+import synthetic  # noqa: E402
+
+METRIC = "SWA+sink prefill TFLOP/s (W=128, 64q/8kv) + decode HBM GB/s, % of roofline"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+FLOP_PER_PAIR = 2 * (192 + 128)      # QK^T and PV per unmasked (query head, key) pair
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _ensure_built():
+    if not os.path.exists(hswa.lib_path()):
+        from hybrid_sliding_window_amd.build import build
+        build()
+    hswa.load()
+
+
+def window_pairs(n, window):
+    """Unmasked (query, key) pairs of a causal window per head."""
+    i = np.arange(n, dtype=np.int64)
+    return int(np.minimum(i + 1, window).sum()) if window > 0 else int(((i + 1)).sum())
+
+
+def timed(fn, steps, warmup):
+    """Warm up, then time `steps` calls with an event pair around each one on
+    the current stream (where the library enqueues its kernels)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in zip(starts, ends):
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]   # ms
+    return wall, per
+
+
+def _traffic(kernel_key, launches_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if any."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        return t.get(kernel_key)
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(x, wl, budget_s):
+    """The oracle, untuned, on a time-bounded sample of query rows."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    n, window = wl["n"], wl["window"]
+    k = x["k"].double().cpu().numpy()
+    v = x["v"].double().cpu().numpy()
+    sink = x["sink"].double().cpu().numpy()
+    rng = np.random.default_rng(7)
+    order = rng.permutation(n)
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    chunk = 64
+    while True:
+        rows = np.sort(order[done:done + chunk])
+        qr = x["q"][:, torch.from_numpy(rows).to(x["q"].device)].double().cpu().numpy()
+        oracle.prefill_rows(None, k, v, rows, sink=sink, window=window,
+                            rope_theta=wl["rope_theta"], rotary_fraction=wl["rotary_fraction"],
+                            q_rows=qr)
+        flops += float(np.minimum(rows + 1, window).sum()) * wl["hq"] * FLOP_PER_PAIR
+        done += len(rows)
+        if time.perf_counter() - t0 >= budget_s or done >= n:
+            break
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} random query rows of {n} (all 64 heads), fp64 NumPy, {el:.1f} s; "
+                      f"useful FLOPs of the sampled rows over wall time"}
+
+
+def secondary(steps, warmup):
+    out = {}
+    dev = "cuda"
+    # GA prefill, n = 32768, 64 q / 4 kv heads, full causal
+    wl = synthetic.WORKLOADS["ga_prefill_n32768"]
+    x = synthetic.prefill_inputs(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, "bf16", wl["seed"], dev,
+                                 None)
+    ws = torch.empty(hswa.prefill_workspace_size(wl["n"], 192, wl["rotary_fraction"]),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty(1, wl["n"], wl["hq"], 128, dtype=torch.bfloat16, device=dev)
+    fn = lambda: hswa.ga_prefill(x["q"], x["k"], x["v"], rope_theta=wl["rope_theta"],  # noqa: E731
+                                 rotary_fraction=wl["rotary_fraction"], out=o, workspace=ws)
+    _, per = timed(fn, max(3, steps // 4), 1)
+    flops = window_pairs(wl["n"], 0) * wl["hq"] * FLOP_PER_PAIR
+    t = float(np.mean(per)) / 1e3
+    out["ga_prefill_n32768"] = {"tflops": flops / t / 1e12, "ms": t * 1e3,
+                                "frac_of_bf16_peak": flops / t / 1e12 / BF16_PEAK_TFLOPS}
+    _log(f"GA prefill {out['ga_prefill_n32768']}")
+    del x, o, ws
+    torch.cuda.empty_cache()
+
+    # Hybrid decode: 64 sequences at p ~ U[131072, 262143]
+    wl = synthetic.WORKLOADS["hybrid_decode_b64"]
+    pos = synthetic.decode_positions(wl["B"], *wl["pos_range"], wl["seed"])
+    maxp = wl["pos_range"][1]
+    sw, ga = wl["swa"], wl["ga"]
+    # ring: rotate over 8 buffer sets (> 256 MB) so the cache is not served from the MALL
+    sets = [synthetic.ring_decode_inputs(wl["B"], sw["hq"], sw["hkv"], sw["window"], 192, 128, "bf16",
+                                         wl["seed"] + 100 * r, pos, dev, sw["sink_range"])
+            for r in range(8)]
+    wsr = torch.empty(hswa.decode_workspace_size(hswa.KV_RING, wl["B"], sw["hq"], 128, sw["window"],
+                                                 maxp), dtype=torch.uint8, device=dev)
+    orr = torch.empty(wl["B"], sw["hq"], 128, dtype=torch.bfloat16, device=dev)
+    it = [0]
+
+    def ring_step():
+        d = sets[it[0] % len(sets)]
+        it[0] += 1
+        hswa.swa_sink_decode(d["q"], d["k"], d["v"], d["pos"], maxp, layout=hswa.KV_RING,
+                             sink=d["sink"], window=sw["window"], out=orr, workspace=wsr)
+    _, per = timed(ring_step, 40, 8)
+    ring_bytes = wl["B"] * sw["window"] * sw["hkv"] * (192 + 128) * 2 + wl["B"] * sw["hq"] * (192 + 128) * 2
+    t = float(np.mean(per)) / 1e3
+    out["decode_swa_ring"] = {"gbps": ring_bytes / t / 1e9, "us": t * 1e6, "bytes": ring_bytes,
+                              "frac_of_hbm_peak": ring_bytes / t / 1e9 / HBM_PEAK_GBPS,
+                              "note": "8 rotated buffer sets (353 MB) to defeat MALL residency"}
+    _log(f"decode ring {out['decode_swa_ring']}")
+    del sets
+    c = synthetic.contiguous_decode_inputs(wl["B"], ga["hq"], ga["hkv"], 192, 128, "bf16",
+                                           wl["seed"], pos, dev, None)
+    wsc = torch.empty(hswa.decode_workspace_size(hswa.KV_CONTIGUOUS, wl["B"], ga["hq"], 128, 0, maxp),
+                      dtype=torch.uint8, device=dev)
+    oc = torch.empty(wl["B"], ga["hq"], 128, dtype=torch.bfloat16, device=dev)
+    fn = lambda: hswa.swa_sink_decode(c["q"], c["k"], c["v"], c["pos"], maxp,  # noqa: E731
+                                      layout=hswa.KV_CONTIGUOUS, seq_offsets=c["seq_offsets"],
+                                      window=0, out=oc, workspace=wsc)
+    _, per = timed(fn, 10, 2)
+    keys = int((pos + 1).sum())
+    ga_bytes = keys * ga["hkv"] * (192 + 128) * 2 + wl["B"] * ga["hq"] * (192 + 128) * 2
+    t = float(np.mean(per)) / 1e3
+    out["decode_ga_contiguous"] = {"gbps": ga_bytes / t / 1e9, "ms": t * 1e3, "bytes": ga_bytes,
+                                   "frac_of_hbm_peak": ga_bytes / t / 1e9 / HBM_PEAK_GBPS}
+    _log(f"decode GA {out['decode_ga_contiguous']}")
+    del c, wsc
+    torch.cuda.empty_cache()
+
+    # Sparse prefill, n = 65536, 128 recent + <= 1024 selected
+    wl = synthetic.WORKLOADS["sparse_prefill_n65536"]
+    x = synthetic.sparse_inputs(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, "bf16", wl["seed"],
+                                wl["recent"], wl["max_sel"], dev, wl["sink_range"])
+    o = torch.empty(1, wl["n"], wl["hq"], 128, dtype=torch.bfloat16, device=dev)
+    fn = lambda: hswa.sparse_sink_attn(x["q"], x["k"], x["v"], x["sel_idx"], x["sel_count"],  # noqa: E731
+                                       x["sink"], recent_window=wl["recent"], out=o)
+    _, per = timed(fn, 5, 1)
+    i = np.arange(wl["n"])
+    pairs = int((np.minimum(1024, np.maximum(0, i - 128)) + np.minimum(i + 1, 128)).sum()) * wl["hkv"]
+    flops = pairs * (wl["hq"] // wl["hkv"]) * FLOP_PER_PAIR
+    gathered = pairs * (192 + 128) * 2
+    t = float(np.mean(per)) / 1e3
+    out["sparse_prefill_n65536"] = {"tflops": flops / t / 1e12, "ms": t * 1e3,
+                                    "gathered_kv_gbps": gathered / t / 1e9}
+    _log(f"sparse {out['sparse_prefill_n65536']}")
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path "
+              "(the sharding plan is design only).", file=sys.stderr)
+        sys.exit(2)
+    _ensure_built()
+    dev = "cuda"
+    wl = synthetic.WORKLOADS["swa_prefill_n32768"]
+    x = synthetic.prefill_inputs(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, "bf16", wl["seed"], dev,
+                                 wl["sink_range"])
+    o = torch.empty(1, wl["n"], wl["hq"], 128, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(hswa.prefill_workspace_size(wl["n"], 192, wl["rotary_fraction"]),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        hswa.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=wl["window"],
+                              rope_theta=wl["rope_theta"], rotary_fraction=wl["rotary_fraction"],
+                              out=o, workspace=ws)
+
+    torch.cuda.synchronize()
+    wall, per = timed(step, args.steps, args.warmup)
+    ms_step = wall * 1e3 / args.steps
+    flops = window_pairs(wl["n"], wl["window"]) * wl["hq"] * FLOP_PER_PAIR
+    value = flops * args.steps / wall / 1e12
+    n, hq, hkv = wl["n"], wl["hq"], wl["hkv"]
+    alg_bytes = n * (hq * 192 + hkv * 192 + hkv * 128 + hq * 128) * 2
+    kern_s = float(np.mean(per)) / 1e3
+    achieved = alg_bytes / kern_s / 1e9
+    _log(f"prefill: {ms_step:.3f} ms/step wall, {kern_s * 1e3:.3f} ms/launch (events), "
+         f"{value:.1f} TFLOP/s, {achieved:.0f} GB/s")
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "swa_prefill_n32768", "batch": 1, "seq_len": n, "hq": hq,
+                   "hkv": hkv, "d_qk": 192, "d_v": 128, "window": wl["window"],
+                   "rope_theta": wl["rope_theta"], "rotary_fraction": wl["rotary_fraction"],
+                   "sink": "U(-2,2) per head", "useful_gflop_per_step": flops / 1e9},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": _traffic("prefill_bf16_kernel:swa_prefill_n32768", alg_bytes),
+                     "kernel": "prefill_bf16_kernel",
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "launch_ms": kern_s * 1e3,
+                     "frac_of_bf16_mfma_peak": value / BF16_PEAK_TFLOPS},
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_seconds)
+        _log(f"cpu baseline {rec['cpu_baseline']}")
+    del x, o, ws
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        rec["secondary"] = secondary(args.steps, args.warmup)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

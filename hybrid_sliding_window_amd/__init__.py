@@ -1,0 +1,24 @@
+"""Sliding-window attention with a learnable sink on MI355X (gfx950).
+
+A thin Python binding over the C ABI of libhswa.so (include/hswa.h).  It
+only marshals arguments: torch supplies device memory and the current HIP
+stream, and every step of the computation runs in the library's kernels.
+There is no fallback: if the library is missing, load() raises.
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTED_SYMBOLS,
+    HswaError,
+    KV_CONTIGUOUS,
+    KV_RING,
+    decode_workspace_size,
+    ga_prefill,
+    lib_path,
+    load,
+    prefill_workspace_size,
+    sparse_sink_attn,
+    sparse_workspace_size,
+    swa_sink_decode,
+    swa_sink_prefill,
+    version,
+)

@@ -1,0 +1,206 @@
+"""ctypes binding of libhswa.so.  Argument marshalling only."""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libhswa.so")
+_lib = None
+
+HSWA_F32, HSWA_BF16 = 0, 1
+KV_RING, KV_CONTIGUOUS = 0, 1
+_STATUS = {0: "HSWA_OK", 1: "HSWA_ERR_INVALID_ARGUMENT", 2: "HSWA_ERR_UNSUPPORTED",
+           3: "HSWA_ERR_HIP"}
+
+_vp, _i, _ll, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_size_t
+
+# Every symbol include/hswa.h declares, with (restype, argtypes).
+_SIGNATURES = {
+    "hswa_prefill_workspace_size": (_sz, [_i, _i, _f]),
+    "swa_sink_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _f, _f,
+                              _ll, _i, _vp, _sz, _vp]),
+    "ga_prefill": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _f, _ll, _i, _vp, _sz,
+                        _vp]),
+    "hswa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i, _ll]),
+    "swa_sink_decode": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _ll,
+                             _f, _f, _f, _i, _vp, _sz, _vp]),
+    "hswa_sparse_workspace_size": (_sz, [_i, _i, _f]),
+    "sparse_sink_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                              _f, _f, _f, _ll, _i, _vp, _sz, _vp]),
+    "hswa_last_error": (ctypes.c_char_p, []),
+    "hswa_version": (ctypes.c_char_p, []),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+
+class HswaError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        self.status_name = _STATUS.get(status, str(status))
+        super().__init__(f"{self.status_name}: {message}")
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def load():
+    """Load libhswa.so (built by hybrid_sliding_window_amd.build); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m hybrid_sliding_window_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def version():
+    return load().hswa_version().decode()
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return HSWA_F32
+    if t.dtype == torch.bfloat16:
+        return HSWA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _check_same(ref, *ts):
+    for t in ts:
+        if t is None:
+            continue
+        if t.device != ref.device:
+            raise ValueError("all tensors must live on the same device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _raise(status):
+    if status != 0:
+        raise HswaError(status, load().hswa_last_error().decode())
+
+
+def _sink(sink, q):
+    if sink is None:
+        return None
+    if sink.dtype != torch.float32 or sink.device != q.device or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous float32 tensor on the query's device")
+    return sink
+
+
+def _workspace(nbytes, device):
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def prefill_workspace_size(seqlen, d_qk, rotary_fraction):
+    return load().hswa_prefill_workspace_size(seqlen, d_qk, rotary_fraction)
+
+
+def sparse_workspace_size(seqlen, d_qk, rotary_fraction):
+    return load().hswa_sparse_workspace_size(seqlen, d_qk, rotary_fraction)
+
+
+def decode_workspace_size(layout, batch, hq, d_v, window, max_pos):
+    return load().hswa_decode_workspace_size(layout, batch, hq, d_v, window, max_pos)
+
+
+def swa_sink_prefill(q, k, v, sink=None, window=128, scale=0.0, rope_theta=10000.0,
+                     rotary_fraction=0.0, pos_offset=0, out=None, workspace=None):
+    """q [B,n,Hq,d_qk], k [B,n,Hkv,d_qk], v [B,n,Hkv,d_v] -> o [B,n,Hq,d_v]."""
+    lib = load()
+    B, n, hq, dqk = q.shape
+    hkv, dv = k.shape[2], v.shape[3]
+    sink = _sink(sink, q)
+    o = out if out is not None else torch.empty((B, n, hq, dv), dtype=q.dtype, device=q.device)
+    _check_same(q, k, v, o)
+    need = lib.hswa_prefill_workspace_size(n, dqk, rotary_fraction)
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    st = lib.swa_sink_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(o), B, n, hq, hkv, dqk,
+                              dv, window, scale, rope_theta, rotary_fraction, pos_offset,
+                              _dtype_code(q), _ptr(ws), 0 if ws is None else ws.numel(), _stream(q))
+    _raise(st)
+    return o
+
+
+def ga_prefill(q, k, v, scale=0.0, rope_theta=1.0e7, rotary_fraction=0.0, pos_offset=0,
+               out=None, workspace=None):
+    """Full causal attention without a sink (GA layer)."""
+    lib = load()
+    B, n, hq, dqk = q.shape
+    hkv, dv = k.shape[2], v.shape[3]
+    o = out if out is not None else torch.empty((B, n, hq, dv), dtype=q.dtype, device=q.device)
+    _check_same(q, k, v, o)
+    need = lib.hswa_prefill_workspace_size(n, dqk, rotary_fraction)
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    st = lib.ga_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, n, hq, hkv, dqk, dv, scale,
+                        rope_theta, rotary_fraction, pos_offset, _dtype_code(q), _ptr(ws),
+                        0 if ws is None else ws.numel(), _stream(q))
+    _raise(st)
+    return o
+
+
+def swa_sink_decode(q, k_cache, v_cache, pos, max_pos, layout=KV_RING, seq_offsets=None,
+                    sink=None, window=128, scale=0.0, rope_theta=10000.0, rotary_fraction=0.0,
+                    out=None, workspace=None):
+    """q [B,Hq,d_qk] against a ring [B,W,Hkv,d] or packed [rows,Hkv,d] cache -> o [B,Hq,d_v]."""
+    lib = load()
+    B, hq, dqk = q.shape
+    hkv, dv = k_cache.shape[-2], v_cache.shape[-1]
+    sink = _sink(sink, q)
+    if pos.dtype != torch.int64:
+        raise TypeError("pos must be int64")
+    if seq_offsets is not None and seq_offsets.dtype != torch.int64:
+        raise TypeError("seq_offsets must be int64")
+    o = out if out is not None else torch.empty((B, hq, dv), dtype=q.dtype, device=q.device)
+    _check_same(q, k_cache, v_cache, o, pos, seq_offsets)
+    need = lib.hswa_decode_workspace_size(layout, B, hq, dv, window, int(max_pos))
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    st = lib.swa_sink_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), layout, _ptr(seq_offsets),
+                             _ptr(pos), _ptr(sink), _ptr(o), B, hq, hkv, dqk, dv, window,
+                             int(max_pos), scale, rope_theta, rotary_fraction, _dtype_code(q),
+                             _ptr(ws), 0 if ws is None else ws.numel(), _stream(q))
+    _raise(st)
+    return o
+
+
+def sparse_sink_attn(q, k, v, sel_idx, sel_count, sink=None, recent_window=128, scale=0.0,
+                     rope_theta=10000.0, rotary_fraction=0.0, pos_offset=0, out=None,
+                     workspace=None):
+    """Recent window plus selected tokens per (query, kv head) -> o [B,n,Hq,d_v]."""
+    lib = load()
+    B, n, hq, dqk = q.shape
+    hkv, dv = k.shape[2], v.shape[3]
+    max_sel = sel_idx.shape[-1]
+    sink = _sink(sink, q)
+    if sel_idx.dtype != torch.int32 or sel_count.dtype != torch.int32:
+        raise TypeError("sel_idx and sel_count must be int32")
+    o = out if out is not None else torch.empty((B, n, hq, dv), dtype=q.dtype, device=q.device)
+    _check_same(q, k, v, o, sel_idx, sel_count)
+    need = lib.hswa_sparse_workspace_size(n, dqk, rotary_fraction)
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    st = lib.sparse_sink_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(sel_idx), _ptr(sel_count), max_sel,
+                              recent_window, _ptr(sink), _ptr(o), B, n, hq, hkv, dqk, dv, scale,
+                              rope_theta, rotary_fraction, pos_offset, _dtype_code(q), _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(q))
+    _raise(st)
+    return o

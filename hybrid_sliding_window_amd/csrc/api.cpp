@@ -1,0 +1,287 @@
+// C ABI of the library: argument validation, workspace layout and dispatch
+// to the kernels.  Every check happens before anything is enqueued, so a
+// non-OK status leaves the outputs and the stream untouched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "../../include/hswa.h"
+#include "launch.h"
+
+using hswa::AttnArgs;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hswa_status_t fail(hswa_status_t st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+hswa_status_t ok() {
+  g_last_error.clear();
+  return HSWA_OK;
+}
+
+hswa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(HSWA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Half the number of rotated dims: R/2 = floor(fraction * d / 2).
+int rotary_half(int d_qk, float rotary_fraction) {
+  return (int)std::floor((double)rotary_fraction * (double)d_qk / 2.0);
+}
+
+const int kMaxGenericDim = 256;
+
+// Checks common to every entry point.  Returns HSWA_OK or the failing status.
+hswa_status_t check_common(int batch, int hq, int hkv, int d_qk, int d_v, float scale,
+                           float rope_theta, float rotary_fraction, hswa_dtype_t dtype) {
+  if (batch < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "batch must be >= 0");
+  if (hq <= 0 || hkv <= 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "head counts must be > 0");
+  if (hq % hkv != 0)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "hq must be a multiple of hkv (GQA groups)");
+  if (d_qk <= 0 || d_v <= 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "head dims must be > 0");
+  if (!(scale >= 0.f) || std::isinf(scale))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "scale must be finite and >= 0 (0 = 1/sqrt(d_qk))");
+  if (!(rotary_fraction >= 0.f && rotary_fraction <= 1.f))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "rotary_fraction must lie in [0, 1]");
+  if (rotary_half(d_qk, rotary_fraction) > 0 && !(rope_theta > 0.f && std::isfinite(rope_theta)))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "rope_theta must be finite and > 0 when RoPE is on");
+  if (dtype != HSWA_F32 && dtype != HSWA_BF16)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "dtype must be HSWA_F32 or HSWA_BF16");
+  return HSWA_OK;
+}
+
+AttnArgs base_args(int batch, int n, int hq, int hkv, int d_qk, int d_v, float scale,
+                   float rope_theta, float rotary_fraction) {
+  AttnArgs a{};
+  a.B = batch;
+  a.n = n;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d_qk = d_qk;
+  a.d_v = d_v;
+  a.half = rotary_half(d_qk, rotary_fraction);
+  a.scale = (scale > 0.f) ? scale : (float)(1.0 / std::sqrt((double)d_qk));
+  a.rope_theta = (double)rope_theta;
+  return a;
+}
+
+bool generic_fits(int d_qk, int d_v) { return d_qk <= kMaxGenericDim && d_v <= kMaxGenericDim; }
+
+size_t table_bytes(int seqlen, int d_qk, float rotary_fraction) {
+  if (seqlen <= 0 || d_qk <= 0 || !(rotary_fraction >= 0.f && rotary_fraction <= 1.f)) return 0;
+  const int half = rotary_half(d_qk, rotary_fraction);
+  return round256((size_t)seqlen * (size_t)half * sizeof(float2));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hswa_last_error(void) { return g_last_error.c_str(); }
+
+const char* hswa_version(void) { return "hswa 0.1.0 (gfx950)"; }
+
+size_t hswa_prefill_workspace_size(int seqlen, int d_qk, float rotary_fraction) {
+  return table_bytes(seqlen, d_qk, rotary_fraction);
+}
+
+size_t hswa_sparse_workspace_size(int seqlen, int d_qk, float rotary_fraction) {
+  return table_bytes(seqlen, d_qk, rotary_fraction);
+}
+
+hswa_status_t swa_sink_prefill(const void* q, const void* k, const void* v, const float* sink,
+                               void* o, int batch, int seqlen, int hq, int hkv, int d_qk,
+                               int d_v, int window, float scale, float rope_theta,
+                               float rotary_fraction, long long pos_offset, hswa_dtype_t dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  hswa_status_t st =
+      check_common(batch, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction, dtype);
+  if (st != HSWA_OK) return st;
+  if (seqlen < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "seqlen must be >= 0");
+  if (window < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "window must be >= 0 (0 = full causal)");
+  if (batch == 0 || seqlen == 0) return ok();
+  if (!q || !k || !v || !o) return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-null");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v and o must be 16-byte aligned");
+  if ((long long)batch * seqlen * hq * (long long)(d_qk > d_v ? d_qk : d_v) > (1LL << 56))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "tensor too large");
+  const size_t need = table_bytes(seqlen, d_qk, rotary_fraction);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_prefill_workspace_size()");
+    if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  }
+
+  AttnArgs a = base_args(batch, seqlen, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.sink = sink;
+  a.window = (window >= seqlen) ? 0 : window;
+  a.pos_offset = pos_offset;
+  a.rope = static_cast<const float2*>(workspace);
+
+  const bool use_mfma = (dtype == HSWA_BF16) && hswa::prefill_bf16_supported(a);
+  if (!use_mfma && !generic_fits(d_qk, d_v))
+    return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.half > 0) {
+    hipError_t e = hswa::launch_rope_table(static_cast<float2*>(workspace), pos_offset, seqlen,
+                                           a.half, a.rope_theta, s);
+    if (e != hipSuccess) return hip_status(e, "rope table launch");
+  }
+  hipError_t e = use_mfma ? hswa::launch_prefill_bf16(a, s)
+                          : hswa::launch_generic(a, hswa::MODE_PREFILL, dtype == HSWA_BF16, s);
+  return hip_status(e, "prefill launch");
+}
+
+hswa_status_t ga_prefill(const void* q, const void* k, const void* v, void* o, int batch,
+                         int seqlen, int hq, int hkv, int d_qk, int d_v, float scale,
+                         float rope_theta, float rotary_fraction, long long pos_offset,
+                         hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return swa_sink_prefill(q, k, v, nullptr, o, batch, seqlen, hq, hkv, d_qk, d_v, 0, scale,
+                          rope_theta, rotary_fraction, pos_offset, dtype, workspace,
+                          workspace_bytes, stream);
+}
+
+size_t hswa_decode_workspace_size(hswa_kv_layout_t layout, int batch, int hq, int d_v, int window,
+                                  long long max_pos) {
+  if (batch <= 0 || hq <= 0 || d_v <= 0 || max_pos < 0) return 0;
+  if (layout != HSWA_KV_RING && layout != HSWA_KV_CONTIGUOUS) return 0;
+  if (layout == HSWA_KV_RING && window <= 0) return 0;
+  int split_keys = 0, nsplit = 0;
+  hswa::decode_split_plan(layout == HSWA_KV_RING ? 0 : 1, window, max_pos, &split_keys, &nsplit);
+  const size_t per = (size_t)batch * hq * (size_t)nsplit;
+  return round256(per * (size_t)d_v * sizeof(float)) + round256(per * 2 * sizeof(float));
+}
+
+hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_cache,
+                              hswa_kv_layout_t layout, const long long* seq_offsets,
+                              const long long* pos, const float* sink, void* o, int batch,
+                              int hq, int hkv, int d_qk, int d_v, int window, long long max_pos,
+                              float scale, float rope_theta, float rotary_fraction,
+                              hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  hswa_status_t st =
+      check_common(batch, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction, dtype);
+  if (st != HSWA_OK) return st;
+  if (layout != HSWA_KV_RING && layout != HSWA_KV_CONTIGUOUS)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "layout must be HSWA_KV_RING or HSWA_KV_CONTIGUOUS");
+  if (window < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "window must be >= 0");
+  if (layout == HSWA_KV_RING && window == 0)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "a ring cache needs window > 0 (its slot count)");
+  if (layout == HSWA_KV_RING && seq_offsets)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "seq_offsets must be NULL for a ring cache");
+  if (layout == HSWA_KV_CONTIGUOUS && !seq_offsets)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "seq_offsets is required for a contiguous cache");
+  if (max_pos < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "max_pos must be >= 0");
+  if (batch == 0) return ok();
+  if (!q || !k_cache || !v_cache || !o || !pos)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, caches, pos and o must be non-null");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, caches and o must be 16-byte aligned");
+  if (batch > 65535) return fail(HSWA_ERR_UNSUPPORTED, "batch above 65535");
+
+  AttnArgs a = base_args(batch, 0, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction);
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.o = o;
+  a.sink = sink;
+  a.seq_offsets = seq_offsets;
+  a.pos = pos;
+  a.window = window;
+  a.max_pos = max_pos;
+  const int lay = (layout == HSWA_KV_RING) ? 0 : 1;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == HSWA_BF16 && hswa::decode_bf16_supported(a)) {
+    const size_t need = hswa_decode_workspace_size(layout, batch, hq, d_v, window, max_pos);
+    if (!workspace || workspace_bytes < need)
+      return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_decode_workspace_size()");
+    if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    hswa::decode_split_plan(lay, window, max_pos, &a.split_keys, &a.nsplit);
+    a.ws = static_cast<float*>(workspace);
+    // the (m, l) pairs follow the partial outputs, each region 256-byte aligned
+    const size_t per = (size_t)batch * hq * (size_t)a.nsplit;
+    const size_t obytes = round256(per * (size_t)d_v * sizeof(float));
+    if (obytes != per * (size_t)d_v * sizeof(float)) {
+      // keep the kernel's simple indexing: partial outputs fill their region exactly
+      // (d_v = 128 floats per entry makes every region a multiple of 512 bytes)
+      return fail(HSWA_ERR_UNSUPPORTED, "decode partial layout needs d_v * 4 to be a multiple of 256");
+    }
+    return hip_status(hswa::launch_decode_bf16(a, lay, s), "decode launch");
+  }
+  if (!generic_fits(d_qk, d_v)) return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
+  return hip_status(hswa::launch_generic(a, lay == 0 ? hswa::MODE_DECODE_RING
+                                                     : hswa::MODE_DECODE_CONTIG,
+                                         dtype == HSWA_BF16, s),
+                    "decode launch");
+}
+
+hswa_status_t sparse_sink_attn(const void* q, const void* k, const void* v, const int* sel_idx,
+                               const int* sel_count, int max_sel, int recent_window,
+                               const float* sink, void* o, int batch, int seqlen, int hq,
+                               int hkv, int d_qk, int d_v, float scale, float rope_theta,
+                               float rotary_fraction, long long pos_offset, hswa_dtype_t dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  hswa_status_t st =
+      check_common(batch, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction, dtype);
+  if (st != HSWA_OK) return st;
+  if (seqlen < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "seqlen must be >= 0");
+  if (max_sel < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "max_sel must be >= 0");
+  if (recent_window < 1) return fail(HSWA_ERR_INVALID_ARGUMENT, "recent_window must be >= 1");
+  if (batch == 0 || seqlen == 0) return ok();
+  if (!q || !k || !v || !o || !sel_count || (max_sel > 0 && !sel_idx))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v, o, sel_idx and sel_count must be non-null");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v and o must be 16-byte aligned");
+  const size_t need = table_bytes(seqlen, d_qk, rotary_fraction);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_sparse_workspace_size()");
+    if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  }
+
+  AttnArgs a = base_args(batch, seqlen, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.sink = sink;
+  a.sel_idx = sel_idx;
+  a.sel_count = sel_count;
+  a.max_sel = max_sel;
+  a.recent = recent_window;
+  a.pos_offset = pos_offset;
+  a.rope = static_cast<const float2*>(workspace);
+
+  const bool use_mfma = (dtype == HSWA_BF16) && hswa::sparse_bf16_supported(a);
+  if (!use_mfma && !generic_fits(d_qk, d_v))
+    return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.half > 0) {
+    hipError_t e = hswa::launch_rope_table(static_cast<float2*>(workspace), pos_offset, seqlen,
+                                           a.half, a.rope_theta, s);
+    if (e != hipSuccess) return hip_status(e, "rope table launch");
+  }
+  hipError_t e = use_mfma ? hswa::launch_sparse_bf16(a, s)
+                          : hswa::launch_generic(a, hswa::MODE_SPARSE, dtype == HSWA_BF16, s);
+  return hip_status(e, "sparse launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+// Device helpers shared by the gfx950 kernels: bf16 packing, 16-byte
+// loads and stores, MFMA operand types, wavefront reductions and the
+// workgroup-to-XCD remapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hswa {
+
+typedef uint16_t bf16_t;                                     // raw bfloat16 bits
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));   // MFMA operand
+typedef float f32x4 __attribute__((ext_vector_type(4)));     // 16x16 MFMA accumulator
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+// Status codes mirrored from hswa.h for the internal launchers.
+enum { ST_OK = 0, ST_INVALID = 1, ST_UNSUPPORTED = 2, ST_HIP = 3 };
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Low / high bfloat16 of a packed dword, widened exactly to fp32.
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 values rounded to nearest-even bfloat16 and packed (lo, hi).
+// On gfx950 this is the hardware v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t p;
+  p[0] = (__bf16)lo;
+  p[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+__device__ __forceinline__ void st8(void* p, uint2 v) { *reinterpret_cast<uint2*>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Element e (0..7) of eight packed bfloat16 values, widened to fp32.
+__device__ __forceinline__ float elem_bf16(const uint4& v, int e) {
+  uint32_t w = (e < 2) ? v.x : (e < 4) ? v.y : (e < 6) ? v.z : v.w;
+  return (e & 1) ? hi_bf16(w) : lo_bf16(w);
+}
+
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+  f[0] = lo_bf16(v.x); f[1] = hi_bf16(v.x);
+  f[2] = lo_bf16(v.y); f[3] = hi_bf16(v.y);
+  f[4] = lo_bf16(v.z); f[5] = hi_bf16(v.z);
+  f[6] = lo_bf16(v.w); f[7] = hi_bf16(v.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  uint4 r;
+  r.x = pack_bf16x2(f[0], f[1]);
+  r.y = pack_bf16x2(f[2], f[3]);
+  r.z = pack_bf16x2(f[4], f[5]);
+  r.w = pack_bf16x2(f[6], f[7]);
+  return r;
+}
+
+// D = A * B + C on the 16x16x32 bf16 matrix core.  With lane l = 16*g + c:
+// A holds row c, k-block g (8 values); B holds column c, k-block g; D holds
+// rows 4*g .. 4*g+3 of column c.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Max / sum across the four lanes l, l^16, l^32, l^48 (same column c).
+__device__ __forceinline__ float max_across_groups(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float sum_across_groups(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (id % 8).  This maps the
+// hardware id to a logical id such that each XCD receives one contiguous
+// range of logical ids, so neighbouring tiles share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+  const int q = nwg >> 3, rem = nwg & 7;
+  const int x = bid & 7, slot = bid >> 3;
+  return (x < rem) ? x * (q + 1) + slot : rem * (q + 1) + (x - rem) * q + slot;
+}
+
+// Heavy / light interleave for causal work: 0 -> nb-1, 1 -> 0, 2 -> nb-2, ...
+// Any contiguous run of indices then carries a balanced amount of work.
+__device__ __forceinline__ int zigzag(int k, int nb) {
+  return (k & 1) ? (k >> 1) : (nb - 1 - (k >> 1));
+}
+
+}  // namespace hswa

@@ -1,0 +1,210 @@
+// Generic sink attention: one wavefront per query row, any head dims
+// (d_qk, d_v <= 256), any GQA group, fp32 or bf16 storage, every key set.
+//
+// This is the fp32 path (exact to ~1e-6) and the path for shapes the
+// matrix-core kernels do not cover.  Per key it forms the score with a
+// wavefront reduction and updates a running (max, sum, output) triple; the
+// result equals the two-pass definition of "MiMo-V2-Flash: Hybrid Sliding
+// Window Attention Architecture" (rslog.cc) section 4.4 up to rounding:
+// m starts at the sink and the sink's exp(sink - m) starts the sum.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace hswa {
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static __device__ __forceinline__ float get(const float* p, long long i) { return p[i]; }
+  static __device__ __forceinline__ void put(float* p, long long i, float x) { p[i] = x; }
+};
+template <>
+struct Elem<bf16_t> {
+  static __device__ __forceinline__ float get(const bf16_t* p, long long i) {
+    return bf16_to_f32(p[i]);
+  }
+  static __device__ __forceinline__ void put(bf16_t* p, long long i, float x) {
+    p[i] = f32_to_bf16_bits(x);
+  }
+};
+
+constexpr int kGenMaxPerLane = 4;  // dims per lane: 4 * 64 = 256
+
+// Rotated value of dim d of a row: dim r < half pairs with r + half.
+template <typename T>
+__device__ __forceinline__ float rotated(const T* row, int d, int half, float c, float s) {
+  if (d < half) return Elem<T>::get(row, d) * c - Elem<T>::get(row, d + half) * s;
+  return Elem<T>::get(row, d) * c + Elem<T>::get(row, d - half) * s;
+}
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
+  const int lane = threadIdx.x;
+  const long long row = blockIdx.x;
+  const int h = (int)(row % a.hq);
+  const long long outer = row / a.hq;          // prefill/sparse: b*n + i; decode: b
+  const int G = a.hq / a.hkv;
+  const int g = h / G;
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  T* o = static_cast<T*>(a.o);
+  const int R = 2 * a.half;
+
+  long long b, i = 0;
+  const T* qrow;
+  if (MODE == MODE_PREFILL || MODE == MODE_SPARSE) {
+    b = outer / a.n;
+    i = outer % a.n;
+    qrow = q + ((b * a.n + i) * a.hq + h) * (long long)a.d_qk;
+  } else {
+    b = outer;
+    qrow = q + (b * a.hq + h) * (long long)a.d_qk;
+  }
+  T* orow = o + row * (long long)a.d_v;
+
+  // ---- key range of this row ------------------------------------------
+  long long p = 0, kbase = 0, lo = 0, hi = -1;   // keys lo..hi (rows kbase + j)
+  bool ok = true;
+  if (MODE == MODE_PREFILL) {
+    lo = (a.window > 0) ? (i - a.window + 1 > 0 ? i - a.window + 1 : 0) : 0;
+    hi = i;
+    kbase = b * a.n;
+  } else if (MODE == MODE_SPARSE) {
+    lo = (i - a.recent + 1 > 0) ? i - a.recent + 1 : 0;
+    hi = i;
+    kbase = b * a.n;
+  } else if (MODE == MODE_DECODE_RING) {
+    p = a.pos[b];
+    ok = (p >= 0) && (p <= a.max_pos);
+    lo = 0;
+    hi = (p < a.window - 1) ? p : a.window - 1;      // slots written so far
+    kbase = b * a.window;
+  } else {
+    p = a.pos[b];
+    const long long off = a.seq_offsets[b], len = a.seq_offsets[b + 1] - off;
+    ok = (p >= 0) && (p <= a.max_pos) && (p < len);
+    lo = (a.window > 0) ? (p - a.window + 1 > 0 ? p - a.window + 1 : 0) : 0;
+    hi = p;
+    kbase = off;
+  }
+  if (!ok) {
+    for (int d = lane; d < a.d_v; d += 64) Elem<T>::put(orow, d, __builtin_nanf(""));
+    return;
+  }
+
+  // ---- rotated query in registers ------------------------------------
+  float qd[kGenMaxPerLane];
+#pragma unroll
+  for (int u = 0; u < kGenMaxPerLane; ++u) {
+    const int d = lane + 64 * u;
+    qd[u] = 0.f;
+    if (d >= a.d_qk) continue;
+    if (d < R) {
+      const int r = (d < a.half) ? d : d - a.half;
+      float c, s;
+      if (MODE == MODE_PREFILL || MODE == MODE_SPARSE) {
+        const float2 cs = a.rope[i * a.half + r];
+        c = cs.x;
+        s = cs.y;
+      } else {
+        const double ang = (double)p * pow(a.rope_theta, -(double)r / (double)a.half);
+        double sd, cd;
+        sincos(ang, &sd, &cd);
+        c = (float)cd;
+        s = (float)sd;
+      }
+      qd[u] = rotated(qrow, d, a.half, c, s);
+    } else {
+      qd[u] = Elem<T>::get(qrow, d);
+    }
+  }
+
+  // ---- running softmax state, seeded with the sink --------------------
+  float m = a.sink ? a.sink[h] : kNegInf;
+  float l = (m > kNegInf) ? 1.f : 0.f;
+  float od[kGenMaxPerLane] = {0.f, 0.f, 0.f, 0.f};
+
+  auto visit = [&](long long j) {
+    const T* krow = k + ((kbase + j) * a.hkv + g) * (long long)a.d_qk;
+    const T* vrow = v + ((kbase + j) * a.hkv + g) * (long long)a.d_v;
+    const bool rot_k = (MODE == MODE_PREFILL || MODE == MODE_SPARSE) && R > 0;
+    float part = 0.f;
+#pragma unroll
+    for (int u = 0; u < kGenMaxPerLane; ++u) {
+      const int d = lane + 64 * u;
+      if (d >= a.d_qk) continue;
+      float kv;
+      if (rot_k && d < R) {
+        const float2 cs = a.rope[j * a.half + ((d < a.half) ? d : d - a.half)];
+        kv = rotated(krow, d, a.half, cs.x, cs.y);
+      } else {
+        kv = Elem<T>::get(krow, d);
+      }
+      part += qd[u] * kv;
+    }
+    const float sc = wave_sum(part) * a.scale;
+    const float mn = fmaxf(m, sc);
+    const float alpha = expf(m - mn);           // m = -inf gives 0
+    const float pj = expf(sc - mn);
+    l = l * alpha + pj;
+#pragma unroll
+    for (int u = 0; u < kGenMaxPerLane; ++u) {
+      const int d = lane + 64 * u;
+      if (d < a.d_v) od[u] = od[u] * alpha + pj * Elem<T>::get(vrow, d);
+    }
+    m = mn;
+  };
+
+  if (MODE == MODE_SPARSE) {
+    const long long li = (b * a.n + i) * a.hkv + g;
+    int cnt = a.sel_count[li];
+    cnt = cnt < 0 ? 0 : (cnt > a.max_sel ? a.max_sel : cnt);
+    const int* sel = a.sel_idx + li * a.max_sel;
+    for (int t = 0; t < cnt; ++t) {
+      const long long j = sel[t];
+      if (j >= 0 && j <= i - a.recent) visit(j);
+    }
+  }
+  for (long long j = lo; j <= hi; ++j) visit(j);
+
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+#pragma unroll
+  for (int u = 0; u < kGenMaxPerLane; ++u) {
+    const int d = lane + 64 * u;
+    if (d < a.d_v) Elem<T>::put(orow, d, od[u] * inv);
+  }
+}
+
+template <typename T>
+static hipError_t launch_t(const AttnArgs& a, int mode, hipStream_t stream) {
+  long long rows = (mode == MODE_PREFILL || mode == MODE_SPARSE)
+                       ? (long long)a.B * a.n * a.hq
+                       : (long long)a.B * a.hq;
+  if (rows == 0) return hipSuccess;
+  dim3 grid((unsigned)rows), block(64);
+  switch (mode) {
+    case MODE_PREFILL:
+      hipLaunchKernelGGL((generic_attn_kernel<T, MODE_PREFILL>), grid, block, 0, stream, a);
+      break;
+    case MODE_SPARSE:
+      hipLaunchKernelGGL((generic_attn_kernel<T, MODE_SPARSE>), grid, block, 0, stream, a);
+      break;
+    case MODE_DECODE_RING:
+      hipLaunchKernelGGL((generic_attn_kernel<T, MODE_DECODE_RING>), grid, block, 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL((generic_attn_kernel<T, MODE_DECODE_CONTIG>), grid, block, 0, stream, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_generic(const AttnArgs& a, int mode, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_t<bf16_t>(a, mode, stream) : launch_t<float>(a, mode, stream);
+}
+
+}  // namespace hswa

@@ -1,0 +1,52 @@
+// Internal launcher interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace hswa {
+
+// Which key set a query row reads.
+enum Mode { MODE_PREFILL = 0, MODE_SPARSE = 1, MODE_DECODE_RING = 2, MODE_DECODE_CONTIG = 3 };
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* sink;              // [hq] or null
+  void* o;
+  const int* sel_idx;             // sparse: [B, n, hkv, max_sel]
+  const int* sel_count;           // sparse: [B, n, hkv]
+  const long long* seq_offsets;   // decode contiguous: [B + 1]
+  const long long* pos;           // decode: [B]
+  const float2* rope;             // prefill / sparse: cos/sin table [n][half]
+  int B, n, hq, hkv, d_qk, d_v;
+  int window;                     // prefill: 0 = full causal; decode: ring size or window
+  int half;                       // R / 2 (0 = no RoPE)
+  int max_sel, recent;            // sparse
+  float scale;                    // factor on q.k (natural-log units)
+  double rope_theta;
+  long long pos_offset;           // RoPE position of token 0 (prefill / sparse)
+  long long max_pos;              // decode: host bound on pos[b]
+  float* ws;                      // decode: split partials
+  int split_keys, nsplit;         // decode: keys per split, splits per (b, kv head)
+};
+
+// cos/sin table: table[t][r] = (cos, sin)((pos0 + t) * theta^(-r/half)).
+hipError_t launch_rope_table(float2* table, long long pos0, int npos, int half, double theta,
+                             hipStream_t stream);
+
+// Any shape, any key set, fp32 or bf16 storage: one wavefront per query row.
+hipError_t launch_generic(const AttnArgs& a, int mode, bool bf16, hipStream_t stream);
+
+// bf16 matrix-core kernels for d_qk = 192, d_v = 128.
+bool prefill_bf16_supported(const AttnArgs& a);
+hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
+
+bool decode_bf16_supported(const AttnArgs& a);
+void decode_split_plan(int layout, int window, long long max_pos, int* split_keys, int* nsplit);
+hipError_t launch_decode_bf16(const AttnArgs& a, int layout, hipStream_t stream);
+
+bool sparse_bf16_supported(const AttnArgs& a);
+hipError_t launch_sparse_bf16(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace hswa

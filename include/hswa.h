@@ -1,0 +1,162 @@
+/*
+ * hswa.h - sliding-window attention with a learnable per-head sink, its
+ * full-causal sibling, single-token decode and token-level sparse attention,
+ * as a C ABI for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (all entry points) is the one written out in
+ * "MiMo-V2-Flash: Hybrid Sliding Window Attention Architecture" (rslog.cc):
+ * for query row i of query head h with key set J_i,
+ *     a_ij = (q~_i . k~_j) * scale                        (section 1.2 / 2.3)
+ *     m_i  = max(max_j a_ij, sink_h)                      (section 4.4)
+ *     s_ij = exp(a_ij - m_i) / (exp(sink_h - m_i) + sum_j' exp(a_ij' - m_i))
+ *     o_i  = sum_j s_ij v_j                               (section 4.4)
+ * where q~, k~ carry partial RoPE on the first R dims and V is not rotated.
+ * The sink has no value vector: it only enlarges the denominator.
+ *
+ * Conventions shared by every entry point
+ *  - Tensor pointers are DEVICE pointers owned by the caller, dense
+ *    (row-major, no padding) and 16-byte aligned.  The library never
+ *    allocates, frees or synchronises, and keeps no state between calls
+ *    except the thread-local text behind hswa_last_error().
+ *  - dtype selects the element type of q, k, v and o (HSWA_F32 or
+ *    HSWA_BF16).  Arithmetic accumulates in fp32.  sink is always fp32.
+ *  - sink: fp32 [hq] device pointer, one value per QUERY head, in the units
+ *    of the scaled scores a_ij; NULL means no sink (the -inf limit, i.e.
+ *    the ordinary softmax).  A -inf entry disables the sink for that head.
+ *    Entries must be finite or -inf.
+ *  - scale: the factor on q.k; pass 0 for the default 1/sqrt(d_qk).
+ *  - Partial RoPE: R = largest even integer <= rotary_fraction * d_qk.
+ *    Dim r (r < R/2) pairs with dim r + R/2 and turns by the angle
+ *    pos * rope_theta^(-2r/R); dims >= R are untouched.  rotary_fraction 0
+ *    disables RoPE.  ("MiMo-V2.6-Flash hybrid SWA" (pwwt.cn), section 5,
+ *    gives the fraction 0.334 and the bases 1e4 / 1e7; the pairing is a
+ *    reading, the pages do not fix it.)
+ *  - GQA: query head h reads kv head h / (hq / hkv); hq % hkv == 0.
+ *  - stream: a hipStream_t passed as void*; NULL is the null stream.  Every
+ *    call only enqueues work on it and returns.
+ *  - workspace: caller-owned device scratch of at least the size the
+ *    matching *_workspace_size() query returns (may be NULL when that size
+ *    is 0).  Its contents on entry do not matter; it must not be shared by
+ *    calls that may run at the same time.
+ *  - Errors: every argument is validated before anything is enqueued.  On
+ *    a non-OK status nothing has been enqueued and the outputs are
+ *    untouched; hswa_last_error() describes the problem.  HSWA_ERR_HIP means
+ *    the HIP runtime reported an error at launch.
+ */
+#ifndef HSWA_H
+#define HSWA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSWA_OK = 0,
+  HSWA_ERR_INVALID_ARGUMENT = 1,
+  HSWA_ERR_UNSUPPORTED = 2,
+  HSWA_ERR_HIP = 3
+} hswa_status_t;
+
+typedef enum { HSWA_F32 = 0, HSWA_BF16 = 1 } hswa_dtype_t;
+
+typedef enum { HSWA_KV_RING = 0, HSWA_KV_CONTIGUOUS = 1 } hswa_kv_layout_t;
+
+/* Bytes of workspace swa_sink_prefill / ga_prefill need: the cos/sin table
+ * of the seqlen positions (seqlen * R/2 * 8 bytes, 0 without RoPE). */
+size_t hswa_prefill_workspace_size(int seqlen, int d_qk, float rotary_fraction);
+
+/*
+ * Sliding-window prefill with a sink: the SWA layer of rslog.cc section 4.4.
+ *   q [batch, seqlen, hq, d_qk], k [batch, seqlen, hkv, d_qk],
+ *   v [batch, seqlen, hkv, d_v]  ->  o [batch, seqlen, hq, d_v].
+ * Query token i (0-based) attends to keys max(0, i - window + 1) .. i, the
+ * causal window of section 2.1 (W tokens including itself).  window <= 0
+ * means the full causal prefix.  Token i has RoPE position pos_offset + i.
+ */
+hswa_status_t swa_sink_prefill(const void* q, const void* k, const void* v, const float* sink,
+                               void* o, int batch, int seqlen, int hq, int hkv, int d_qk,
+                               int d_v, int window, float scale, float rope_theta,
+                               float rotary_fraction, long long pos_offset, hswa_dtype_t dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Global-attention prefill: the GA layer of rslog.cc sections 1 and 5 (full
+ * causal key set, no sink term).  Same layouts as swa_sink_prefill; it is
+ * that call with window = 0 and sink = NULL.
+ */
+hswa_status_t ga_prefill(const void* q, const void* k, const void* v, void* o, int batch,
+                         int seqlen, int hq, int hkv, int d_qk, int d_v, float scale,
+                         float rope_theta, float rotary_fraction, long long pos_offset,
+                         hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Bytes of workspace swa_sink_decode needs for `batch` sequences whose
+ * positions are all <= max_pos (split partial results, fp32). */
+size_t hswa_decode_workspace_size(hswa_kv_layout_t layout, int batch, int hq, int d_v,
+                                  int window, long long max_pos);
+
+/*
+ * Single-token decode: one new query per sequence against its KV cache.
+ *   q [batch, hq, d_qk] (RoPE at position pos[b] is applied in the call; the
+ *   cache holds keys already rotated when they were written), o [batch, hq, d_v].
+ *   pos: int64 [batch] DEVICE array, the position of each sequence's query;
+ *   the caller has already written that token's key and value into the cache.
+ *   max_pos: host-side upper bound on every pos[b] (sizes the launch).
+ * HSWA_KV_RING ("MiMo v2.5 inference optimisation" (youngju.dev): the SWA pool
+ *   holds only the window):
+ *   k_cache [batch, window, hkv, d_qk], v_cache [batch, window, hkv, d_v];
+ *   token t lives in slot t mod window; slots not yet written (pos < window-1)
+ *   are ignored.  seq_offsets must be NULL and window > 0.
+ * HSWA_KV_CONTIGUOUS (the full-attention pool, O(sequence length)):
+ *   k_cache [total_rows, hkv, d_qk], v_cache [total_rows, hkv, d_v];
+ *   sequence b owns rows seq_offsets[b] .. seq_offsets[b+1]-1 (int64 [batch+1]
+ *   DEVICE array) and its token t is row seq_offsets[b] + t.  The query
+ *   attends to tokens max(0, pos-window+1) .. pos (window > 0) or 0 .. pos
+ *   (window == 0: a GA layer).
+ * A sequence whose pos is negative, above max_pos, or (contiguous) not below
+ * its row count gets NaN outputs; nothing outside the cache is read.
+ */
+hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_cache,
+                              hswa_kv_layout_t layout, const long long* seq_offsets,
+                              const long long* pos, const float* sink, void* o, int batch,
+                              int hq, int hkv, int d_qk, int d_v, int window, long long max_pos,
+                              float scale, float rope_theta, float rotary_fraction,
+                              hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Bytes of workspace sparse_sink_attn needs (the cos/sin table, 0 without RoPE). */
+size_t hswa_sparse_workspace_size(int seqlen, int d_qk, float rotary_fraction);
+
+/*
+ * Token-level sparse attention on one shared cache ("MiMo-V3 HySparse2"
+ * (aideepthink.cn), section 4): query i of kv group g attends to the
+ * recent_window most recent tokens max(0, i-recent_window+1) .. i plus the
+ * selected tokens sel_idx[b, i, g, 0 : sel_count[b, i, g]].
+ *   q [batch, seqlen, hq, d_qk], k/v [batch, seqlen, hkv, d_qk / d_v],
+ *   sel_idx int32 [batch, seqlen, hkv, max_sel], sel_count int32 [batch, seqlen, hkv],
+ *   o [batch, seqlen, hq, d_v].  Token i has RoPE position pos_offset + i.
+ * Caller contract: each list is sorted ascending and distinct, and every
+ * entry lies in [0, i - recent_window].  Entries outside that range are
+ * skipped (so nothing outside k/v is read); counts are clamped to
+ * [0, max_sel].
+ */
+hswa_status_t sparse_sink_attn(const void* q, const void* k, const void* v, const int* sel_idx,
+                               const int* sel_count, int max_sel, int recent_window,
+                               const float* sink, void* o, int batch, int seqlen, int hq,
+                               int hkv, int d_qk, int d_v, float scale, float rope_theta,
+                               float rotary_fraction, long long pos_offset, hswa_dtype_t dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text for the last non-OK status returned on this thread ("" if none). */
+const char* hswa_last_error(void);
+
+/* Library version string. */
+const char* hswa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSWA_H */

@@ -164,24 +164,26 @@ def _check_heads(hq, hkv):
 # ----------------------------------------------------------------------------
 
 def prefill_rows(q, k, v, rows, sink=None, window=128, scale=None,
-                 rope_theta=10000.0, rotary_fraction=0.0, pos_offset=0):
+                 rope_theta=10000.0, rotary_fraction=0.0, pos_offset=0, q_rows=None):
     """Prefill outputs for the query rows listed in `rows` only.
 
     q: [B, n, Hq, d_qk], k: [B, n, Hkv, d_qk], v: [B, n, Hkv, d_v].
     Token i sits at RoPE position pos_offset + i.  Query head h reads kv head
     h // (Hq/Hkv) (reading: contiguous GQA groups).  Returns [B, len(rows), Hq, d_v].
+    q_rows, when given, is q[:, rows] already (q itself may then be None).
     """
-    q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
-    B, n, hq, d = q.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    q_sel = np.asarray(q_rows) if q_rows is not None else np.asarray(q)[:, rows]
+    B, _, hq, d = q_sel.shape
+    n = k.shape[1]
     hkv = k.shape[2]
     G = _check_heads(hq, hkv)
-    rows = np.asarray(rows, dtype=np.int64)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     s_all = _sink_vector(sink, hq)
-    qr = rope(q[:, rows], pos_offset + rows, rope_theta, rotary_fraction)
+    qr = rope(q_sel, pos_offset + rows, rope_theta, rotary_fraction)
     kr = rope(k, pos_offset + np.arange(n), rope_theta, rotary_fraction)
     vv = np.asarray(v, dtype=np.float64)
     out = np.zeros((B, len(rows), hq, v.shape[-1]), dtype=np.float64)
@@ -296,29 +298,35 @@ def swa_sink_decode_contiguous(q, k, v, seq_offsets, pos, sink=None, window=None
 # ----------------------------------------------------------------------------
 
 def sparse_rows(q, k, v, sel_idx, sel_count, rows, sink, recent=128, scale=None,
-                rope_theta=10000.0, rotary_fraction=0.0, pos_offset=0):
+                rope_theta=10000.0, rotary_fraction=0.0, pos_offset=0, restricted=False):
     """Sparse attention outputs for the query rows listed in `rows`.
 
     q: [B, n, Hq, d_qk]; k: [B, n, Hkv, d_qk]; v: [B, n, Hkv, d_v];
     sel_idx: [B, n, Hkv, max_sel] int; sel_count: [B, n, Hkv] int.
     Query i of kv group g attends to sparse_keys(i, sel_idx[b,i,g], count, recent).
+    With restricted=True, q, sel_idx and sel_count hold only the listed rows
+    (their second axis runs over `rows`).
     """
-    q = np.asarray(q)
-    B, n, hq, d = q.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    q_sel = np.asarray(q) if restricted else np.asarray(q)[:, rows]
+    if not restricted:
+        sel_idx = np.asarray(sel_idx)[:, rows]
+        sel_count = np.asarray(sel_count)[:, rows]
+    B, _, hq, d = q_sel.shape
+    n = k.shape[1]
     hkv = k.shape[2]
     G = _check_heads(hq, hkv)
-    rows = np.asarray(rows, dtype=np.int64)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     s_all = _sink_vector(sink, hq)
-    qr = rope(q[:, rows], pos_offset + rows, rope_theta, rotary_fraction)
+    qr = rope(q_sel, pos_offset + rows, rope_theta, rotary_fraction)
     kr = rope(k, pos_offset + np.arange(n), rope_theta, rotary_fraction)
     vv = np.asarray(v, dtype=np.float64)
     out = np.zeros((B, len(rows), hq, v.shape[-1]), dtype=np.float64)
     for b in range(B):
         for t, i in enumerate(rows):
             for g in range(hkv):
-                J = sparse_keys(int(i), sel_idx[b, i, g], int(sel_count[b, i, g]), recent)
+                J = sparse_keys(int(i), sel_idx[b, t, g], int(sel_count[b, t, g]), recent)
                 hs = slice(g * G, (g + 1) * G)
                 out[b, t, hs] = attend_row(qr[b, t, hs], kr[b, J, g], vv[b, J, g],
                                            s_all[hs], scale)

@@ -1,0 +1,139 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, sizes workspaces, and rejects bad arguments before enqueuing any
+work.  None of these calls reach the GPU, so they run without one."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import hybrid_sliding_window_amd as hswa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hswa.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+FAKE = 0x10000          # 16-byte aligned fake device address, never dereferenced
+MISALIGNED = 0x10008
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hswa.lib_path()):
+        from hybrid_sliding_window_amd.build import build
+        build()
+    return hswa.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_and_binding_agree(lib):
+    declared = _declared()
+    assert set(declared) == set(hswa.EXPORTED_SYMBOLS), declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} is declared but not exported"
+
+
+def test_version_string(lib):
+    assert hswa.version().startswith("hswa")
+
+
+def test_workspace_sizes(lib):
+    # cos/sin table: seqlen * R/2 * 8 bytes, R = 64 at d = 192 and fraction 0.334
+    assert hswa.prefill_workspace_size(32768, 192, 0.334) == 32768 * 32 * 8
+    assert hswa.prefill_workspace_size(1000, 192, 0.0) == 0
+    assert hswa.sparse_workspace_size(100, 192, 0.334) == ((100 * 32 * 8 + 255) // 256) * 256
+    # decode: fp32 partial (O, m, l) per (sequence, head, split)
+    ring = hswa.decode_workspace_size(hswa.KV_RING, 64, 64, 128, 128, 262143)
+    assert ring == 64 * 64 * 4 * 128 * 4 + ((64 * 64 * 4 * 2 * 4 + 255) // 256) * 256
+    contig = hswa.decode_workspace_size(hswa.KV_CONTIGUOUS, 64, 64, 128, 0, 262143)
+    assert contig == 64 * 64 * 256 * 128 * 4 + 64 * 64 * 256 * 2 * 4
+    assert hswa.decode_workspace_size(hswa.KV_RING, 64, 64, 128, 0, 10) == 0
+
+
+def _prefill(lib, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, sink=None, o=FAKE, batch=1, seqlen=16, hq=4, hkv=2,
+                d_qk=192, d_v=128, window=8, scale=0.0, theta=1e4, frac=0.0, pos_offset=0,
+                dtype=1, ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    return lib.swa_sink_prefill(*args.values())
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, q=None) == INVALID
+    assert "non-null" in lib.hswa_last_error().decode()
+    assert _prefill(lib, hq=5) == INVALID                 # not a multiple of hkv
+    assert _prefill(lib, hkv=0) == INVALID
+    assert _prefill(lib, d_qk=0) == INVALID
+    assert _prefill(lib, window=-1) == INVALID
+    assert _prefill(lib, dtype=7) == INVALID
+    assert _prefill(lib, scale=-1.0) == INVALID
+    assert _prefill(lib, frac=1.5) == INVALID
+    assert _prefill(lib, frac=0.334, theta=0.0) == INVALID
+    assert _prefill(lib, o=MISALIGNED) == INVALID
+    assert _prefill(lib, frac=0.334) == INVALID           # workspace missing
+    assert _prefill(lib, frac=0.334, ws=FAKE, ws_bytes=8) == INVALID
+    assert _prefill(lib, d_qk=300) == UNSUPPORTED          # generic path caps head dims at 256
+    assert _prefill(lib, d_qk=300, dtype=0) == UNSUPPORTED
+    # empty work is a successful no-op that never touches the device
+    assert _prefill(lib, seqlen=0, q=None) == OK
+    assert _prefill(lib, batch=0, q=None) == OK
+    assert lib.hswa_last_error().decode() == ""
+
+
+def test_decode_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, layout=0, offs=None, pos=FAKE, sink=None, o=FAKE, batch=2,
+                 hq=4, hkv=2, d_qk=192, d_v=128, window=128, max_pos=1000, scale=0.0, theta=1e4,
+                 frac=0.0, dtype=1, ws=None, ws_bytes=0, stream=None)
+        a.update(kw)
+        return lib.swa_sink_decode(*a.values())
+    assert call(layout=5) == INVALID
+    assert call(window=0) == INVALID                       # ring needs its slot count
+    assert call(offs=FAKE) == INVALID                      # ring takes no offsets
+    assert call(layout=1) == INVALID                       # contiguous needs offsets
+    assert call(pos=None) == INVALID
+    assert call(max_pos=-1) == INVALID
+    assert call() == INVALID                               # workspace missing
+    assert call(batch=0) == OK
+
+
+def test_sparse_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, idx=FAKE, cnt=FAKE, max_sel=16, recent=8, sink=None,
+                 o=FAKE, batch=1, seqlen=32, hq=4, hkv=2, d_qk=192, d_v=128, scale=0.0, theta=1e4,
+                 frac=0.0, pos_offset=0, dtype=1, ws=None, ws_bytes=0, stream=None)
+        a.update(kw)
+        return lib.sparse_sink_attn(*a.values())
+    assert call(recent=0) == INVALID
+    assert call(max_sel=-1) == INVALID
+    assert call(cnt=None) == INVALID
+    assert call(idx=None) == INVALID
+    assert call(frac=0.334) == INVALID                     # workspace missing
+    assert call(seqlen=0) == OK
+
+
+def test_binding_rejects_bad_tensors(lib):
+    import torch
+    q = torch.zeros(1, 4, 2, 192, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        hswa._binding._dtype_code(q)
+    with pytest.raises(ValueError):
+        hswa._binding._sink(torch.zeros(2, dtype=torch.float64), q)
+
+
+def test_product_path_does_not_use_the_oracle():
+    """The package never imports the CPU oracle or falls back to the CPU."""
+    pkg = os.path.join(ROOT, "hybrid_sliding_window_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("the oracle", ""), f
+                assert "scaled_dot_product_attention" not in text, f

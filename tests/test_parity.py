@@ -1,0 +1,413 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle.
+
+Tolerances (from the problem statement of the method and the arithmetic):
+  * fp32 storage: max |gpu - oracle| <= 1e-5;
+  * bf16 storage (fp32 accumulation): max-abs <= 2e-2 and
+    rel-L2 = ||gpu - oracle||_2 / ||oracle||_2 <= 5e-3.
+The bf16 budget: the only roundings in the kernels are the RoPE-rotated
+dims of q~ and k~ to bf16, P to bf16 before the PV product and the final
+store; each is a relative 2^-9 step, together ~2e-3 rel-L2.
+
+Small cases span several tiles and a ragged tail and are checked element by
+element over the whole output; the full-size workloads (the same launch
+configuration the benchmark times) are checked on sampled rows.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+BF16_MAX, BF16_RL2, F32_MAX = 2e-2, 5e-3, 1e-5
+
+
+def _np(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def _check(name, got, ref, fp32=False):
+    g = _np(got) if isinstance(got, torch.Tensor) else got
+    d = g - ref
+    mx = float(np.abs(d).max()) if d.size else 0.0
+    rl2 = float(np.linalg.norm(d) / max(np.linalg.norm(ref), 1e-300))
+    print(f"[parity] {name}: max_abs={mx:.3e} rel_l2={rl2:.3e}", flush=True)
+    assert np.isfinite(g).all(), f"{name}: non-finite output"
+    if fp32:
+        assert mx <= F32_MAX, f"{name}: max_abs {mx}"
+    else:
+        assert mx <= BF16_MAX and rl2 <= BF16_RL2, f"{name}: max_abs {mx} rel_l2 {rl2}"
+
+
+def _prefill_case(B, n, hq, hkv, dtype, seed, sink_range=(-2.0, 2.0)):
+    return synthetic.prefill_inputs(B, n, hq, hkv, 192, 128, dtype, seed, DEV, sink_range)
+
+
+def _host(x):
+    q, k, v = (_np(x[t]) for t in "qkv")
+    s = None if x["sink"] is None else _np(x["sink"])
+    return q, k, v, s
+
+
+# ---------------------------------------------------------------------------
+# Tiny fp32 SWA+sink (n = 512, 2 q heads over 1 kv head, no RoPE)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("window,with_sink", [(128, True), (128, False), (512, True), (512, False)])
+def test_tiny_fp32_prefill(gpu_lib, window, with_sink):
+    x = _prefill_case(1, 512, 2, 1, "f32", 1, sink_range=(-3.0, 3.0) if with_sink else None)
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=window)
+    q, k, v, s = _host(x)
+    ref = oracle.swa_sink_prefill(q, k, v, s, window=window)
+    _check(f"tiny fp32 W={window} sink={with_sink}", o, ref, fp32=True)
+    if window == 512 and not with_sink:
+        # W >= n without a sink is plain causal softmax attention
+        _check("tiny fp32 W=n vs causal", o, oracle.ga_prefill(q, k, v), fp32=True)
+        og = gpu_lib.ga_prefill(x["q"], x["k"], x["v"])
+        _check("tiny fp32 ga_prefill", og, oracle.ga_prefill(q, k, v), fp32=True)
+
+
+# ---------------------------------------------------------------------------
+# bf16 prefill, whole outputs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,n,hq,hkv,window", [
+    (1, 1000, 64, 8, 128),     # SWA layer heads, ragged tail (1000 = 62.5 blocks of 16)
+    (2, 333, 16, 16, 128),     # MHA (G = 1): 128-token blocks
+    (1, 517, 32, 4, 128),      # G = 8 with batch of one
+    (1, 130, 64, 1, 128),      # G = 64: 2 tokens per block
+    (1, 300, 8, 4, 1),         # window of one token
+    (1, 300, 8, 4, 7),         # narrow window
+    (1, 90, 16, 2, 128),       # n < W
+    (1, 1, 64, 8, 128),        # a single token
+])
+def test_swa_prefill_bf16(gpu_lib, B, n, hq, hkv, window):
+    x = _prefill_case(B, n, hq, hkv, "bf16", 20 + n)
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=window,
+                                 rope_theta=1.0e4, rotary_fraction=0.334)
+    q, k, v, s = _host(x)
+    ref = oracle.swa_sink_prefill(q, k, v, s, window=window, rope_theta=1.0e4, rotary_fraction=0.334)
+    _check(f"swa bf16 B={B} n={n} {hq}/{hkv} W={window}", o, ref)
+
+
+@pytest.mark.parametrize("B,n,hq,hkv", [(1, 700, 64, 4), (2, 257, 8, 8), (1, 1030, 16, 1)])
+def test_ga_prefill_bf16(gpu_lib, B, n, hq, hkv):
+    x = _prefill_case(B, n, hq, hkv, "bf16", 40 + n, sink_range=None)
+    o = gpu_lib.ga_prefill(x["q"], x["k"], x["v"], rope_theta=1.0e7, rotary_fraction=0.334)
+    q, k, v, _ = _host(x)
+    ref = oracle.ga_prefill(q, k, v, rope_theta=1.0e7, rotary_fraction=0.334)
+    _check(f"ga bf16 B={B} n={n} {hq}/{hkv}", o, ref)
+
+
+@pytest.mark.parametrize("frac", [0.0, 2.0 / 3.0, 1.0])
+def test_prefill_rotary_widths(gpu_lib, frac):
+    """R = 0, 128 and 192 rotated dims (the MFMA path pairs r with r + R/2 in lane)."""
+    x = _prefill_case(1, 200, 16, 2, "bf16", 61)
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=64, rope_theta=500.0,
+                                 rotary_fraction=frac, pos_offset=1000)
+    q, k, v, s = _host(x)
+    ref = oracle.swa_sink_prefill(q, k, v, s, window=64, rope_theta=500.0, rotary_fraction=frac,
+                                  pos_offset=1000)
+    _check(f"rotary fraction {frac:.3f}", o, ref)
+
+
+@pytest.mark.parametrize("qmul", [2.0, 4.0])
+def test_sink_sensitive_case(gpu_lib, qmul):
+    """Large sinks U(2, 6) (the sink absorbs a large share of each row) and a
+    sharpened q: a kernel that dropped or mis-scaled the sink term fails here
+    even where the plain workload cannot tell.
+
+    At q x 4 the score perturbation from rounding the rotated q~ and k~ to
+    bf16 grows with |q| (four times the q x 1 case, whose max-abs error is
+    ~8.5e-3), and rows collapse onto single keys with |o| up to ~5; the
+    max-abs bar there is 5e-2, derived from that scaling, with rel-L2 still
+    <= 5e-3."""
+    x = _prefill_case(1, 600, 64, 8, "bf16", 62, sink_range=(2.0, 6.0))
+    x["q"] = (x["q"].float() * qmul).to(torch.bfloat16)
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=128, rope_theta=1.0e4,
+                                 rotary_fraction=0.334)
+    q, k, v, s = _host(x)
+    ref = oracle.swa_sink_prefill(q, k, v, s, window=128, rope_theta=1.0e4, rotary_fraction=0.334)
+    if qmul <= 2.0:
+        _check(f"sink-sensitive q x {qmul}", o, ref)
+    else:
+        g = _np(o)
+        d = np.abs(g - ref)
+        rl2 = float(np.linalg.norm(g - ref) / np.linalg.norm(ref))
+        print(f"[parity] sink-sensitive q x {qmul}: max_abs={d.max():.3e} rel_l2={rl2:.3e} "
+              f"max|o|={np.abs(ref).max():.2f}", flush=True)
+        assert rl2 <= BF16_RL2
+        assert d.max() <= 5e-2
+    no_sink = oracle.swa_sink_prefill(q, k, v, None, window=128, rope_theta=1.0e4,
+                                      rotary_fraction=0.334)
+    assert np.abs(_np(o) - no_sink).max() > 0.1          # the sink visibly matters here
+
+
+def test_weight_sum_closed_form_on_gpu(gpu_lib):
+    """V = 1: every output equals the attention weight sum, which is < 1 with a
+    sink and exactly 1 without one (the invariant of the pages' comparison table)."""
+    x = _prefill_case(1, 400, 16, 2, "bf16", 63)
+    ones = torch.ones_like(x["v"])
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], ones, x["sink"], window=128)
+    o0 = gpu_lib.swa_sink_prefill(x["q"], x["k"], ones, None, window=128)
+    q, k, _, s = _host(x)
+    ref = oracle.swa_sink_prefill(q, k, np.ones_like(_np(ones)), s, window=128)
+    _check("V=1 weight sum", o, ref)
+    assert (ref < 1.0).all()            # the sink takes a share of every row
+    assert (_np(o) <= 1.0).all()        # bf16 output: sums just below 1 may round to 1
+    assert np.abs(_np(o0) - 1.0).max() <= 2e-2
+
+
+def test_prefill_deterministic(gpu_lib):
+    x = _prefill_case(1, 700, 64, 8, "bf16", 64)
+    a = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=128, rope_theta=1.0e4,
+                                 rotary_fraction=0.334)
+    b = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=128, rope_theta=1.0e4,
+                                 rotary_fraction=0.334)
+    assert torch.equal(a, b)
+
+
+def test_prefill_generic_shapes(gpu_lib):
+    """Head dims the matrix-core kernel does not take run on the generic kernel."""
+    x = synthetic.prefill_inputs(1, 150, 6, 3, 64, 96, "bf16", 65, DEV)
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=32, rope_theta=1.0e4,
+                                 rotary_fraction=0.25)
+    q, k, v, s = _host(x)
+    ref = oracle.swa_sink_prefill(q, k, v, s, window=32, rope_theta=1.0e4, rotary_fraction=0.25)
+    _check("generic bf16 d=64/96", o, ref)
+    xf = synthetic.prefill_inputs(1, 150, 6, 3, 64, 96, "f32", 66, DEV)
+    of = gpu_lib.ga_prefill(xf["q"], xf["k"], xf["v"], rope_theta=1.0e4, rotary_fraction=0.25)
+    q, k, v, _ = _host(xf)
+    _check("generic f32 GA d=64/96", of, oracle.ga_prefill(q, k, v, rope_theta=1.0e4,
+                                                           rotary_fraction=0.25), fp32=True)
+
+
+def test_empty_inputs(gpu_lib):
+    x = _prefill_case(1, 0, 8, 2, "bf16", 67)
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=128)
+    assert o.shape == (1, 0, 8, 128)
+
+
+# ---------------------------------------------------------------------------
+# Full-size prefill workloads, sampled rows
+# ---------------------------------------------------------------------------
+
+def _sample_rows(n, seed, k=96):
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(64, n - 64), size=k, replace=False)
+    return np.unique(np.concatenate([np.arange(64), mid, np.arange(n - 64, n)]))
+
+
+def test_swa_prefill_full_size(gpu_lib):
+    wl = synthetic.WORKLOADS["swa_prefill_n32768"]
+    x = _prefill_case(1, wl["n"], wl["hq"], wl["hkv"], "bf16", wl["seed"], wl["sink_range"])
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=wl["window"],
+                                 rope_theta=wl["rope_theta"], rotary_fraction=wl["rotary_fraction"])
+    rows = _sample_rows(wl["n"], 71)
+    ridx = torch.from_numpy(rows).to(DEV)
+    ref = oracle.prefill_rows(None, _np(x["k"]), _np(x["v"]), rows, sink=_np(x["sink"]),
+                              window=wl["window"], rope_theta=wl["rope_theta"],
+                              rotary_fraction=wl["rotary_fraction"], q_rows=_np(x["q"][:, ridx]))
+    _check("swa full size (sampled rows)", o[:, ridx], ref)
+
+
+def test_ga_prefill_full_size(gpu_lib):
+    wl = synthetic.WORKLOADS["ga_prefill_n32768"]
+    x = _prefill_case(1, wl["n"], wl["hq"], wl["hkv"], "bf16", wl["seed"], None)
+    o = gpu_lib.ga_prefill(x["q"], x["k"], x["v"], rope_theta=wl["rope_theta"],
+                           rotary_fraction=wl["rotary_fraction"])
+    rng = np.random.default_rng(72)
+    rows = np.unique(np.concatenate([np.arange(8), rng.choice(wl["n"], 40, replace=False),
+                                     np.arange(wl["n"] - 8, wl["n"])]))
+    ridx = torch.from_numpy(rows).to(DEV)
+    ref = oracle.prefill_rows(None, _np(x["k"]), _np(x["v"]), rows, sink=None, window=None,
+                              rope_theta=wl["rope_theta"], rotary_fraction=wl["rotary_fraction"],
+                              q_rows=_np(x["q"][:, ridx]))
+    _check("ga full size (sampled rows)", o[:, ridx], ref)
+
+
+# ---------------------------------------------------------------------------
+# Decode
+# ---------------------------------------------------------------------------
+
+def _ring_case(pos, hq=64, hkv=8, W=128, seed=80, dtype="bf16", sink=(-2.0, 2.0)):
+    pos = torch.as_tensor(pos, dtype=torch.int64)
+    return synthetic.ring_decode_inputs(len(pos), hq, hkv, W, 192, 128, dtype, seed, pos, DEV, sink)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ring_decode(gpu_lib, dtype):
+    pos = [0, 1, 5, 126, 127, 128, 1000, 131072, 262143, 77777]
+    d = _ring_case(pos, dtype=dtype)
+    o = gpu_lib.swa_sink_decode(d["q"], d["k"], d["v"], d["pos"], max(pos), layout=gpu_lib.KV_RING,
+                                sink=d["sink"], window=128)
+    ref = oracle.swa_sink_decode_ring(_np(d["q"]), _np(d["k"]), _np(d["v"]), np.array(pos),
+                                      _np(d["sink"]))
+    _check(f"ring decode {dtype}", o, ref, fp32=(dtype == "f32"))
+
+
+def test_ring_decode_rope_large_positions(gpu_lib):
+    """q rotated in the call at p up to 2.6e5 (angles in fp64): base 1e4."""
+    pos = [3, 200, 131072, 200001, 262143]
+    d = _ring_case(pos, seed=81)
+    o = gpu_lib.swa_sink_decode(d["q"], d["k"], d["v"], d["pos"], 262143, layout=gpu_lib.KV_RING,
+                                sink=d["sink"], window=128, rope_theta=1.0e4, rotary_fraction=0.334)
+    ref = oracle.swa_sink_decode_ring(_np(d["q"]), _np(d["k"]), _np(d["v"]), np.array(pos),
+                                      _np(d["sink"]), rope_theta=1.0e4, rotary_fraction=0.334)
+    _check("ring decode rope", o, ref)
+
+
+def _contig_case(pos, hq=64, hkv=4, seed=90, dtype="bf16", sink=None, extra=0):
+    pos = torch.as_tensor(pos, dtype=torch.int64)
+    return synthetic.contiguous_decode_inputs(len(pos), hq, hkv, 192, 128, dtype, seed, pos, DEV,
+                                              sink, extra_rows=extra)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_contiguous_decode(gpu_lib, dtype):
+    pos = [0, 31, 32, 1000, 5000, 20000, 777]
+    d = _contig_case(pos, dtype=dtype, extra=3)
+    o = gpu_lib.swa_sink_decode(d["q"], d["k"], d["v"], d["pos"], 20000,
+                                layout=gpu_lib.KV_CONTIGUOUS, seq_offsets=d["seq_offsets"],
+                                window=0, rope_theta=1.0e7, rotary_fraction=0.334)
+    ref = oracle.swa_sink_decode_contiguous(_np(d["q"]), _np(d["k"]), _np(d["v"]),
+                                            d["seq_offsets"].cpu().numpy(), np.array(pos), None,
+                                            None, rope_theta=1.0e7, rotary_fraction=0.334)
+    _check(f"contiguous GA decode {dtype}", o, ref, fp32=(dtype == "f32"))
+
+
+def test_contiguous_windowed_decode(gpu_lib):
+    pos = [0, 100, 127, 128, 4000]
+    d = _contig_case(pos, hq=64, hkv=8, seed=91, sink=(-2.0, 2.0))
+    o = gpu_lib.swa_sink_decode(d["q"], d["k"], d["v"], d["pos"], 4000,
+                                layout=gpu_lib.KV_CONTIGUOUS, seq_offsets=d["seq_offsets"],
+                                sink=d["sink"], window=128)
+    ref = oracle.swa_sink_decode_contiguous(_np(d["q"]), _np(d["k"]), _np(d["v"]),
+                                            d["seq_offsets"].cpu().numpy(), np.array(pos),
+                                            _np(d["sink"]), 128)
+    _check("contiguous SWA decode", o, ref)
+
+
+def test_decode_contract_violations_give_nan(gpu_lib):
+    pos = [10, 500]
+    d = _contig_case(pos, seed=92)
+    bad = torch.tensor([10, 600], dtype=torch.int64, device=DEV)   # 600 >= rows of sequence 1
+    o = gpu_lib.swa_sink_decode(d["q"], d["k"], d["v"], bad, 600, layout=gpu_lib.KV_CONTIGUOUS,
+                                seq_offsets=d["seq_offsets"], window=0)
+    on = _np(o)
+    assert np.isfinite(on[0]).all() and np.isnan(on[1]).all()
+    r = _ring_case([5, 50], hq=16, hkv=2, seed=93)
+    o2 = gpu_lib.swa_sink_decode(r["q"], r["k"], r["v"], r["pos"], 20, layout=gpu_lib.KV_RING,
+                                 sink=r["sink"], window=128)          # 50 > max_pos
+    on2 = _np(o2)
+    assert np.isfinite(on2[0]).all() and np.isnan(on2[1]).all()
+
+
+def test_decode_matches_prefill_row(gpu_lib):
+    """Decode at p over a ring filled from a sequence equals prefill row p (both on GPU)."""
+    L, W = 300, 128
+    x = _prefill_case(1, L, 64, 8, "bf16", 94)
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=W)
+    p = L - 1
+    ring_k = torch.zeros(1, W, 8, 192, dtype=torch.bfloat16, device=DEV)
+    ring_v = torch.zeros(1, W, 8, 128, dtype=torch.bfloat16, device=DEV)
+    for t in range(p - W + 1, p + 1):
+        ring_k[0, t % W] = x["k"][0, t]
+        ring_v[0, t % W] = x["v"][0, t]
+    od = gpu_lib.swa_sink_decode(x["q"][:, p].contiguous(), ring_k, ring_v,
+                                 torch.tensor([p], device=DEV), p, layout=gpu_lib.KV_RING,
+                                 sink=x["sink"], window=W)
+    assert (od.float() - o[:, p].float()).abs().max().item() <= 2e-2
+
+
+def test_hybrid_decode_full_size(gpu_lib):
+    wl = synthetic.WORKLOADS["hybrid_decode_b64"]
+    pos = synthetic.decode_positions(wl["B"], *wl["pos_range"], wl["seed"])
+    sw = wl["swa"]
+    d = synthetic.ring_decode_inputs(wl["B"], sw["hq"], sw["hkv"], sw["window"], 192, 128, "bf16",
+                                     wl["seed"], pos, DEV, sw["sink_range"])
+    o = gpu_lib.swa_sink_decode(d["q"], d["k"], d["v"], d["pos"], wl["pos_range"][1],
+                                layout=gpu_lib.KV_RING, sink=d["sink"], window=sw["window"])
+    ref = oracle.swa_sink_decode_ring(_np(d["q"]), _np(d["k"]), _np(d["v"]), pos.numpy(),
+                                      _np(d["sink"]))
+    _check("hybrid decode SWA ring (all 64 sequences)", o, ref)
+    del d
+    ga = wl["ga"]
+    c = synthetic.contiguous_decode_inputs(wl["B"], ga["hq"], ga["hkv"], 192, 128, "bf16",
+                                           wl["seed"], pos, DEV, None)
+    og = gpu_lib.swa_sink_decode(c["q"], c["k"], c["v"], c["pos"], wl["pos_range"][1],
+                                 layout=gpu_lib.KV_CONTIGUOUS, seq_offsets=c["seq_offsets"],
+                                 window=0)
+    offs = c["seq_offsets"].cpu().numpy()
+    seqs = np.array([int(pos.argmin()), int(pos.argmax()), 17])
+
+    def loader(b):
+        lo, hi = int(offs[b]), int(offs[b + 1])
+        return _np(c["k"][lo:hi]), _np(c["v"][lo:hi])
+
+    refg = oracle.swa_sink_decode_contiguous(_np(c["q"]), None, None, offs, pos.numpy(), None,
+                                             None, seqs=seqs, kv_loader=loader)
+    _check("hybrid decode GA contiguous (sampled sequences)", og[torch.from_numpy(seqs)], refg)
+
+
+# ---------------------------------------------------------------------------
+# Sparse
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,hq,hkv,recent,max_sel,frac", [
+    (1500, 64, 4, 128, 1024, 0.0),    # the workload's shape at a size the oracle covers
+    (400, 16, 2, 32, 64, 0.334),      # sampling at small n, RoPE on
+    (300, 8, 8, 16, 20, 0.0),         # G = 1
+])
+def test_sparse_bf16(gpu_lib, n, hq, hkv, recent, max_sel, frac):
+    x = synthetic.sparse_inputs(1, n, hq, hkv, 192, 128, "bf16", 100 + n, recent, max_sel, DEV)
+    o = gpu_lib.sparse_sink_attn(x["q"], x["k"], x["v"], x["sel_idx"], x["sel_count"], x["sink"],
+                                 recent_window=recent, rope_theta=1.0e4, rotary_fraction=frac)
+    q, k, v, s = _host(x)
+    ref = oracle.sparse_sink_attn(q, k, v, x["sel_idx"].cpu().numpy(), x["sel_count"].cpu().numpy(),
+                                  s, recent=recent, rope_theta=1.0e4, rotary_fraction=frac)
+    _check(f"sparse bf16 n={n} {hq}/{hkv} recent={recent} sel={max_sel}", o, ref)
+
+
+def test_sparse_fp32_and_invalid_entries(gpu_lib):
+    n, recent = 200, 16
+    x = synthetic.sparse_inputs(1, n, 4, 2, 192, 128, "f32", 110, recent, 24, DEV)
+    idx = x["sel_idx"].clone()
+    idx[0, 150, 0, 0] = 10_000        # out of range: skipped by contract
+    idx[0, 151, 1, 3] = 151           # inside the recent window: skipped
+    o = gpu_lib.sparse_sink_attn(x["q"], x["k"], x["v"], idx, x["sel_count"], x["sink"],
+                                 recent_window=recent)
+    q, k, v, s = _host(x)
+    clean = x["sel_idx"].cpu().numpy().copy()
+    cnt = x["sel_count"].cpu().numpy().copy()
+    for (i, g, j) in ((150, 0, 0), (151, 1, 3)):
+        row = [t for t in clean[0, i, g, :cnt[0, i, g]] if t != clean[0, i, g, j]]
+        clean[0, i, g, :len(row)] = row
+        cnt[0, i, g] = len(row)
+    ref = oracle.sparse_sink_attn(q, k, v, clean, cnt, s, recent=recent)
+    _check("sparse fp32 with skipped entries", o, ref, fp32=True)
+    # same through the bf16 matrix-core kernel
+    xb = {t: (x[t].to(torch.bfloat16) if t in "qkv" else x[t]) for t in x}
+    ob = gpu_lib.sparse_sink_attn(xb["q"], xb["k"], xb["v"], idx, x["sel_count"], x["sink"],
+                                  recent_window=recent)
+    refb = oracle.sparse_sink_attn(*(_np(xb[t]) for t in "qkv"), clean, cnt, s, recent=recent)
+    _check("sparse bf16 with skipped entries", ob, refb)
+
+
+def test_sparse_full_size(gpu_lib):
+    wl = synthetic.WORKLOADS["sparse_prefill_n65536"]
+    x = synthetic.sparse_inputs(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, "bf16", wl["seed"],
+                                wl["recent"], wl["max_sel"], DEV, wl["sink_range"])
+    o = gpu_lib.sparse_sink_attn(x["q"], x["k"], x["v"], x["sel_idx"], x["sel_count"], x["sink"],
+                                 recent_window=wl["recent"])
+    rows = _sample_rows(wl["n"], 120)
+    ridx = torch.from_numpy(rows).to(DEV)
+    ref = oracle.sparse_rows(_np(x["q"][:, ridx]), _np(x["k"]), _np(x["v"]),
+                             x["sel_idx"][:, ridx].cpu().numpy(), x["sel_count"][:, ridx].cpu().numpy(),
+                             rows, _np(x["sink"]), recent=wl["recent"], restricted=True)
+    _check("sparse full size (sampled rows)", o[:, ridx], ref)
