@@ -120,14 +120,43 @@ def cpu_baseline(x, wl, budget_s):
                       f"useful FLOPs of the sampled rows over wall time"}
 
 
-def secondary(steps, warmup):
+def copy_calibration(steps, warmup):
+    """A plain device copy of known size: the reference for scaling the
+    profiler's HBM byte counters (FETCH_SIZE / WRITE_SIZE)."""
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    _, per = timed(lambda: dst.copy_(src), steps, warmup)
+    t = float(np.mean(per)) / 1e3
+    return {"copy_bytes_each_way": nbytes, "gbps_read_plus_write": 2 * nbytes / t / 1e9,
+            "us": t * 1e6}
+
+
+def only(which, steps, warmup):
+    if which == "copy":
+        return {"copy": copy_calibration(steps, warmup)}
+    parts = {"ga": ["ga"], "decode": ["decode"], "sparse": ["sparse"]}[which]
+    return secondary(steps, warmup, parts)
+
+
+def secondary(steps, warmup, parts=("ga", "decode", "sparse")):
     out = {}
     dev = "cuda"
+    if "ga" in parts:
+        _ga(out, steps, warmup, dev)
+    if "decode" in parts:
+        _decode(out, dev)
+    if "sparse" in parts:
+        _sparse(out, dev)
+    return out
+
+
+def _ga(out, steps, warmup, dev):
     # GA prefill, n = 32768, 64 q / 4 kv heads, full causal
     wl = synthetic.WORKLOADS["ga_prefill_n32768"]
     x = synthetic.prefill_inputs(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, "bf16", wl["seed"], dev,
                                  None)
-    ws = torch.empty(hswa.prefill_workspace_size(wl["n"], 192, wl["rotary_fraction"]),
+    ws = torch.empty(hswa.prefill_workspace_size(1, wl["n"], wl["hkv"], 192, wl["rotary_fraction"]),
                      dtype=torch.uint8, device=dev)
     o = torch.empty(1, wl["n"], wl["hq"], 128, dtype=torch.bfloat16, device=dev)
     fn = lambda: hswa.ga_prefill(x["q"], x["k"], x["v"], rope_theta=wl["rope_theta"],  # noqa: E731
@@ -138,9 +167,9 @@ def secondary(steps, warmup):
     out["ga_prefill_n32768"] = {"tflops": flops / t / 1e12, "ms": t * 1e3,
                                 "frac_of_bf16_peak": flops / t / 1e12 / BF16_PEAK_TFLOPS}
     _log(f"GA prefill {out['ga_prefill_n32768']}")
-    del x, o, ws
-    torch.cuda.empty_cache()
 
+
+def _decode(out, dev):
     # Hybrid decode: 64 sequences at p ~ U[131072, 262143]
     wl = synthetic.WORKLOADS["hybrid_decode_b64"]
     pos = synthetic.decode_positions(wl["B"], *wl["pos_range"], wl["seed"])
@@ -183,9 +212,9 @@ def secondary(steps, warmup):
     out["decode_ga_contiguous"] = {"gbps": ga_bytes / t / 1e9, "ms": t * 1e3, "bytes": ga_bytes,
                                    "frac_of_hbm_peak": ga_bytes / t / 1e9 / HBM_PEAK_GBPS}
     _log(f"decode GA {out['decode_ga_contiguous']}")
-    del c, wsc
-    torch.cuda.empty_cache()
 
+
+def _sparse(out, dev):
     # Sparse prefill, n = 65536, 128 recent + <= 1024 selected
     wl = synthetic.WORKLOADS["sparse_prefill_n65536"]
     x = synthetic.sparse_inputs(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, "bf16", wl["seed"],
@@ -202,7 +231,6 @@ def secondary(steps, warmup):
     out["sparse_prefill_n65536"] = {"tflops": flops / t / 1e12, "ms": t * 1e3,
                                     "gathered_kv_gbps": gathered / t / 1e9}
     _log(f"sparse {out['sparse_prefill_n65536']}")
-    return out
 
 
 def main():
@@ -213,6 +241,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", choices=["prefill", "ga", "decode", "sparse", "copy"], default=None,
+                    help="run one workload only (for profiler runs); prints its figures as JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU: this build has no multi-GPU path "
@@ -220,11 +250,14 @@ def main():
         sys.exit(2)
     _ensure_built()
     dev = "cuda"
+    if args.only and args.only != "prefill":
+        print(json.dumps(only(args.only, args.steps, args.warmup)), flush=True)
+        return
     wl = synthetic.WORKLOADS["swa_prefill_n32768"]
     x = synthetic.prefill_inputs(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, "bf16", wl["seed"], dev,
                                  wl["sink_range"])
     o = torch.empty(1, wl["n"], wl["hq"], 128, dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(hswa.prefill_workspace_size(wl["n"], 192, wl["rotary_fraction"]),
+    ws = torch.empty(hswa.prefill_workspace_size(1, wl["n"], wl["hkv"], 192, wl["rotary_fraction"]),
                      dtype=torch.uint8, device=dev)
 
     def step():
@@ -269,6 +302,9 @@ def main():
                      "launch_ms": kern_s * 1e3,
                      "frac_of_bf16_mfma_peak": value / BF16_PEAK_TFLOPS},
     }
+    if args.only:
+        print(json.dumps(rec), flush=True)
+        return
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_seconds)
         _log(f"cpu baseline {rec['cpu_baseline']}")

@@ -18,7 +18,7 @@ _vp, _i, _ll, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes
 
 # Every symbol include/hswa.h declares, with (restype, argtypes).
 _SIGNATURES = {
-    "hswa_prefill_workspace_size": (_sz, [_i, _i, _f]),
+    "hswa_prefill_workspace_size": (_sz, [_i, _i, _i, _i, _f]),
     "swa_sink_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _f, _f,
                               _ll, _i, _vp, _sz, _vp]),
     "ga_prefill": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _f, _ll, _i, _vp, _sz,
@@ -26,7 +26,7 @@ _SIGNATURES = {
     "hswa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i, _ll]),
     "swa_sink_decode": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _ll,
                              _f, _f, _f, _i, _vp, _sz, _vp]),
-    "hswa_sparse_workspace_size": (_sz, [_i, _i, _f]),
+    "hswa_sparse_workspace_size": (_sz, [_i, _i, _i, _i, _f]),
     "sparse_sink_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i, _i,
                               _f, _f, _f, _ll, _i, _vp, _sz, _vp]),
     "hswa_last_error": (ctypes.c_char_p, []),
@@ -112,12 +112,12 @@ def _workspace(nbytes, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def prefill_workspace_size(seqlen, d_qk, rotary_fraction):
-    return load().hswa_prefill_workspace_size(seqlen, d_qk, rotary_fraction)
+def prefill_workspace_size(batch, seqlen, hkv, d_qk, rotary_fraction):
+    return load().hswa_prefill_workspace_size(batch, seqlen, hkv, d_qk, rotary_fraction)
 
 
-def sparse_workspace_size(seqlen, d_qk, rotary_fraction):
-    return load().hswa_sparse_workspace_size(seqlen, d_qk, rotary_fraction)
+def sparse_workspace_size(batch, seqlen, hkv, d_qk, rotary_fraction):
+    return load().hswa_sparse_workspace_size(batch, seqlen, hkv, d_qk, rotary_fraction)
 
 
 def decode_workspace_size(layout, batch, hq, d_v, window, max_pos):
@@ -133,7 +133,7 @@ def swa_sink_prefill(q, k, v, sink=None, window=128, scale=0.0, rope_theta=10000
     sink = _sink(sink, q)
     o = out if out is not None else torch.empty((B, n, hq, dv), dtype=q.dtype, device=q.device)
     _check_same(q, k, v, o)
-    need = lib.hswa_prefill_workspace_size(n, dqk, rotary_fraction)
+    need = lib.hswa_prefill_workspace_size(B, n, hkv, dqk, rotary_fraction)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     st = lib.swa_sink_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(o), B, n, hq, hkv, dqk,
                               dv, window, scale, rope_theta, rotary_fraction, pos_offset,
@@ -150,7 +150,7 @@ def ga_prefill(q, k, v, scale=0.0, rope_theta=1.0e7, rotary_fraction=0.0, pos_of
     hkv, dv = k.shape[2], v.shape[3]
     o = out if out is not None else torch.empty((B, n, hq, dv), dtype=q.dtype, device=q.device)
     _check_same(q, k, v, o)
-    need = lib.hswa_prefill_workspace_size(n, dqk, rotary_fraction)
+    need = lib.hswa_prefill_workspace_size(B, n, hkv, dqk, rotary_fraction)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     st = lib.ga_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, n, hq, hkv, dqk, dv, scale,
                         rope_theta, rotary_fraction, pos_offset, _dtype_code(q), _ptr(ws),
@@ -196,7 +196,7 @@ def sparse_sink_attn(q, k, v, sel_idx, sel_count, sink=None, recent_window=128, 
         raise TypeError("sel_idx and sel_count must be int32")
     o = out if out is not None else torch.empty((B, n, hq, dv), dtype=q.dtype, device=q.device)
     _check_same(q, k, v, o, sel_idx, sel_count)
-    need = lib.hswa_sparse_workspace_size(n, dqk, rotary_fraction)
+    need = lib.hswa_sparse_workspace_size(B, n, hkv, dqk, rotary_fraction)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     st = lib.sparse_sink_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(sel_idx), _ptr(sel_count), max_sel,
                               recent_window, _ptr(sink), _ptr(o), B, n, hq, hkv, dqk, dv, scale,

@@ -4,7 +4,9 @@
 
 Every HIP source is compiled with packed-fp32 instructions disabled
 (-target-feature -packed-fp32-ops); the host pass warns that it does not
-know the feature, which is harmless.
+know the feature, which is harmless.  -fno-honor-nans lets fmaxf map to a
+single v_max_f32: no kernel computes with NaN (the NaN outputs that flag a
+broken caller contract are stored as bit patterns).
 """
 
 import os
@@ -19,10 +21,10 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhswa.so")
 ARCH = os.environ.get("HSWA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "rope_table.hip", "generic.hip", "prefill_bf16.hip", "decode_bf16.hip",
+SOURCES = ["api.cpp", "rope_prep.hip", "generic.hip", "prefill_bf16.hip", "decode_bf16.hip",
            "sparse_bf16.hip"]
 
-FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
+FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fno-honor-nans",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 

@@ -84,6 +84,36 @@ size_t table_bytes(int seqlen, int d_qk, float rotary_fraction) {
   return round256((size_t)seqlen * (size_t)half * sizeof(float2));
 }
 
+// Rotated copy of K's first R dims (bf16), read by the matrix-core kernels.
+size_t krot_bytes(int batch, int seqlen, int hkv, int d_qk, float rotary_fraction) {
+  if (batch <= 0 || seqlen <= 0 || hkv <= 0 || d_qk <= 0) return 0;
+  if (!(rotary_fraction >= 0.f && rotary_fraction <= 1.f)) return 0;
+  const int half = rotary_half(d_qk, rotary_fraction);
+  return round256((size_t)batch * seqlen * hkv * (size_t)(2 * half) * 2);
+}
+
+// Workspace of prefill and sparse calls: [cos/sin table][rotated K rows].
+size_t rope_workspace_bytes(int batch, int seqlen, int hkv, int d_qk, float rotary_fraction) {
+  const size_t t = table_bytes(seqlen, d_qk, rotary_fraction);
+  return t == 0 ? 0 : t + krot_bytes(batch, seqlen, hkv, d_qk, rotary_fraction);
+}
+
+// Builds the table (and, for the matrix-core kernels, the rotated K rows) on
+// the stream ahead of the attention kernel.
+hipError_t launch_rope_prep(AttnArgs& a, void* workspace, long long pos_offset, bool rotate_k,
+                            hipStream_t s) {
+  if (a.half == 0) return hipSuccess;
+  float2* table = static_cast<float2*>(workspace);
+  const size_t tb = round256((size_t)a.n * a.half * sizeof(float2));
+  uint16_t* krot = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + tb);
+  a.rope = table;
+  a.krot = krot;
+  hipError_t e = hswa::launch_rope_table(table, pos_offset, a.n, a.half, a.rope_theta, s);
+  if (e != hipSuccess || !rotate_k) return e;
+  return hswa::launch_rope_k(static_cast<const uint16_t*>(a.k), table, krot, a.B, a.n, a.hkv,
+                             a.d_qk, a.half, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,12 +122,14 @@ const char* hswa_last_error(void) { return g_last_error.c_str(); }
 
 const char* hswa_version(void) { return "hswa 0.1.0 (gfx950)"; }
 
-size_t hswa_prefill_workspace_size(int seqlen, int d_qk, float rotary_fraction) {
-  return table_bytes(seqlen, d_qk, rotary_fraction);
+size_t hswa_prefill_workspace_size(int batch, int seqlen, int hkv, int d_qk,
+                                   float rotary_fraction) {
+  return rope_workspace_bytes(batch, seqlen, hkv, d_qk, rotary_fraction);
 }
 
-size_t hswa_sparse_workspace_size(int seqlen, int d_qk, float rotary_fraction) {
-  return table_bytes(seqlen, d_qk, rotary_fraction);
+size_t hswa_sparse_workspace_size(int batch, int seqlen, int hkv, int d_qk,
+                                  float rotary_fraction) {
+  return rope_workspace_bytes(batch, seqlen, hkv, d_qk, rotary_fraction);
 }
 
 hswa_status_t swa_sink_prefill(const void* q, const void* k, const void* v, const float* sink,
@@ -116,7 +148,7 @@ hswa_status_t swa_sink_prefill(const void* q, const void* k, const void* v, cons
     return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v and o must be 16-byte aligned");
   if ((long long)batch * seqlen * hq * (long long)(d_qk > d_v ? d_qk : d_v) > (1LL << 56))
     return fail(HSWA_ERR_INVALID_ARGUMENT, "tensor too large");
-  const size_t need = table_bytes(seqlen, d_qk, rotary_fraction);
+  const size_t need = rope_workspace_bytes(batch, seqlen, hkv, d_qk, rotary_fraction);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_prefill_workspace_size()");
@@ -131,17 +163,15 @@ hswa_status_t swa_sink_prefill(const void* q, const void* k, const void* v, cons
   a.sink = sink;
   a.window = (window >= seqlen) ? 0 : window;
   a.pos_offset = pos_offset;
-  a.rope = static_cast<const float2*>(workspace);
 
   const bool use_mfma = (dtype == HSWA_BF16) && hswa::prefill_bf16_supported(a);
   if (!use_mfma && !generic_fits(d_qk, d_v))
     return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a.half > 0) {
-    hipError_t e = hswa::launch_rope_table(static_cast<float2*>(workspace), pos_offset, seqlen,
-                                           a.half, a.rope_theta, s);
-    if (e != hipSuccess) return hip_status(e, "rope table launch");
+  {
+    hipError_t e = launch_rope_prep(a, workspace, pos_offset, use_mfma, s);
+    if (e != hipSuccess) return hip_status(e, "rope preparation launch");
   }
   hipError_t e = use_mfma ? hswa::launch_prefill_bf16(a, s)
                           : hswa::launch_generic(a, hswa::MODE_PREFILL, dtype == HSWA_BF16, s);
@@ -216,14 +246,8 @@ hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_
     if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
     hswa::decode_split_plan(lay, window, max_pos, &a.split_keys, &a.nsplit);
     a.ws = static_cast<float*>(workspace);
-    // the (m, l) pairs follow the partial outputs, each region 256-byte aligned
-    const size_t per = (size_t)batch * hq * (size_t)a.nsplit;
-    const size_t obytes = round256(per * (size_t)d_v * sizeof(float));
-    if (obytes != per * (size_t)d_v * sizeof(float)) {
-      // keep the kernel's simple indexing: partial outputs fill their region exactly
-      // (d_v = 128 floats per entry makes every region a multiple of 512 bytes)
-      return fail(HSWA_ERR_UNSUPPORTED, "decode partial layout needs d_v * 4 to be a multiple of 256");
-    }
+    // the (m, l) pairs follow the partial outputs directly: with d_v = 128 each
+    // entry is 512 bytes, so the output region is already 256-byte aligned
     return hip_status(hswa::launch_decode_bf16(a, lay, s), "decode launch");
   }
   if (!generic_fits(d_qk, d_v)) return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
@@ -250,7 +274,7 @@ hswa_status_t sparse_sink_attn(const void* q, const void* k, const void* v, cons
     return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v, o, sel_idx and sel_count must be non-null");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v and o must be 16-byte aligned");
-  const size_t need = table_bytes(seqlen, d_qk, rotary_fraction);
+  const size_t need = rope_workspace_bytes(batch, seqlen, hkv, d_qk, rotary_fraction);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_sparse_workspace_size()");
@@ -268,16 +292,14 @@ hswa_status_t sparse_sink_attn(const void* q, const void* k, const void* v, cons
   a.max_sel = max_sel;
   a.recent = recent_window;
   a.pos_offset = pos_offset;
-  a.rope = static_cast<const float2*>(workspace);
 
   const bool use_mfma = (dtype == HSWA_BF16) && hswa::sparse_bf16_supported(a);
   if (!use_mfma && !generic_fits(d_qk, d_v))
     return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a.half > 0) {
-    hipError_t e = hswa::launch_rope_table(static_cast<float2*>(workspace), pos_offset, seqlen,
-                                           a.half, a.rope_theta, s);
-    if (e != hipSuccess) return hip_status(e, "rope table launch");
+  {
+    hipError_t e = launch_rope_prep(a, workspace, pos_offset, use_mfma, s);
+    if (e != hipSuccess) return hip_status(e, "rope preparation launch");
   }
   hipError_t e = use_mfma ? hswa::launch_sparse_bf16(a, s)
                           : hswa::launch_generic(a, hswa::MODE_SPARSE, dtype == HSWA_BF16, s);

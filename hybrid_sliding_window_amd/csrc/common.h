@@ -77,6 +77,18 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// gfx950 transposed LDS read of 4 x 16-bit values (ds_read_b64_tr_b16).
+// Within each group of 16 lanes, lane i receives element i % 4 of the 8
+// bytes addressed by lane 4k + i / 4, for k = 0..3.  With a row-major matrix
+// in LDS and lane j addressing M[r0 + j/4][c0 + 4 * (j % 4)], lane i gets the
+// column M[r0 + k][c0 + i], k = 0..3: the k-major operand layout of an MFMA.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_tr4(const void* p) {
+  typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
 // Max / sum across the four lanes l, l^16, l^32, l^48 (same column c).
 __device__ __forceinline__ float max_across_groups(float v) {
   v = fmaxf(v, __shfl_xor(v, 16));

@@ -20,6 +20,9 @@ template <>
 struct Elem<float> {
   static __device__ __forceinline__ float get(const float* p, long long i) { return p[i]; }
   static __device__ __forceinline__ void put(float* p, long long i, float x) { p[i] = x; }
+  static __device__ __forceinline__ void put_nan(float* p, long long i) {
+    reinterpret_cast<uint32_t*>(p)[i] = 0x7fc00000u;
+  }
 };
 template <>
 struct Elem<bf16_t> {
@@ -29,6 +32,7 @@ struct Elem<bf16_t> {
   static __device__ __forceinline__ void put(bf16_t* p, long long i, float x) {
     p[i] = f32_to_bf16_bits(x);
   }
+  static __device__ __forceinline__ void put_nan(bf16_t* p, long long i) { p[i] = 0x7fc0u; }
 };
 
 constexpr int kGenMaxPerLane = 4;  // dims per lane: 4 * 64 = 256
@@ -92,7 +96,7 @@ __global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
     kbase = off;
   }
   if (!ok) {
-    for (int d = lane; d < a.d_v; d += 64) Elem<T>::put(orow, d, __builtin_nanf(""));
+    for (int d = lane; d < a.d_v; d += 64) Elem<T>::put_nan(orow, d);
     return;
   }
 

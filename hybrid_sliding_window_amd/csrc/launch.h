@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace hswa {
 
@@ -19,6 +20,7 @@ struct AttnArgs {
   const long long* seq_offsets;   // decode contiguous: [B + 1]
   const long long* pos;           // decode: [B]
   const float2* rope;             // prefill / sparse: cos/sin table [n][half]
+  const void* krot;               // prefill / sparse bf16: K's first R dims, rotated [B, n, hkv, R]
   int B, n, hq, hkv, d_qk, d_v;
   int window;                     // prefill: 0 = full causal; decode: ring size or window
   int half;                       // R / 2 (0 = no RoPE)
@@ -34,6 +36,10 @@ struct AttnArgs {
 // cos/sin table: table[t][r] = (cos, sin)((pos0 + t) * theta^(-r/half)).
 hipError_t launch_rope_table(float2* table, long long pos0, int npos, int half, double theta,
                              hipStream_t stream);
+
+// krot[row][0:R] = RoPE of k[row][0:R] (bf16) for rows = B * n * hkv, token (row / hkv) % n.
+hipError_t launch_rope_k(const uint16_t* k, const float2* table, uint16_t* krot, int B, int n,
+                         int hkv, int d, int half, hipStream_t stream);
 
 // Any shape, any key set, fp32 or bf16 storage: one wavefront per query row.
 hipError_t launch_generic(const AttnArgs& a, int mode, bool bf16, hipStream_t stream);

@@ -1,0 +1,85 @@
+// Partial-RoPE preparation for a run of consecutive positions.
+//
+// "MiMo-V2.6-Flash hybrid SWA" (pwwt.cn), section 5: about a third of the
+// q/k dims rotate (partial_rotary_factor 0.334), with base 1e4 in SWA layers
+// and 1e7 in GA layers.  Pair r of R/2 turns by pos * theta^(-2r/R).
+//
+// Two kernels, run once per call:
+//  * rope_table_kernel: cos/sin of every (position, pair).  Angles reach
+//    2.6e5 rad for long contexts, where an fp32 product alone loses ~1e-2
+//    rad, so the angle is formed and evaluated in fp64 and rounded once.
+//  * rope_k_kernel: the first R dims of every K row, rotated and rounded to
+//    bf16 once.  Attention kernels read these instead of re-rotating a key
+//    for every query block whose window covers it.
+#include "common.h"
+#include "launch.h"
+
+namespace hswa {
+
+__global__ void rope_table_kernel(float2* __restrict__ table, long long pos0, int npos, int half,
+                                  double theta) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)npos * half) return;
+  const int r = (int)(idx % half);
+  const long long t = idx / half;
+  const double inv_freq = pow(theta, -(double)r / (double)half);
+  const double angle = (double)(pos0 + t) * inv_freq;
+  double s, c;
+  sincos(angle, &s, &c);
+  table[idx] = make_float2((float)c, (float)s);
+}
+
+// One thread per (K row, 8-dim chunk c < R/16): rotates dims 8c..8c+7 with
+// their partners R/2 further on and writes both to the rotated-K buffer
+// krot [rows, R].  rows = B * n * hkv; row t of token j uses table row j.
+__global__ void rope_k_kernel(const bf16_t* __restrict__ k, const float2* __restrict__ table,
+                              bf16_t* __restrict__ krot, long long rows, int n, int hkv, int d,
+                              int half) {
+  const int cpr = half >> 3;                   // chunk pairs per row
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * cpr) return;
+  const long long row = idx / cpr;
+  const int c = (int)(idx - row * cpr);
+  const long long j = (row / hkv) % n;         // token index of the row
+  const bf16_t* src = k + row * d;
+  float f0[8], f1[8];
+  unpack8(ld16(src + 8 * c), f0);
+  unpack8(ld16(src + 8 * c + half), f1);
+  const float2* t = table + j * half + 8 * c;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float2 cs = t[e];
+    const float y0 = f0[e] * cs.x - f1[e] * cs.y;
+    const float y1 = f1[e] * cs.x + f0[e] * cs.y;
+    f0[e] = y0;
+    f1[e] = y1;
+  }
+  bf16_t* dst = krot + row * (2 * half);
+  st16(dst + 8 * c, pack8(f0));
+  st16(dst + 8 * c + half, pack8(f1));
+}
+
+hipError_t launch_rope_table(float2* table, long long pos0, int npos, int half, double theta,
+                             hipStream_t stream) {
+  const long long total = (long long)npos * half;
+  if (total == 0) return hipSuccess;
+  const int threads = 256;
+  const long long blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, table,
+                     pos0, npos, half, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_k(const uint16_t* k, const float2* table, uint16_t* krot, int B, int n,
+                         int hkv, int d, int half, hipStream_t stream) {
+  const long long rows = (long long)B * n * hkv;
+  const long long total = rows * (half >> 3);
+  if (total == 0) return hipSuccess;
+  const int threads = 256;
+  const long long blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(rope_k_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, k, table,
+                     krot, rows, n, hkv, d, half);
+  return hipGetLastError();
+}
+
+}  // namespace hswa

@@ -11,7 +11,8 @@
 // list is the selected indices followed by the recent window; lanes 0..31
 // resolve the 32 key rows of a tile and hand them to the other lanes with
 // cross-lane reads.  K rows are gathered straight into A-operand registers
-// (rotated there when RoPE is on), V rows through a small LDS transpose.
+// (their rotated dims from the copy rotated once per call), V rows through a
+// small LDS transpose.
 // Workgroups are remapped so that consecutive queries of one kv head run on
 // one XCD and share the recent window in its L2.
 #include "common.h"
@@ -74,6 +75,8 @@ __global__ __launch_bounds__(64) void sparse_bf16_kernel(AttnArgs a) {
 
   const bf16_t* __restrict__ Kp = static_cast<const bf16_t*>(a.k);
   const bf16_t* __restrict__ Vp = static_cast<const bf16_t*>(a.v);
+  const bf16_t* __restrict__ Kr = static_cast<const bf16_t*>(a.krot);
+  const int R = 2 * a.half;
 
   // q of head g*G + c, rotated at position i and rounded once to bf16.
   bf16x8 qf[KS];
@@ -123,15 +126,18 @@ __global__ __launch_bounds__(64) void sparse_bf16_kernel(AttnArgs a) {
         myj = rlo + (t - cnt);
       }
     }
+    // K rows straight into A-operand registers; k-steps inside the rotated
+    // dims come from the rotated copy made once per call.
     uint4 kr[2][KS];
-    int jk[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      jk[sub] = __shfl(myj, sub * 16 + c);
-      if (jk[sub] >= 0) {
-        const bf16_t* kp = Kp + ((tokbase + jk[sub]) * a.hkv + g) * D + 8 * grp;
+      const int j = __shfl(myj, sub * 16 + c);
+      if (j >= 0) {
+        const long long row = (tokbase + j) * a.hkv + g;
+        const bf16_t* kp = Kp + row * D + 8 * grp;
+        const bf16_t* kq = Kr + row * R + 8 * grp;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[sub][ks] = ld16(kp + 32 * ks);
+        for (int ks = 0; ks < KS; ++ks) kr[sub][ks] = ld16((32 * ks < R) ? kq + 32 * ks : kp + 32 * ks);
       } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kr[sub][ks] = make_uint4(0, 0, 0, 0);
@@ -147,18 +153,6 @@ __global__ __launch_bounds__(64) void sparse_bf16_kernel(AttnArgs a) {
         const int j = __shfl(myj, 4 * kq + q4);
         vr[w][q4] = (j >= 0) ? ld16(Vp + ((tokbase + j) * a.hkv + g) * DV + 8 * dc)
                              : make_uint4(0, 0, 0, 0);
-      }
-    }
-    if (a.half > 0) {
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        if (jk[sub] < 0) continue;
-        float f[KS][8];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) unpack8(kr[sub][ks], f[ks]);
-        rotate_any(f, a.rope + (long long)jk[sub] * a.half, a.half, grp);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[sub][ks] = pack8(f[ks]);
       }
     }
 

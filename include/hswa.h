@@ -64,8 +64,11 @@ typedef enum { HSWA_F32 = 0, HSWA_BF16 = 1 } hswa_dtype_t;
 typedef enum { HSWA_KV_RING = 0, HSWA_KV_CONTIGUOUS = 1 } hswa_kv_layout_t;
 
 /* Bytes of workspace swa_sink_prefill / ga_prefill need: the cos/sin table
- * of the seqlen positions (seqlen * R/2 * 8 bytes, 0 without RoPE). */
-size_t hswa_prefill_workspace_size(int seqlen, int d_qk, float rotary_fraction);
+ * of the seqlen positions (seqlen * R/2 * 8 bytes) followed by a rotated copy
+ * of K's first R dims (batch * seqlen * hkv * R * 2 bytes), each rounded up
+ * to 256 bytes; 0 without RoPE. */
+size_t hswa_prefill_workspace_size(int batch, int seqlen, int hkv, int d_qk,
+                                   float rotary_fraction);
 
 /*
  * Sliding-window prefill with a sink: the SWA layer of rslog.cc section 4.4.
@@ -126,8 +129,10 @@ hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_
                               hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                               void* stream);
 
-/* Bytes of workspace sparse_sink_attn needs (the cos/sin table, 0 without RoPE). */
-size_t hswa_sparse_workspace_size(int seqlen, int d_qk, float rotary_fraction);
+/* Bytes of workspace sparse_sink_attn needs: same layout and size as
+ * hswa_prefill_workspace_size (0 without RoPE). */
+size_t hswa_sparse_workspace_size(int batch, int seqlen, int hkv, int d_qk,
+                                  float rotary_fraction);
 
 /*
  * Token-level sparse attention on one shared cache ("MiMo-V3 HySparse2"

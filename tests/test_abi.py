@@ -45,10 +45,12 @@ def test_version_string(lib):
 
 
 def test_workspace_sizes(lib):
-    # cos/sin table: seqlen * R/2 * 8 bytes, R = 64 at d = 192 and fraction 0.334
-    assert hswa.prefill_workspace_size(32768, 192, 0.334) == 32768 * 32 * 8
-    assert hswa.prefill_workspace_size(1000, 192, 0.0) == 0
-    assert hswa.sparse_workspace_size(100, 192, 0.334) == ((100 * 32 * 8 + 255) // 256) * 256
+    # cos/sin table (seqlen * R/2 * 8 bytes) then rotated K dims (B * n * hkv * R * 2 bytes),
+    # each rounded up to 256 bytes; R = 64 at d = 192 and fraction 0.334
+    assert hswa.prefill_workspace_size(1, 32768, 8, 192, 0.334) == 32768 * 32 * 8 + 32768 * 8 * 64 * 2
+    assert hswa.prefill_workspace_size(2, 1000, 4, 192, 0.0) == 0
+    r256 = lambda x: ((x + 255) // 256) * 256  # noqa: E731
+    assert hswa.sparse_workspace_size(1, 100, 3, 192, 0.334) == r256(100 * 32 * 8) + r256(100 * 3 * 64 * 2)
     # decode: fp32 partial (O, m, l) per (sequence, head, split)
     ring = hswa.decode_workspace_size(hswa.KV_RING, 64, 64, 128, 128, 262143)
     assert ring == 64 * 64 * 4 * 128 * 4 + ((64 * 64 * 4 * 2 * 4 + 255) // 256) * 256
