@@ -77,13 +77,25 @@ def timed(fn, steps, warmup):
     return wall, per
 
 
-def _traffic(kernel_key, launches_bytes):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if any."""
+def _traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary.
+
+    FETCH_SIZE and WRITE_SIZE were each taken in a run of their own and scaled
+    by what the same counters read for a plain 1 GiB copy.  The entry records
+    the hash of the kernel source it was measured on; once the source has
+    changed the figure no longer applies and None is returned."""
+    import hashlib
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-        return t.get(kernel_key)
-    except (OSError, ValueError):
+            entry = json.load(f).get(kernel_key)
+        if entry is None:
+            return None
+        src = os.path.join(ROOT, entry["source"])
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if not digest.startswith(entry["source_sha256_prefix"]):
+            return None
+        return entry["bytes"]
+    except (OSError, ValueError, KeyError):
         return None
 
 
@@ -296,7 +308,7 @@ def main():
                    "sink": "U(-2,2) per head", "useful_gflop_per_step": flops / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": _traffic("prefill_bf16_kernel:swa_prefill_n32768", alg_bytes),
+                     "traffic": _traffic("prefill_bf16_kernel:swa_prefill_n32768"),
                      "kernel": "prefill_bf16_kernel",
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "launch_ms": kern_s * 1e3,
