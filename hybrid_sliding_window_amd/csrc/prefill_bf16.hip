@@ -60,6 +60,18 @@ constexpr int VPITCH = DV * 2 + 32;    // V row pitch in LDS (bytes)
 constexpr int KBYTES = BK * KPITCH;    // 12800
 constexpr int VBYTES = BK * VPITCH;    // 9216
 constexpr int STAGE_BYTES = KBYTES + VBYTES;
+constexpr int OPITCH = DV * 2 + 16;    // output row pitch in LDS (bytes) for the store transpose
+constexpr int QSLOTS = D / 8 + 1;      // 16-byte slots per q row in LDS (400 B pitch, one pad)
+constexpr int QBYTES_W = 13 * 1024;    // per-wavefront q region: 32 rows x 25 slots -> 13 x 1 KB
+constexpr int SMEM_BYTES = (2 * STAGE_BYTES > 4 * QBYTES_W) ? 2 * STAGE_BYTES : 4 * QBYTES_W;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// 16 bytes per lane, global -> LDS at lds_base + 16 * lane (lds_base uniform).
+__device__ __forceinline__ void g2lds16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_base, 16, 0, 0);
+}
 constexpr int KCHUNKS = BK * (D / 8);   // 16-byte K chunks per tile: 768
 constexpr int VCHUNKS = BK * (DV / 8);  // 16-byte V chunks per tile: 512
 constexpr float kLazy = 8.f;
@@ -101,7 +113,7 @@ __global__ __launch_bounds__(512 / CB, 4 / CB) void prefill_bf16_kernel(AttnArgs
   constexpr int NTHREADS = 512 / CB;
   constexpr int KPER = (KCHUNKS + NTHREADS - 1) / NTHREADS;
   constexpr int VPER = VCHUNKS / NTHREADS;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -199,27 +211,41 @@ __global__ __launch_bounds__(512 / CB, 4 / CB) void prefill_bf16_kernel(AttnArgs
   const int tw1 = min(n - 1, i0 + ((wave * 16 * CB + 16 * CB - 1) >> log2g));
   const bool wave_live = tw0 < n;
 
-  // ---- q loads, then tile 0, then rotate q ---------------------------------
-  uint4 qraw[CB][KS];
+  // ---- q: straight into LDS, then tile 0, then operands and rotation ------
+  // Each wavefront's 32 q rows are four runs of 3 KB (G heads of one token
+  // are contiguous), so every 1 KB load instruction reads whole cache lines.
+  // Slot s of the wavefront's region holds row s / 25, chunk s % 25 (chunk
+  // 24 and slots past row 31 are padding, loaded from a valid address).
+  static_assert(CB == 2, "the q staging assumes 32 rows per wavefront");
+  unsigned char* qlds = smem + wave * QBYTES_W;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const bf16_t* qrow = Qp + ((tokbase + (rv[cb] ? tok[cb] : i0)) * a.hq + head[cb]) * D + 8 * grp;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qraw[cb][ks] = ld16(qrow + 32 * ks);
+  for (int i = 0; i < QBYTES_W / 1024; ++i) {
+    const int slot = 64 * i + lane;
+    const int rr = min(slot / QSLOTS, 31);
+    int ch = slot - (slot / QSLOTS) * QSLOTS;
+    if (ch >= D / 8 || slot >= 32 * QSLOTS) ch = 0;
+    const int r = wave * 32 + rr;
+    const int tk = min(i0 + (r >> log2g), n - 1);
+    const int hd = g * G + (r & (G - 1));
+    g2lds16(Qp + ((tokbase + tk) * a.hq + hd) * D + 8 * ch, qlds + 1024 * i);
   }
   load_tile(kstart);
 
   bf16x8 qf[CB][KS];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
+    uint4 qraw[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[cb][ks] = as_bf16x8(qraw[cb][ks]);
+    for (int ks = 0; ks < KS; ++ks) {
+      qraw[ks] = ld16(qlds + (cb * 16 + c) * (QSLOTS * 16) + (4 * ks + grp) * 16);
+      qf[cb][ks] = as_bf16x8(qraw[ks]);
+    }
     if (a.half > 0 && rv[cb]) {
       const float2* trow = a.rope + (long long)tok[cb] * a.half;
       switch (a.half >> 5) {
-        case 1: rotate_q<1>(qf[cb], qraw[cb], trow, grp); break;
-        case 2: rotate_q<2>(qf[cb], qraw[cb], trow, grp); break;
-        default: rotate_q<3>(qf[cb], qraw[cb], trow, grp); break;
+        case 1: rotate_q<1>(qf[cb], qraw, trow, grp); break;
+        case 2: rotate_q<2>(qf[cb], qraw, trow, grp); break;
+        default: rotate_q<3>(qf[cb], qraw, trow, grp); break;
       }
     }
   }
@@ -245,6 +271,7 @@ __global__ __launch_bounds__(512 / CB, 4 / CB) void prefill_bf16_kernel(AttnArgs
   const int koffA = c * KPITCH + grp * 16;                               // K row c, chunk grp
   const int voffA = KBYTES + (4 * grp + (c >> 2)) * VPITCH + 8 * (c & 3);  // transpose origin
 
+  __syncthreads();   // every wavefront has its q operands; the region becomes stage 0
   store_tile(0);
   if (ntiles > 1) load_tile(kstart + BK);
 
@@ -347,19 +374,37 @@ __global__ __launch_bounds__(512 / CB, 4 / CB) void prefill_bf16_kernel(AttnArgs
   }
 
   // ---- epilogue: o = O / l, rounded to bf16 -----------------------------
-  float lt[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) lt[cb] = __shfl(lacc[cb][0], c);   // from lane (grp 0, c)
+  // The O^T fragments go through LDS (the staging buffers are free once
+  // every wavefront has left the loop) so that the global stores are 16 bytes
+  // per lane and each instruction covers four whole 256-byte rows.
+  float inv[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    if (!rv[cb]) continue;
-    const float inv = (lt[cb] > 0.f) ? 1.f / lt[cb] : 0.f;
-    bf16_t* orow = Op + ((tokbase + tok[cb]) * a.hq + head[cb]) * DV + 4 * grp;
+    const float lt = __shfl(lacc[cb][0], c);   // row sum sits in lane (grp 0, c)
+    inv[cb] = (lt > 0.f) ? 1.f / lt : 0.f;
+  }
+  __syncthreads();
+  unsigned char* obuf = smem + wave * (16 * CB) * OPITCH;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const uint2 w = make_uint2(pack_bf16x2(acc[cb][t][0] * inv, acc[cb][t][1] * inv),
-                                 pack_bf16x2(acc[cb][t][2] * inv, acc[cb][t][3] * inv));
-      st8(orow + 16 * t, w);
+      const uint2 w = make_uint2(pack_bf16x2(acc[cb][t][0] * inv[cb], acc[cb][t][1] * inv[cb]),
+                                 pack_bf16x2(acc[cb][t][2] * inv[cb], acc[cb][t][3] * inv[cb]));
+      st8(obuf + (cb * 16 + c) * OPITCH + (16 * t + 4 * grp) * 2, w);
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int i = 0; i < CB * 16 * (DV / 8) / 64; ++i) {
+    const int idx = lane + 64 * i;
+    const int rr = idx >> 4, ch = idx & 15;       // row of this wavefront, 16-byte chunk
+    const int r = wave * 16 * CB + rr;
+    const int tk = i0 + (r >> log2g);
+    if (tk < n) {
+      const int hd = g * G + (r & (G - 1));
+      st16(Op + ((tokbase + tk) * a.hq + hd) * DV + 8 * ch, ld16(obuf + rr * OPITCH + 16 * ch));
     }
   }
 }
