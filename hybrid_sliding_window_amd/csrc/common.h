@@ -11,6 +11,8 @@ namespace hswa {
 typedef uint16_t bf16_t;                                     // raw bfloat16 bits
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));   // MFMA operand
 typedef float f32x4 __attribute__((ext_vector_type(4)));     // 16x16 MFMA accumulator
+typedef float f32x16 __attribute__((ext_vector_type(16)));   // 32x32 MFMA accumulator
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -73,6 +75,20 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
 // rows 4*g .. 4*g+3 of column c.
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D = A * B + C on the 32x32x16 bf16 matrix core.  With lane l = 32*h + i:
+// A holds row i, k = 8h .. 8h+7; B holds column i, k = 8h .. 8h+7; element
+// v of D is row 8*(v/4) + 4*h + v%4 of column i.  On gfx950 it sustains
+// twice the flops per cycle of the 16x16x32 form.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// c + lo + hi of a packed bf16 pair, in fp32 (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float c) {
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, c, false);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
