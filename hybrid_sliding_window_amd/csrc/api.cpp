@@ -188,6 +188,9 @@ hswa_status_t ga_prefill(const void* q, const void* k, const void* v, void* o, i
                           workspace_bytes, stream);
 }
 
+// Query dims the bf16 decode kernel handles (its rotated-q buffer size).
+constexpr size_t kDecodeQDims = 192;
+
 size_t hswa_decode_workspace_size(hswa_kv_layout_t layout, int batch, int hq, int d_v, int window,
                                   long long max_pos) {
   if (batch <= 0 || hq <= 0 || d_v <= 0 || max_pos < 0) return 0;
@@ -196,7 +199,8 @@ size_t hswa_decode_workspace_size(hswa_kv_layout_t layout, int batch, int hq, in
   int split_keys = 0, nsplit = 0;
   hswa::decode_split_plan(layout == HSWA_KV_RING ? 0 : 1, window, max_pos, &split_keys, &nsplit);
   const size_t per = (size_t)batch * hq * (size_t)nsplit;
-  return round256(per * (size_t)d_v * sizeof(float)) + round256(per * 2 * sizeof(float));
+  return round256(per * (size_t)d_v * sizeof(float)) + round256(per * 2 * sizeof(float)) +
+         round256((size_t)batch * hq * kDecodeQDims * 2);
 }
 
 hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -247,7 +251,11 @@ hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_
     hswa::decode_split_plan(lay, window, max_pos, &a.split_keys, &a.nsplit);
     a.ws = static_cast<float*>(workspace);
     // the (m, l) pairs follow the partial outputs directly: with d_v = 128 each
-    // entry is 512 bytes, so the output region is already 256-byte aligned
+    // entry is 512 bytes, so the output region is already 256-byte aligned;
+    // the rotated queries follow the (m, l) region
+    const size_t per = (size_t)batch * hq * (size_t)a.nsplit;
+    a.qrot = static_cast<unsigned char*>(workspace) + round256(per * (size_t)d_v * sizeof(float)) +
+             round256(per * 2 * sizeof(float));
     return hip_status(hswa::launch_decode_bf16(a, lay, s), "decode launch");
   }
   if (!generic_fits(d_qk, d_v)) return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");

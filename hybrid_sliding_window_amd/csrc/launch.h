@@ -21,6 +21,7 @@ struct AttnArgs {
   const long long* pos;           // decode: [B]
   const float2* rope;             // prefill / sparse: cos/sin table [n][half]
   const void* krot;               // prefill / sparse bf16: K's first R dims, rotated [B, n, hkv, R]
+  void* qrot;                     // decode bf16: q rotated to pos[b] [B, hq, d_qk] (workspace)
   int B, n, hq, hkv, d_qk, d_v;
   int window;                     // prefill: 0 = full causal; decode: ring size or window
   int half;                       // R / 2 (0 = no RoPE)

@@ -96,7 +96,8 @@ hswa_status_t ga_prefill(const void* q, const void* k, const void* v, void* o, i
                          void* stream);
 
 /* Bytes of workspace swa_sink_decode needs for `batch` sequences whose
- * positions are all <= max_pos (split partial results, fp32). */
+ * positions are all <= max_pos: split partial results (fp32), then the
+ * query rotated to its position (bf16, 192 dims per head). */
 size_t hswa_decode_workspace_size(hswa_kv_layout_t layout, int batch, int hq, int d_v,
                                   int window, long long max_pos);
 

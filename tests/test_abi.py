@@ -51,11 +51,14 @@ def test_workspace_sizes(lib):
     assert hswa.prefill_workspace_size(2, 1000, 4, 192, 0.0) == 0
     r256 = lambda x: ((x + 255) // 256) * 256  # noqa: E731
     assert hswa.sparse_workspace_size(1, 100, 3, 192, 0.334) == r256(100 * 32 * 8) + r256(100 * 3 * 64 * 2)
-    # decode: fp32 partial (O, m, l) per (sequence, head, split)
+    # decode: fp32 partial (O, m, l) per (sequence, head, split), then q rotated
+    # to its position (bf16, 192 dims); the ring splits 128 keys in 4, a
+    # 262144-key prefix in 64 splits of 4096
+    qrot = 64 * 64 * 192 * 2
     ring = hswa.decode_workspace_size(hswa.KV_RING, 64, 64, 128, 128, 262143)
-    assert ring == 64 * 64 * 4 * 128 * 4 + ((64 * 64 * 4 * 2 * 4 + 255) // 256) * 256
+    assert ring == 64 * 64 * 4 * 128 * 4 + r256(64 * 64 * 4 * 2 * 4) + qrot
     contig = hswa.decode_workspace_size(hswa.KV_CONTIGUOUS, 64, 64, 128, 0, 262143)
-    assert contig == 64 * 64 * 256 * 128 * 4 + 64 * 64 * 256 * 2 * 4
+    assert contig == 64 * 64 * 64 * 128 * 4 + 64 * 64 * 64 * 2 * 4 + qrot
     assert hswa.decode_workspace_size(hswa.KV_RING, 64, 64, 128, 0, 10) == 0
 
 
