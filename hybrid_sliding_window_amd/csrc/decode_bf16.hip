@@ -7,20 +7,19 @@
 // sequence).  Decode reads the whole cache once per step, so the kernel is a
 // stream over K and V at HBM rate.
 //
-// Split-K.  A wavefront owns (sequence b, kv head g, split s) and reads
-// `split_keys` consecutive keys of that sequence, 32 per tile.  The four
-// wavefronts of a workgroup take four neighbouring kv heads of the same
-// keys, so together they read whole cache rows ([row][kv head][dim]) rather
-// than one head's stripe of each.  Its G query
-// heads form the N side of 16x16x32 MFMAs (S^T = K . Q^T, then
-// O^T += V^T . P^T).  K fragments go from HBM straight into registers in
-// the A operand layout and V into LDS (global_load_lds), from where the PV
-// product reads V^T with ds_read_b64_tr_b16.  A wavefront waits for its
-// tile before computing it; the latency is hidden by occupancy instead:
-// at 128 VGPRs and 9 KB of LDS each, four wavefronts per SIMD keep a tile
-// each in flight while others compute.  The query arrives rotated to its
-// position by a small preparation kernel, so no fp64 work (or its
-// registers) sits in this one.  Each split leaves an
+// Split-K.  A workgroup owns (sequence b, four neighbouring kv heads, split
+// s) and reads `split_keys` consecutive keys of that sequence, 16 per tile.
+// The cache rows are [row][kv head][dim], so the four heads' K (4 x 384 B)
+// and V (4 x 256 B) of a row are contiguous: the workgroup streams whole
+// row runs into LDS with global_load_lds, each 1 KB load instruction
+// covering 1 KB of contiguous cache, and a wavefront then takes its own
+// head's stripe from LDS.  Two LDS stages: tile t+1 is requested before tile
+// t is computed.  Rows are stored unpadded with an XOR swizzle (applied on
+// the global side of the copy) so that the MFMA operand reads hit distinct
+// banks.  Per wavefront, the G query heads of its kv head form the N side of
+// the MFMAs: S^T = K . Q^T on the 16x16x32 form, then O^T += V^T . P^T on
+// the 16x16x16 form, whose k-index matches the key order S^T leaves in a
+// lane, with V^T read by ds_read_b64_tr_b16.  Each split leaves an
 // unnormalised partial (m, l, O) in base 2 in the workspace.
 //
 // Combine.  Per (b, h): M = max(sink, m_s), denominator
@@ -39,11 +38,16 @@ constexpr int D = 192;
 constexpr int DV = 128;
 constexpr int KS = D / 32;
 constexpr int NT = DV / 16;
-constexpr int BK = 32;
-constexpr int VPITCH = DV * 2 + 32;       // V row pitch in LDS (bytes): conflict-free transposed reads
-constexpr int VSLOTS = VPITCH / 16;       // 18 16-byte slots per row (16 data + 2 pad)
-constexpr int VINSTR = BK * VSLOTS / 64;  // 9 load instructions of 1 KB per tile
-constexpr int VSTAGE = VINSTR * 1024;
+constexpr int BK = 16;                    // keys per tile
+constexpr int HG = 4;                     // kv heads per workgroup (one per wavefront)
+constexpr int KROW = HG * D * 2;          // 1536 B: the group's K of one cache row
+constexpr int VROW = HG * DV * 2;         // 1024 B: its V
+constexpr int KTILE = BK * KROW;          // 24 KB
+constexpr int VTILE = BK * VROW;          // 16 KB
+constexpr int KINSTR = KTILE / 1024;      // 24 load instructions of 1 KB
+constexpr int VINSTR = VTILE / 1024;      // 16
+constexpr int DMA_PER_WAVE = (KINSTR + VINSTR) / HG;   // 10
+static_assert((KINSTR + VINSTR) % HG == 0 && KINSTR % HG == 0, "even split of the loads");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -97,56 +101,76 @@ __global__ __launch_bounds__(64) void decode_rope_q_kernel(AttnArgs a, int layou
   }
 }
 
-__global__ __launch_bounds__(256, 3) void decode_split_kernel(AttnArgs a, int layout) {
-  __shared__ __attribute__((aligned(16))) unsigned char vstages[4 * VSTAGE];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
-  const int g = 4 * blockIdx.x + wave, s = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, c = lane & 15, grp = lane >> 4;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256, 2) void decode_split_kernel(AttnArgs a, int layout) {
+  __shared__ __attribute__((aligned(16))) unsigned char kst0[KTILE];
+  __shared__ __attribute__((aligned(16))) unsigned char vst0[VTILE];
+  __shared__ __attribute__((aligned(16))) unsigned char kst1[KTILE];
+  __shared__ __attribute__((aligned(16))) unsigned char vst1[VTILE];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
+  const int gx = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+  const int g = HG * gx + wave;
+  const int lane = tid & 63, c = lane & 15, grp = lane >> 4;
   const int G = a.hq / a.hkv;
-  if (g >= a.hkv) return;   // no workgroup barrier below: wavefronts are independent
-  unsigned char* vstage = vstages + wave * VSTAGE;
 
   long long p, row0, len;
-  if (!key_range(a, layout, b, &p, &row0, &len)) return;
+  if (!key_range(a, layout, b, &p, &row0, &len)) return;   // uniform over the workgroup
   const long long ks0 = (long long)s * a.split_keys;
   if (ks0 >= len) return;
   const long long ks1 = (ks0 + a.split_keys < len) ? ks0 + a.split_keys : len;
-  const int ntile = (int)((ks1 - ks0 + BK - 1) / BK);
-
-  // Split-relative addressing: the split's first row is a wave-uniform base
-  // and a key's offset, below split_keys * hkv * D elements, fits 32 bits.
   const int nkeys = (int)(ks1 - ks0);
-  const bf16_t* __restrict__ Kb =
-      static_cast<const bf16_t*>(a.k) + ((row0 + ks0) * a.hkv + g) * (long long)D;
-  const bf16_t* __restrict__ Vb =
-      static_cast<const bf16_t*>(a.v) + ((row0 + ks0) * a.hkv + g) * (long long)DV;
-  const int kstride = a.hkv * D, vstride = a.hkv * DV;   // elements from one key to the next
+  const int ntile = (nkeys + BK - 1) / BK;
 
-  // K fragments of the tile at key k0: keys k0 + 16 sub + c (clamped into the
-  // split; the extra keys are masked), 8 dims at 32 ks + 8 grp.
-  auto load_k = [&](int k0, uint4 (&kr)[2][KS]) {
+  // ---- this lane's 16-byte slots of a tile ------------------------------------
+  // Load instruction ii = wave + 4u fills LDS bytes [1024 ii', +1024) of the
+  // K stage (ii < 24, ii' = ii) or the V stage (ii' = ii - 24).  K slot s is
+  // row s / 96, physical chunk pc = s % 96 holding logical chunk pc ^ row%16
+  // (XOR on the low four bits, within its aligned 256 B); V slot s is row
+  // s / 64, physical 32-byte unit (s % 64) / 2 holding logical unit
+  // unit ^ row%8.  Rows past the split reload its last key (masked later).
+  const unsigned char* kbase = static_cast<const unsigned char*>(a.k) +
+                               (((row0 + ks0) * a.hkv + HG * gx) * (long long)D) * 2;
+  const unsigned char* vbase = static_cast<const unsigned char*>(a.v) +
+                               (((row0 + ks0) * a.hkv + HG * gx) * (long long)DV) * 2;
+  const int kstride = a.hkv * D * 2, vstride = a.hkv * DV * 2;   // bytes per cache row
+  int drow[DMA_PER_WAVE], doff[DMA_PER_WAVE];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int key = min(k0 + sub * 16 + c, nkeys - 1);
-      const bf16_t* kp = Kb + (key * kstride + 8 * grp);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kr[sub][ks] = ld16(kp + 32 * ks);
-    }
-  };
-  // V tile at key k0 into an LDS stage: instruction ii, lane -> slot
-  // 64 ii + lane = (row / 18, chunk % 18); pad chunks reload chunk 0.
-  auto load_v = [&](int k0, unsigned char* st) {
-#pragma unroll
-    for (int ii = 0; ii < VINSTR; ++ii) {
+  for (int u = 0; u < DMA_PER_WAVE; ++u) {
+    const int ii = wave + HG * u;
+    if (ii < KINSTR) {
       const int sl = 64 * ii + lane;
-      const int row = sl / VSLOTS;
-      int ch = sl - row * VSLOTS;
-      if (ch >= DV / 8) ch = 0;
-      const int key = min(k0 + row, nkeys - 1);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(Vb + (key * vstride + 8 * ch)),
-                                       (lds_void_t*)(st + 1024 * ii), 16, 0, 0);
+      const int row = sl / 96, pc = sl - row * 96;
+      drow[u] = row;
+      doff[u] = 16 * (pc ^ (row & 15));
+    } else {
+      const int sl = 64 * (ii - KINSTR) + lane;
+      const int row = sl >> 6, pc = sl & 63;
+      drow[u] = row;
+      doff[u] = 32 * ((pc >> 1) ^ (row & 7)) + 16 * (pc & 1);
+    }
+  }
+  // Addresses are a wave-uniform base plus a 32-bit per-lane offset (a
+  // split spans at most split_keys * hkv * 384 bytes, and key and row
+  // stride both fit 24 bits), the saddr form of the load: one 24-bit
+  // multiply-add per instruction.
+  auto issue = [&](int k0, unsigned char* kd, unsigned char* vd) {
+#pragma unroll
+    for (int u = 0; u < DMA_PER_WAVE; ++u) {
+      const int ii = wave + HG * u;
+      const int key = min(k0 + drow[u], nkeys - 1);
+      if (u < KINSTR / HG)   // wave-uniform: the first six instructions are K, the rest V
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(kbase + (__umul24(key, kstride) + doff[u])),
+                                         (lds_void_t*)(kd + 1024 * ii), 16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(vbase + (__umul24(key, vstride) + doff[u])),
+                                         (lds_void_t*)(vd + 1024 * (ii - KINSTR)), 16, 0, 0);
     }
   };
+  static_assert(KINSTR / HG == 6, "the K/V split of a wavefront's loads");
+
+  issue(0, kst0, vst0);
 
   // q of head g*G + c (rotated to position p by the preparation kernel when
   // RoPE is on); columns c >= G are padding.
@@ -158,6 +182,7 @@ __global__ __launch_bounds__(256, 3) void decode_split_kernel(AttnArgs a, int la
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = as_bf16x8(c < G ? ld16(qrow + 32 * ks) : make_uint4(0, 0, 0, 0));
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): q and tile 0 have landed
 
   const float c2 = a.scale * kLog2e;   // raw score -> base-2 units
   float m = kNegInf, l = 0.f;
@@ -165,63 +190,67 @@ __global__ __launch_bounds__(256, 3) void decode_split_kernel(AttnArgs a, int la
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // transpose origin of the V^T operand: key 4 grp + c / 4, column 4 (c % 4)
-  const int voff = (4 * grp + (c >> 2)) * VPITCH + 8 * (c & 3);
+  // per-lane LDS offsets: K row c, logical chunk 24 wave + 4 ks + grp; the
+  // transposed V read of lane (c, grp): row 4 grp + c/4, bytes 8 (c%4) of the
+  // logical 32-byte unit 8 wave + tt
+  const int krow = c * KROW;
+  const int vr = 4 * grp + (c >> 2);
+  const int vrow = vr * VROW + 8 * (c & 3);
 
-  for (int t = 0; t < ntile; ++t) {
+  auto tile = [&](int t, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
+                  unsigned char* vn) __attribute__((always_inline)) {
+    // Tile t's loads are this wavefront's only ones in flight.  The wait is
+    // explicit: the compiler does not reliably carry a pending LDS-DMA
+    // write across the loop back-edge into the barrier's fence.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();   // every wavefront's share of tile t has landed; tile t-1 is consumed
+    if (t + 1 < ntile) issue((t + 1) * BK, kn, vn);
     const int k0 = t * BK;
-    uint4 kc[2][KS];
-    load_v(k0, vstage);   // the previous tile's V reads have completed
-    load_k(k0, kc);
-    f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      sc[0] = mfma16(as_bf16x8(kc[0][ks]), qf[ks], sc[0]);
-      sc[1] = mfma16(as_bf16x8(kc[1][ks]), qf[ks], sc[1]);
+      const int q = 24 * wave + 4 * ks + grp;
+      sc = mfma16(as_bf16x8(ld16(kc + krow + 16 * (q ^ c))), qf[ks], sc);
     }
-    if (k0 + BK > nkeys) {
+    // Branch-free on purpose: the first VALU read of an MFMA result needs
+    // wait states after it, and with a branch between them the compiler
+    // did not insert them on the path that skips the branch body.
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (k0 + sub * 16 + 4 * grp + r >= nkeys) sc[sub][r] = kNegInf;
-    }
-
-    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    for (int r = 0; r < 4; ++r) sc[r] = (k0 + 4 * grp + r < nkeys) ? sc[r] : kNegInf;
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = max_across_groups(mx) * c2;   // base-2 units
     const float mn = fmaxf(m, mx);
     const float ms = (mn == kNegInf) ? 0.f : mn;
     const float alpha = fast_exp2(m - ms);
-    float pv[8];
+    float pv[4];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pv[sub * 4 + r] = fast_exp2(fmaf(sc[sub][r], c2, -ms));
-    const uint4 pk = pack8(pv);
+    for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(fmaf(sc[r], c2, -ms));
+    const uint2 pk = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
     // l sums the bf16 P that weight V
-    float ps = add_bf16_pair(pk.x, 0.f);
-    ps = add_bf16_pair(pk.y, ps);
-    ps = add_bf16_pair(pk.z, ps);
-    ps = add_bf16_pair(pk.w, ps);
-    l = l * alpha + ps;
+    l = l * alpha + add_bf16_pair(pk.y, add_bf16_pair(pk.x, 0.f));
     m = mn;
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[tt] *= alpha;
-    const bf16x8 pb = as_bf16x8(pk);
-
-    // -- O^T += V^T . P^T (keys 4 grp + r and 16 + 4 grp + r, as P^T holds them)
-    const unsigned char* vb = vstage + voff;
+    const v4i16 pb = __builtin_bit_cast(v4i16, pk);
+    // -- O^T += V^T . P^T: lane (c, grp) holds keys 4 grp + r, the k-index of
+    //    the 16x16x16 form; the transposed read gives V[4 grp + r][16 tt + c]
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
-      const uint2 lo = lds_tr4(vb + 32 * tt);
-      const uint2 hi = lds_tr4(vb + 16 * VPITCH + 32 * tt);
-      acc[tt] = mfma16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, acc[tt]);
+      const uint2 vt = lds_tr4(vc + vrow + 32 * ((8 * wave + tt) ^ (vr & 7)));
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, vt), pb,
+                                                         acc[tt], 0, 0, 0);
     }
+  };
+
+  int t = 0;
+  for (; t + 2 <= ntile; t += 2) {
+    tile(t, kst0, vst0, kst1, vst1);
+    tile(t + 1, kst1, vst1, kst0, vst0);
   }
+  if (t < ntile) tile(t, kst0, vst0, kst1, vst1);
 
   l = sum_across_groups(l);
-  if (c < G) {
+  if (g < a.hkv && c < G) {
     const long long idx = ((long long)b * a.hq + g * G + c) * a.nsplit + s;
     float* wo = a.ws + idx * DV + 4 * grp;
 #pragma unroll
@@ -268,7 +297,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(AttnArgs a, int layo
 
 bool decode_bf16_supported(const AttnArgs& a) {
   const int G = a.hq / a.hkv;
-  return a.d_qk == D && a.d_v == DV && G >= 1 && G <= 16 && 2 * a.half <= D;
+  return a.d_qk == D && a.d_v == DV && G >= 1 && G <= 16 && a.hkv % HG == 0 && 2 * a.half <= D;
 }
 
 // Keys per split and splits per (sequence, kv head).  Short key sets (the
@@ -305,7 +334,7 @@ hipError_t launch_decode_bf16(const AttnArgs& a, int layout, hipStream_t stream)
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  dim3 g1((unsigned)((a.hkv + 3) / 4), (unsigned)a.nsplit, (unsigned)a.B);
+  dim3 g1((unsigned)(a.hkv / HG), (unsigned)a.nsplit, (unsigned)a.B);
   hipLaunchKernelGGL(decode_split_kernel, g1, dim3(256), 0, stream, a, layout);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

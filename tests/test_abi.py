@@ -95,7 +95,7 @@ def test_prefill_validation(lib):
 def test_decode_validation(lib):
     def call(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, layout=0, offs=None, pos=FAKE, sink=None, o=FAKE, batch=2,
-                 hq=4, hkv=2, d_qk=192, d_v=128, window=128, max_pos=1000, scale=0.0, theta=1e4,
+                 hq=8, hkv=4, d_qk=192, d_v=128, window=128, max_pos=1000, scale=0.0, theta=1e4,
                  frac=0.0, dtype=1, ws=None, ws_bytes=0, stream=None)
         a.update(kw)
         return lib.swa_sink_decode(*a.values())

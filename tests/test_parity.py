@@ -343,6 +343,11 @@ def test_hybrid_decode_full_size(gpu_lib):
     og = gpu_lib.swa_sink_decode(c["q"], c["k"], c["v"], c["pos"], wl["pos_range"][1],
                                  layout=gpu_lib.KV_CONTIGUOUS, seq_offsets=c["seq_offsets"],
                                  window=0)
+    # bitwise repeatable: every tile is read only after its loads have landed
+    og2 = gpu_lib.swa_sink_decode(c["q"], c["k"], c["v"], c["pos"], wl["pos_range"][1],
+                                  layout=gpu_lib.KV_CONTIGUOUS, seq_offsets=c["seq_offsets"],
+                                  window=0)
+    assert torch.equal(og, og2)
     offs = c["seq_offsets"].cpu().numpy()
     seqs = np.array([int(pos.argmin()), int(pos.argmax()), 17])
 
