@@ -308,8 +308,9 @@ def main():
                    "sink": "U(-2,2) per head", "useful_gflop_per_step": flops / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": _traffic("prefill_bf16_kernel:swa_prefill_n32768"),
-                     "kernel": "prefill_bf16_kernel",
+                     "traffic": _traffic("prefill_persist_kernel:swa_prefill_n32768"),
+                     "kernel": "prefill_persist_kernel",
+                     "launch_scope": "one swa_sink_prefill call: RoPE prep kernels + prefill kernel",
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "launch_ms": kern_s * 1e3,
                      "frac_of_bf16_mfma_peak": value / BF16_PEAK_TFLOPS},

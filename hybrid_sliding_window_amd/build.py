@@ -21,8 +21,13 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhswa.so")
 ARCH = os.environ.get("HSWA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "rope_prep.hip", "generic.hip", "prefill_bf16.hip", "decode_bf16.hip",
-           "sparse_bf16.hip"]
+SOURCES = ["api.cpp", "rope_prep.hip", "generic.hip", "prefill_bf16.hip", "prefill_persist.hip",
+           "decode_bf16.hip", "sparse_bf16.hip"]
+
+# Per-source flags.  The persistent prefill runs one wavefront per SIMD and
+# keeps its accumulators in ordinary VGPRs (the VALU rescales them in place);
+# without this the allocator parks them in AGPRs and copies them every tile.
+EXTRA_FLAGS = {"prefill_persist.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fno-honor-nans",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -38,7 +43,8 @@ def _hipcc():
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc()] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([_hipcc()] + FLAGS + EXTRA_FLAGS.get(src, []) + lang +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(line for line in res.stderr.splitlines() if noise not in line)

@@ -173,8 +173,9 @@ hswa_status_t swa_sink_prefill(const void* q, const void* k, const void* v, cons
     hipError_t e = launch_rope_prep(a, workspace, pos_offset, use_mfma, s);
     if (e != hipSuccess) return hip_status(e, "rope preparation launch");
   }
-  hipError_t e = use_mfma ? hswa::launch_prefill_bf16(a, s)
-                          : hswa::launch_generic(a, hswa::MODE_PREFILL, dtype == HSWA_BF16, s);
+  hipError_t e = !use_mfma ? hswa::launch_generic(a, hswa::MODE_PREFILL, dtype == HSWA_BF16, s)
+                 : hswa::prefill_persist_supported(a) ? hswa::launch_prefill_persist(a, s)
+                                                      : hswa::launch_prefill_bf16(a, s);
   return hip_status(e, "prefill launch");
 }
 

@@ -49,6 +49,12 @@ hipError_t launch_generic(const AttnArgs& a, int mode, bool bf16, hipStream_t st
 bool prefill_bf16_supported(const AttnArgs& a);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
 
+// Persistent variant of the bf16 prefill for GQA groups >= 8, rotary
+// half-widths 0, 16 or 32 and at most 256 q heads: one workgroup per CU
+// streams its items' K/V tiles and next q block while it computes.
+bool prefill_persist_supported(const AttnArgs& a);
+hipError_t launch_prefill_persist(const AttnArgs& a, hipStream_t stream);
+
 bool decode_bf16_supported(const AttnArgs& a);
 void decode_split_plan(int layout, int window, long long max_pos, int* split_keys, int* nsplit);
 hipError_t launch_decode_bf16(const AttnArgs& a, int layout, hipStream_t stream);

@@ -104,6 +104,34 @@ def test_ga_prefill_bf16(gpu_lib, B, n, hq, hkv):
     _check(f"ga bf16 B={B} n={n} {hq}/{hkv}", o, ref)
 
 
+@pytest.mark.parametrize("B,n,hq,hkv,window,frac,sink", [
+    (2, 611, 64, 8, 128, 0.334, True),    # items of two sequences in one stream
+    (1, 403, 64, 2, 33, 0.334, True),     # G = 32, window not a multiple of the tile
+    (1, 77, 128, 1, 128, 0.17, True),     # G = 128 (one token per block), R = 32
+    (1, 500, 64, 8, 128, 0.0, False),     # no RoPE, no sink
+    (3, 129, 32, 4, 1, 0.334, True),      # one-token window
+    (1, 960, 16, 2, 300, 0.17, False),    # window wider than the 32-key tile stream start
+])
+def test_persistent_prefill_shapes(gpu_lib, B, n, hq, hkv, window, frac, sink):
+    """Shapes routed to the persistent prefill (G >= 8, R in {0, 32, 64})."""
+    x = _prefill_case(B, n, hq, hkv, "bf16", 90 + n, sink_range=(-2.0, 2.0) if sink else None)
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=window,
+                                 rope_theta=1.0e4, rotary_fraction=frac, pos_offset=17)
+    q, k, v, s = _host(x)
+    ref = oracle.swa_sink_prefill(q, k, v, s, window=window, rope_theta=1.0e4,
+                                  rotary_fraction=frac, pos_offset=17)
+    _check(f"persistent B={B} n={n} {hq}/{hkv} W={window} R/2={int(frac * 96)}", o, ref)
+
+
+@pytest.mark.parametrize("B,n,hq,hkv", [(3, 250, 64, 8), (1, 515, 128, 4)])
+def test_persistent_ga_shapes(gpu_lib, B, n, hq, hkv):
+    x = _prefill_case(B, n, hq, hkv, "bf16", 95 + n, sink_range=None)
+    o = gpu_lib.ga_prefill(x["q"], x["k"], x["v"], rope_theta=1.0e7, rotary_fraction=0.334)
+    q, k, v, _ = _host(x)
+    ref = oracle.ga_prefill(q, k, v, rope_theta=1.0e7, rotary_fraction=0.334)
+    _check(f"persistent ga B={B} n={n} {hq}/{hkv}", o, ref)
+
+
 @pytest.mark.parametrize("frac", [0.0, 2.0 / 3.0, 1.0])
 def test_prefill_rotary_widths(gpu_lib, frac):
     """R = 0, 128 and 192 rotated dims (the MFMA path pairs r with r + R/2 in lane)."""
