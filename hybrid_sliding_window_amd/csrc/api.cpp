@@ -99,15 +99,21 @@ size_t rope_workspace_bytes(int batch, int seqlen, int hkv, int d_qk, float rota
 }
 
 // Builds the table (and, for the matrix-core kernels, the rotated K rows) on
-// the stream ahead of the attention kernel.
+// the stream ahead of the attention kernel.  Without need_table (kernels that
+// rotate q themselves) only the rotated K rows are built, by one kernel that
+// evaluates its own cos/sin.
 hipError_t launch_rope_prep(AttnArgs& a, void* workspace, long long pos_offset, bool rotate_k,
-                            hipStream_t s) {
+                            bool need_table, hipStream_t s) {
   if (a.half == 0) return hipSuccess;
   float2* table = static_cast<float2*>(workspace);
   const size_t tb = round256((size_t)a.n * a.half * sizeof(float2));
   uint16_t* krot = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + tb);
   a.rope = table;
   a.krot = krot;
+  if (rotate_k && !need_table) {
+    return hswa::launch_rope_k_direct(static_cast<const uint16_t*>(a.k), krot, a.B, a.n, a.hkv,
+                                      a.d_qk, a.half, pos_offset, a.rope_theta, s);
+  }
   hipError_t e = hswa::launch_rope_table(table, pos_offset, a.n, a.half, a.rope_theta, s);
   if (e != hipSuccess || !rotate_k) return e;
   return hswa::launch_rope_k(static_cast<const uint16_t*>(a.k), table, krot, a.B, a.n, a.hkv,
@@ -170,7 +176,8 @@ hswa_status_t swa_sink_prefill(const void* q, const void* k, const void* v, cons
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   {
-    hipError_t e = launch_rope_prep(a, workspace, pos_offset, use_mfma, s);
+    hipError_t e = launch_rope_prep(a, workspace, pos_offset, use_mfma,
+                                    !(use_mfma && hswa::prefill_persist_supported(a)), s);
     if (e != hipSuccess) return hip_status(e, "rope preparation launch");
   }
   hipError_t e = !use_mfma ? hswa::launch_generic(a, hswa::MODE_PREFILL, dtype == HSWA_BF16, s)
@@ -307,7 +314,7 @@ hswa_status_t sparse_sink_attn(const void* q, const void* k, const void* v, cons
     return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
   hipStream_t s = static_cast<hipStream_t>(stream);
   {
-    hipError_t e = launch_rope_prep(a, workspace, pos_offset, use_mfma, s);
+    hipError_t e = launch_rope_prep(a, workspace, pos_offset, use_mfma, true, s);
     if (e != hipSuccess) return hip_status(e, "rope preparation launch");
   }
   hipError_t e = use_mfma ? hswa::launch_sparse_bf16(a, s)

@@ -42,6 +42,11 @@ hipError_t launch_rope_table(float2* table, long long pos0, int npos, int half, 
 hipError_t launch_rope_k(const uint16_t* k, const float2* table, uint16_t* krot, int B, int n,
                          int hkv, int d, int half, hipStream_t stream);
 
+// The same without a table: cos/sin evaluated per element (fp64 angle in
+// revolutions, reduced, hardware sine/cosine).  Requires half <= 64.
+hipError_t launch_rope_k_direct(const uint16_t* k, uint16_t* krot, int B, int n, int hkv, int d,
+                                int half, long long pos0, double theta, hipStream_t stream);
+
 // Any shape, any key set, fp32 or bf16 storage: one wavefront per query row.
 hipError_t launch_generic(const AttnArgs& a, int mode, bool bf16, hipStream_t stream);
 

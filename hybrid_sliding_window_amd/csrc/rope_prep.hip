@@ -59,6 +59,44 @@ __global__ void rope_k_kernel(const bf16_t* __restrict__ k, const float2* __rest
   st16(dst + 8 * c + half, pack8(f1));
 }
 
+// The same rotation of K without a table, for attention kernels that also
+// rotate q without one: the pair's frequency theta^(-r/half) (fp64, once per
+// block into LDS) times the position gives the angle in revolutions in fp64,
+// which is reduced to [0, 1) before the hardware sine and cosine (which take
+// revolutions) evaluate it in fp32.
+constexpr int kMaxHalf = 64;
+__global__ void rope_k_direct_kernel(const bf16_t* __restrict__ k, bf16_t* __restrict__ krot,
+                                     long long rows, int n, int hkv, int d, int half,
+                                     long long pos0, double theta) {
+  __shared__ double rev[kMaxHalf];
+  if ((int)threadIdx.x < half)
+    rev[threadIdx.x] = pow(theta, -(double)threadIdx.x / (double)half) * 0.15915494309189535;
+  __syncthreads();
+  const int cpr = half >> 3;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * cpr) return;
+  const long long row = idx / cpr;
+  const int c = (int)(idx - row * cpr);
+  const double pos = (double)(pos0 + (row / hkv) % n);
+  const bf16_t* src = k + row * d;
+  float f0[8], f1[8];
+  unpack8(ld16(src + 8 * c), f0);
+  unpack8(ld16(src + 8 * c + half), f1);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const double turns = pos * rev[8 * c + e];
+    const float f = (float)(turns - floor(turns));
+    const float co = __builtin_amdgcn_cosf(f), si = __builtin_amdgcn_sinf(f);
+    const float y0 = f0[e] * co - f1[e] * si;
+    const float y1 = f1[e] * co + f0[e] * si;
+    f0[e] = y0;
+    f1[e] = y1;
+  }
+  bf16_t* dst = krot + row * (2 * half);
+  st16(dst + 8 * c, pack8(f0));
+  st16(dst + 8 * c + half, pack8(f1));
+}
+
 hipError_t launch_rope_table(float2* table, long long pos0, int npos, int half, double theta,
                              hipStream_t stream) {
   const long long total = (long long)npos * half;
@@ -79,6 +117,19 @@ hipError_t launch_rope_k(const uint16_t* k, const float2* table, uint16_t* krot,
   const long long blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(rope_k_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, k, table,
                      krot, rows, n, hkv, d, half);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_k_direct(const uint16_t* k, uint16_t* krot, int B, int n, int hkv, int d,
+                                int half, long long pos0, double theta, hipStream_t stream) {
+  const long long rows = (long long)B * n * hkv;
+  const long long total = rows * (half >> 3);
+  if (total == 0) return hipSuccess;
+  if (half > kMaxHalf) return hipErrorInvalidValue;
+  const int threads = 256;
+  const long long blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(rope_k_direct_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, k,
+                     krot, rows, n, hkv, d, half, pos0, theta);
   return hipGetLastError();
 }
 
