@@ -163,6 +163,22 @@ def secondary(steps, warmup, parts=("ga", "decode", "sparse")):
     return out
 
 
+def measured_peaks(steps, warmup):
+    """On-box reference rates next to the spec peaks: a large bf16 GEMM
+    (hipBLASLt through torch.matmul; dense, no sparsity) and a plain device
+    copy of 1 GiB."""
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    c = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    _, per = timed(lambda: torch.matmul(a, b, out=c), steps, warmup)
+    t = float(np.median(per)) / 1e3
+    gemm = 2 * 8192 ** 3 / t / 1e12
+    del a, b, c
+    copy = copy_calibration(steps, warmup)
+    return {"bf16_gemm_8192_tflops": gemm, "copy_1gib_gbps_read_plus_write": copy["gbps_read_plus_write"],
+            "spec_bf16_tflops": BF16_PEAK_TFLOPS, "spec_hbm_gbps": HBM_PEAK_GBPS}
+
+
 def _ga(out, steps, warmup, dev):
     # GA prefill, n = 32768, 64 q / 4 kv heads, full causal
     wl = synthetic.WORKLOADS["ga_prefill_n32768"]
@@ -177,6 +193,7 @@ def _ga(out, steps, warmup, dev):
     flops = window_pairs(wl["n"], 0) * wl["hq"] * FLOP_PER_PAIR
     t = float(np.mean(per)) / 1e3
     out["ga_prefill_n32768"] = {"tflops": flops / t / 1e12, "ms": t * 1e3,
+                                "ms_median": float(np.median(per)), "ms_min": float(np.min(per)),
                                 "frac_of_bf16_peak": flops / t / 1e12 / BF16_PEAK_TFLOPS}
     _log(f"GA prefill {out['ga_prefill_n32768']}")
 
@@ -313,6 +330,8 @@ def main():
                      "launch_scope": "one swa_sink_prefill call: RoPE prep kernels + prefill kernel",
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "launch_ms": kern_s * 1e3,
+                     "launch_ms_median": float(np.median(per)),
+                     "launch_ms_min": float(np.min(per)),
                      "frac_of_bf16_mfma_peak": value / BF16_PEAK_TFLOPS},
     }
     if args.only:
@@ -325,6 +344,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_secondary:
         rec["secondary"] = secondary(args.steps, args.warmup)
+        rec["measured_peaks"] = measured_peaks(args.steps, args.warmup)
+        _log(f"measured peaks {rec['measured_peaks']}")
     print(json.dumps(rec), flush=True)
 
 
