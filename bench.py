@@ -14,8 +14,9 @@ Printed as one JSON line, with
   * cpu_baseline: the fp64 oracle timed on a bounded row sample of the same
     workload on the host cores;
   * secondary: the siblings measured the same way (GA prefill TFLOP/s,
-    hybrid decode HBM GB/s for the ring and contiguous caches, sparse
-    prefill TFLOP/s).
+    16K-token prefill chunks behind empty and long cached prefixes, hybrid
+    decode HBM GB/s for the ring and contiguous caches, sparse prefill
+    TFLOP/s).
 """
 
 import argparse
@@ -147,15 +148,17 @@ def copy_calibration(steps, warmup):
 def only(which, steps, warmup):
     if which == "copy":
         return {"copy": copy_calibration(steps, warmup)}
-    parts = {"ga": ["ga"], "decode": ["decode"], "sparse": ["sparse"]}[which]
+    parts = {"ga": ["ga"], "chunk": ["chunk"], "decode": ["decode"], "sparse": ["sparse"]}[which]
     return secondary(steps, warmup, parts)
 
 
-def secondary(steps, warmup, parts=("ga", "decode", "sparse")):
+def secondary(steps, warmup, parts=("ga", "chunk", "decode", "sparse")):
     out = {}
     dev = "cuda"
     if "ga" in parts:
         _ga(out, steps, warmup, dev)
+    if "chunk" in parts:
+        _chunk(out, steps, warmup, dev)
     if "decode" in parts:
         _decode(out, dev)
     if "sparse" in parts:
@@ -196,6 +199,38 @@ def _ga(out, steps, warmup, dev):
                                 "ms_median": float(np.median(per)), "ms_min": float(np.min(per)),
                                 "frac_of_bf16_peak": flops / t / 1e12 / BF16_PEAK_TFLOPS}
     _log(f"GA prefill {out['ga_prefill_n32768']}")
+
+
+def _chunk(out, steps, warmup, dev):
+    # Chunked prefill: one 16384-token chunk behind a cached prefix; the SWA
+    # layer's cost does not depend on the prefix, the GA layer's grows with it
+    for name in ("swa_chunk_q16384_prefix1048576", "ga_chunk_q16384_prefix114688"):
+        wl = synthetic.WORKLOADS[name]
+        res = {}
+        for prefix in (0, wl["kv_len"] - wl["q_len"]):
+            kv = prefix + wl["q_len"]
+            x = synthetic.chunk_inputs(1, wl["q_len"], kv, wl["hq"], wl["hkv"], 192, 128, "bf16",
+                                       wl["seed"], dev, wl["sink_range"])
+            ws = torch.empty(hswa.prefill_workspace_size(1, kv, wl["hkv"], 192,
+                                                         wl["rotary_fraction"]),
+                             dtype=torch.uint8, device=dev)
+            o = torch.empty(1, wl["q_len"], wl["hq"], 128, dtype=torch.bfloat16, device=dev)
+            fn = lambda: hswa.swa_sink_prefill_chunk(  # noqa: E731
+                x["q"], x["k"], x["v"], x["sink"], window=wl["window"],
+                rope_theta=wl["rope_theta"], rotary_fraction=wl["rotary_fraction"], out=o,
+                workspace=ws)
+            _, per = timed(fn, max(3, steps // 4), 1)
+            p = np.arange(prefix, kv, dtype=np.int64)
+            pairs = int((np.minimum(p + 1, wl["window"]) if wl["window"] > 0 else p + 1).sum())
+            flops = pairs * wl["hq"] * FLOP_PER_PAIR
+            t = float(np.median(per)) / 1e3
+            res[f"prefix_{prefix}"] = {"ms_median": t * 1e3, "tflops": flops / t / 1e12,
+                                       "tokens_per_s": wl["q_len"] / t}
+            del x, ws, o
+        lo, hi = res["prefix_0"], res[f"prefix_{wl['kv_len'] - wl['q_len']}"]
+        res["tokens_per_s_ratio_long_vs_empty_prefix"] = hi["tokens_per_s"] / lo["tokens_per_s"]
+        out[name] = res
+        _log(f"{name} {res}")
 
 
 def _decode(out, dev):
@@ -270,7 +305,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["prefill", "ga", "decode", "sparse", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "ga", "chunk", "decode", "sparse", "copy"], default=None,
                     help="run one workload only (for profiler runs); prints its figures as JSON")
     args = ap.parse_args()
     if args.gpus != 1:

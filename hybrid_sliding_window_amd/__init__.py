@@ -20,5 +20,6 @@ from ._binding import (  # noqa: F401
     sparse_workspace_size,
     swa_sink_decode,
     swa_sink_prefill,
+    swa_sink_prefill_chunk,
     version,
 )

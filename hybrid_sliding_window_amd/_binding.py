@@ -21,6 +21,8 @@ _SIGNATURES = {
     "hswa_prefill_workspace_size": (_sz, [_i, _i, _i, _i, _f]),
     "swa_sink_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _f, _f,
                               _ll, _i, _vp, _sz, _vp]),
+    "swa_sink_prefill_chunk": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f,
+                                    _f, _f, _ll, _i, _vp, _sz, _vp]),
     "ga_prefill": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _f, _ll, _i, _vp, _sz,
                         _vp]),
     "hswa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i, _ll]),
@@ -138,6 +140,28 @@ def swa_sink_prefill(q, k, v, sink=None, window=128, scale=0.0, rope_theta=10000
     st = lib.swa_sink_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(o), B, n, hq, hkv, dqk,
                               dv, window, scale, rope_theta, rotary_fraction, pos_offset,
                               _dtype_code(q), _ptr(ws), 0 if ws is None else ws.numel(), _stream(q))
+    _raise(st)
+    return o
+
+
+def swa_sink_prefill_chunk(q, k, v, sink=None, window=128, scale=0.0, rope_theta=10000.0,
+                           rotary_fraction=0.0, pos_offset=0, out=None, workspace=None):
+    """The last q_len positions of sequences of kv_len tokens (a chunk behind a
+    cached prefix): q [B,q_len,Hq,d_qk], k [B,kv_len,Hkv,d_qk],
+    v [B,kv_len,Hkv,d_v] -> o [B,q_len,Hq,d_v].  window=0 with sink=None is
+    the GA layer's chunk."""
+    lib = load()
+    B, nq, hq, dqk = q.shape
+    n, hkv, dv = k.shape[1], k.shape[2], v.shape[3]
+    sink = _sink(sink, q)
+    o = out if out is not None else torch.empty((B, nq, hq, dv), dtype=q.dtype, device=q.device)
+    _check_same(q, k, v, o)
+    need = lib.hswa_prefill_workspace_size(B, n, hkv, dqk, rotary_fraction)
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    st = lib.swa_sink_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(o), B, nq, n, hq,
+                                    hkv, dqk, dv, window, scale, rope_theta, rotary_fraction,
+                                    pos_offset, _dtype_code(q), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(q))
     _raise(st)
     return o
 

@@ -66,6 +66,8 @@ AttnArgs base_args(int batch, int n, int hq, int hkv, int d_qk, int d_v, float s
   AttnArgs a{};
   a.B = batch;
   a.n = n;
+  a.nq = n;
+  a.qoff = 0;
   a.hq = hq;
   a.hkv = hkv;
   a.d_qk = d_qk;
@@ -101,9 +103,11 @@ size_t rope_workspace_bytes(int batch, int seqlen, int hkv, int d_qk, float rota
 // Builds the table (and, for the matrix-core kernels, the rotated K rows) on
 // the stream ahead of the attention kernel.  Without need_table (kernels that
 // rotate q themselves) only the rotated K rows are built, by one kernel that
-// evaluates its own cos/sin.
-hipError_t launch_rope_prep(AttnArgs& a, void* workspace, long long pos_offset, bool rotate_k,
-                            bool need_table, hipStream_t s) {
+// evaluates its own cos/sin.  Only positions first..n-1 are prepared: no
+// query of the call reads a key before `first` (a chunk behind a long
+// prefix in a windowed layer).
+hipError_t launch_rope_prep(AttnArgs& a, void* workspace, long long pos_offset, int first,
+                            bool rotate_k, bool need_table, hipStream_t s) {
   if (a.half == 0) return hipSuccess;
   float2* table = static_cast<float2*>(workspace);
   const size_t tb = round256((size_t)a.n * a.half * sizeof(float2));
@@ -111,13 +115,74 @@ hipError_t launch_rope_prep(AttnArgs& a, void* workspace, long long pos_offset, 
   a.rope = table;
   a.krot = krot;
   if (rotate_k && !need_table) {
-    return hswa::launch_rope_k_direct(static_cast<const uint16_t*>(a.k), krot, a.B, a.n, a.hkv,
-                                      a.d_qk, a.half, pos_offset, a.rope_theta, s);
+    return hswa::launch_rope_k_direct(static_cast<const uint16_t*>(a.k), krot, a.B, a.n, first,
+                                      a.hkv, a.d_qk, a.half, pos_offset, a.rope_theta, s);
   }
-  hipError_t e = hswa::launch_rope_table(table, pos_offset, a.n, a.half, a.rope_theta, s);
+  hipError_t e = hswa::launch_rope_table(table + (size_t)first * a.half, pos_offset + first,
+                                         a.n - first, a.half, a.rope_theta, s);
   if (e != hipSuccess || !rotate_k) return e;
-  return hswa::launch_rope_k(static_cast<const uint16_t*>(a.k), table, krot, a.B, a.n, a.hkv,
-                             a.d_qk, a.half, s);
+  return hswa::launch_rope_k(static_cast<const uint16_t*>(a.k), table, krot, a.B, a.n, first,
+                             a.hkv, a.d_qk, a.half, s);
+}
+
+// Prefill of the last q_len tokens of sequences of kv_len tokens (q_len ==
+// kv_len: the whole sequence).  Query token t sits at sequence position
+// kv_len - q_len + t.
+hswa_status_t prefill_impl(const void* q, const void* k, const void* v, const float* sink, void* o,
+                           int batch, int q_len, int kv_len, int hq, int hkv, int d_qk, int d_v,
+                           int window, float scale, float rope_theta, float rotary_fraction,
+                           long long pos_offset, hswa_dtype_t dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  hswa_status_t st =
+      check_common(batch, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction, dtype);
+  if (st != HSWA_OK) return st;
+  if (kv_len < 0 || q_len < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "lengths must be >= 0");
+  if (q_len > kv_len) return fail(HSWA_ERR_INVALID_ARGUMENT, "q_len must not exceed kv_len");
+  if (window < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "window must be >= 0 (0 = full causal)");
+  if (batch == 0 || q_len == 0) return ok();
+  if (!q || !k || !v || !o) return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-null");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v and o must be 16-byte aligned");
+  if ((long long)batch * kv_len * hq * (long long)(d_qk > d_v ? d_qk : d_v) > (1LL << 56))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "tensor too large");
+  const size_t need = rope_workspace_bytes(batch, kv_len, hkv, d_qk, rotary_fraction);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_prefill_workspace_size()");
+    if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  }
+
+  AttnArgs a = base_args(batch, kv_len, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction);
+  a.nq = q_len;
+  a.qoff = kv_len - q_len;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.sink = sink;
+  a.window = (window >= kv_len) ? 0 : window;
+  a.pos_offset = pos_offset;
+
+  // the per-block bf16 kernel covers whole sequences only; chunks of the
+  // shapes it serves run on the generic kernel
+  const bool persist = (dtype == HSWA_BF16) && hswa::prefill_persist_supported(a);
+  const bool per_block = !persist && (dtype == HSWA_BF16) && q_len == kv_len &&
+                         hswa::prefill_bf16_supported(a);
+  const bool use_mfma = persist || per_block;
+  if (!use_mfma && !generic_fits(d_qk, d_v))
+    return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  {
+    // first key position any query of the call reads
+    const int first = (a.window > 0 && a.qoff - a.window + 1 > 0) ? a.qoff - a.window + 1 : 0;
+    hipError_t e = launch_rope_prep(a, workspace, pos_offset, first, use_mfma, !persist, s);
+    if (e != hipSuccess) return hip_status(e, "rope preparation launch");
+  }
+  hipError_t e = persist     ? hswa::launch_prefill_persist(a, s)
+                 : per_block ? hswa::launch_prefill_bf16(a, s)
+                             : hswa::launch_generic(a, hswa::MODE_PREFILL, dtype == HSWA_BF16, s);
+  return hip_status(e, "prefill launch");
 }
 
 }  // namespace
@@ -143,47 +208,21 @@ hswa_status_t swa_sink_prefill(const void* q, const void* k, const void* v, cons
                                int d_v, int window, float scale, float rope_theta,
                                float rotary_fraction, long long pos_offset, hswa_dtype_t dtype,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  hswa_status_t st =
-      check_common(batch, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction, dtype);
-  if (st != HSWA_OK) return st;
   if (seqlen < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "seqlen must be >= 0");
-  if (window < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "window must be >= 0 (0 = full causal)");
-  if (batch == 0 || seqlen == 0) return ok();
-  if (!q || !k || !v || !o) return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v and o must be non-null");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v and o must be 16-byte aligned");
-  if ((long long)batch * seqlen * hq * (long long)(d_qk > d_v ? d_qk : d_v) > (1LL << 56))
-    return fail(HSWA_ERR_INVALID_ARGUMENT, "tensor too large");
-  const size_t need = rope_workspace_bytes(batch, seqlen, hkv, d_qk, rotary_fraction);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need)
-      return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_prefill_workspace_size()");
-    if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-  }
+  return prefill_impl(q, k, v, sink, o, batch, seqlen, seqlen, hq, hkv, d_qk, d_v, window, scale,
+                      rope_theta, rotary_fraction, pos_offset, dtype, workspace, workspace_bytes,
+                      stream);
+}
 
-  AttnArgs a = base_args(batch, seqlen, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction);
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.sink = sink;
-  a.window = (window >= seqlen) ? 0 : window;
-  a.pos_offset = pos_offset;
-
-  const bool use_mfma = (dtype == HSWA_BF16) && hswa::prefill_bf16_supported(a);
-  if (!use_mfma && !generic_fits(d_qk, d_v))
-    return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  {
-    hipError_t e = launch_rope_prep(a, workspace, pos_offset, use_mfma,
-                                    !(use_mfma && hswa::prefill_persist_supported(a)), s);
-    if (e != hipSuccess) return hip_status(e, "rope preparation launch");
-  }
-  hipError_t e = !use_mfma ? hswa::launch_generic(a, hswa::MODE_PREFILL, dtype == HSWA_BF16, s)
-                 : hswa::prefill_persist_supported(a) ? hswa::launch_prefill_persist(a, s)
-                                                      : hswa::launch_prefill_bf16(a, s);
-  return hip_status(e, "prefill launch");
+hswa_status_t swa_sink_prefill_chunk(const void* q, const void* k, const void* v,
+                                     const float* sink, void* o, int batch, int q_len,
+                                     int kv_len, int hq, int hkv, int d_qk, int d_v, int window,
+                                     float scale, float rope_theta, float rotary_fraction,
+                                     long long pos_offset, hswa_dtype_t dtype, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return prefill_impl(q, k, v, sink, o, batch, q_len, kv_len, hq, hkv, d_qk, d_v, window, scale,
+                      rope_theta, rotary_fraction, pos_offset, dtype, workspace, workspace_bytes,
+                      stream);
 }
 
 hswa_status_t ga_prefill(const void* q, const void* k, const void* v, void* o, int batch,
@@ -314,7 +353,7 @@ hswa_status_t sparse_sink_attn(const void* q, const void* k, const void* v, cons
     return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
   hipStream_t s = static_cast<hipStream_t>(stream);
   {
-    hipError_t e = launch_rope_prep(a, workspace, pos_offset, use_mfma, true, s);
+    hipError_t e = launch_rope_prep(a, workspace, pos_offset, 0, use_mfma, true, s);
     if (e != hipSuccess) return hip_status(e, "rope preparation launch");
   }
   hipError_t e = use_mfma ? hswa::launch_sparse_bf16(a, s)

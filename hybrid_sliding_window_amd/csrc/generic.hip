@@ -49,7 +49,7 @@ __global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
   const int lane = threadIdx.x;
   const long long row = blockIdx.x;
   const int h = (int)(row % a.hq);
-  const long long outer = row / a.hq;          // prefill/sparse: b*n + i; decode: b
+  const long long outer = row / a.hq;          // prefill: b*nq + t; sparse: b*n + i; decode: b
   const int G = a.hq / a.hkv;
   const int g = h / G;
   const T* q = static_cast<const T*>(a.q);
@@ -58,12 +58,17 @@ __global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
   T* o = static_cast<T*>(a.o);
   const int R = 2 * a.half;
 
-  long long b, i = 0;
+  long long b, i = 0;   // i: sequence position of the query (prefill / sparse)
   const T* qrow;
-  if (MODE == MODE_PREFILL || MODE == MODE_SPARSE) {
+  if (MODE == MODE_PREFILL) {
+    // query token t of a chunk sits at position qoff + t
+    b = outer / a.nq;
+    i = a.qoff + outer % a.nq;
+    qrow = q + row * (long long)a.d_qk;
+  } else if (MODE == MODE_SPARSE) {
     b = outer / a.n;
     i = outer % a.n;
-    qrow = q + ((b * a.n + i) * a.hq + h) * (long long)a.d_qk;
+    qrow = q + row * (long long)a.d_qk;
   } else {
     b = outer;
     qrow = q + (b * a.hq + h) * (long long)a.d_qk;
@@ -185,9 +190,9 @@ __global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
 
 template <typename T>
 static hipError_t launch_t(const AttnArgs& a, int mode, hipStream_t stream) {
-  long long rows = (mode == MODE_PREFILL || mode == MODE_SPARSE)
-                       ? (long long)a.B * a.n * a.hq
-                       : (long long)a.B * a.hq;
+  long long rows = (mode == MODE_PREFILL)  ? (long long)a.B * a.nq * a.hq
+                   : (mode == MODE_SPARSE) ? (long long)a.B * a.n * a.hq
+                                           : (long long)a.B * a.hq;
   if (rows == 0) return hipSuccess;
   dim3 grid((unsigned)rows), block(64);
   switch (mode) {

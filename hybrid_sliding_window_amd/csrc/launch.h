@@ -22,7 +22,9 @@ struct AttnArgs {
   const float2* rope;             // prefill / sparse: cos/sin table [n][half]
   const void* krot;               // prefill / sparse bf16: K's first R dims, rotated [B, n, hkv, R]
   void* qrot;                     // decode bf16: q rotated to pos[b] [B, hq, d_qk] (workspace)
-  int B, n, hq, hkv, d_qk, d_v;
+  int B, n, hq, hkv, d_qk, d_v;   // n: tokens of K/V (and q unless chunked)
+  int nq;                         // prefill: query tokens per sequence (n unless chunked)
+  int qoff;                       // prefill: sequence position of query token 0 (n - nq)
   int window;                     // prefill: 0 = full causal; decode: ring size or window
   int half;                       // R / 2 (0 = no RoPE)
   int max_sel, recent;            // sparse
@@ -38,14 +40,16 @@ struct AttnArgs {
 hipError_t launch_rope_table(float2* table, long long pos0, int npos, int half, double theta,
                              hipStream_t stream);
 
-// krot[row][0:R] = RoPE of k[row][0:R] (bf16) for rows = B * n * hkv, token (row / hkv) % n.
+// krot[row][0:R] = RoPE of k[row][0:R] (bf16) for the rows [B, n, hkv] of
+// tokens first..n-1 (token (row / hkv) % n); other rows are not written.
 hipError_t launch_rope_k(const uint16_t* k, const float2* table, uint16_t* krot, int B, int n,
-                         int hkv, int d, int half, hipStream_t stream);
+                         int first, int hkv, int d, int half, hipStream_t stream);
 
 // The same without a table: cos/sin evaluated per element (fp64 angle in
 // revolutions, reduced, hardware sine/cosine).  Requires half <= 64.
-hipError_t launch_rope_k_direct(const uint16_t* k, uint16_t* krot, int B, int n, int hkv, int d,
-                                int half, long long pos0, double theta, hipStream_t stream);
+hipError_t launch_rope_k_direct(const uint16_t* k, uint16_t* krot, int B, int n, int first,
+                                int hkv, int d, int half, long long pos0, double theta,
+                                hipStream_t stream);
 
 // Any shape, any key set, fp32 or bf16 storage: one wavefront per query row.
 hipError_t launch_generic(const AttnArgs& a, int mode, bool bf16, hipStream_t stream);

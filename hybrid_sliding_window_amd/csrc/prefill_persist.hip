@@ -205,9 +205,13 @@ __device__ __forceinline__ void rotate_q(u32x4 (&qf)[KS], const double* rev, dou
   }
 }
 
-// One item: kv head g of sequence b, query tokens [i0, i0 + T).
+// One item: kv head g of sequence b, the query tokens at sequence positions
+// [i0, i0 + T).  The queries are the last nq of the n positions (qoff =
+// n - nq), so the q / o row of position p is qbase + p and the K / V row of
+// key position j is kbase + j.
 struct Item {
-  long long tokbase;   // b * n
+  long long kbase;   // b * n
+  long long qbase;   // b * nq - qoff
   int g, i0, kstart, kend, ntiles;
 };
 
@@ -217,8 +221,9 @@ __device__ __forceinline__ Item make_item(const AttnArgs& a, int k, int nblk, in
   const int blk = k - bg * nblk;
   const int b = bg / a.hkv;
   it.g = bg - b * a.hkv;
-  it.tokbase = (long long)b * a.n;
-  it.i0 = blk * T;
+  it.kbase = (long long)b * a.n;
+  it.qbase = (long long)b * a.nq - a.qoff;
+  it.i0 = a.qoff + blk * T;
   it.kstart = (a.window > 0) ? max(0, it.i0 - a.window + 1) : 0;
   it.kend = min(a.n, it.i0 + T);
   it.ntiles = (it.kend - it.kstart + BK - 1) / BK;
@@ -327,7 +332,7 @@ __global__ __launch_bounds__(512, 1) void prefill_persist_kernel(AttnArgs a, int
     if (tile_wave) {
       const int j0 = pc.kstart + pt * BK;
       const int lim = pc.kend - 1 - j0;
-      const long long rb = (pc.tokbase + j0) * hkv + pc.g;
+      const long long rb = (pc.kbase + j0) * hkv + pc.g;
       const bf16_t* kb = Kp + rb * D;
       const bf16_t* rbp = Kr + rb * R;
       const bf16_t* vb = Vp + rb * DV;
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(512, 1) void prefill_persist_kernel(AttnArgs a, int
   const int qrow0 = qsl0 / 24, qpc0 = qsl0 - qrow0 * 24;
   auto issue_q = [&](const Item& c, int part) {
     if (!tile_wave) {
-      const bf16_t* qb = Qp + ((c.tokbase + c.i0) * hq + c.g * G) * (long long)D;
+      const bf16_t* qb = Qp + ((c.qbase + c.i0) * hq + c.g * G) * (long long)D;
       const int tlim = n - 1 - c.i0;
       int row = qrow0 + (QCOPY * 32 / 3) * part, pc = qpc0;   // QCOPY copies = QCOPY * 32 / 3 rows
 #pragma unroll
@@ -567,7 +572,7 @@ __global__ __launch_bounds__(512, 1) void prefill_persist_kernel(AttnArgs a, int
     const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
     if (tw0 < n) {   // the wavefront's first row is a real token: 8 stores issued
       if (rv) {
-        bf16_t* orow = Op + ((c.tokbase + tok) * hq + head) * DV + 16 * h;
+        bf16_t* orow = Op + ((c.qbase + tok) * hq + head) * DV + 16 * h;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           float f[16];
@@ -595,7 +600,7 @@ hipError_t launch_prefill_persist(const AttnArgs& a, hipStream_t stream) {
   int log2g = 0;
   while ((1 << log2g) < G) ++log2g;
   const int T = ROWS >> log2g;
-  const int nblk = (a.n + T - 1) / T;
+  const int nblk = (a.nq + T - 1) / T;
   const long long items = (long long)a.B * a.hkv * nblk;
   if (items == 0) return hipSuccess;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;

@@ -29,18 +29,31 @@ __global__ void rope_table_kernel(float2* __restrict__ table, long long pos0, in
   table[idx] = make_float2((float)c, (float)s);
 }
 
+// Row `u` of the rows of tokens first..n-1 of every sequence (B * (n -
+// first) * hkv of them) is row kv_row of K and krot, of token j.
+__device__ __forceinline__ void tail_row(long long u, int n, int first, int hkv,
+                                         long long* kv_row, long long* j) {
+  const long long per_seq = (long long)(n - first) * hkv;
+  const long long b = u / per_seq;
+  const long long rem = u - b * per_seq;
+  *kv_row = (b * n + first) * hkv + rem;
+  *j = first + rem / hkv;
+}
+
 // One thread per (K row, 8-dim chunk c < R/16): rotates dims 8c..8c+7 with
 // their partners R/2 further on and writes both to the rotated-K buffer
-// krot [rows, R].  rows = B * n * hkv; row t of token j uses table row j.
+// krot [B * n * hkv, R].  Only the rows of tokens first..n-1 are written
+// (rows = B * (n - first) * hkv); token j uses table row j.
 __global__ void rope_k_kernel(const bf16_t* __restrict__ k, const float2* __restrict__ table,
-                              bf16_t* __restrict__ krot, long long rows, int n, int hkv, int d,
-                              int half) {
+                              bf16_t* __restrict__ krot, long long rows, int n, int first,
+                              int hkv, int d, int half) {
   const int cpr = half >> 3;                   // chunk pairs per row
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= rows * cpr) return;
-  const long long row = idx / cpr;
-  const int c = (int)(idx - row * cpr);
-  const long long j = (row / hkv) % n;         // token index of the row
+  const long long u = idx / cpr;
+  const int c = (int)(idx - u * cpr);
+  long long row, j;
+  tail_row(u, n, first, hkv, &row, &j);
   const bf16_t* src = k + row * d;
   float f0[8], f1[8];
   unpack8(ld16(src + 8 * c), f0);
@@ -66,7 +79,7 @@ __global__ void rope_k_kernel(const bf16_t* __restrict__ k, const float2* __rest
 // revolutions) evaluate it in fp32.
 constexpr int kMaxHalf = 64;
 __global__ void rope_k_direct_kernel(const bf16_t* __restrict__ k, bf16_t* __restrict__ krot,
-                                     long long rows, int n, int hkv, int d, int half,
+                                     long long rows, int n, int first, int hkv, int d, int half,
                                      long long pos0, double theta) {
   __shared__ double rev[kMaxHalf];
   if ((int)threadIdx.x < half)
@@ -75,9 +88,11 @@ __global__ void rope_k_direct_kernel(const bf16_t* __restrict__ k, bf16_t* __res
   const int cpr = half >> 3;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= rows * cpr) return;
-  const long long row = idx / cpr;
-  const int c = (int)(idx - row * cpr);
-  const double pos = (double)(pos0 + (row / hkv) % n);
+  const long long u = idx / cpr;
+  const int c = (int)(idx - u * cpr);
+  long long row, j;
+  tail_row(u, n, first, hkv, &row, &j);
+  const double pos = (double)(pos0 + j);
   const bf16_t* src = k + row * d;
   float f0[8], f1[8];
   unpack8(ld16(src + 8 * c), f0);
@@ -109,27 +124,28 @@ hipError_t launch_rope_table(float2* table, long long pos0, int npos, int half, 
 }
 
 hipError_t launch_rope_k(const uint16_t* k, const float2* table, uint16_t* krot, int B, int n,
-                         int hkv, int d, int half, hipStream_t stream) {
-  const long long rows = (long long)B * n * hkv;
+                         int first, int hkv, int d, int half, hipStream_t stream) {
+  const long long rows = (long long)B * (n - first) * hkv;
   const long long total = rows * (half >> 3);
   if (total == 0) return hipSuccess;
   const int threads = 256;
   const long long blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(rope_k_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, k, table,
-                     krot, rows, n, hkv, d, half);
+                     krot, rows, n, first, hkv, d, half);
   return hipGetLastError();
 }
 
-hipError_t launch_rope_k_direct(const uint16_t* k, uint16_t* krot, int B, int n, int hkv, int d,
-                                int half, long long pos0, double theta, hipStream_t stream) {
-  const long long rows = (long long)B * n * hkv;
+hipError_t launch_rope_k_direct(const uint16_t* k, uint16_t* krot, int B, int n, int first,
+                                int hkv, int d, int half, long long pos0, double theta,
+                                hipStream_t stream) {
+  const long long rows = (long long)B * (n - first) * hkv;
   const long long total = rows * (half >> 3);
   if (total == 0) return hipSuccess;
   if (half > kMaxHalf) return hipErrorInvalidValue;
   const int threads = 256;
   const long long blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(rope_k_direct_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, k,
-                     krot, rows, n, hkv, d, half, pos0, theta);
+                     krot, rows, n, first, hkv, d, half, pos0, theta);
   return hipGetLastError();
 }
 

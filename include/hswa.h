@@ -95,6 +95,30 @@ hswa_status_t ga_prefill(const void* q, const void* k, const void* v, void* o, i
                          hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * Chunked prefill: the last q_len tokens of sequences of kv_len tokens whose
+ * earlier tokens (a cached prefix) already have K and V: the fixed-size
+ * prefill chunks of "MiMo v2.5 inference optimisation" (youngju.dev), section
+ * on KV-cache restructuring and scheduling (16K-token chunks, throughput falling
+ * as the prefix grows).  The same operation as swa_sink_prefill restricted to
+ * those query rows.
+ *   q [batch, q_len, hq, d_qk] (query token t is sequence position
+ *   kv_len - q_len + t), k [batch, kv_len, hkv, d_qk],
+ *   v [batch, kv_len, hkv, d_v]  ->  o [batch, q_len, hq, d_v].
+ * Position p attends to keys max(0, p - window + 1) .. p (window <= 0 or
+ * >= kv_len: the full causal prefix, the GA layer with sink = NULL).
+ * RoPE position of sequence position p is pos_offset + p, for q and k.
+ * Requires 0 <= q_len <= kv_len; q_len == kv_len is swa_sink_prefill.
+ * Workspace: hswa_prefill_workspace_size(batch, kv_len, hkv, d_qk,
+ * rotary_fraction).
+ */
+hswa_status_t swa_sink_prefill_chunk(const void* q, const void* k, const void* v,
+                                     const float* sink, void* o, int batch, int q_len,
+                                     int kv_len, int hq, int hkv, int d_qk, int d_v, int window,
+                                     float scale, float rope_theta, float rotary_fraction,
+                                     long long pos_offset, hswa_dtype_t dtype, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace swa_sink_decode needs for `batch` sequences whose
  * positions are all <= max_pos: split partial results (fp32), then the
  * query rotated to its position (bf16, 192 dims per head). */

@@ -16,8 +16,10 @@ two-pass direct summation (max first, then exponentials and sums):
     rotary factor).
   * "MiMo-V3 HySparse2" (aideepthink.cn), section 4: forced-recent window of
     128 tokens plus up to 1024 selected tokens in one sparse attention.
-  * "MiMo v2.5 inference optimisation" (youngju.dev), dual-pool KV cache:
-    the SWA pool holds W slots, the full-attention pool holds the sequence.
+  * "MiMo v2.5 inference optimisation" (youngju.dev), KV-cache restructuring
+    and scheduling: the dual-pool KV cache (the SWA pool holds W slots, the
+    full-attention pool holds the sequence) and prefill in fixed-size chunks
+    behind a cached prefix.
 
 Every function is pinned by tests in tests/test_oracle_pins.py against
 closed forms, library routines and brute force.  The RoPE pairing
@@ -34,6 +36,7 @@ from .attention import (  # noqa: F401
     sparse_keys,
     attend_row,
     swa_sink_prefill,
+    swa_sink_prefill_chunk,
     ga_prefill,
     swa_sink_decode_ring,
     swa_sink_decode_contiguous,

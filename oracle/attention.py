@@ -206,6 +206,27 @@ def swa_sink_prefill(q, k, v, sink, window=128, scale=None, rope_theta=10000.0,
                         pos_offset=pos_offset)
 
 
+def swa_sink_prefill_chunk(q, k, v, sink, window=128, scale=None, rope_theta=10000.0,
+                           rotary_fraction=0.0, pos_offset=0):
+    """Chunked prefill ("MiMo v2.5 inference optimisation" (youngju.dev),
+    section on KV-cache restructuring and scheduling: long prefills run in
+    fixed-size chunks behind the tokens already cached).
+
+    q: [B, q_len, Hq, d_qk], the last q_len tokens; k, v: [B, kv_len, ...],
+    the cached prefix followed by the chunk.  Query token t sits at sequence
+    position kv_len - q_len + t and attends exactly as that row of the whole
+    prefill does (window=0 or None with sink=None: the GA layer).
+    """
+    q = np.asarray(q)
+    q_len, n = q.shape[1], np.asarray(k).shape[1]
+    if q_len > n:
+        raise ValueError("a chunk cannot be longer than its sequence")
+    rows = n - q_len + np.arange(q_len)
+    return prefill_rows(None, k, v, rows, sink=sink, window=window, scale=scale,
+                        rope_theta=rope_theta, rotary_fraction=rotary_fraction,
+                        pos_offset=pos_offset, q_rows=q)
+
+
 def ga_prefill(q, k, v, scale=None, rope_theta=1.0e7, rotary_fraction=0.0, pos_offset=0):
     """GA layer (rslog.cc section 1 and section 5): full causal set, no sink."""
     n = np.asarray(q).shape[1]

@@ -11,6 +11,7 @@ from .workloads import (  # noqa: F401
     normal,
     uniform,
     prefill_inputs,
+    chunk_inputs,
     ring_decode_inputs,
     contiguous_decode_inputs,
     decode_positions,

@@ -39,6 +39,19 @@ WORKLOADS = {
     "ga_prefill_n32768": dict(kind="prefill", seed=3, B=1, n=32768, hq=64, hkv=4, d_qk=192,
                               d_v=128, window=0, dtype="bf16", sink_range=None,
                               rope_theta=1.0e7, rotary_fraction=0.334),
+    # Chunked prefill ("MiMo v2.5 inference optimisation", youngju.dev, KV-cache
+    # restructuring and scheduling: fixed 16K-token chunks, prefixes up to 1M
+    # tokens): one 16384-token chunk behind a 2^20-token cached prefix (SWA
+    # layer) and behind a 114688-token prefix (GA layer, kv_len 131072).
+    "swa_chunk_q16384_prefix1048576": dict(kind="chunk", seed=6, B=1, q_len=16384,
+                                           kv_len=16384 + 1048576, hq=64, hkv=8, d_qk=192,
+                                           d_v=128, window=128, dtype="bf16",
+                                           sink_range=(-2.0, 2.0), rope_theta=1.0e4,
+                                           rotary_fraction=0.334),
+    "ga_chunk_q16384_prefix114688": dict(kind="chunk", seed=7, B=1, q_len=16384,
+                                         kv_len=131072, hq=64, hkv=4, d_qk=192, d_v=128,
+                                         window=0, dtype="bf16", sink_range=None,
+                                         rope_theta=1.0e7, rotary_fraction=0.334),
     # Hybrid decode step: 64 sequences, one token each at p in [131072, 262143].
     "hybrid_decode_b64": dict(kind="decode", seed=4, B=64, pos_range=(131072, 262143),
                               d_qk=192, d_v=128, dtype="bf16",
@@ -89,6 +102,20 @@ def prefill_inputs(B, n, hq, hkv, d_qk, d_v, dtype, seed, device="cpu", sink_ran
     q = normal((B, n, hq, d_qk), tensor_seed(seed, TID_Q), device, dtype)
     k = normal((B, n, hkv, d_qk), tensor_seed(seed, TID_K), device, dtype)
     v = normal((B, n, hkv, d_v), tensor_seed(seed, TID_V), device, dtype)
+    sink = None
+    if sink_range is not None:
+        sink = uniform((hq,), sink_range[0], sink_range[1], tensor_seed(seed, TID_SINK), device)
+    return dict(q=q, k=k, v=v, sink=sink)
+
+
+def chunk_inputs(B, q_len, kv_len, hq, hkv, d_qk, d_v, dtype, seed, device="cpu",
+                 sink_range=(-2.0, 2.0)):
+    """A prefill chunk: q [B,q_len,Hq,d_qk] for the last q_len positions, and
+    k [B,kv_len,Hkv,d_qk], v [B,kv_len,Hkv,d_v] for the whole sequence (the
+    cached prefix followed by the chunk), sink [Hq] (or None)."""
+    q = normal((B, q_len, hq, d_qk), tensor_seed(seed, TID_Q), device, dtype)
+    k = normal((B, kv_len, hkv, d_qk), tensor_seed(seed, TID_K), device, dtype)
+    v = normal((B, kv_len, hkv, d_v), tensor_seed(seed, TID_V), device, dtype)
     sink = None
     if sink_range is not None:
         sink = uniform((hq,), sink_range[0], sink_range[1], tensor_seed(seed, TID_SINK), device)

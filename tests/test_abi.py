@@ -92,6 +92,25 @@ def test_prefill_validation(lib):
     assert lib.hswa_last_error().decode() == ""
 
 
+def test_prefill_chunk_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, sink=None, o=FAKE, batch=1, q_len=16, kv_len=40, hq=4,
+                 hkv=2, d_qk=192, d_v=128, window=8, scale=0.0, theta=1e4, frac=0.0,
+                 pos_offset=0, dtype=1, ws=None, ws_bytes=0, stream=None)
+        a.update(kw)
+        return lib.swa_sink_prefill_chunk(*a.values())
+    assert call(q_len=41) == INVALID                       # longer than its sequence
+    assert "q_len" in lib.hswa_last_error().decode()
+    assert call(q_len=-1) == INVALID
+    assert call(kv_len=-1, q_len=0) == INVALID
+    assert call(k=None) == INVALID
+    assert call(frac=0.334) == INVALID                     # workspace missing (sized by kv_len)
+    assert call(frac=0.334, ws=FAKE, ws_bytes=(16 * 32 * 8 + 255) // 256 * 256) == INVALID
+    assert call(d_qk=300) == UNSUPPORTED
+    assert call(q_len=0, q=None) == OK                     # empty chunk: nothing to do
+    assert call(batch=0, q=None) == OK
+
+
 def test_decode_validation(lib):
     def call(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, layout=0, offs=None, pos=FAKE, sink=None, o=FAKE, batch=2,

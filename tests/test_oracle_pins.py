@@ -350,10 +350,39 @@ def pin_p12_large_sink_is_stable(O):
     assert np.abs(got[0, :, 1] - ref[0, :, 1]).max() < 1e-12
 
 
+def pin_p13_chunk(O):
+    """A chunk behind a cached prefix (youngju.dev, KV-cache restructuring and
+    scheduling: fixed-size prefill chunks) gives the last rows of the whole
+    prefill: against the scalar brute force (RoPE, sinks, G = 2) and torch SDPA
+    with a rectangular window mask."""
+    rng = np.random.default_rng(29)
+    n, d, dv = 9, 8, 4
+    q = rng.standard_normal((1, n, 4, d)) * 1.5
+    k = rng.standard_normal((1, n, 2, d)) * 1.5
+    v = rng.standard_normal((1, n, 2, dv))
+    sink = np.array([-1.0, 0.0, 0.5, 2.0])
+    for W in (1, 3, None):
+        ref = _brute_prefill(q, k, v, sink, W, 3.0, 0.5)
+        for ql in (1, 4, n):
+            got = O.swa_sink_prefill_chunk(q[:, n - ql:], k, v, sink, window=0 if W is None else W,
+                                           rope_theta=3.0, rotary_fraction=0.5)
+            assert got.shape == (1, ql, 4, dv)
+            assert np.abs(got - ref[:, n - ql:]).max() < 1e-12, (W, ql)
+    q, k, v, s = _inputs(2, 40, 8, 2, seed=31)
+    ql = 13
+    i = np.arange(40 - ql, 40)[:, None]
+    j = np.arange(40)[None, :]
+    for W in (5, 16):
+        allowed = ((j <= i) & (j >= i - W + 1))[None]
+        ref = _sdpa(q[:, 40 - ql:], k, v, allowed, s, 1 / math.sqrt(192))
+        got = O.swa_sink_prefill_chunk(q[:, 40 - ql:], k, v, s, window=W)
+        assert np.abs(got - ref).max() < 1e-12, W
+
+
 PINS = [pin_p1_no_sink_is_masked_softmax, pin_p2_wide_window_is_causal, pin_p3_sink_as_extra_key,
         pin_p4_weights_sum, pin_p5_unit_window, pin_p6_zero_query, pin_p7_brute_force,
         pin_p8_rope, pin_p9_gqa, pin_p10_decode_equals_prefill_row, pin_p11_sparse,
-        pin_p12_large_sink_is_stable]
+        pin_p12_large_sink_is_stable, pin_p13_chunk]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -383,6 +412,7 @@ MUTANTS = {
     "sparse_drops_selection": ("return np.union1d(sel, rec)", "return rec"),
     "sparse_recent_too_wide": ("lo = max(0, i - recent + 1)", "lo = max(0, i - recent)"),
     "sink_in_numerator": ("out[g] = (e @ vj) / den", "out[g] = (e @ vj + math.exp(min(sink[g] - m[g], 0.0))) / den"),
+    "chunk_rows_from_zero": ("rows = n - q_len + np.arange(q_len)", "rows = np.arange(q_len)"),
     "decode_query_not_rotated": ("qb = rope(q[b][None], np.array([p]), rope_theta, rotary_fraction)[0]\n        slots",
                                  "qb = np.asarray(q[b], dtype=np.float64)\n        slots"),
 }
@@ -463,6 +493,13 @@ def test_workloads_use_page_constants():
     assert wl["swa_prefill_n32768"]["rotary_fraction"] == GOLD["partial_rotary_factor"]["value"]
     assert wl["sparse_prefill_n65536"]["recent"] == GOLD["sparse_recent"]["value"]
     assert wl["sparse_prefill_n65536"]["max_sel"] == GOLD["sparse_selected"]["value"]
+    for name in ("swa_chunk_q16384_prefix1048576", "ga_chunk_q16384_prefix114688"):
+        assert wl[name]["q_len"] == GOLD["prefill_chunk_tokens"]["value"]
+    swc = wl["swa_chunk_q16384_prefix1048576"]
+    assert swc["kv_len"] - swc["q_len"] == GOLD["longest_prefix_tokens"]["value"]
+    assert (swc["hq"], swc["hkv"], swc["window"]) == (*GOLD["swa_heads_q_kv"]["value"], W)
+    gac = wl["ga_chunk_q16384_prefix114688"]
+    assert (gac["hq"], gac["hkv"], gac["window"]) == (*GOLD["ga_heads_q_kv"]["value"], 0)
     dec = wl["hybrid_decode_b64"]
     assert dec["swa"]["window"] == W
     assert (dec["swa"]["hq"], dec["swa"]["hkv"]) == tuple(GOLD["swa_heads_q_kv"]["value"])

@@ -260,6 +260,96 @@ def test_ga_prefill_full_size(gpu_lib):
 
 
 # ---------------------------------------------------------------------------
+# Chunked prefill: the last q_len positions behind a cached prefix
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,q_len,kv_len,hq,hkv,window,dtype,frac", [
+    (2, 300, 1000, 64, 8, 128, "bf16", 0.334),   # persistent kernel, ragged chunk and prefix
+    (1, 1, 777, 64, 8, 128, "bf16", 0.334),      # a single query behind the prefix
+    (1, 100, 150, 64, 8, 128, "bf16", 0.334),    # window reaches back to position 0
+    (1, 250, 900, 64, 4, 0, "bf16", 0.334),      # GA chunk (G = 16)
+    (1, 33, 400, 128, 1, 33, "bf16", 0.17),      # G = 128, R = 32, odd window
+    (1, 200, 700, 16, 8, 128, "bf16", 0.334),    # G = 2: generic kernel
+    (1, 130, 600, 4, 2, 64, "f32", 0.334),       # fp32: generic kernel
+    (1, 90, 90, 64, 8, 128, "bf16", 0.334),      # the whole sequence is the chunk
+])
+def test_prefill_chunk(gpu_lib, B, q_len, kv_len, hq, hkv, window, dtype, frac):
+    sink = (-2.0, 2.0) if window > 0 else None
+    x = synthetic.chunk_inputs(B, q_len, kv_len, hq, hkv, 192, 128, dtype, 300 + q_len, DEV, sink)
+    o = gpu_lib.swa_sink_prefill_chunk(x["q"], x["k"], x["v"], x["sink"], window=window,
+                                       rope_theta=1.0e4, rotary_fraction=frac, pos_offset=5)
+    assert o.shape == (B, q_len, hq, 128)
+    q, k, v, s = _host(x)
+    ref = oracle.swa_sink_prefill_chunk(q, k, v, s, window=window, rope_theta=1.0e4,
+                                        rotary_fraction=frac, pos_offset=5)
+    _check(f"chunk {dtype} B={B} q={q_len} kv={kv_len} {hq}/{hkv} W={window}", o, ref,
+           fp32=(dtype == "f32"))
+
+
+@pytest.mark.parametrize("hq,hkv,window", [(64, 8, 128), (64, 4, 0), (16, 8, 128)])
+def test_prefill_chunk_is_rows_of_whole_prefill(gpu_lib, hq, hkv, window):
+    """A chunk starting on a query-block boundary (a multiple of 128 positions)
+    walks the same tiles in the same order as the whole prefill does for those
+    rows, so its output is bit-for-bit those rows; other starts agree within
+    rounding."""
+    x = _prefill_case(1, 1100, hq, hkv, "bf16", 310, (-2.0, 2.0) if window else None)
+    kw = dict(window=window, rope_theta=1.0e4, rotary_fraction=0.334, pos_offset=3)
+    whole = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], **kw)
+    for start in (512, 768, 1023, 333):
+        part = gpu_lib.swa_sink_prefill_chunk(x["q"][:, start:].contiguous(), x["k"], x["v"],
+                                              x["sink"], **kw)
+        if start % 128 == 0 and hq // hkv >= 8:
+            assert torch.equal(part, whole[:, start:]), start
+        else:
+            _check(f"chunk at {start} vs whole prefill {hq}/{hkv}", part, _np(whole[:, start:]))
+
+
+def test_prefill_chunk_empty(gpu_lib):
+    x = synthetic.chunk_inputs(1, 0, 64, 64, 8, 192, 128, "bf16", 320, DEV)
+    o = gpu_lib.swa_sink_prefill_chunk(x["q"], x["k"], x["v"], x["sink"], window=128)
+    assert o.shape == (1, 0, 64, 128)
+
+
+def test_swa_chunk_full_size(gpu_lib):
+    """16K-token chunk behind a 2^20-token prefix, sampled rows.  The oracle
+    sees only the keys from the first one any query of the chunk reads
+    (position kv_len - q_len - W + 1) on, with the RoPE offset moved by the
+    same amount: the window makes the output invariant to that shift."""
+    wl = synthetic.WORKLOADS["swa_chunk_q16384_prefix1048576"]
+    x = synthetic.chunk_inputs(1, wl["q_len"], wl["kv_len"], wl["hq"], wl["hkv"], 192, 128,
+                               "bf16", wl["seed"], DEV, wl["sink_range"])
+    o = gpu_lib.swa_sink_prefill_chunk(x["q"], x["k"], x["v"], x["sink"], window=wl["window"],
+                                       rope_theta=wl["rope_theta"],
+                                       rotary_fraction=wl["rotary_fraction"])
+    first = wl["kv_len"] - wl["q_len"] - wl["window"] + 1
+    rows = _sample_rows(wl["q_len"], 73)
+    ridx = torch.from_numpy(rows).to(DEV)
+    ref = oracle.prefill_rows(None, _np(x["k"][:, first:]), _np(x["v"][:, first:]),
+                              rows + wl["window"] - 1, sink=_np(x["sink"]), window=wl["window"],
+                              rope_theta=wl["rope_theta"], rotary_fraction=wl["rotary_fraction"],
+                              pos_offset=first, q_rows=_np(x["q"][:, ridx]))
+    _check("swa chunk 16K after 1M (sampled rows)", o[:, ridx], ref)
+
+
+def test_ga_chunk_full_size(gpu_lib):
+    wl = synthetic.WORKLOADS["ga_chunk_q16384_prefix114688"]
+    x = synthetic.chunk_inputs(1, wl["q_len"], wl["kv_len"], wl["hq"], wl["hkv"], 192, 128,
+                               "bf16", wl["seed"], DEV, None)
+    o = gpu_lib.swa_sink_prefill_chunk(x["q"], x["k"], x["v"], None, window=0,
+                                       rope_theta=wl["rope_theta"],
+                                       rotary_fraction=wl["rotary_fraction"])
+    rng = np.random.default_rng(74)
+    rows = np.unique(np.concatenate([np.arange(4), rng.choice(wl["q_len"], 24, replace=False),
+                                     np.arange(wl["q_len"] - 4, wl["q_len"])]))
+    ridx = torch.from_numpy(rows).to(DEV)
+    ref = oracle.prefill_rows(None, _np(x["k"]), _np(x["v"]),
+                              rows + wl["kv_len"] - wl["q_len"], sink=None, window=None,
+                              rope_theta=wl["rope_theta"], rotary_fraction=wl["rotary_fraction"],
+                              q_rows=_np(x["q"][:, ridx]))
+    _check("ga chunk 16K after 112K (sampled rows)", o[:, ridx], ref)
+
+
+# ---------------------------------------------------------------------------
 # Decode
 # ---------------------------------------------------------------------------
 
