@@ -19,7 +19,9 @@ two-pass direct summation (max first, then exponentials and sums):
   * "MiMo v2.5 inference optimisation" (youngju.dev), KV-cache restructuring
     and scheduling: the dual-pool KV cache (the SWA pool holds W slots, the
     full-attention pool holds the sequence) and prefill in fixed-size chunks
-    behind a cached prefix.
+    behind a cached prefix; the closing section's FP8 cache (with
+    aideepthink.cn section 5), read as OCP E4M3 codes with one scale per kv
+    head.
 
 Every function is pinned by tests in tests/test_oracle_pins.py against
 closed forms, library routines and brute force.  The RoPE pairing
@@ -40,6 +42,10 @@ from .attention import (  # noqa: F401
     ga_prefill,
     swa_sink_decode_ring,
     swa_sink_decode_contiguous,
+    e4m3_value,
+    dequantise_kv,
+    swa_sink_decode_ring_fp8,
+    swa_sink_decode_contiguous_fp8,
     sparse_sink_attn,
     prefill_rows,
     sparse_rows,

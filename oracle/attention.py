@@ -315,6 +315,61 @@ def swa_sink_decode_contiguous(q, k, v, seq_offsets, pos, sink=None, window=None
 
 
 # ----------------------------------------------------------------------------
+# FP8 KV cache: E4M3 codes with one scale per kv head
+# ----------------------------------------------------------------------------
+
+def e4m3_value(codes):
+    """Value of FP8 E4M3 codes (uint8), in float64.
+
+    The pages store the KV cache in "FP8" (youngju.dev "MiMo v2.5 inference
+    optimisation", closing section; aideepthink.cn "MiMo-V3 HySparse2",
+    section 5) without naming the encoding.  Reading: the OCP E4M3 format:
+    sign bit 7, exponent e in bits 6-3 with bias 7, mantissa m in bits 2-0;
+    e > 0 is (1 + m/8) * 2^(e-7), e = 0 is the subnormal m * 2^-9; there are
+    no infinities and exponent 15 with mantissa 7 is NaN.
+    """
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where((e == 15) & (m == 7), np.nan, sign * mag)
+
+
+def dequantise_kv(codes, scale):
+    """Cache values from codes [..., Hkv, d] and per-kv-head scales [Hkv]."""
+    return e4m3_value(codes) * np.asarray(scale, dtype=np.float64)[:, None]
+
+
+def swa_sink_decode_ring_fp8(q, k_codes, v_codes, k_scale, v_scale, pos, sink, scale=None,
+                             rope_theta=10000.0, rotary_fraction=0.0, seqs=None):
+    """Ring-cache decode over E4M3 caches: the ring decode on the cache values."""
+    return swa_sink_decode_ring(q, dequantise_kv(k_codes, k_scale),
+                                dequantise_kv(v_codes, v_scale), pos, sink, scale=scale,
+                                rope_theta=rope_theta, rotary_fraction=rotary_fraction,
+                                seqs=seqs)
+
+
+def swa_sink_decode_contiguous_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_offsets, pos,
+                                   sink=None, window=None, scale=None, rope_theta=1.0e7,
+                                   rotary_fraction=0.0, seqs=None, kv_loader=None):
+    """Contiguous-cache decode over E4M3 caches.  `kv_loader(b)`, if given,
+    returns the codes (k_b, v_b) of one sequence."""
+    loader = None
+    if kv_loader is not None:
+        def loader(b):
+            kb, vb = kv_loader(b)
+            return dequantise_kv(kb, k_scale), dequantise_kv(vb, v_scale)
+        k = v = None
+    else:
+        k, v = dequantise_kv(k_codes, k_scale), dequantise_kv(v_codes, v_scale)
+    return swa_sink_decode_contiguous(q, k, v, seq_offsets, pos, sink=sink, window=window,
+                                      scale=scale, rope_theta=rope_theta,
+                                      rotary_fraction=rotary_fraction, seqs=seqs,
+                                      kv_loader=loader)
+
+
+# ----------------------------------------------------------------------------
 # Token-level sparse attention on one shared cache
 # ----------------------------------------------------------------------------
 

@@ -14,6 +14,10 @@ from .workloads import (  # noqa: F401
     chunk_inputs,
     ring_decode_inputs,
     contiguous_decode_inputs,
+    kv_scales,
+    e4m3_codes,
+    ring_decode_inputs_fp8,
+    contiguous_decode_inputs_fp8,
     decode_positions,
     sparse_selection,
     sparse_inputs,

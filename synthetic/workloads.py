@@ -8,6 +8,9 @@ Recipe (the same for every workload):
     bfloat16 with round-to-nearest-even;
   * per-head sinks ~ U(lo, hi) in float32;
   * decode positions ~ U{lo .. hi} drawn on the host;
+  * FP8 caches: per-kv-head scales ~ U(lo, hi) in float32, K and V drawn
+    as above in float32, divided by their head's scale and cast to E4M3
+    codes by torch (round-to-nearest-even; magnitudes stay below 448);
   * sparse selections: for query i and kv head g, `avail = max(0, i - recent)`
     candidates [0, avail); all of them when avail <= max_sel, otherwise
     max_sel distinct ones drawn uniformly (Floyd's sampling), sorted
@@ -25,6 +28,7 @@ import torch
 # Tensor ids inside one workload seed space.
 TID_Q, TID_K, TID_V, TID_SINK, TID_POS, TID_SEL = 1, 2, 3, 4, 5, 6
 TID_K_GA, TID_V_GA, TID_Q_GA = 12, 13, 11
+TID_KSCALE, TID_VSCALE = 21, 22
 
 WORKLOADS = {
     # Tiny fp32 SWA+sink prefill, no RoPE; also run with sink = -inf and W = 512.
@@ -57,6 +61,11 @@ WORKLOADS = {
                               d_qk=192, d_v=128, dtype="bf16",
                               swa=dict(hq=64, hkv=8, window=128, sink_range=(-2.0, 2.0)),
                               ga=dict(hq=64, hkv=4, window=0, sink_range=None)),
+    # The same decode step over FP8 (E4M3) caches with per-kv-head scales.
+    "hybrid_decode_fp8_b64": dict(kind="decode_fp8", seed=8, B=64, pos_range=(131072, 262143),
+                                  d_qk=192, d_v=128, dtype="bf16", scale_range=(0.02, 0.04),
+                                  swa=dict(hq=64, hkv=8, window=128, sink_range=(-2.0, 2.0)),
+                                  ga=dict(hq=64, hkv=4, window=0, sink_range=None)),
     # Token-level sparse prefill: n = 65536, 64 q / 4 kv heads, 128 recent + <= 1024 selected.
     "sparse_prefill_n65536": dict(kind="sparse", seed=5, B=1, n=65536, hq=64, hkv=4, d_qk=192,
                                   d_v=128, recent=128, max_sel=1024, dtype="bf16",
@@ -164,6 +173,56 @@ def contiguous_decode_inputs(B, hq, hkv, d_qk, d_v, dtype, seed, pos, device="cp
     if sink_range is not None:
         sink = uniform((hq,), sink_range[0], sink_range[1], tensor_seed(seed, TID_SINK), device)
     return dict(q=q, k=k, v=v, sink=sink, pos=pos.to(device), seq_offsets=offs.to(device))
+
+
+def kv_scales(hkv, lo, hi, seed, device="cpu"):
+    """Per-kv-head FP8 scales of K and V, float32 [hkv] each."""
+    return (uniform((hkv,), lo, hi, tensor_seed(seed, TID_KSCALE), device),
+            uniform((hkv,), lo, hi, tensor_seed(seed, TID_VSCALE), device))
+
+
+def e4m3_codes(x, scale):
+    """E4M3 codes (uint8) of x / scale[head] for x [..., Hkv, d] float32."""
+    return (x / scale[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def ring_decode_inputs_fp8(B, hq, hkv, window, d_qk, d_v, seed, pos, device="cpu",
+                           sink_range=(-2.0, 2.0), scale_range=(0.02, 0.04), qdtype="bf16"):
+    """q [B,Hq,d_qk] and an E4M3 ring cache k [B,W,Hkv,d_qk], v [B,W,Hkv,d_v] (uint8)
+    with scales k_scale, v_scale [Hkv]."""
+    ks, vs = kv_scales(hkv, scale_range[0], scale_range[1], seed, device)
+    q = normal((B, hq, d_qk), tensor_seed(seed, TID_Q), device, qdtype)
+    k = e4m3_codes(normal((B, window, hkv, d_qk), tensor_seed(seed, TID_K), device, "f32"), ks)
+    v = e4m3_codes(normal((B, window, hkv, d_v), tensor_seed(seed, TID_V), device, "f32"), vs)
+    sink = None
+    if sink_range is not None:
+        sink = uniform((hq,), sink_range[0], sink_range[1], tensor_seed(seed, TID_SINK), device)
+    return dict(q=q, k=k, v=v, k_scale=ks, v_scale=vs, sink=sink, pos=pos.to(device))
+
+
+def contiguous_decode_inputs_fp8(B, hq, hkv, d_qk, d_v, seed, pos, device="cpu", sink_range=None,
+                                 extra_rows=0, scale_range=(0.02, 0.04), qdtype="bf16"):
+    """q [B,Hq,d_qk] and a packed E4M3 cache (layout as contiguous_decode_inputs),
+    with scales k_scale, v_scale [Hkv]."""
+    ks, vs = kv_scales(hkv, scale_range[0], scale_range[1], seed, device)
+    lens = pos.to(torch.int64).cpu() + 1 + int(extra_rows)
+    offs = torch.zeros(B + 1, dtype=torch.int64)
+    offs[1:] = torch.cumsum(lens, 0)
+    total = int(offs[-1])
+    q = normal((B, hq, d_qk), tensor_seed(seed, TID_Q_GA), device, qdtype)
+    k = torch.empty((total, hkv, d_qk), dtype=torch.uint8, device=device)
+    v = torch.empty((total, hkv, d_v), dtype=torch.uint8, device=device)
+    for b in range(B):
+        lo, hi = int(offs[b]), int(offs[b + 1])
+        k[lo:hi] = e4m3_codes(normal((hi - lo, hkv, d_qk), tensor_seed(seed, TID_K_GA, b), device,
+                                     "f32"), ks)
+        v[lo:hi] = e4m3_codes(normal((hi - lo, hkv, d_v), tensor_seed(seed, TID_V_GA, b), device,
+                                     "f32"), vs)
+    sink = None
+    if sink_range is not None:
+        sink = uniform((hq,), sink_range[0], sink_range[1], tensor_seed(seed, TID_SINK), device)
+    return dict(q=q, k=k, v=v, k_scale=ks, v_scale=vs, sink=sink, pos=pos.to(device),
+                seq_offsets=offs.to(device))
 
 
 def sparse_selection(B, n, hkv, recent, max_sel, seed, device="cpu", chunk_rows=8192):

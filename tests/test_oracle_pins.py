@@ -379,10 +379,54 @@ def pin_p13_chunk(O):
         assert np.abs(got - ref).max() < 1e-12, W
 
 
+def pin_p14_fp8_cache(O):
+    """FP8 KV cache: the E4M3 value of every code against torch's
+    float8_e4m3fn (a library routine), the format's landmark values, and
+    the FP8 decodes against the plain decodes on caches torch dequantised."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = O.e4m3_value(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]) and np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+    # largest finite, smallest subnormal, smallest normal, one, NaN, negative zero
+    lm = O.e4m3_value(np.array([0x7E, 0x01, 0x08, 0x38, 0x7F, 0xFF, 0x80, 0xFE], dtype=np.uint8))
+    assert list(lm[[0, 1, 2, 3, 7]]) == [448.0, 2.0 ** -9, 2.0 ** -6, 1.0, -448.0]
+    assert np.isnan(lm[4]) and np.isnan(lm[5]) and lm[6] == 0.0 and np.signbit(lm[6])
+
+    def tdeq(c, s):
+        return (torch.from_numpy(c).view(torch.float8_e4m3fn).double()
+                * torch.from_numpy(s).double()[:, None]).numpy()
+    rng = np.random.default_rng(41)
+    B, W, hq, hkv, d, dv = 2, 8, 4, 2, 16, 8
+    kc = rng.integers(0, 126, (B, W, hkv, d), dtype=np.uint8) | rng.choice([0, 128], (B, W, hkv, d)).astype(np.uint8)
+    vc = rng.integers(0, 126, (B, W, hkv, dv), dtype=np.uint8)
+    ks, vs = np.array([0.5, 0.03]), np.array([0.25, 2.0])
+    q = rng.standard_normal((B, hq, d))
+    pos = np.array([3, 40])
+    sink = np.array([0.0, -1.0, 1.0, 2.0])
+    got = O.swa_sink_decode_ring_fp8(q, kc, vc, ks, vs, pos, sink, rope_theta=3.0, rotary_fraction=0.5)
+    ref = O.swa_sink_decode_ring(q, tdeq(kc, ks), tdeq(vc, vs), pos, sink, rope_theta=3.0,
+                                 rotary_fraction=0.5)
+    assert np.abs(got - ref).max() < 1e-12
+    offs = np.array([0, 5, 17])
+    kc2 = rng.integers(0, 126, (17, hkv, d), dtype=np.uint8)
+    vc2 = rng.integers(128, 254, (17, hkv, dv), dtype=np.uint8)
+    pos2 = np.array([4, 9])
+    got = O.swa_sink_decode_contiguous_fp8(q, kc2, vc2, ks, vs, offs, pos2, window=None)
+    ref = O.swa_sink_decode_contiguous(q, tdeq(kc2, ks), tdeq(vc2, vs), offs, pos2, window=None)
+    assert np.abs(got - ref).max() < 1e-12
+    # the same through the per-sequence loader (codes of one sequence at a time)
+    got = O.swa_sink_decode_contiguous_fp8(
+        q, None, None, ks, vs, offs, pos2, window=None,
+        kv_loader=lambda b: (kc2[offs[b]:offs[b + 1]], vc2[offs[b]:offs[b + 1]]))
+    assert np.abs(got - ref).max() < 1e-12
+
+
 PINS = [pin_p1_no_sink_is_masked_softmax, pin_p2_wide_window_is_causal, pin_p3_sink_as_extra_key,
         pin_p4_weights_sum, pin_p5_unit_window, pin_p6_zero_query, pin_p7_brute_force,
         pin_p8_rope, pin_p9_gqa, pin_p10_decode_equals_prefill_row, pin_p11_sparse,
-        pin_p12_large_sink_is_stable, pin_p13_chunk]
+        pin_p12_large_sink_is_stable, pin_p13_chunk, pin_p14_fp8_cache]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -413,6 +457,12 @@ MUTANTS = {
     "sparse_recent_too_wide": ("lo = max(0, i - recent + 1)", "lo = max(0, i - recent)"),
     "sink_in_numerator": ("out[g] = (e @ vj) / den", "out[g] = (e @ vj + math.exp(min(sink[g] - m[g], 0.0))) / den"),
     "chunk_rows_from_zero": ("rows = n - q_len + np.arange(q_len)", "rows = np.arange(q_len)"),
+    "e4m3_bias_8": ("np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
+    "e4m3_subnormal_as_normal": ("np.where(e == 0, m * 2.0 ** -9,", "np.where(e < 0, m * 2.0 ** -9,"),
+    "fp8_v_scale_dropped": ("dequantise_kv(v_codes, v_scale), pos, sink, scale=scale,",
+                            "e4m3_value(v_codes), pos, sink, scale=scale,"),
+    "fp8_scales_swapped": ("return dequantise_kv(kb, k_scale), dequantise_kv(vb, v_scale)",
+                           "return dequantise_kv(kb, v_scale), dequantise_kv(vb, k_scale)"),
     "decode_query_not_rotated": ("qb = rope(q[b][None], np.array([p]), rope_theta, rotary_fraction)[0]\n        slots",
                                  "qb = np.asarray(q[b], dtype=np.float64)\n        slots"),
 }
