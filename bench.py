@@ -148,11 +148,12 @@ def copy_calibration(steps, warmup):
 def only(which, steps, warmup):
     if which == "copy":
         return {"copy": copy_calibration(steps, warmup)}
-    parts = {"ga": ["ga"], "chunk": ["chunk"], "decode": ["decode"], "sparse": ["sparse"]}[which]
+    parts = {"ga": ["ga"], "chunk": ["chunk"], "decode": ["decode"], "decode_fp8": ["decode_fp8"],
+             "sparse": ["sparse"]}[which]
     return secondary(steps, warmup, parts)
 
 
-def secondary(steps, warmup, parts=("ga", "chunk", "decode", "sparse")):
+def secondary(steps, warmup, parts=("ga", "chunk", "decode", "decode_fp8", "sparse")):
     out = {}
     dev = "cuda"
     if "ga" in parts:
@@ -161,6 +162,8 @@ def secondary(steps, warmup, parts=("ga", "chunk", "decode", "sparse")):
         _chunk(out, steps, warmup, dev)
     if "decode" in parts:
         _decode(out, dev)
+    if "decode_fp8" in parts:
+        _decode_fp8(out, dev)
     if "sparse" in parts:
         _sparse(out, dev)
     return out
@@ -278,6 +281,53 @@ def _decode(out, dev):
     _log(f"decode GA {out['decode_ga_contiguous']}")
 
 
+def _decode_fp8(out, dev):
+    # The hybrid decode step over E4M3 caches (one byte per element)
+    wl = synthetic.WORKLOADS["hybrid_decode_fp8_b64"]
+    pos = synthetic.decode_positions(wl["B"], *wl["pos_range"], wl["seed"])
+    maxp = wl["pos_range"][1]
+    sw, ga = wl["swa"], wl["ga"]
+    # ring: 16 buffer sets (336 MB) so that the caches are not served from the MALL
+    sets = [synthetic.ring_decode_inputs_fp8(wl["B"], sw["hq"], sw["hkv"], sw["window"], 192, 128,
+                                             wl["seed"] + 100 * r, pos, dev, sw["sink_range"],
+                                             wl["scale_range"])
+            for r in range(16)]
+    wsr = torch.empty(hswa.decode_workspace_size(hswa.KV_RING, wl["B"], sw["hq"], 128, sw["window"],
+                                                 maxp), dtype=torch.uint8, device=dev)
+    orr = torch.empty(wl["B"], sw["hq"], 128, dtype=torch.bfloat16, device=dev)
+    it = [0]
+
+    def ring_step():
+        d = sets[it[0] % len(sets)]
+        it[0] += 1
+        hswa.swa_sink_decode_fp8(d["q"], d["k"], d["v"], d["k_scale"], d["v_scale"], d["pos"], maxp,
+                                 layout=hswa.KV_RING, sink=d["sink"], window=sw["window"], out=orr,
+                                 workspace=wsr)
+    _, per = timed(ring_step, 40, 8)
+    ring_bytes = wl["B"] * sw["window"] * sw["hkv"] * (192 + 128) + wl["B"] * sw["hq"] * (192 + 128) * 2
+    t = float(np.median(per)) / 1e3
+    out["decode_fp8_swa_ring"] = {"gbps": ring_bytes / t / 1e9, "us": t * 1e6, "bytes": ring_bytes,
+                                  "frac_of_hbm_peak": ring_bytes / t / 1e9 / HBM_PEAK_GBPS}
+    _log(f"decode fp8 ring {out['decode_fp8_swa_ring']}")
+    del sets
+    c = synthetic.contiguous_decode_inputs_fp8(wl["B"], ga["hq"], ga["hkv"], 192, 128, wl["seed"],
+                                               pos, dev, None, scale_range=wl["scale_range"])
+    wsc = torch.empty(hswa.decode_workspace_size(hswa.KV_CONTIGUOUS, wl["B"], ga["hq"], 128, 0, maxp),
+                      dtype=torch.uint8, device=dev)
+    oc = torch.empty(wl["B"], ga["hq"], 128, dtype=torch.bfloat16, device=dev)
+    fn = lambda: hswa.swa_sink_decode_fp8(c["q"], c["k"], c["v"], c["k_scale"],  # noqa: E731
+                                          c["v_scale"], c["pos"], maxp, layout=hswa.KV_CONTIGUOUS,
+                                          seq_offsets=c["seq_offsets"], window=0, out=oc,
+                                          workspace=wsc)
+    _, per = timed(fn, 10, 2)
+    keys = int((pos + 1).sum())
+    ga_bytes = keys * ga["hkv"] * (192 + 128) + wl["B"] * ga["hq"] * (192 + 128) * 2
+    t = float(np.median(per)) / 1e3
+    out["decode_fp8_ga_contiguous"] = {"gbps": ga_bytes / t / 1e9, "ms": t * 1e3, "bytes": ga_bytes,
+                                       "frac_of_hbm_peak": ga_bytes / t / 1e9 / HBM_PEAK_GBPS}
+    _log(f"decode fp8 GA {out['decode_fp8_ga_contiguous']}")
+
+
 def _sparse(out, dev):
     # Sparse prefill, n = 65536, 128 recent + <= 1024 selected
     wl = synthetic.WORKLOADS["sparse_prefill_n65536"]
@@ -305,7 +355,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["prefill", "ga", "chunk", "decode", "sparse", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "ga", "chunk", "decode", "decode_fp8", "sparse", "copy"], default=None,
                     help="run one workload only (for profiler runs); prints its figures as JSON")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     sparse_sink_attn,
     sparse_workspace_size,
     swa_sink_decode,
+    swa_sink_decode_fp8,
     swa_sink_prefill,
     swa_sink_prefill_chunk,
     version,

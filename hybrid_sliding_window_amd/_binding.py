@@ -28,6 +28,8 @@ _SIGNATURES = {
     "hswa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i, _ll]),
     "swa_sink_decode": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _ll,
                              _f, _f, _f, _i, _vp, _sz, _vp]),
+    "swa_sink_decode_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                                 _i, _i, _ll, _f, _f, _f, _i, _vp, _sz, _vp]),
     "hswa_sparse_workspace_size": (_sz, [_i, _i, _i, _i, _f]),
     "sparse_sink_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i, _i,
                               _f, _f, _f, _ll, _i, _vp, _sz, _vp]),
@@ -203,6 +205,43 @@ def swa_sink_decode(q, k_cache, v_cache, pos, max_pos, layout=KV_RING, seq_offse
                              _ptr(pos), _ptr(sink), _ptr(o), B, hq, hkv, dqk, dv, window,
                              int(max_pos), scale, rope_theta, rotary_fraction, _dtype_code(q),
                              _ptr(ws), 0 if ws is None else ws.numel(), _stream(q))
+    _raise(st)
+    return o
+
+
+def _fp8_cache(t):
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("an FP8 cache holds E4M3 codes: uint8 or float8_e4m3fn")
+    return t
+
+
+def swa_sink_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, pos, max_pos, layout=KV_RING,
+                        seq_offsets=None, sink=None, window=128, scale=0.0, rope_theta=10000.0,
+                        rotary_fraction=0.0, out=None, workspace=None):
+    """swa_sink_decode over E4M3 caches: the value of a code is e4m3(code) times
+    k_scale[g] (K) or v_scale[g] (V) of its kv head g."""
+    lib = load()
+    B, hq, dqk = q.shape
+    hkv, dv = k_cache.shape[-2], v_cache.shape[-1]
+    _fp8_cache(k_cache)
+    _fp8_cache(v_cache)
+    for t in (k_scale, v_scale):
+        if t.dtype != torch.float32 or t.numel() != hkv:
+            raise ValueError("k_scale and v_scale must be float32 with one entry per kv head")
+    sink = _sink(sink, q)
+    if pos.dtype != torch.int64:
+        raise TypeError("pos must be int64")
+    if seq_offsets is not None and seq_offsets.dtype != torch.int64:
+        raise TypeError("seq_offsets must be int64")
+    o = out if out is not None else torch.empty((B, hq, dv), dtype=q.dtype, device=q.device)
+    _check_same(q, k_cache, v_cache, o, pos, seq_offsets, k_scale, v_scale)
+    need = lib.hswa_decode_workspace_size(layout, B, hq, dv, window, int(max_pos))
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    st = lib.swa_sink_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                 _ptr(v_scale), layout, _ptr(seq_offsets), _ptr(pos), _ptr(sink),
+                                 _ptr(o), B, hq, hkv, dqk, dv, window, int(max_pos), scale,
+                                 rope_theta, rotary_fraction, _dtype_code(q), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(q))
     _raise(st)
     return o
 

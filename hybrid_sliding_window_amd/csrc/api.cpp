@@ -181,8 +181,79 @@ hswa_status_t prefill_impl(const void* q, const void* k, const void* v, const fl
   }
   hipError_t e = persist     ? hswa::launch_prefill_persist(a, s)
                  : per_block ? hswa::launch_prefill_bf16(a, s)
-                             : hswa::launch_generic(a, hswa::MODE_PREFILL, dtype == HSWA_BF16, s);
+                             : hswa::launch_generic(a, hswa::MODE_PREFILL, dtype == HSWA_BF16, false, s);
   return hip_status(e, "prefill launch");
+}
+
+// Decode over bf16 / fp32 caches (kv_fp8 false) or E4M3 caches with per-kv-head
+// scales (kv_fp8 true).
+hswa_status_t decode_impl(const void* q, const void* k_cache, const void* v_cache, bool kv_fp8,
+                          const float* k_scale, const float* v_scale, hswa_kv_layout_t layout,
+                          const long long* seq_offsets, const long long* pos, const float* sink,
+                          void* o, int batch, int hq, int hkv, int d_qk, int d_v, int window,
+                          long long max_pos, float scale, float rope_theta, float rotary_fraction,
+                          hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  hswa_status_t st =
+      check_common(batch, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction, dtype);
+  if (st != HSWA_OK) return st;
+  if (layout != HSWA_KV_RING && layout != HSWA_KV_CONTIGUOUS)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "layout must be HSWA_KV_RING or HSWA_KV_CONTIGUOUS");
+  if (window < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "window must be >= 0");
+  if (layout == HSWA_KV_RING && window == 0)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "a ring cache needs window > 0 (its slot count)");
+  if (layout == HSWA_KV_RING && seq_offsets)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "seq_offsets must be NULL for a ring cache");
+  if (layout == HSWA_KV_CONTIGUOUS && !seq_offsets)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "seq_offsets is required for a contiguous cache");
+  if (max_pos < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "max_pos must be >= 0");
+  if (batch == 0) return ok();
+  if (!q || !k_cache || !v_cache || !o || !pos)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, caches, pos and o must be non-null");
+  if (kv_fp8 && (!k_scale || !v_scale))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "FP8 caches need k_scale and v_scale");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, caches and o must be 16-byte aligned");
+  if (batch > 65535) return fail(HSWA_ERR_UNSUPPORTED, "batch above 65535");
+
+  AttnArgs a = base_args(batch, 0, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction);
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.o = o;
+  a.sink = sink;
+  a.seq_offsets = seq_offsets;
+  a.pos = pos;
+  a.window = window;
+  a.max_pos = max_pos;
+  a.kscale = k_scale;
+  a.vscale = v_scale;
+  const int lay = (layout == HSWA_KV_RING) ? 0 : 1;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool mfma = dtype == HSWA_BF16 && (kv_fp8 ? hswa::decode_fp8_supported(a)
+                                                  : hswa::decode_bf16_supported(a));
+  if (mfma) {
+    const size_t need = hswa_decode_workspace_size(layout, batch, hq, d_v, window, max_pos);
+    if (!workspace || workspace_bytes < need)
+      return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_decode_workspace_size()");
+    if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    hswa::decode_split_plan(lay, window, max_pos, &a.split_keys, &a.nsplit);
+    a.ws = static_cast<float*>(workspace);
+    // the (m, l) pairs follow the partial outputs directly: with d_v = 128 each
+    // entry is 512 bytes, so the output region is already 256-byte aligned;
+    // the rotated queries follow the (m, l) region
+    const size_t per = (size_t)batch * hq * (size_t)a.nsplit;
+    a.qrot = static_cast<unsigned char*>(workspace) + round256(per * (size_t)d_v * sizeof(float)) +
+             round256(per * 2 * sizeof(float));
+    return hip_status(kv_fp8 ? hswa::launch_decode_fp8(a, lay, s) : hswa::launch_decode_bf16(a, lay, s),
+                      "decode launch");
+  }
+  if (!generic_fits(d_qk, d_v)) return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
+  return hip_status(hswa::launch_generic(a, lay == 0 ? hswa::MODE_DECODE_RING
+                                                     : hswa::MODE_DECODE_CONTIG,
+                                         dtype == HSWA_BF16, kv_fp8, s),
+                    "decode launch");
 }
 
 }  // namespace
@@ -257,59 +328,22 @@ hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_
                               float scale, float rope_theta, float rotary_fraction,
                               hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  hswa_status_t st =
-      check_common(batch, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction, dtype);
-  if (st != HSWA_OK) return st;
-  if (layout != HSWA_KV_RING && layout != HSWA_KV_CONTIGUOUS)
-    return fail(HSWA_ERR_INVALID_ARGUMENT, "layout must be HSWA_KV_RING or HSWA_KV_CONTIGUOUS");
-  if (window < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "window must be >= 0");
-  if (layout == HSWA_KV_RING && window == 0)
-    return fail(HSWA_ERR_INVALID_ARGUMENT, "a ring cache needs window > 0 (its slot count)");
-  if (layout == HSWA_KV_RING && seq_offsets)
-    return fail(HSWA_ERR_INVALID_ARGUMENT, "seq_offsets must be NULL for a ring cache");
-  if (layout == HSWA_KV_CONTIGUOUS && !seq_offsets)
-    return fail(HSWA_ERR_INVALID_ARGUMENT, "seq_offsets is required for a contiguous cache");
-  if (max_pos < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "max_pos must be >= 0");
-  if (batch == 0) return ok();
-  if (!q || !k_cache || !v_cache || !o || !pos)
-    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, caches, pos and o must be non-null");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
-    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, caches and o must be 16-byte aligned");
-  if (batch > 65535) return fail(HSWA_ERR_UNSUPPORTED, "batch above 65535");
+  return decode_impl(q, k_cache, v_cache, false, nullptr, nullptr, layout, seq_offsets, pos, sink,
+                     o, batch, hq, hkv, d_qk, d_v, window, max_pos, scale, rope_theta,
+                     rotary_fraction, dtype, workspace, workspace_bytes, stream);
+}
 
-  AttnArgs a = base_args(batch, 0, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction);
-  a.q = q;
-  a.k = k_cache;
-  a.v = v_cache;
-  a.o = o;
-  a.sink = sink;
-  a.seq_offsets = seq_offsets;
-  a.pos = pos;
-  a.window = window;
-  a.max_pos = max_pos;
-  const int lay = (layout == HSWA_KV_RING) ? 0 : 1;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == HSWA_BF16 && hswa::decode_bf16_supported(a)) {
-    const size_t need = hswa_decode_workspace_size(layout, batch, hq, d_v, window, max_pos);
-    if (!workspace || workspace_bytes < need)
-      return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_decode_workspace_size()");
-    if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-    hswa::decode_split_plan(lay, window, max_pos, &a.split_keys, &a.nsplit);
-    a.ws = static_cast<float*>(workspace);
-    // the (m, l) pairs follow the partial outputs directly: with d_v = 128 each
-    // entry is 512 bytes, so the output region is already 256-byte aligned;
-    // the rotated queries follow the (m, l) region
-    const size_t per = (size_t)batch * hq * (size_t)a.nsplit;
-    a.qrot = static_cast<unsigned char*>(workspace) + round256(per * (size_t)d_v * sizeof(float)) +
-             round256(per * 2 * sizeof(float));
-    return hip_status(hswa::launch_decode_bf16(a, lay, s), "decode launch");
-  }
-  if (!generic_fits(d_qk, d_v)) return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
-  return hip_status(hswa::launch_generic(a, lay == 0 ? hswa::MODE_DECODE_RING
-                                                     : hswa::MODE_DECODE_CONTIG,
-                                         dtype == HSWA_BF16, s),
-                    "decode launch");
+hswa_status_t swa_sink_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                  const float* k_scale, const float* v_scale,
+                                  hswa_kv_layout_t layout, const long long* seq_offsets,
+                                  const long long* pos, const float* sink, void* o, int batch,
+                                  int hq, int hkv, int d_qk, int d_v, int window,
+                                  long long max_pos, float scale, float rope_theta,
+                                  float rotary_fraction, hswa_dtype_t dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return decode_impl(q, k_cache, v_cache, true, k_scale, v_scale, layout, seq_offsets, pos, sink,
+                     o, batch, hq, hkv, d_qk, d_v, window, max_pos, scale, rope_theta,
+                     rotary_fraction, dtype, workspace, workspace_bytes, stream);
 }
 
 hswa_status_t sparse_sink_attn(const void* q, const void* k, const void* v, const int* sel_idx,
@@ -357,7 +391,7 @@ hswa_status_t sparse_sink_attn(const void* q, const void* k, const void* v, cons
     if (e != hipSuccess) return hip_status(e, "rope preparation launch");
   }
   hipError_t e = use_mfma ? hswa::launch_sparse_bf16(a, s)
-                          : hswa::launch_generic(a, hswa::MODE_SPARSE, dtype == HSWA_BF16, s);
+                          : hswa::launch_generic(a, hswa::MODE_SPARSE, dtype == HSWA_BF16, false, s);
   return hip_status(e, "sparse launch");
 }
 

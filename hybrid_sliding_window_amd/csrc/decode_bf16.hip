@@ -29,6 +29,7 @@
 #include <math.h>
 
 #include "common.h"
+#include "decode_keys.h"
 #include "launch.h"
 
 namespace hswa {
@@ -51,27 +52,6 @@ static_assert((KINSTR + VINSTR) % HG == 0 && KINSTR % HG == 0, "even split of th
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
-
-// Key range of sequence b: `len` keys, key t is cache row `row0 + t`.
-// Returns false for a position the caller's contract rules out.
-__device__ __forceinline__ bool key_range(const AttnArgs& a, int layout, int b, long long* p_out,
-                                          long long* row0, long long* len) {
-  const long long p = a.pos[b];
-  *p_out = p;
-  if (p < 0 || p > a.max_pos) return false;
-  if (layout == 0) {  // ring: slots 0 .. min(p, W-1) hold tokens
-    *row0 = (long long)b * a.window;
-    *len = (p + 1 < a.window) ? p + 1 : a.window;
-    return true;
-  }
-  const long long off = a.seq_offsets[b];
-  const long long rows = a.seq_offsets[b + 1] - off;
-  if (p >= rows) return false;
-  const long long lo = (a.window > 0 && p - a.window + 1 > 0) ? p - a.window + 1 : 0;
-  *row0 = off + lo;
-  *len = p - lo + 1;
-  return true;
-}
 
 }  // namespace
 
@@ -326,21 +306,29 @@ void decode_split_plan(int layout, int window, long long max_pos, int* split_key
   *nsplit = (int)((lmax + sk - 1) / sk);
 }
 
-hipError_t launch_decode_bf16(const AttnArgs& a, int layout, hipStream_t stream) {
+hipError_t launch_decode_rope_q(const AttnArgs& a, int layout, hipStream_t stream) {
+  if (a.B == 0 || a.half == 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_rope_q_kernel, dim3((unsigned)a.hq, (unsigned)a.B), dim3(64), 0, stream,
+                     a, layout);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const AttnArgs& a, int layout, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
-  if (a.half > 0) {
-    hipLaunchKernelGGL(decode_rope_q_kernel, dim3((unsigned)a.hq, (unsigned)a.B), dim3(64), 0, stream,
-                       a, layout);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  dim3 g1((unsigned)(a.hkv / HG), (unsigned)a.nsplit, (unsigned)a.B);
-  hipLaunchKernelGGL(decode_split_kernel, g1, dim3(256), 0, stream, a, layout);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   dim3 g2((unsigned)a.hq, (unsigned)a.B);
   hipLaunchKernelGGL(decode_combine_kernel, g2, dim3(64), 0, stream, a, layout);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_bf16(const AttnArgs& a, int layout, hipStream_t stream) {
+  if (a.B == 0) return hipSuccess;
+  hipError_t e = launch_decode_rope_q(a, layout, stream);
+  if (e != hipSuccess) return e;
+  dim3 g1((unsigned)(a.hkv / HG), (unsigned)a.nsplit, (unsigned)a.B);
+  hipLaunchKernelGGL(decode_split_kernel, g1, dim3(256), 0, stream, a, layout);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_decode_combine(a, layout, stream);
 }
 
 }  // namespace hswa

@@ -34,6 +34,14 @@ struct Elem<bf16_t> {
   }
   static __device__ __forceinline__ void put_nan(bf16_t* p, long long i) { p[i] = 0x7fc0u; }
 };
+// OCP E4M3 codes of an FP8 cache (read only); the hardware conversion is exact.
+typedef uint8_t e4m3_t;
+template <>
+struct Elem<e4m3_t> {
+  static __device__ __forceinline__ float get(const e4m3_t* p, long long i) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)p[i], 0);
+  }
+};
 
 constexpr int kGenMaxPerLane = 4;  // dims per lane: 4 * 64 = 256
 
@@ -44,8 +52,11 @@ __device__ __forceinline__ float rotated(const T* row, int d, int half, float c,
   return Elem<T>::get(row, d) * c + Elem<T>::get(row, d - half) * s;
 }
 
-template <typename T, int MODE>
+// T: storage of q and o; TKV: storage of k and v (T, or E4M3 codes whose
+// values are code * kscale[g] / vscale[g] in the decode modes).
+template <typename T, typename TKV, int MODE>
 __global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
+  constexpr bool kFp8 = sizeof(TKV) == 1;
   const int lane = threadIdx.x;
   const long long row = blockIdx.x;
   const int h = (int)(row % a.hq);
@@ -53,8 +64,8 @@ __global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
   const int G = a.hq / a.hkv;
   const int g = h / G;
   const T* q = static_cast<const T*>(a.q);
-  const T* k = static_cast<const T*>(a.k);
-  const T* v = static_cast<const T*>(a.v);
+  const TKV* k = static_cast<const TKV*>(a.k);
+  const TKV* v = static_cast<const TKV*>(a.v);
   T* o = static_cast<T*>(a.o);
   const int R = 2 * a.half;
 
@@ -137,9 +148,11 @@ __global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
   float l = (m > kNegInf) ? 1.f : 0.f;
   float od[kGenMaxPerLane] = {0.f, 0.f, 0.f, 0.f};
 
+  const float ksc = kFp8 ? a.kscale[g] : 1.f;
+  const float vsc = kFp8 ? a.vscale[g] : 1.f;
   auto visit = [&](long long j) {
-    const T* krow = k + ((kbase + j) * a.hkv + g) * (long long)a.d_qk;
-    const T* vrow = v + ((kbase + j) * a.hkv + g) * (long long)a.d_v;
+    const TKV* krow = k + ((kbase + j) * a.hkv + g) * (long long)a.d_qk;
+    const TKV* vrow = v + ((kbase + j) * a.hkv + g) * (long long)a.d_v;
     const bool rot_k = (MODE == MODE_PREFILL || MODE == MODE_SPARSE) && R > 0;
     float part = 0.f;
 #pragma unroll
@@ -151,11 +164,11 @@ __global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
         const float2 cs = a.rope[j * a.half + ((d < a.half) ? d : d - a.half)];
         kv = rotated(krow, d, a.half, cs.x, cs.y);
       } else {
-        kv = Elem<T>::get(krow, d);
+        kv = Elem<TKV>::get(krow, d);
       }
       part += qd[u] * kv;
     }
-    const float sc = wave_sum(part) * a.scale;
+    const float sc = wave_sum(part) * (a.scale * ksc);
     const float mn = fmaxf(m, sc);
     const float alpha = expf(m - mn);           // m = -inf gives 0
     const float pj = expf(sc - mn);
@@ -163,7 +176,7 @@ __global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < kGenMaxPerLane; ++u) {
       const int d = lane + 64 * u;
-      if (d < a.d_v) od[u] = od[u] * alpha + pj * Elem<T>::get(vrow, d);
+      if (d < a.d_v) od[u] = od[u] * alpha + pj * Elem<TKV>::get(vrow, d);
     }
     m = mn;
   };
@@ -180,7 +193,7 @@ __global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
   }
   for (long long j = lo; j <= hi; ++j) visit(j);
 
-  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+  const float inv = (l > 0.f) ? vsc / l : 0.f;
 #pragma unroll
   for (int u = 0; u < kGenMaxPerLane; ++u) {
     const int d = lane + 64 * u;
@@ -188,7 +201,7 @@ __global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
   }
 }
 
-template <typename T>
+template <typename T, typename TKV>
 static hipError_t launch_t(const AttnArgs& a, int mode, hipStream_t stream) {
   long long rows = (mode == MODE_PREFILL)  ? (long long)a.B * a.nq * a.hq
                    : (mode == MODE_SPARSE) ? (long long)a.B * a.n * a.hq
@@ -197,23 +210,42 @@ static hipError_t launch_t(const AttnArgs& a, int mode, hipStream_t stream) {
   dim3 grid((unsigned)rows), block(64);
   switch (mode) {
     case MODE_PREFILL:
-      hipLaunchKernelGGL((generic_attn_kernel<T, MODE_PREFILL>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((generic_attn_kernel<T, TKV, MODE_PREFILL>), grid, block, 0, stream, a);
       break;
     case MODE_SPARSE:
-      hipLaunchKernelGGL((generic_attn_kernel<T, MODE_SPARSE>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((generic_attn_kernel<T, TKV, MODE_SPARSE>), grid, block, 0, stream, a);
       break;
     case MODE_DECODE_RING:
-      hipLaunchKernelGGL((generic_attn_kernel<T, MODE_DECODE_RING>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((generic_attn_kernel<T, TKV, MODE_DECODE_RING>), grid, block, 0, stream,
+                         a);
       break;
     default:
-      hipLaunchKernelGGL((generic_attn_kernel<T, MODE_DECODE_CONTIG>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((generic_attn_kernel<T, TKV, MODE_DECODE_CONTIG>), grid, block, 0,
+                         stream, a);
       break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_generic(const AttnArgs& a, int mode, bool bf16, hipStream_t stream) {
-  return bf16 ? launch_t<bf16_t>(a, mode, stream) : launch_t<float>(a, mode, stream);
+// FP8 caches are a decode format: only the two decode modes are built for them.
+template <typename T>
+static hipError_t launch_fp8(const AttnArgs& a, int mode, hipStream_t stream) {
+  dim3 grid((unsigned)((long long)a.B * a.hq)), block(64);
+  if (a.B == 0) return hipSuccess;
+  if (mode == MODE_DECODE_RING)
+    hipLaunchKernelGGL((generic_attn_kernel<T, e4m3_t, MODE_DECODE_RING>), grid, block, 0,
+                       stream, a);
+  else if (mode == MODE_DECODE_CONTIG)
+    hipLaunchKernelGGL((generic_attn_kernel<T, e4m3_t, MODE_DECODE_CONTIG>), grid, block, 0,
+                       stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_generic(const AttnArgs& a, int mode, bool bf16, bool kv_fp8, hipStream_t stream) {
+  if (kv_fp8) return bf16 ? launch_fp8<bf16_t>(a, mode, stream) : launch_fp8<float>(a, mode, stream);
+  return bf16 ? launch_t<bf16_t, bf16_t>(a, mode, stream) : launch_t<float, float>(a, mode, stream);
 }
 
 }  // namespace hswa

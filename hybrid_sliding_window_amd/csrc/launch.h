@@ -22,6 +22,8 @@ struct AttnArgs {
   const float2* rope;             // prefill / sparse: cos/sin table [n][half]
   const void* krot;               // prefill / sparse bf16: K's first R dims, rotated [B, n, hkv, R]
   void* qrot;                     // decode bf16: q rotated to pos[b] [B, hq, d_qk] (workspace)
+  const float* kscale;            // decode FP8 caches: per-kv-head value of one K code unit [hkv]
+  const float* vscale;            // the same for V
   int B, n, hq, hkv, d_qk, d_v;   // n: tokens of K/V (and q unless chunked)
   int nq;                         // prefill: query tokens per sequence (n unless chunked)
   int qoff;                       // prefill: sequence position of query token 0 (n - nq)
@@ -52,7 +54,8 @@ hipError_t launch_rope_k_direct(const uint16_t* k, uint16_t* krot, int B, int n,
                                 hipStream_t stream);
 
 // Any shape, any key set, fp32 or bf16 storage: one wavefront per query row.
-hipError_t launch_generic(const AttnArgs& a, int mode, bool bf16, hipStream_t stream);
+// kv_fp8 (decode modes only): K/V are E4M3 codes scaled by kscale / vscale.
+hipError_t launch_generic(const AttnArgs& a, int mode, bool bf16, bool kv_fp8, hipStream_t stream);
 
 // bf16 matrix-core kernels for d_qk = 192, d_v = 128.
 bool prefill_bf16_supported(const AttnArgs& a);
@@ -67,6 +70,14 @@ hipError_t launch_prefill_persist(const AttnArgs& a, hipStream_t stream);
 bool decode_bf16_supported(const AttnArgs& a);
 void decode_split_plan(int layout, int window, long long max_pos, int* split_keys, int* nsplit);
 hipError_t launch_decode_bf16(const AttnArgs& a, int layout, hipStream_t stream);
+// The two kernels around a decode split kernel: q rotated to its position
+// (no-op without RoPE) and the combine of the split partials with the sink.
+hipError_t launch_decode_rope_q(const AttnArgs& a, int layout, hipStream_t stream);
+hipError_t launch_decode_combine(const AttnArgs& a, int layout, hipStream_t stream);
+
+// Decode over E4M3 caches (same shapes as the bf16 decode kernel).
+bool decode_fp8_supported(const AttnArgs& a);
+hipError_t launch_decode_fp8(const AttnArgs& a, int layout, hipStream_t stream);
 
 bool sparse_bf16_supported(const AttnArgs& a);
 hipError_t launch_sparse_bf16(const AttnArgs& a, hipStream_t stream);

@@ -154,6 +154,32 @@ hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_
                               hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * Single-token decode over an FP8 KV cache: a cache narrowed by the window
+ * and stored in FP8 ("MiMo v2.5 inference optimisation" (youngju.dev),
+ * closing section: the two savings stack; "MiMo-V3 HySparse2"
+ * (aideepthink.cn), section 5, sizes its KV cache in FP8).  Same operation,
+ * layouts, pos / max_pos / seq_offsets contract, workspace
+ * (hswa_decode_workspace_size) and error behaviour as swa_sink_decode,
+ * except:
+ *   k_cache, v_cache hold one byte per element, an OCP FP8 E4M3 code
+ *   (sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities;
+ *   S.1111.111 is NaN and must not occur);
+ *   k_scale, v_scale: fp32 [hkv] DEVICE arrays: element d of kv head g's key
+ *   has the value e4m3(code) * k_scale[g], of its value vector
+ *   e4m3(code) * v_scale[g].
+ * dtype selects q and o (HSWA_BF16 or HSWA_F32).  E4M3 values are exact in
+ * bf16, so the cache enters the products unrounded.
+ */
+hswa_status_t swa_sink_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                  const float* k_scale, const float* v_scale,
+                                  hswa_kv_layout_t layout, const long long* seq_offsets,
+                                  const long long* pos, const float* sink, void* o, int batch,
+                                  int hq, int hkv, int d_qk, int d_v, int window,
+                                  long long max_pos, float scale, float rope_theta,
+                                  float rotary_fraction, hswa_dtype_t dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace sparse_sink_attn needs: same layout and size as
  * hswa_prefill_workspace_size (0 without RoPE). */
 size_t hswa_sparse_workspace_size(int batch, int seqlen, int hkv, int d_qk,

@@ -29,7 +29,7 @@ def lib():
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_]+)\s*\(", text, flags=re.M)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)
     return sorted(set(names))
 
 
@@ -126,6 +126,23 @@ def test_decode_validation(lib):
     assert call(max_pos=-1) == INVALID
     assert call() == INVALID                               # workspace missing
     assert call(batch=0) == OK
+
+
+def test_decode_fp8_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, layout=0, offs=None, pos=FAKE, sink=None,
+                 o=FAKE, batch=2, hq=8, hkv=4, d_qk=192, d_v=128, window=128, max_pos=1000,
+                 scale=0.0, theta=1e4, frac=0.0, dtype=1, ws=None, ws_bytes=0, stream=None)
+        a.update(kw)
+        return lib.swa_sink_decode_fp8(*a.values())
+    assert call(ks=None) == INVALID
+    assert "k_scale" in lib.hswa_last_error().decode()
+    assert call(vs=None) == INVALID
+    assert call(layout=1) == INVALID                       # contiguous needs offsets
+    assert call(window=0) == INVALID                       # ring needs its slot count
+    assert call(k=MISALIGNED) == INVALID
+    assert call() == INVALID                               # workspace missing
+    assert call(batch=0, ks=None) == OK
 
 
 def test_sparse_validation(lib):

@@ -479,6 +479,99 @@ def test_hybrid_decode_full_size(gpu_lib):
 
 
 # ---------------------------------------------------------------------------
+# Decode over FP8 (E4M3) caches with per-kv-head scales
+# ---------------------------------------------------------------------------
+
+def _codes(t):
+    return t.cpu().numpy()
+
+
+@pytest.mark.parametrize("qdtype", ["bf16", "f32"])
+def test_ring_decode_fp8(gpu_lib, qdtype):
+    """bf16 q: matrix-core kernel; fp32 q: generic kernel."""
+    pos = [0, 1, 5, 126, 127, 128, 1000, 131072, 262143, 77777]
+    d = synthetic.ring_decode_inputs_fp8(len(pos), 64, 8, 128, 192, 128, 180,
+                                         torch.tensor(pos), DEV, qdtype=qdtype)
+    o = gpu_lib.swa_sink_decode_fp8(d["q"], d["k"], d["v"], d["k_scale"], d["v_scale"], d["pos"],
+                                    max(pos), layout=gpu_lib.KV_RING, sink=d["sink"], window=128,
+                                    rope_theta=1.0e4, rotary_fraction=0.334)
+    ref = oracle.swa_sink_decode_ring_fp8(_np(d["q"]), _codes(d["k"]), _codes(d["v"]),
+                                          _np(d["k_scale"]), _np(d["v_scale"]), np.array(pos),
+                                          _np(d["sink"]), rope_theta=1.0e4, rotary_fraction=0.334)
+    _check(f"ring decode fp8 cache, q {qdtype}", o, ref, fp32=(qdtype == "f32"))
+
+
+@pytest.mark.parametrize("hq,hkv,window,sink,qdtype", [
+    (64, 4, 0, None, "bf16"),            # GA layer: matrix-core kernel
+    (64, 8, 128, (-2.0, 2.0), "bf16"),   # windowed SWA layer over the contiguous pool
+    (24, 3, 0, None, "bf16"),            # hkv not a multiple of 4: generic kernel
+    (64, 2, 0, None, "bf16"),            # G = 32: generic kernel
+    (16, 4, 64, (-1.0, 1.0), "f32"),     # fp32 q / o: generic kernel
+])
+def test_contiguous_decode_fp8(gpu_lib, hq, hkv, window, sink, qdtype):
+    pos = [0, 31, 32, 1000, 5000, 777]
+    d = synthetic.contiguous_decode_inputs_fp8(len(pos), hq, hkv, 192, 128, 190 + hq + hkv,
+                                               torch.tensor(pos), DEV, sink, extra_rows=2,
+                                               qdtype=qdtype)
+    o = gpu_lib.swa_sink_decode_fp8(d["q"], d["k"], d["v"], d["k_scale"], d["v_scale"], d["pos"],
+                                    5000, layout=gpu_lib.KV_CONTIGUOUS,
+                                    seq_offsets=d["seq_offsets"], sink=d["sink"], window=window,
+                                    rope_theta=1.0e7, rotary_fraction=0.334)
+    ref = oracle.swa_sink_decode_contiguous_fp8(
+        _np(d["q"]), _codes(d["k"]), _codes(d["v"]), _np(d["k_scale"]), _np(d["v_scale"]),
+        d["seq_offsets"].cpu().numpy(), np.array(pos), None if sink is None else _np(d["sink"]),
+        window or None, rope_theta=1.0e7, rotary_fraction=0.334)
+    _check(f"contiguous decode fp8 {hq}/{hkv} W={window} q {qdtype}", o, ref,
+           fp32=(qdtype == "f32"))
+
+
+def test_decode_fp8_contract_violations_give_nan(gpu_lib):
+    pos = [10, 500]
+    d = synthetic.contiguous_decode_inputs_fp8(2, 64, 4, 192, 128, 195, torch.tensor(pos), DEV)
+    bad = torch.tensor([10, 600], dtype=torch.int64, device=DEV)
+    o = gpu_lib.swa_sink_decode_fp8(d["q"], d["k"], d["v"], d["k_scale"], d["v_scale"], bad, 600,
+                                    layout=gpu_lib.KV_CONTIGUOUS, seq_offsets=d["seq_offsets"],
+                                    window=0)
+    on = _np(o)
+    assert np.isfinite(on[0]).all() and np.isnan(on[1]).all()
+
+
+def test_hybrid_decode_fp8_full_size(gpu_lib):
+    wl = synthetic.WORKLOADS["hybrid_decode_fp8_b64"]
+    pos = synthetic.decode_positions(wl["B"], *wl["pos_range"], wl["seed"])
+    sw, ga = wl["swa"], wl["ga"]
+    d = synthetic.ring_decode_inputs_fp8(wl["B"], sw["hq"], sw["hkv"], sw["window"], 192, 128,
+                                         wl["seed"], pos, DEV, sw["sink_range"], wl["scale_range"])
+    o = gpu_lib.swa_sink_decode_fp8(d["q"], d["k"], d["v"], d["k_scale"], d["v_scale"], d["pos"],
+                                    wl["pos_range"][1], layout=gpu_lib.KV_RING, sink=d["sink"],
+                                    window=sw["window"])
+    ref = oracle.swa_sink_decode_ring_fp8(_np(d["q"]), _codes(d["k"]), _codes(d["v"]),
+                                          _np(d["k_scale"]), _np(d["v_scale"]), pos.numpy(),
+                                          _np(d["sink"]))
+    _check("hybrid decode fp8 SWA ring (all 64 sequences)", o, ref)
+    del d
+    c = synthetic.contiguous_decode_inputs_fp8(wl["B"], ga["hq"], ga["hkv"], 192, 128, wl["seed"],
+                                               pos, DEV, None, scale_range=wl["scale_range"])
+    args = (c["q"], c["k"], c["v"], c["k_scale"], c["v_scale"], c["pos"], wl["pos_range"][1])
+    og = gpu_lib.swa_sink_decode_fp8(*args, layout=gpu_lib.KV_CONTIGUOUS,
+                                     seq_offsets=c["seq_offsets"], window=0)
+    og2 = gpu_lib.swa_sink_decode_fp8(*args, layout=gpu_lib.KV_CONTIGUOUS,
+                                      seq_offsets=c["seq_offsets"], window=0)
+    assert torch.equal(og, og2)
+    offs = c["seq_offsets"].cpu().numpy()
+    seqs = np.array([int(pos.argmin()), int(pos.argmax()), 17])
+
+    def loader(b):
+        lo, hi = int(offs[b]), int(offs[b + 1])
+        return _codes(c["k"][lo:hi]), _codes(c["v"][lo:hi])
+
+    refg = oracle.swa_sink_decode_contiguous_fp8(_np(c["q"]), None, None, _np(c["k_scale"]),
+                                                 _np(c["v_scale"]), offs, pos.numpy(), None, None,
+                                                 seqs=seqs, kv_loader=loader)
+    _check("hybrid decode fp8 GA contiguous (sampled sequences)", og[torch.from_numpy(seqs)], refg)
+
+
+# ---------------------------------------------------------------------------
 # Sparse
 # ---------------------------------------------------------------------------
 
