@@ -49,4 +49,5 @@ from .attention import (  # noqa: F401
     sparse_sink_attn,
     prefill_rows,
     sparse_rows,
+    sparse_rows_fp8,
 )

@@ -416,3 +416,14 @@ def sparse_sink_attn(q, k, v, sel_idx, sel_count, sink, recent=128, scale=None,
     return sparse_rows(q, k, v, sel_idx, sel_count, np.arange(n), sink, recent=recent,
                        scale=scale, rope_theta=rope_theta, rotary_fraction=rotary_fraction,
                        pos_offset=pos_offset)
+
+
+def sparse_rows_fp8(q, k_codes, v_codes, k_scale, v_scale, sel_idx, sel_count, rows, sink,
+                    recent=128, scale=None, rope_theta=10000.0, rotary_fraction=0.0,
+                    pos_offset=0, restricted=False):
+    """Sparse attention over E4M3 K/V codes: sparse_rows on the cache values
+    (RoPE rotates those values)."""
+    return sparse_rows(q, dequantise_kv(k_codes, k_scale), dequantise_kv(v_codes, v_scale),
+                       sel_idx, sel_count, rows, sink, recent=recent, scale=scale,
+                       rope_theta=rope_theta, rotary_fraction=rotary_fraction,
+                       pos_offset=pos_offset, restricted=restricted)

@@ -21,4 +21,5 @@ from .workloads import (  # noqa: F401
     decode_positions,
     sparse_selection,
     sparse_inputs,
+    sparse_inputs_fp8,
 )

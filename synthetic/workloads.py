@@ -275,6 +275,18 @@ def sparse_selection(B, n, hkv, recent, max_sel, seed, device="cpu", chunk_rows=
     return idx, cnt
 
 
+def sparse_inputs_fp8(B, n, hq, hkv, d_qk, d_v, seed, recent=128, max_sel=1024, device="cpu",
+                      sink_range=(-2.0, 2.0), scale_range=(0.02, 0.04), qdtype="bf16"):
+    """sparse_inputs with K/V as E4M3 codes (uint8) and scales k_scale, v_scale [Hkv]."""
+    d = prefill_inputs(B, n, hq, hkv, d_qk, d_v, "f32", seed, device, sink_range)
+    ks, vs = kv_scales(hkv, scale_range[0], scale_range[1], seed, device)
+    d.update(q=d["q"].to(_torch_dtype(qdtype)), k=e4m3_codes(d["k"], ks), v=e4m3_codes(d["v"], vs),
+             k_scale=ks, v_scale=vs)
+    idx, cnt = sparse_selection(B, n, hkv, recent, max_sel, seed, device)
+    d.update(sel_idx=idx, sel_count=cnt)
+    return d
+
+
 def sparse_inputs(B, n, hq, hkv, d_qk, d_v, dtype, seed, recent=128, max_sel=1024,
                   device="cpu", sink_range=(-2.0, 2.0)):
     d = prefill_inputs(B, n, hq, hkv, d_qk, d_v, dtype, seed, device, sink_range)

@@ -416,6 +416,25 @@ def pin_p14_fp8_cache(O):
     got = O.swa_sink_decode_contiguous_fp8(q, kc2, vc2, ks, vs, offs, pos2, window=None)
     ref = O.swa_sink_decode_contiguous(q, tdeq(kc2, ks), tdeq(vc2, vs), offs, pos2, window=None)
     assert np.abs(got - ref).max() < 1e-12
+    # sparse attention over E4M3 K/V, RoPE rotating the key values
+    n, mx = 24, 5
+    kc3 = rng.integers(0, 126, (1, n, hkv, d), dtype=np.uint8)
+    vc3 = rng.integers(0, 254, (1, n, hkv, dv), dtype=np.uint8) & 0xF7   # no NaN codes
+    q3 = rng.standard_normal((1, n, hq, d))
+    idx = np.full((1, n, hkv, mx), -1, dtype=np.int64)
+    cnt = np.zeros((1, n, hkv), dtype=np.int64)
+    for i in range(n):
+        for g in range(hkv):
+            avail = max(0, i - 3)
+            pick = np.sort(rng.choice(avail, size=min(mx, avail), replace=False)) if avail else []
+            idx[0, i, g, :len(pick)] = pick
+            cnt[0, i, g] = len(pick)
+    rows = np.arange(n)
+    got_s = O.sparse_rows_fp8(q3, kc3, vc3, ks, vs, idx, cnt, rows, sink, recent=4,
+                              rope_theta=3.0, rotary_fraction=0.5)
+    ref_s = O.sparse_rows(q3, tdeq(kc3, ks), tdeq(vc3, vs), idx, cnt, rows, sink, recent=4,
+                          rope_theta=3.0, rotary_fraction=0.5)
+    assert np.abs(got_s - ref_s).max() < 1e-12
     # the same through the per-sequence loader (codes of one sequence at a time)
     got = O.swa_sink_decode_contiguous_fp8(
         q, None, None, ks, vs, offs, pos2, window=None,
@@ -461,6 +480,8 @@ MUTANTS = {
     "e4m3_subnormal_as_normal": ("np.where(e == 0, m * 2.0 ** -9,", "np.where(e < 0, m * 2.0 ** -9,"),
     "fp8_v_scale_dropped": ("dequantise_kv(v_codes, v_scale), pos, sink, scale=scale,",
                             "e4m3_value(v_codes), pos, sink, scale=scale,"),
+    "sparse_fp8_k_scale_dropped": ("return sparse_rows(q, dequantise_kv(k_codes, k_scale),",
+                                   "return sparse_rows(q, e4m3_value(k_codes),"),
     "fp8_scales_swapped": ("return dequantise_kv(kb, k_scale), dequantise_kv(vb, v_scale)",
                            "return dequantise_kv(kb, v_scale), dequantise_kv(vb, k_scale)"),
     "decode_query_not_rotated": ("qb = rope(q[b][None], np.array([p]), rope_theta, rotary_fraction)[0]\n        slots",
