@@ -149,11 +149,11 @@ def only(which, steps, warmup):
     if which == "copy":
         return {"copy": copy_calibration(steps, warmup)}
     parts = {"ga": ["ga"], "chunk": ["chunk"], "decode": ["decode"], "decode_fp8": ["decode_fp8"],
-             "sparse": ["sparse"]}[which]
+             "sparse": ["sparse"], "sparse_fp8": ["sparse_fp8"]}[which]
     return secondary(steps, warmup, parts)
 
 
-def secondary(steps, warmup, parts=("ga", "chunk", "decode", "decode_fp8", "sparse")):
+def secondary(steps, warmup, parts=("ga", "chunk", "decode", "decode_fp8", "sparse", "sparse_fp8")):
     out = {}
     dev = "cuda"
     if "ga" in parts:
@@ -166,6 +166,8 @@ def secondary(steps, warmup, parts=("ga", "chunk", "decode", "decode_fp8", "spar
         _decode_fp8(out, dev)
     if "sparse" in parts:
         _sparse(out, dev)
+    if "sparse_fp8" in parts:
+        _sparse_fp8(out, dev)
     return out
 
 
@@ -347,6 +349,26 @@ def _sparse(out, dev):
     _log(f"sparse {out['sparse_prefill_n65536']}")
 
 
+def _sparse_fp8(out, dev):
+    # The sparse workload over E4M3 K/V (one byte per gathered element)
+    wl = synthetic.WORKLOADS["sparse_prefill_n65536"]
+    x = synthetic.sparse_inputs_fp8(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, wl["seed"],
+                                    wl["recent"], wl["max_sel"], dev, wl["sink_range"])
+    o = torch.empty(1, wl["n"], wl["hq"], 128, dtype=torch.bfloat16, device=dev)
+    fn = lambda: hswa.sparse_sink_attn_fp8(x["q"], x["k"], x["v"], x["k_scale"],  # noqa: E731
+                                           x["v_scale"], x["sel_idx"], x["sel_count"], x["sink"],
+                                           recent_window=wl["recent"], out=o)
+    _, per = timed(fn, 5, 1)
+    i = np.arange(wl["n"])
+    pairs = int((np.minimum(1024, np.maximum(0, i - 128)) + np.minimum(i + 1, 128)).sum()) * wl["hkv"]
+    flops = pairs * (wl["hq"] // wl["hkv"]) * FLOP_PER_PAIR
+    gathered = pairs * (192 + 128)
+    t = float(np.median(per)) / 1e3
+    out["sparse_fp8_prefill_n65536"] = {"tflops": flops / t / 1e12, "ms": t * 1e3,
+                                        "gathered_kv_gbps": gathered / t / 1e9}
+    _log(f"sparse fp8 {out['sparse_fp8_prefill_n65536']}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,7 +377,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["prefill", "ga", "chunk", "decode", "decode_fp8", "sparse", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "ga", "chunk", "decode", "decode_fp8", "sparse", "sparse_fp8", "copy"], default=None,
                     help="run one workload only (for profiler runs); prints its figures as JSON")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     load,
     prefill_workspace_size,
     sparse_sink_attn,
+    sparse_sink_attn_fp8,
     sparse_workspace_size,
     swa_sink_decode,
     swa_sink_decode_fp8,

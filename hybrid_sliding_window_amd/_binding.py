@@ -33,6 +33,8 @@ _SIGNATURES = {
     "hswa_sparse_workspace_size": (_sz, [_i, _i, _i, _i, _f]),
     "sparse_sink_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i, _i,
                               _f, _f, _f, _ll, _i, _vp, _sz, _vp]),
+    "sparse_sink_attn_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i,
+                                  _i, _i, _i, _f, _f, _f, _ll, _i, _vp, _sz, _vp]),
     "hswa_last_error": (ctypes.c_char_p, []),
     "hswa_version": (ctypes.c_char_p, []),
 }
@@ -265,5 +267,34 @@ def sparse_sink_attn(q, k, v, sel_idx, sel_count, sink=None, recent_window=128, 
                               recent_window, _ptr(sink), _ptr(o), B, n, hq, hkv, dqk, dv, scale,
                               rope_theta, rotary_fraction, pos_offset, _dtype_code(q), _ptr(ws),
                               0 if ws is None else ws.numel(), _stream(q))
+    _raise(st)
+    return o
+
+
+def sparse_sink_attn_fp8(q, k, v, k_scale, v_scale, sel_idx, sel_count, sink=None,
+                         recent_window=128, scale=0.0, rope_theta=10000.0, rotary_fraction=0.0,
+                         pos_offset=0, out=None, workspace=None):
+    """sparse_sink_attn over E4M3 K/V codes with per-kv-head scales."""
+    lib = load()
+    B, n, hq, dqk = q.shape
+    hkv, dv = k.shape[2], v.shape[3]
+    max_sel = sel_idx.shape[-1]
+    _fp8_cache(k)
+    _fp8_cache(v)
+    for t in (k_scale, v_scale):
+        if t.dtype != torch.float32 or t.numel() != hkv:
+            raise ValueError("k_scale and v_scale must be float32 with one entry per kv head")
+    sink = _sink(sink, q)
+    if sel_idx.dtype != torch.int32 or sel_count.dtype != torch.int32:
+        raise TypeError("sel_idx and sel_count must be int32")
+    o = out if out is not None else torch.empty((B, n, hq, dv), dtype=q.dtype, device=q.device)
+    _check_same(q, k, v, o, sel_idx, sel_count, k_scale, v_scale)
+    need = lib.hswa_sparse_workspace_size(B, n, hkv, dqk, rotary_fraction)
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    st = lib.sparse_sink_attn_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
+                                  _ptr(sel_idx), _ptr(sel_count), max_sel, recent_window,
+                                  _ptr(sink), _ptr(o), B, n, hq, hkv, dqk, dv, scale, rope_theta,
+                                  rotary_fraction, pos_offset, _dtype_code(q), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(q))
     _raise(st)
     return o

@@ -107,7 +107,7 @@ size_t rope_workspace_bytes(int batch, int seqlen, int hkv, int d_qk, float rota
 // query of the call reads a key before `first` (a chunk behind a long
 // prefix in a windowed layer).
 hipError_t launch_rope_prep(AttnArgs& a, void* workspace, long long pos_offset, int first,
-                            bool rotate_k, bool need_table, hipStream_t s) {
+                            bool rotate_k, bool need_table, hipStream_t s, bool k_e4m3 = false) {
   if (a.half == 0) return hipSuccess;
   float2* table = static_cast<float2*>(workspace);
   const size_t tb = round256((size_t)a.n * a.half * sizeof(float2));
@@ -121,6 +121,9 @@ hipError_t launch_rope_prep(AttnArgs& a, void* workspace, long long pos_offset, 
   hipError_t e = hswa::launch_rope_table(table + (size_t)first * a.half, pos_offset + first,
                                          a.n - first, a.half, a.rope_theta, s);
   if (e != hipSuccess || !rotate_k) return e;
+  if (k_e4m3)
+    return hswa::launch_rope_k_e4m3(static_cast<const uint8_t*>(a.k), table, krot, a.B, a.n, first,
+                                    a.hkv, a.d_qk, a.half, s);
   return hswa::launch_rope_k(static_cast<const uint16_t*>(a.k), table, krot, a.B, a.n, first,
                              a.hkv, a.d_qk, a.half, s);
 }
@@ -256,6 +259,64 @@ hswa_status_t decode_impl(const void* q, const void* k_cache, const void* v_cach
                     "decode launch");
 }
 
+// Token-level sparse attention over bf16 / fp32 K/V (kv_fp8 false) or E4M3
+// K/V codes with per-kv-head scales (kv_fp8 true).
+hswa_status_t sparse_impl(const void* q, const void* k, const void* v, bool kv_fp8,
+                          const float* k_scale, const float* v_scale, const int* sel_idx,
+                          const int* sel_count, int max_sel, int recent_window, const float* sink,
+                          void* o, int batch, int seqlen, int hq, int hkv, int d_qk, int d_v,
+                          float scale, float rope_theta, float rotary_fraction,
+                          long long pos_offset, hswa_dtype_t dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  hswa_status_t st =
+      check_common(batch, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction, dtype);
+  if (st != HSWA_OK) return st;
+  if (seqlen < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "seqlen must be >= 0");
+  if (max_sel < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "max_sel must be >= 0");
+  if (recent_window < 1) return fail(HSWA_ERR_INVALID_ARGUMENT, "recent_window must be >= 1");
+  if (batch == 0 || seqlen == 0) return ok();
+  if (!q || !k || !v || !o || !sel_count || (max_sel > 0 && !sel_idx))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v, o, sel_idx and sel_count must be non-null");
+  if (kv_fp8 && (!k_scale || !v_scale))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "FP8 K/V need k_scale and v_scale");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v and o must be 16-byte aligned");
+  const size_t need = rope_workspace_bytes(batch, seqlen, hkv, d_qk, rotary_fraction);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_sparse_workspace_size()");
+    if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  }
+
+  AttnArgs a = base_args(batch, seqlen, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.sink = sink;
+  a.sel_idx = sel_idx;
+  a.sel_count = sel_count;
+  a.max_sel = max_sel;
+  a.recent = recent_window;
+  a.pos_offset = pos_offset;
+  a.kscale = k_scale;
+  a.vscale = v_scale;
+
+  const bool use_mfma = (dtype == HSWA_BF16) && (kv_fp8 ? hswa::sparse_fp8_supported(a)
+                                                         : hswa::sparse_bf16_supported(a));
+  if (!use_mfma && !generic_fits(d_qk, d_v))
+    return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  {
+    hipError_t e = launch_rope_prep(a, workspace, pos_offset, 0, use_mfma, true, s, kv_fp8);
+    if (e != hipSuccess) return hip_status(e, "rope preparation launch");
+  }
+  hipError_t e = !use_mfma ? hswa::launch_generic(a, hswa::MODE_SPARSE, dtype == HSWA_BF16, kv_fp8, s)
+                 : kv_fp8  ? hswa::launch_sparse_fp8(a, s)
+                           : hswa::launch_sparse_bf16(a, s);
+  return hip_status(e, "sparse launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -352,47 +413,22 @@ hswa_status_t sparse_sink_attn(const void* q, const void* k, const void* v, cons
                                int hkv, int d_qk, int d_v, float scale, float rope_theta,
                                float rotary_fraction, long long pos_offset, hswa_dtype_t dtype,
                                void* workspace, size_t workspace_bytes, void* stream) {
-  hswa_status_t st =
-      check_common(batch, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction, dtype);
-  if (st != HSWA_OK) return st;
-  if (seqlen < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "seqlen must be >= 0");
-  if (max_sel < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "max_sel must be >= 0");
-  if (recent_window < 1) return fail(HSWA_ERR_INVALID_ARGUMENT, "recent_window must be >= 1");
-  if (batch == 0 || seqlen == 0) return ok();
-  if (!q || !k || !v || !o || !sel_count || (max_sel > 0 && !sel_idx))
-    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v, o, sel_idx and sel_count must be non-null");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, v and o must be 16-byte aligned");
-  const size_t need = rope_workspace_bytes(batch, seqlen, hkv, d_qk, rotary_fraction);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need)
-      return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_sparse_workspace_size()");
-    if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-  }
+  return sparse_impl(q, k, v, false, nullptr, nullptr, sel_idx, sel_count, max_sel, recent_window,
+                     sink, o, batch, seqlen, hq, hkv, d_qk, d_v, scale, rope_theta,
+                     rotary_fraction, pos_offset, dtype, workspace, workspace_bytes, stream);
+}
 
-  AttnArgs a = base_args(batch, seqlen, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction);
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.sink = sink;
-  a.sel_idx = sel_idx;
-  a.sel_count = sel_count;
-  a.max_sel = max_sel;
-  a.recent = recent_window;
-  a.pos_offset = pos_offset;
-
-  const bool use_mfma = (dtype == HSWA_BF16) && hswa::sparse_bf16_supported(a);
-  if (!use_mfma && !generic_fits(d_qk, d_v))
-    return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  {
-    hipError_t e = launch_rope_prep(a, workspace, pos_offset, 0, use_mfma, true, s);
-    if (e != hipSuccess) return hip_status(e, "rope preparation launch");
-  }
-  hipError_t e = use_mfma ? hswa::launch_sparse_bf16(a, s)
-                          : hswa::launch_generic(a, hswa::MODE_SPARSE, dtype == HSWA_BF16, false, s);
-  return hip_status(e, "sparse launch");
+hswa_status_t sparse_sink_attn_fp8(const void* q, const void* k, const void* v,
+                                   const float* k_scale, const float* v_scale, const int* sel_idx,
+                                   const int* sel_count, int max_sel, int recent_window,
+                                   const float* sink, void* o, int batch, int seqlen, int hq,
+                                   int hkv, int d_qk, int d_v, float scale, float rope_theta,
+                                   float rotary_fraction, long long pos_offset,
+                                   hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return sparse_impl(q, k, v, true, k_scale, v_scale, sel_idx, sel_count, max_sel, recent_window,
+                     sink, o, batch, seqlen, hq, hkv, d_qk, d_v, scale, rope_theta,
+                     rotary_fraction, pos_offset, dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

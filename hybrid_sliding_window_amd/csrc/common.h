@@ -105,6 +105,21 @@ __device__ __forceinline__ uint2 lds_tr4(const void* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// Codes 2w, 2w + 1 of the 4 E4M3 codes in v (w = 0 or 1) as a packed bf16
+// pair.  The hardware conversion to fp32 is exact, and every E4M3 value is a
+// bf16 value, so keeping the upper halves is exact too.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t v) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(v, HI);
+  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+}
+
+// 8 E4M3 codes -> 8 bf16 (element e from byte e).
+__device__ __forceinline__ uint4 widen8(uint2 w) {
+  return make_uint4(e4m3_pair<false>(w.x), e4m3_pair<true>(w.x), e4m3_pair<false>(w.y),
+                    e4m3_pair<true>(w.y));
+}
+
 // Max / sum across the four lanes l, l^16, l^32, l^48 (same column c).
 __device__ __forceinline__ float max_across_groups(float v) {
   v = fmaxf(v, __shfl_xor(v, 16));

@@ -52,20 +52,6 @@ static_assert(KINSTR % HG == 0 && VINSTR % HG == 0, "even split of the loads");
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-// Codes 2w, 2w + 1 of the 4 bytes in v (w = 0 or 1) as a packed bf16 pair.
-// The conversion to fp32 is exact and so is keeping its upper half.
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3_pair(uint32_t v) {
-  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(v, HI);
-  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
-}
-
-// 8 codes -> 8 bf16 (element e from byte e).
-__device__ __forceinline__ uint4 widen8(uint2 w) {
-  return make_uint4(e4m3_pair<false>(w.x), e4m3_pair<true>(w.x), e4m3_pair<false>(w.y),
-                    e4m3_pair<true>(w.y));
-}
-
 }  // namespace
 
 __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, int layout) {

@@ -53,7 +53,7 @@ __device__ __forceinline__ float rotated(const T* row, int d, int half, float c,
 }
 
 // T: storage of q and o; TKV: storage of k and v (T, or E4M3 codes whose
-// values are code * kscale[g] / vscale[g] in the decode modes).
+// values are code * kscale[g] / vscale[g]; decode and sparse modes).
 template <typename T, typename TKV, int MODE>
 __global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
   constexpr bool kFp8 = sizeof(TKV) == 1;
@@ -227,12 +227,15 @@ static hipError_t launch_t(const AttnArgs& a, int mode, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// FP8 caches are a decode format: only the two decode modes are built for them.
+// E4M3 K/V: the decode modes and sparse attention are built for them.
 template <typename T>
 static hipError_t launch_fp8(const AttnArgs& a, int mode, hipStream_t stream) {
-  dim3 grid((unsigned)((long long)a.B * a.hq)), block(64);
-  if (a.B == 0) return hipSuccess;
-  if (mode == MODE_DECODE_RING)
+  const long long rows = (mode == MODE_SPARSE) ? (long long)a.B * a.n * a.hq : (long long)a.B * a.hq;
+  if (rows == 0) return hipSuccess;
+  dim3 grid((unsigned)rows), block(64);
+  if (mode == MODE_SPARSE)
+    hipLaunchKernelGGL((generic_attn_kernel<T, e4m3_t, MODE_SPARSE>), grid, block, 0, stream, a);
+  else if (mode == MODE_DECODE_RING)
     hipLaunchKernelGGL((generic_attn_kernel<T, e4m3_t, MODE_DECODE_RING>), grid, block, 0,
                        stream, a);
   else if (mode == MODE_DECODE_CONTIG)

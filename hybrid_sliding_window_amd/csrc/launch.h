@@ -47,6 +47,11 @@ hipError_t launch_rope_table(float2* table, long long pos0, int npos, int half, 
 hipError_t launch_rope_k(const uint16_t* k, const float2* table, uint16_t* krot, int B, int n,
                          int first, int hkv, int d, int half, hipStream_t stream);
 
+// The same for K stored as E4M3 codes (krot = bf16 rotation of the codes'
+// values, no scale applied).
+hipError_t launch_rope_k_e4m3(const uint8_t* k, const float2* table, uint16_t* krot, int B, int n,
+                              int first, int hkv, int d, int half, hipStream_t stream);
+
 // The same without a table: cos/sin evaluated per element (fp64 angle in
 // revolutions, reduced, hardware sine/cosine).  Requires half <= 64.
 hipError_t launch_rope_k_direct(const uint16_t* k, uint16_t* krot, int B, int n, int first,
@@ -54,7 +59,7 @@ hipError_t launch_rope_k_direct(const uint16_t* k, uint16_t* krot, int B, int n,
                                 hipStream_t stream);
 
 // Any shape, any key set, fp32 or bf16 storage: one wavefront per query row.
-// kv_fp8 (decode modes only): K/V are E4M3 codes scaled by kscale / vscale.
+// kv_fp8 (decode and sparse modes): K/V are E4M3 codes scaled by kscale / vscale.
 hipError_t launch_generic(const AttnArgs& a, int mode, bool bf16, bool kv_fp8, hipStream_t stream);
 
 // bf16 matrix-core kernels for d_qk = 192, d_v = 128.
@@ -81,5 +86,9 @@ hipError_t launch_decode_fp8(const AttnArgs& a, int layout, hipStream_t stream);
 
 bool sparse_bf16_supported(const AttnArgs& a);
 hipError_t launch_sparse_bf16(const AttnArgs& a, hipStream_t stream);
+// The same over E4M3 K/V codes with per-kv-head scales (kscale, vscale);
+// rotary half-widths 0 or 32.
+bool sparse_fp8_supported(const AttnArgs& a);
+hipError_t launch_sparse_fp8(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace hswa

@@ -72,6 +72,43 @@ __global__ void rope_k_kernel(const bf16_t* __restrict__ k, const float2* __rest
   st16(dst + 8 * c + half, pack8(f1));
 }
 
+// The same for K stored as E4M3 codes: the codes' values (exact in fp32)
+// are rotated and rounded to bf16 once.  The per-head scale is not applied:
+// rotation is linear, so the attention kernel multiplies the whole score by
+// it instead.
+__global__ void rope_k_e4m3_kernel(const uint8_t* __restrict__ k, const float2* __restrict__ table,
+                                   bf16_t* __restrict__ krot, long long rows, int n, int first,
+                                   int hkv, int d, int half) {
+  const int cpr = half >> 3;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * cpr) return;
+  const long long u = idx / cpr;
+  const int c = (int)(idx - u * cpr);
+  long long row, j;
+  tail_row(u, n, first, hkv, &row, &j);
+  const uint8_t* src = k + row * d;
+  const uint2 w0 = *reinterpret_cast<const uint2*>(src + 8 * c);
+  const uint2 w1 = *reinterpret_cast<const uint2*>(src + 8 * c + half);
+  float f0[8], f1[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    f0[e] = __builtin_amdgcn_cvt_f32_fp8((int)((e < 4 ? w0.x : w0.y) >> (8 * (e & 3))), 0);
+    f1[e] = __builtin_amdgcn_cvt_f32_fp8((int)((e < 4 ? w1.x : w1.y) >> (8 * (e & 3))), 0);
+  }
+  const float2* t = table + j * half + 8 * c;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float2 cs = t[e];
+    const float y0 = f0[e] * cs.x - f1[e] * cs.y;
+    const float y1 = f1[e] * cs.x + f0[e] * cs.y;
+    f0[e] = y0;
+    f1[e] = y1;
+  }
+  bf16_t* dst = krot + row * (2 * half);
+  st16(dst + 8 * c, pack8(f0));
+  st16(dst + 8 * c + half, pack8(f1));
+}
+
 // The same rotation of K without a table, for attention kernels that also
 // rotate q without one: the pair's frequency theta^(-r/half) (fp64, once per
 // block into LDS) times the position gives the angle in revolutions in fp64,
@@ -132,6 +169,18 @@ hipError_t launch_rope_k(const uint16_t* k, const float2* table, uint16_t* krot,
   const long long blocks = (total + threads - 1) / threads;
   hipLaunchKernelGGL(rope_k_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, k, table,
                      krot, rows, n, first, hkv, d, half);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_k_e4m3(const uint8_t* k, const float2* table, uint16_t* krot, int B, int n,
+                              int first, int hkv, int d, int half, hipStream_t stream) {
+  const long long rows = (long long)B * (n - first) * hkv;
+  const long long total = rows * (half >> 3);
+  if (total == 0) return hipSuccess;
+  const int threads = 256;
+  const long long blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(rope_k_e4m3_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, k,
+                     table, krot, rows, n, first, hkv, d, half);
   return hipGetLastError();
 }
 

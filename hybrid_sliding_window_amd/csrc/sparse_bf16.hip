@@ -15,6 +15,11 @@
 // small LDS transpose.
 // Workgroups are remapped so that consecutive queries of one kv head run on
 // one XCD and share the recent window in its L2.
+//
+// The FP8 instantiation reads K/V as E4M3 codes (8 codes per operand slot,
+// widened exactly to bf16 in registers); the rotated dims come from the copy
+// rotated once per call from the codes' values.  k_scale multiplies the
+// score, v_scale the output.
 #include "common.h"
 #include "launch.h"
 
@@ -62,8 +67,11 @@ __device__ __forceinline__ void rotate_any(float (&f)[KS][8], const float2* trow
 
 }  // namespace
 
-__global__ __launch_bounds__(64) void sparse_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t svt[DV * VSTR];
+// FP8: K/V are E4M3 codes; NR (FP8 only): k-steps inside the rotated dims
+// (R / 32, a compile-time constant so that every gather of a tile is issued
+// before the first is used).
+template <bool FP8, int NR>
+__device__ __forceinline__ void sparse_attn(const AttnArgs& a, bf16_t* svt) {
   const int lane = threadIdx.x, c = lane & 15, grp = lane >> 4;
   const int n = a.n;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -75,6 +83,8 @@ __global__ __launch_bounds__(64) void sparse_bf16_kernel(AttnArgs a) {
 
   const bf16_t* __restrict__ Kp = static_cast<const bf16_t*>(a.k);
   const bf16_t* __restrict__ Vp = static_cast<const bf16_t*>(a.v);
+  const uint8_t* __restrict__ Kc = static_cast<const uint8_t*>(a.k);   // E4M3 codes (FP8)
+  const uint8_t* __restrict__ Vc = static_cast<const uint8_t*>(a.v);
   const bf16_t* __restrict__ Kr = static_cast<const bf16_t*>(a.krot);
   const int R = 2 * a.half;
 
@@ -98,7 +108,7 @@ __global__ __launch_bounds__(64) void sparse_bf16_kernel(AttnArgs a) {
     for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(pack8(f[ks]));
   }
 
-  const float c2 = a.scale * kLog2e;   // raw score -> base-2 units
+  const float c2 = a.scale * kLog2e * (FP8 ? a.kscale[g] : 1.f);   // raw score -> base-2 units
   const float s2 = (c < G && a.sink) ? a.sink[g * G + c] * kLog2e : kNegInf;
   float m = s2;
   float l = (grp == 0 && s2 > kNegInf) ? 1.f : 0.f;
@@ -129,30 +139,69 @@ __global__ __launch_bounds__(64) void sparse_bf16_kernel(AttnArgs a) {
     // K rows straight into A-operand registers; k-steps inside the rotated
     // dims come from the rotated copy made once per call.
     uint4 kr[2][KS];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int j = __shfl(myj, sub * 16 + c);
-      if (j >= 0) {
-        const long long row = (tokbase + j) * a.hkv + g;
-        const bf16_t* kp = Kp + row * D + 8 * grp;
-        const bf16_t* kq = Kr + row * R + 8 * grp;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[sub][ks] = ld16((32 * ks < R) ? kq + 32 * ks : kp + 32 * ks);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[sub][ks] = make_uint4(0, 0, 0, 0);
-      }
-    }
     uint4 vr[2][4];
+    if (FP8) {
+      // every gather first (codes of the unrotated k-steps, rotated bf16 dims,
+      // V codes), then the widening
+      uint2 k8[2][KS], v8[2][4];
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const int u = lane + 64 * w;
-      const int kq = u & 7, dc = u >> 3;
+      for (int sub = 0; sub < 2; ++sub) {
+        const int j = __shfl(myj, sub * 16 + c);
+        const long long row = (tokbase + (j >= 0 ? j : 0)) * a.hkv + g;
+        const bf16_t* kq = Kr + row * (32 * NR) + 8 * grp;
+        const uint8_t* kp = Kc + row * D + 8 * grp;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int j = __shfl(myj, 4 * kq + q4);
-        vr[w][q4] = (j >= 0) ? ld16(Vp + ((tokbase + j) * a.hkv + g) * DV + 8 * dc)
-                             : make_uint4(0, 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks < NR) kr[sub][ks] = (j >= 0) ? ld16(kq + 32 * ks) : make_uint4(0, 0, 0, 0);
+          else k8[sub][ks] = (j >= 0) ? *reinterpret_cast<const uint2*>(kp + 32 * ks)
+                                      : make_uint2(0, 0);
+        }
+      }
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int u = lane + 64 * w;
+        const int kq = u & 7, dc = u >> 3;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int j = __shfl(myj, 4 * kq + q4);
+          const long long vo = ((tokbase + (j >= 0 ? j : 0)) * a.hkv + g) * DV + 8 * dc;
+          v8[w][q4] = (j >= 0) ? *reinterpret_cast<const uint2*>(Vc + vo) : make_uint2(0, 0);
+        }
+      }
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int ks = NR; ks < KS; ++ks) kr[sub][ks] = widen8(k8[sub][ks]);
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) vr[w][q4] = widen8(v8[w][q4]);
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int j = __shfl(myj, sub * 16 + c);
+        if (j >= 0) {
+          const long long row = (tokbase + j) * a.hkv + g;
+          const bf16_t* kq = Kr + row * R + 8 * grp;
+          const bf16_t* kp = Kp + row * D + 8 * grp;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            kr[sub][ks] = ld16((32 * ks < R) ? kq + 32 * ks : kp + 32 * ks);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) kr[sub][ks] = make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int u = lane + 64 * w;
+        const int kq = u & 7, dc = u >> 3;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int j = __shfl(myj, 4 * kq + q4);
+          vr[w][q4] = (j >= 0) ? ld16(Vp + ((tokbase + j) * a.hkv + g) * DV + 8 * dc)
+                               : make_uint4(0, 0, 0, 0);
+        }
       }
     }
 
@@ -215,7 +264,7 @@ __global__ __launch_bounds__(64) void sparse_bf16_kernel(AttnArgs a) {
 
   const float lt = sum_across_groups(l);
   if (c < G) {
-    const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+    const float inv = (lt > 0.f) ? (FP8 ? a.vscale[g] : 1.f) / lt : 0.f;
     bf16_t* orow = static_cast<bf16_t*>(a.o) + ((tokbase + i) * a.hq + g * G + c) * DV + 4 * grp;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -224,6 +273,18 @@ __global__ __launch_bounds__(64) void sparse_bf16_kernel(AttnArgs a) {
       st8(orow + 16 * t, w);
     }
   }
+}
+
+__global__ __launch_bounds__(64) void sparse_bf16_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t svt[DV * VSTR];
+  sparse_attn<false, 0>(a, svt);
+}
+
+// NR: rotated k-steps (rotary half-width 0 or 32)
+template <int NR>
+__global__ __launch_bounds__(64) void sparse_fp8_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t svt[DV * VSTR];
+  sparse_attn<true, NR>(a, svt);
 }
 
 bool sparse_bf16_supported(const AttnArgs& a) {
@@ -237,6 +298,23 @@ hipError_t launch_sparse_bf16(const AttnArgs& a, hipStream_t stream) {
   if (total == 0) return hipSuccess;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(sparse_bf16_kernel, dim3((unsigned)total), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+bool sparse_fp8_supported(const AttnArgs& a) {
+  return sparse_bf16_supported(a) && (a.half == 0 || a.half == 32);
+}
+
+hipError_t launch_sparse_fp8(const AttnArgs& a, hipStream_t stream) {
+  const long long total = (long long)a.B * a.hkv * a.n;
+  if (total == 0) return hipSuccess;
+  if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (a.half == 0)
+    hipLaunchKernelGGL(sparse_fp8_kernel<0>, dim3((unsigned)total), dim3(64), 0, stream, a);
+  else if (a.half == 32)
+    hipLaunchKernelGGL(sparse_fp8_kernel<2>, dim3((unsigned)total), dim3(64), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

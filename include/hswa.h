@@ -205,6 +205,28 @@ hswa_status_t sparse_sink_attn(const void* q, const void* k, const void* v, cons
                                float rotary_fraction, long long pos_offset, hswa_dtype_t dtype,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sparse_sink_attn over FP8 K/V: the sparse attention of "MiMo-V3
+ * HySparse2" (aideepthink.cn), section 4, on one shared cache kept in FP8
+ * (the same page, section 5, sizes its KV cache in FP8).  Same operation,
+ * layouts, selection contract, workspace (hswa_sparse_workspace_size) and
+ * error behaviour as sparse_sink_attn, except:
+ *   k, v hold one byte per element, an OCP FP8 E4M3 code (as
+ *   swa_sink_decode_fp8; NaN codes must not occur);
+ *   k_scale, v_scale: fp32 [hkv] DEVICE arrays; element d of token j's key in
+ *   kv head g is e4m3(code) * k_scale[g], of its value e4m3(code) * v_scale[g].
+ * RoPE (rotary_fraction > 0) rotates those key values at their positions, as
+ * for sparse_sink_attn.  dtype selects q and o (HSWA_BF16 or HSWA_F32).
+ */
+hswa_status_t sparse_sink_attn_fp8(const void* q, const void* k, const void* v,
+                                   const float* k_scale, const float* v_scale, const int* sel_idx,
+                                   const int* sel_count, int max_sel, int recent_window,
+                                   const float* sink, void* o, int batch, int seqlen, int hq,
+                                   int hkv, int d_qk, int d_v, float scale, float rope_theta,
+                                   float rotary_fraction, long long pos_offset,
+                                   hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* Text for the last non-OK status returned on this thread ("" if none). */
 const char* hswa_last_error(void);
 

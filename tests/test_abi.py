@@ -160,6 +160,21 @@ def test_sparse_validation(lib):
     assert call(seqlen=0) == OK
 
 
+def test_sparse_fp8_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, idx=FAKE, cnt=FAKE, max_sel=16, recent=8,
+                 sink=None, o=FAKE, batch=1, seqlen=32, hq=4, hkv=2, d_qk=192, d_v=128, scale=0.0,
+                 theta=1e4, frac=0.0, pos_offset=0, dtype=1, ws=None, ws_bytes=0, stream=None)
+        a.update(kw)
+        return lib.sparse_sink_attn_fp8(*a.values())
+    assert call(ks=None) == INVALID
+    assert "k_scale" in lib.hswa_last_error().decode()
+    assert call(vs=None) == INVALID
+    assert call(recent=0) == INVALID
+    assert call(frac=0.334) == INVALID                     # workspace missing
+    assert call(seqlen=0, ks=None) == OK
+
+
 def test_binding_rejects_bad_tensors(lib):
     import torch
     q = torch.zeros(1, 4, 2, 192, dtype=torch.float16)

@@ -627,3 +627,45 @@ def test_sparse_full_size(gpu_lib):
                              x["sel_idx"][:, ridx].cpu().numpy(), x["sel_count"][:, ridx].cpu().numpy(),
                              rows, _np(x["sink"]), recent=wl["recent"], restricted=True)
     _check("sparse full size (sampled rows)", o[:, ridx], ref)
+
+
+# ---------------------------------------------------------------------------
+# Sparse attention over FP8 (E4M3) K/V
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,hq,hkv,recent,max_sel,frac,qdtype", [
+    (1500, 64, 4, 128, 1024, 0.0, "bf16"),   # the workload's shape: matrix-core kernel
+    (400, 16, 2, 32, 64, 0.334, "bf16"),     # RoPE on the key values (rotated copy from codes)
+    (300, 64, 2, 16, 20, 0.0, "bf16"),       # G = 32: generic kernel
+    (200, 8, 2, 16, 24, 0.334, "f32"),       # fp32 q / o: generic kernel with RoPE
+])
+def test_sparse_fp8(gpu_lib, n, hq, hkv, recent, max_sel, frac, qdtype):
+    x = synthetic.sparse_inputs_fp8(1, n, hq, hkv, 192, 128, 130 + n, recent, max_sel, DEV,
+                                    qdtype=qdtype)
+    o = gpu_lib.sparse_sink_attn_fp8(x["q"], x["k"], x["v"], x["k_scale"], x["v_scale"],
+                                     x["sel_idx"], x["sel_count"], x["sink"], recent_window=recent,
+                                     rope_theta=1.0e4, rotary_fraction=frac, pos_offset=9)
+    ref = oracle.sparse_rows_fp8(_np(x["q"]), _codes(x["k"]), _codes(x["v"]), _np(x["k_scale"]),
+                                 _np(x["v_scale"]), x["sel_idx"].cpu().numpy(),
+                                 x["sel_count"].cpu().numpy(), np.arange(n), _np(x["sink"]),
+                                 recent=recent, rope_theta=1.0e4, rotary_fraction=frac,
+                                 pos_offset=9)
+    _check(f"sparse fp8 n={n} {hq}/{hkv} recent={recent} sel={max_sel} q {qdtype}", o, ref,
+           fp32=(qdtype == "f32"))
+
+
+def test_sparse_fp8_full_size(gpu_lib):
+    wl = synthetic.WORKLOADS["sparse_prefill_n65536"]
+    x = synthetic.sparse_inputs_fp8(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, wl["seed"],
+                                    wl["recent"], wl["max_sel"], DEV, wl["sink_range"])
+    o = gpu_lib.sparse_sink_attn_fp8(x["q"], x["k"], x["v"], x["k_scale"], x["v_scale"],
+                                     x["sel_idx"], x["sel_count"], x["sink"],
+                                     recent_window=wl["recent"])
+    rows = _sample_rows(wl["n"], 121)
+    ridx = torch.from_numpy(rows).to(DEV)
+    ref = oracle.sparse_rows_fp8(_np(x["q"][:, ridx]), _codes(x["k"]), _codes(x["v"]),
+                                 _np(x["k_scale"]), _np(x["v_scale"]),
+                                 x["sel_idx"][:, ridx].cpu().numpy(),
+                                 x["sel_count"][:, ridx].cpu().numpy(), rows, _np(x["sink"]),
+                                 recent=wl["recent"], restricted=True)
+    _check("sparse fp8 full size (sampled rows)", o[:, ridx], ref)
