@@ -42,6 +42,8 @@ from .attention import (  # noqa: F401
     ga_prefill,
     swa_sink_decode_ring,
     swa_sink_decode_contiguous,
+    decode_multi_ring,
+    decode_multi_contiguous,
     e4m3_value,
     dequantise_kv,
     swa_sink_decode_ring_fp8,

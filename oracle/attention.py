@@ -315,6 +315,85 @@ def swa_sink_decode_contiguous(q, k, v, seq_offsets, pos, sink=None, window=None
 
 
 # ----------------------------------------------------------------------------
+# Multi-token decode: the last accepted token and its drafts (MTP verification)
+# ----------------------------------------------------------------------------
+
+def decode_multi_ring(q, k_ring, v_ring, pos, sink, window, scale=None, rope_theta=10000.0,
+                      rotary_fraction=0.0):
+    """One verification step of multi-token prediction against a ring cache.
+
+    The MTP drafts are checked by the main model in one forward pass ("visual
+    reading: MiMo MTP/SWA, not MLA" (syt-nju.github.io), MTP section: three
+    draft tokens verified at almost no extra cost; youngju.dev, architecture
+    section: the 3-layer MTP).  q: [B, T, Hq, d]: query t of sequence b is
+    the token at position pos[b] + t (the last accepted one, then T - 1
+    drafts); each attends causally, also among the drafts, to positions
+    max(0, p - W + 1) .. p.  k_ring: [B, S, Hkv, d], v_ring: [B, S, Hkv, dv]
+    hold token j in slot j mod S, written up to position pos[b] + T - 1.
+    Reading: the ring needs S >= W + T - 1 slots, or the drafts would have
+    overwritten keys the first queries still see; checked here.
+    Returns [B, T, Hq, dv].
+    """
+    q = np.asarray(q)
+    B, T, hq, d = q.shape
+    S = k_ring.shape[1]
+    hkv = k_ring.shape[2]
+    G = _check_heads(hq, hkv)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s_all = _sink_vector(sink, hq)
+    out = np.zeros((B, T, hq, v_ring.shape[-1]), dtype=np.float64)
+    for b in range(B):
+        newest = int(pos[b]) + T - 1
+        held = ring_slot_positions(newest, S)
+        kb = np.asarray(k_ring[b], dtype=np.float64)
+        vb = np.asarray(v_ring[b], dtype=np.float64)
+        for t in range(T):
+            p = int(pos[b]) + t
+            J = window_keys(p, window)
+            slots = np.mod(J, S)
+            if not np.array_equal(held[slots], J):
+                raise ValueError("the ring no longer holds every key of query t: S < W + T - 1")
+            qt = rope(q[b, t][None], np.array([p]), rope_theta, rotary_fraction)[0]
+            for g in range(hkv):
+                hs = slice(g * G, (g + 1) * G)
+                out[b, t, hs] = attend_row(qt[hs], kb[slots, g], vb[slots, g], s_all[hs], scale)
+    return out
+
+
+def decode_multi_contiguous(q, k, v, seq_offsets, pos, sink=None, window=None, scale=None,
+                            rope_theta=1.0e7, rotary_fraction=0.0):
+    """decode_multi_ring's step against a contiguous per-sequence cache:
+    sequence b owns rows seq_offsets[b] .. seq_offsets[b+1]-1, its token j is
+    row seq_offsets[b] + j, and rows up to position pos[b] + T - 1 are
+    written.  window None: the full causal prefix (a GA layer)."""
+    q = np.asarray(q)
+    B, T, hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s_all = _sink_vector(sink, hq)
+    out = None
+    for b in range(B):
+        lo, hi = int(seq_offsets[b]), int(seq_offsets[b + 1])
+        kb = np.asarray(k[lo:hi], dtype=np.float64)
+        vb = np.asarray(v[lo:hi], dtype=np.float64)
+        if int(pos[b]) + T - 1 >= kb.shape[0]:
+            raise ValueError("every query position must index a row of its sequence")
+        hkv = kb.shape[1]
+        G = _check_heads(hq, hkv)
+        if out is None:
+            out = np.zeros((B, T, hq, vb.shape[-1]), dtype=np.float64)
+        for t in range(T):
+            p = int(pos[b]) + t
+            J = window_keys(p, window)
+            qt = rope(q[b, t][None], np.array([p]), rope_theta, rotary_fraction)[0]
+            for g in range(hkv):
+                hs = slice(g * G, (g + 1) * G)
+                out[b, t, hs] = attend_row(qt[hs], kb[J, g], vb[J, g], s_all[hs], scale)
+    return out
+
+
+# ----------------------------------------------------------------------------
 # FP8 KV cache: E4M3 codes with one scale per kv head
 # ----------------------------------------------------------------------------
 

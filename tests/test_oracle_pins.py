@@ -442,10 +442,50 @@ def pin_p14_fp8_cache(O):
     assert np.abs(got - ref).max() < 1e-12
 
 
+def pin_p15_multi_token_decode(O):
+    """MTP verification step (syt-nju.github.io MTP section): T queries at
+    p .. p + T - 1 over a ring of S >= W + T - 1 slots or a contiguous cache
+    equal those rows of the scalar brute-force prefill of the sequence (RoPE,
+    sinks, G = 2, causal among the drafts); a ring of W slots is refused."""
+    rng = np.random.default_rng(43)
+    L, d, dv, hq, hkv = 11, 8, 4, 4, 2
+    q = rng.standard_normal((1, L, hq, d)) * 1.5
+    k = rng.standard_normal((1, L, hkv, d)) * 1.5
+    v = rng.standard_normal((1, L, hkv, dv))
+    sink = np.array([-1.0, 0.0, 0.5, 2.0])
+    for W in (1, 3, 5):
+        ref = _brute_prefill(q, k, v, sink, W, 3.0, 0.5)
+        for T in (1, 2, 4):
+            p = L - T                      # first query position
+            S = W + T - 1 + 1              # one slot to spare
+            kr = np.zeros((1, S, hkv, d))
+            vr = np.zeros((1, S, hkv, dv))
+            # the ring after writing tokens 0 .. L-1 (the raw keys: the cache
+            # holds them as written; rotation happens in the reference too)
+            for j in range(L):
+                kr[0, j % S], vr[0, j % S] = O.rope(k[:, j:j + 1], np.array([j]), 3.0, 0.5)[0, 0], v[0, j]
+            got = O.decode_multi_ring(q[:, p:], kr, vr, np.array([p]), sink, W, rope_theta=3.0,
+                                      rotary_fraction=0.5)
+            assert np.abs(got - ref[:, p:]).max() < 1e-12, (W, T)
+            kc = O.rope(k[0], np.arange(L), 3.0, 0.5)
+            got = O.decode_multi_contiguous(q[:, p:], kc, v[0], np.array([0, L]), np.array([p]), sink,
+                                            W, rope_theta=3.0, rotary_fraction=0.5)
+            assert np.abs(got - ref[:, p:]).max() < 1e-12, (W, T)
+            if T > 1:
+                small = np.zeros((1, W, hkv, d))
+                with pytest.raises(ValueError):
+                    O.decode_multi_ring(q[:, p:], small, small[..., :dv], np.array([p]), sink, W)
+    # GA (no window, no sink) against SDPA over the whole sequence
+    ref = _sdpa(q, k, v, _window_mask(L, None), None, 1 / math.sqrt(d))
+    got = O.decode_multi_contiguous(q[:, L - 4:], k[0], v[0], np.array([0, L]), np.array([L - 4]))
+    assert np.abs(got - ref[:, L - 4:]).max() < 1e-12
+
+
 PINS = [pin_p1_no_sink_is_masked_softmax, pin_p2_wide_window_is_causal, pin_p3_sink_as_extra_key,
         pin_p4_weights_sum, pin_p5_unit_window, pin_p6_zero_query, pin_p7_brute_force,
         pin_p8_rope, pin_p9_gqa, pin_p10_decode_equals_prefill_row, pin_p11_sparse,
-        pin_p12_large_sink_is_stable, pin_p13_chunk, pin_p14_fp8_cache]
+        pin_p12_large_sink_is_stable, pin_p13_chunk, pin_p14_fp8_cache,
+        pin_p15_multi_token_decode]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -476,6 +516,9 @@ MUTANTS = {
     "sparse_recent_too_wide": ("lo = max(0, i - recent + 1)", "lo = max(0, i - recent)"),
     "sink_in_numerator": ("out[g] = (e @ vj) / den", "out[g] = (e @ vj + math.exp(min(sink[g] - m[g], 0.0))) / den"),
     "chunk_rows_from_zero": ("rows = n - q_len + np.arange(q_len)", "rows = np.arange(q_len)"),
+    "multi_ring_slot_by_window": ("slots = np.mod(J, S)", "slots = np.mod(J, window)"),
+    "multi_query_not_causal_among_drafts": ("            p = int(pos[b]) + t\n            J = window_keys(p, window)\n            qt",
+                                            "            p = int(pos[b]) + t\n            J = window_keys(int(pos[b]) + T - 1, window)\n            qt"),
     "e4m3_bias_8": ("np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
     "e4m3_subnormal_as_normal": ("np.where(e == 0, m * 2.0 ** -9,", "np.where(e < 0, m * 2.0 ** -9,"),
     "fp8_v_scale_dropped": ("dequantise_kv(v_codes, v_scale), pos, sink, scale=scale,",
