@@ -148,12 +148,14 @@ def copy_calibration(steps, warmup):
 def only(which, steps, warmup):
     if which == "copy":
         return {"copy": copy_calibration(steps, warmup)}
-    parts = {"ga": ["ga"], "chunk": ["chunk"], "decode": ["decode"], "decode_fp8": ["decode_fp8"],
+    parts = {"ga": ["ga"], "chunk": ["chunk"], "decode": ["decode"], "decode_mtp": ["decode_mtp"],
+             "decode_fp8": ["decode_fp8"],
              "sparse": ["sparse"], "sparse_fp8": ["sparse_fp8"]}[which]
     return secondary(steps, warmup, parts)
 
 
-def secondary(steps, warmup, parts=("ga", "chunk", "decode", "decode_fp8", "sparse", "sparse_fp8")):
+def secondary(steps, warmup,
+              parts=("ga", "chunk", "decode", "decode_mtp", "decode_fp8", "sparse", "sparse_fp8")):
     out = {}
     dev = "cuda"
     if "ga" in parts:
@@ -162,6 +164,8 @@ def secondary(steps, warmup, parts=("ga", "chunk", "decode", "decode_fp8", "spar
         _chunk(out, steps, warmup, dev)
     if "decode" in parts:
         _decode(out, dev)
+    if "decode_mtp" in parts:
+        _decode_mtp(out, dev)
     if "decode_fp8" in parts:
         _decode_fp8(out, dev)
     if "sparse" in parts:
@@ -283,6 +287,58 @@ def _decode(out, dev):
     _log(f"decode GA {out['decode_ga_contiguous']}")
 
 
+def _decode_mtp(out, dev):
+    # MTP verification step: 64 sequences x 4 queries (last accepted token + 3 drafts)
+    wl = synthetic.WORKLOADS["mtp_decode_b64_t4"]
+    T = wl["T"]
+    pos = synthetic.decode_positions(wl["B"], *wl["pos_range"], wl["seed"])
+    maxp = wl["pos_range"][1] + T - 1
+    sw, ga = wl["swa"], wl["ga"]
+    sets = [synthetic.multi_ring_inputs(wl["B"], T, sw["hq"], sw["hkv"], sw["slots"], 192, 128,
+                                        "bf16", wl["seed"] + 100 * r, pos, dev, sw["sink_range"])
+            for r in range(8)]
+    wsr = torch.empty(hswa.decode_multi_workspace_size(hswa.KV_RING, wl["B"], T, sw["hq"], 128,
+                                                       sw["window"], sw["slots"], maxp),
+                      dtype=torch.uint8, device=dev)
+    orr = torch.empty(wl["B"], T, sw["hq"], 128, dtype=torch.bfloat16, device=dev)
+    it = [0]
+
+    def ring_step():
+        d = sets[it[0] % len(sets)]
+        it[0] += 1
+        hswa.swa_sink_decode_multi(d["q"], d["k"], d["v"], d["pos"], maxp, layout=hswa.KV_RING,
+                                   ring_slots=sw["slots"], sink=d["sink"], window=sw["window"],
+                                   out=orr, workspace=wsr)
+    _, per = timed(ring_step, 40, 8)
+    ring_bytes = (wl["B"] * sw["slots"] * sw["hkv"] * (192 + 128) * 2 +
+                  wl["B"] * T * sw["hq"] * (192 + 128) * 2)
+    t = float(np.median(per)) / 1e3
+    out["decode_mtp_swa_ring"] = {"gbps": ring_bytes / t / 1e9, "us": t * 1e6, "bytes": ring_bytes,
+                                  "queries_per_s": wl["B"] * T / t}
+    _log(f"MTP decode ring {out['decode_mtp_swa_ring']}")
+    del sets
+    c = synthetic.multi_contiguous_inputs(wl["B"], T, ga["hq"], ga["hkv"], 192, 128, "bf16",
+                                          wl["seed"], pos, dev, None)
+    wsc = torch.empty(hswa.decode_multi_workspace_size(hswa.KV_CONTIGUOUS, wl["B"], T, ga["hq"],
+                                                       128, 0, 0, maxp),
+                      dtype=torch.uint8, device=dev)
+    oc = torch.empty(wl["B"], T, ga["hq"], 128, dtype=torch.bfloat16, device=dev)
+    fn = lambda: hswa.swa_sink_decode_multi(c["q"], c["k"], c["v"], c["pos"], maxp,  # noqa: E731
+                                            layout=hswa.KV_CONTIGUOUS,
+                                            seq_offsets=c["seq_offsets"], window=0, out=oc,
+                                            workspace=wsc)
+    _, per = timed(fn, 10, 2)
+    keys = int((pos + T).sum())
+    ga_bytes = keys * ga["hkv"] * (192 + 128) * 2 + wl["B"] * T * ga["hq"] * (192 + 128) * 2
+    pairs = int(sum(int(p) + 1 + tt for p in pos for tt in range(T)))
+    t = float(np.median(per)) / 1e3
+    out["decode_mtp_ga_contiguous"] = {"gbps": ga_bytes / t / 1e9, "ms": t * 1e3, "bytes": ga_bytes,
+                                       "frac_of_hbm_peak": ga_bytes / t / 1e9 / HBM_PEAK_GBPS,
+                                       "tflops": pairs * ga["hq"] * FLOP_PER_PAIR / t / 1e12,
+                                       "queries_per_s": wl["B"] * T / t}
+    _log(f"MTP decode GA {out['decode_mtp_ga_contiguous']}")
+
+
 def _decode_fp8(out, dev):
     # The hybrid decode step over E4M3 caches (one byte per element)
     wl = synthetic.WORKLOADS["hybrid_decode_fp8_b64"]
@@ -377,7 +433,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["prefill", "ga", "chunk", "decode", "decode_fp8", "sparse", "sparse_fp8", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "ga", "chunk", "decode", "decode_mtp", "decode_fp8", "sparse",
+                             "sparse_fp8", "copy"], default=None,
                     help="run one workload only (for profiler runs); prints its figures as JSON")
     args = ap.parse_args()
     if args.gpus != 1:

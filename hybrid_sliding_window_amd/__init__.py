@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     HswaError,
     KV_CONTIGUOUS,
     KV_RING,
+    decode_multi_workspace_size,
     decode_workspace_size,
     ga_prefill,
     lib_path,
@@ -20,6 +21,7 @@ from ._binding import (  # noqa: F401
     sparse_sink_attn_fp8,
     sparse_workspace_size,
     swa_sink_decode,
+    swa_sink_decode_multi,
     swa_sink_decode_fp8,
     swa_sink_prefill,
     swa_sink_prefill_chunk,

@@ -28,6 +28,9 @@ _SIGNATURES = {
     "hswa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i, _ll]),
     "swa_sink_decode": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _ll,
                              _f, _f, _f, _i, _vp, _sz, _vp]),
+    "hswa_decode_multi_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _ll]),
+    "swa_sink_decode_multi": (_i, [_vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                   _i, _i, _ll, _f, _f, _f, _i, _vp, _sz, _vp]),
     "swa_sink_decode_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                                  _i, _i, _ll, _f, _f, _f, _i, _vp, _sz, _vp]),
     "hswa_sparse_workspace_size": (_sz, [_i, _i, _i, _i, _f]),
@@ -207,6 +210,39 @@ def swa_sink_decode(q, k_cache, v_cache, pos, max_pos, layout=KV_RING, seq_offse
                              _ptr(pos), _ptr(sink), _ptr(o), B, hq, hkv, dqk, dv, window,
                              int(max_pos), scale, rope_theta, rotary_fraction, _dtype_code(q),
                              _ptr(ws), 0 if ws is None else ws.numel(), _stream(q))
+    _raise(st)
+    return o
+
+
+def decode_multi_workspace_size(layout, batch, q_len, hq, d_v, window, ring_slots, max_pos):
+    return load().hswa_decode_multi_workspace_size(layout, batch, q_len, hq, d_v, window,
+                                                   ring_slots, max_pos)
+
+
+def swa_sink_decode_multi(q, k_cache, v_cache, pos, max_pos, layout=KV_RING, ring_slots=0,
+                          seq_offsets=None, sink=None, window=128, scale=0.0, rope_theta=10000.0,
+                          rotary_fraction=0.0, out=None, workspace=None):
+    """q [B,T,Hq,d_qk]: T queries per sequence at pos[b] .. pos[b] + T - 1 against a
+    ring [B,S,Hkv,d] (S = ring_slots >= window + T - 1) or packed [rows,Hkv,d] cache
+    -> o [B,T,Hq,d_v]."""
+    lib = load()
+    B, T, hq, dqk = q.shape
+    hkv, dv = k_cache.shape[-2], v_cache.shape[-1]
+    sink = _sink(sink, q)
+    if pos.dtype != torch.int64:
+        raise TypeError("pos must be int64")
+    if seq_offsets is not None and seq_offsets.dtype != torch.int64:
+        raise TypeError("seq_offsets must be int64")
+    o = out if out is not None else torch.empty((B, T, hq, dv), dtype=q.dtype, device=q.device)
+    _check_same(q, k_cache, v_cache, o, pos, seq_offsets)
+    need = lib.hswa_decode_multi_workspace_size(layout, B, T, hq, dv, window, ring_slots,
+                                                int(max_pos))
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    st = lib.swa_sink_decode_multi(_ptr(q), _ptr(k_cache), _ptr(v_cache), layout, ring_slots,
+                                   _ptr(seq_offsets), _ptr(pos), _ptr(sink), _ptr(o), B, T, hq,
+                                   hkv, dqk, dv, window, int(max_pos), scale, rope_theta,
+                                   rotary_fraction, _dtype_code(q), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(q))
     _raise(st)
     return o
 

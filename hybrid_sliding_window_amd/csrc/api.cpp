@@ -317,6 +317,17 @@ hswa_status_t sparse_impl(const void* q, const void* k, const void* v, bool kv_f
   return hip_status(e, "sparse launch");
 }
 
+// Split plan of a multi-token decode: the longest key range is min(last + 1,
+// S) slots of a ring, or W + q_len - 1 (W > 0) or last + 1 rows of a
+// contiguous cache, where last = max_pos is the largest query position.
+void multi_split_plan(hswa_kv_layout_t layout, int q_len, int window, int ring_slots,
+                      long long max_pos, int* split_keys, int* nsplit) {
+  if (layout == HSWA_KV_RING)
+    hswa::decode_split_plan(0, ring_slots, max_pos, split_keys, nsplit);
+  else
+    hswa::decode_split_plan(1, window > 0 ? window + q_len - 1 : 0, max_pos, split_keys, nsplit);
+}
+
 }  // namespace
 
 extern "C" {
@@ -380,6 +391,85 @@ size_t hswa_decode_workspace_size(hswa_kv_layout_t layout, int batch, int hq, in
   const size_t per = (size_t)batch * hq * (size_t)nsplit;
   return round256(per * (size_t)d_v * sizeof(float)) + round256(per * 2 * sizeof(float)) +
          round256((size_t)batch * hq * kDecodeQDims * 2);
+}
+
+size_t hswa_decode_multi_workspace_size(hswa_kv_layout_t layout, int batch, int q_len, int hq,
+                                        int d_v, int window, int ring_slots, long long max_pos) {
+  if (batch <= 0 || q_len <= 0 || hq <= 0 || d_v <= 0 || max_pos < 0) return 0;
+  if (layout != HSWA_KV_RING && layout != HSWA_KV_CONTIGUOUS) return 0;
+  if (layout == HSWA_KV_RING && ring_slots <= 0) return 0;
+  int split_keys = 0, nsplit = 0;
+  multi_split_plan(layout, q_len, window, ring_slots, max_pos, &split_keys, &nsplit);
+  const size_t rows = (size_t)batch * q_len * hq;
+  const size_t per = rows * (size_t)nsplit;
+  return round256(per * (size_t)d_v * sizeof(float)) + round256(per * 2 * sizeof(float)) +
+         round256(rows * kDecodeQDims * 2);
+}
+
+hswa_status_t swa_sink_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                                    hswa_kv_layout_t layout, int ring_slots,
+                                    const long long* seq_offsets, const long long* pos,
+                                    const float* sink, void* o, int batch, int q_len, int hq,
+                                    int hkv, int d_qk, int d_v, int window, long long max_pos,
+                                    float scale, float rope_theta, float rotary_fraction,
+                                    hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  hswa_status_t st =
+      check_common(batch, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction, dtype);
+  if (st != HSWA_OK) return st;
+  if (layout != HSWA_KV_RING && layout != HSWA_KV_CONTIGUOUS)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "layout must be HSWA_KV_RING or HSWA_KV_CONTIGUOUS");
+  if (q_len < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "q_len must be >= 0");
+  if (window < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "window must be >= 0");
+  if (layout == HSWA_KV_RING) {
+    if (window == 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "a ring cache serves a window > 0");
+    if ((long long)ring_slots < (long long)window + q_len - 1)
+      return fail(HSWA_ERR_INVALID_ARGUMENT, "ring_slots must be >= window + q_len - 1");
+    if (seq_offsets) return fail(HSWA_ERR_INVALID_ARGUMENT, "seq_offsets must be NULL for a ring cache");
+  } else {
+    if (ring_slots != 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "ring_slots must be 0 for a contiguous cache");
+    if (!seq_offsets) return fail(HSWA_ERR_INVALID_ARGUMENT, "seq_offsets is required for a contiguous cache");
+  }
+  if (max_pos < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "max_pos must be >= 0");
+  if (batch == 0 || q_len == 0) return ok();
+  if (!q || !k_cache || !v_cache || !o || !pos)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, caches, pos and o must be non-null");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, caches and o must be 16-byte aligned");
+  if (batch > 65535 || q_len > 65535 || hq > 65535)
+    return fail(HSWA_ERR_UNSUPPORTED, "batch, q_len and hq must be at most 65535");
+
+  AttnArgs a = base_args(batch, 0, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction);
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.o = o;
+  a.sink = sink;
+  a.seq_offsets = seq_offsets;
+  a.pos = pos;
+  a.window = window;
+  a.max_pos = max_pos;
+  a.nq = q_len;
+  a.slots = ring_slots;
+  const int lay = (layout == HSWA_KV_RING) ? 0 : 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == HSWA_BF16 && hswa::decode_multi_supported(a)) {
+    const size_t need = hswa_decode_multi_workspace_size(layout, batch, q_len, hq, d_v, window,
+                                                         ring_slots, max_pos);
+    if (!workspace || workspace_bytes < need)
+      return fail(HSWA_ERR_INVALID_ARGUMENT,
+                  "workspace smaller than hswa_decode_multi_workspace_size()");
+    if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    multi_split_plan(layout, q_len, window, ring_slots, max_pos, &a.split_keys, &a.nsplit);
+    a.ws = static_cast<float*>(workspace);
+    const size_t per = (size_t)batch * q_len * hq * (size_t)a.nsplit;
+    a.qrot = static_cast<unsigned char*>(workspace) + round256(per * (size_t)d_v * sizeof(float)) +
+             round256(per * 2 * sizeof(float));
+    return hip_status(hswa::launch_decode_multi(a, lay, s), "multi-token decode launch");
+  }
+  if (!generic_fits(d_qk, d_v)) return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
+  return hip_status(hswa::launch_decode_multi_generic(a, lay, dtype == HSWA_BF16, s),
+                    "multi-token decode launch");
 }
 
 hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_cache,

@@ -1,0 +1,474 @@
+// Multi-token decode: one verification step of multi-token prediction.
+//
+// The MTP drafts are checked by the main model in one forward pass ("visual
+// reading: MiMo MTP/SWA, not MLA" (syt-nju.github.io), MTP section: with the
+// attention FLOPs saved by SWA the model is memory-bound, and verifying the
+// three drafts costs almost nothing extra).  Sequence b brings T queries at
+// positions pos[b] .. pos[b] + T - 1 (the last accepted token, then T - 1
+// drafts); each attends causally, also among the drafts, to positions
+// max(0, p - W + 1) .. p (W = 0: 0 .. p) of its cache, whose rows up to
+// pos[b] + T - 1 are written.  A ring cache holds token j in slot j mod S
+// with S >= W + T - 1 slots, so that the drafts have not overwritten a key
+// the first query still sees.
+//
+// The split-K stream is the single-token decode's: a workgroup owns
+// (sequence b, four kv heads, split s) and streams its keys in 16-key tiles
+// through LDS with global_load_lds.  Each tile now serves all T * G query
+// columns of a kv head: the N side of the MFMAs is one or two blocks of 16
+// columns (column n = token n / G, head n % G), and past 32 columns two
+// wavefronts share a kv head, each with its half of the columns.  The cache
+// is read once for all T tokens, so the step costs about what a single-token
+// step does while the matrix cores do T times the work.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace hswa {
+namespace {
+
+constexpr int D = 192;
+constexpr int DV = 128;
+constexpr int KS = D / 32;
+constexpr int NT = DV / 16;
+constexpr int BK = 16;                    // keys per tile
+constexpr int HG = 4;                     // kv heads per workgroup
+constexpr int KROW = HG * D * 2;          // 1536 B: the group's K of one cache row
+constexpr int VROW = HG * DV * 2;         // 1024 B: its V
+constexpr int KTILE = BK * KROW;          // 24 KB
+constexpr int VTILE = BK * VROW;          // 16 KB
+constexpr int KINSTR = KTILE / 1024;      // 24 load instructions of 1 KB
+constexpr int VINSTR = VTILE / 1024;      // 16
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Keys of sequence b: cache rows row0 .. row0 + len - 1.  p0 = pos[b].
+// Returns false for a sequence the caller's contract rules out.
+__device__ __forceinline__ bool multi_range(const AttnArgs& a, int layout, int b, long long* p0,
+                                            long long* row0, long long* len) {
+  const long long p = a.pos[b];
+  const long long last = p + a.nq - 1;
+  *p0 = p;
+  if (p < 0 || last > a.max_pos) return false;
+  if (layout == 0) {  // ring: slots 0 .. min(last, S-1) hold tokens
+    *row0 = (long long)b * a.slots;
+    *len = (last + 1 < a.slots) ? last + 1 : a.slots;
+    return true;
+  }
+  const long long off = a.seq_offsets[b];
+  const long long rows = a.seq_offsets[b + 1] - off;
+  if (last >= rows) return false;
+  const long long lo = (a.window > 0 && p - a.window + 1 > 0) ? p - a.window + 1 : 0;
+  *row0 = off + lo;
+  *len = last - lo + 1;
+  return true;
+}
+
+// Sequence position of key kk (0-based in the key range).
+struct KeyPos {
+  long long base;    // contiguous: position of key 0; ring: newest position
+  int nm, S;         // ring: newest mod S, slot count; S = 0 for a contiguous cache
+  __device__ __forceinline__ long long operator()(long long kk) const {
+    if (S == 0) return base + kk;
+    int dd = nm - (int)kk;                   // (newest - slot) mod S
+    dd += (dd < 0) ? S : 0;
+    return base - dd;
+  }
+};
+
+__device__ __forceinline__ KeyPos key_pos(const AttnArgs& a, int layout, long long p0,
+                                          long long row0, long long off) {
+  KeyPos kp;
+  if (layout == 0) {
+    kp.base = p0 + a.nq - 1;
+    kp.S = a.slots;
+    kp.nm = (int)(kp.base % a.slots);
+  } else {
+    kp.base = row0 - off;
+    kp.S = 0;
+    kp.nm = 0;
+  }
+  return kp;
+}
+
+}  // namespace
+
+// q of every (sequence, token, head) rotated to its position p0 + t; the
+// angle in fp64 (positions reach 2.6e5), the rotation in fp32, rounded to bf16.
+__global__ __launch_bounds__(64) void decode_multi_rope_q_kernel(AttnArgs a, int layout) {
+  const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  long long p0, row0, len;
+  if (!multi_range(a, layout, b, &p0, &row0, &len)) return;
+  const long long p = p0 + t;
+  const long long rowi = ((long long)b * a.nq + t) * a.hq + h;
+  const bf16_t* q = static_cast<const bf16_t*>(a.q) + rowi * D;
+  bf16_t* qo = static_cast<bf16_t*>(a.qrot) + rowi * D;
+  const int half = a.half;
+  for (int d = threadIdx.x; d < D; d += 64) {
+    if (d < half) {
+      const float x0 = bf16_to_f32(q[d]), x1 = bf16_to_f32(q[d + half]);
+      const double ang = (double)p * pow(a.rope_theta, -(double)d / (double)half);
+      double sd, cd;
+      sincos(ang, &sd, &cd);
+      const float cs = (float)cd, sn = (float)sd;
+      qo[d] = f32_to_bf16_bits(x0 * cs - x1 * sn);
+      qo[d + half] = f32_to_bf16_bits(x1 * cs + x0 * sn);
+    } else if (d >= 2 * half) {
+      qo[d] = q[d];
+    }
+  }
+}
+
+// NB: 16-column blocks per wavefront; CW: wavefronts per kv head (each with
+// NB * 16 of the T * G columns).
+template <int NB, int CW>
+__global__ __launch_bounds__(256 * CW, 3 - CW) void decode_multi_split_kernel(AttnArgs a,
+                                                                                int layout) {
+  constexpr int NWAVE = HG * CW;
+  constexpr int DMA_PER_WAVE = (KINSTR + VINSTR) / NWAVE;
+  static_assert((KINSTR + VINSTR) % NWAVE == 0 && KINSTR % NWAVE == 0, "even split of the loads");
+  __shared__ __attribute__((aligned(16))) unsigned char kst0[KTILE];
+  __shared__ __attribute__((aligned(16))) unsigned char vst0[VTILE];
+  __shared__ __attribute__((aligned(16))) unsigned char kst1[KTILE];
+  __shared__ __attribute__((aligned(16))) unsigned char vst1[VTILE];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
+  const int hw = wave % HG, ch = wave / HG;                     // kv head in group, column half
+  const int gx = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+  const int g = HG * gx + hw;
+  const int lane = tid & 63, c = lane & 15, grp = lane >> 4;
+  const int G = a.hq / a.hkv, T = a.nq;
+
+  long long p0, row0, len;
+  if (!multi_range(a, layout, b, &p0, &row0, &len)) return;   // uniform over the workgroup
+  const long long ks0 = (long long)s * a.split_keys;
+  if (ks0 >= len) return;
+  const long long ks1 = (ks0 + a.split_keys < len) ? ks0 + a.split_keys : len;
+  const int nkeys = (int)(ks1 - ks0);
+  const int ntile = (nkeys + BK - 1) / BK;
+  const KeyPos kpos = key_pos(a, layout, p0, row0, layout == 0 ? 0 : a.seq_offsets[b]);
+
+  // ---- tile copies: the single-token decode's slot map (K slot s: row s / 96,
+  // physical chunk s % 96 holding logical chunk pc ^ row%16; V slot s: row
+  // s / 64, 32-byte unit (s % 64) / 2 holding unit ^ row%8) -----------------
+  const unsigned char* kbase = static_cast<const unsigned char*>(a.k) +
+                               (((row0 + ks0) * a.hkv + HG * gx) * (long long)D) * 2;
+  const unsigned char* vbase = static_cast<const unsigned char*>(a.v) +
+                               (((row0 + ks0) * a.hkv + HG * gx) * (long long)DV) * 2;
+  const int kstride = a.hkv * D * 2, vstride = a.hkv * DV * 2;
+  int drow[DMA_PER_WAVE], doff[DMA_PER_WAVE];
+#pragma unroll
+  for (int u = 0; u < DMA_PER_WAVE; ++u) {
+    const int ii = wave + NWAVE * u;
+    if (ii < KINSTR) {
+      const int sl = 64 * ii + lane;
+      const int row = sl / 96, pc = sl - row * 96;
+      drow[u] = row;
+      doff[u] = 16 * (pc ^ (row & 15));
+    } else {
+      const int sl = 64 * (ii - KINSTR) + lane;
+      const int row = sl >> 6, pc = sl & 63;
+      drow[u] = row;
+      doff[u] = 32 * ((pc >> 1) ^ (row & 7)) + 16 * (pc & 1);
+    }
+  }
+  auto issue = [&](int k0, unsigned char* kd, unsigned char* vd) {
+#pragma unroll
+    for (int u = 0; u < DMA_PER_WAVE; ++u) {
+      const int ii = wave + NWAVE * u;
+      const int key = min(k0 + drow[u], nkeys - 1);
+      if (u < KINSTR / NWAVE)   // wave-uniform: K instructions first, then V
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(kbase + (__umul24(key, kstride) + doff[u])),
+                                         (lds_void_t*)(kd + 1024 * ii), 16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(vbase + (__umul24(key, vstride) + doff[u])),
+                                         (lds_void_t*)(vd + 1024 * (ii - KINSTR)), 16, 0, 0);
+    }
+  };
+
+  issue(0, kst0, vst0);
+
+  // ---- this lane's query columns: n = 16 (NB ch + nb) + c -------------------
+  bf16x8 qf[NB][KS];
+  int ctok[NB];
+  bool cval[NB];
+  {
+    const bf16_t* qsrc = static_cast<const bf16_t*>(a.half > 0 ? a.qrot : a.q);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = 16 * (NB * ch + nb) + c;
+      cval[nb] = n < T * G;
+      const int tn = cval[nb] ? n / G : 0, hn = cval[nb] ? n - tn * G : 0;
+      ctok[nb] = tn;
+      const bf16_t* qrow =
+          qsrc + (((long long)b * T + tn) * a.hq + g * G + hn) * D + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[nb][ks] = as_bf16x8(cval[nb] ? ld16(qrow + 32 * ks) : make_uint4(0, 0, 0, 0));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): q and tile 0 have landed
+
+  const float c2 = a.scale * kLog2e;
+  const int W = a.window;
+  float m[NB], l[NB];
+  f32x4 acc[NT][NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m[nb] = kNegInf;
+    l[nb] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int krow = c * KROW;
+  const int vr = 4 * grp + (c >> 2);
+  const int vrow = vr * VROW + 8 * (c & 3);
+
+  auto tile = [&](int t, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
+                  unsigned char* vn) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile t's loads are this wavefront's only ones
+    __syncthreads();   // every wavefront's share of tile t has landed; tile t-1 is consumed
+    if (t + 1 < ntile) issue((t + 1) * BK, kn, vn);
+    const int k0 = t * BK;
+    // key 4 grp + r of the tile is visible to column token tn iff it exists
+    // and its position lies in [p0 + tn - W + 1, p0 + tn].  Decided before the
+    // score products, with bitwise logic on 32-bit offsets from p0 (a key
+    // range spans less than 2^31 positions), so that only selects follow the
+    // MFMAs: no branch may sit between them and the first VALU read.
+    bool vis[NB][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rel = (int)(kpos(ks0 + k0 + 4 * grp + r) - p0);
+      const bool here = k0 + 4 * grp + r < nkeys;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        vis[nb][r] = here & (rel <= ctok[nb]) & ((W == 0) | (rel > ctok[nb] - W));
+    }
+    f32x4 sc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int q = 24 * hw + 4 * ks + grp;
+      const bf16x8 kf = as_bf16x8(ld16(kc + krow + 16 * (q ^ c)));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma16(kf, qf[nb][ks], sc[nb]);
+    }
+    uint2 pk[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[nb][r] = vis[nb][r] ? sc[nb][r] : kNegInf;
+      float mx = fmaxf(fmaxf(sc[nb][0], sc[nb][1]), fmaxf(sc[nb][2], sc[nb][3]));
+      mx = max_across_groups(mx) * c2;
+      const float mn = fmaxf(m[nb], mx);
+      const float ms = (mn == kNegInf) ? 0.f : mn;
+      const float alpha = fast_exp2(m[nb] - ms);
+      float pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(fmaf(sc[nb][r], c2, -ms));
+      pk[nb] = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
+      l[nb] = l[nb] * alpha + add_bf16_pair(pk[nb].y, add_bf16_pair(pk[nb].x, 0.f));
+      m[nb] = mn;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) acc[tt][nb] *= alpha;
+    }
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const uint2 vt = lds_tr4(vc + vrow + 32 * ((8 * hw + tt) ^ (vr & 7)));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[tt][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            __builtin_bit_cast(v4i16_t, vt), __builtin_bit_cast(v4i16_t, pk[nb]), acc[tt][nb], 0,
+            0, 0);
+    }
+  };
+
+  int t = 0;
+  for (; t + 2 <= ntile; t += 2) {
+    tile(t, kst0, vst0, kst1, vst1);
+    tile(t + 1, kst1, vst1, kst0, vst0);
+  }
+  if (t < ntile) tile(t, kst0, vst0, kst1, vst1);
+
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float lt = sum_across_groups(l[nb]);
+    if (cval[nb]) {
+      const int n = 16 * (NB * ch + nb) + c;
+      const int hn = n - ctok[nb] * G;
+      const long long idx =
+          (((long long)b * T + ctok[nb]) * a.hq + g * G + hn) * a.nsplit + s;
+      float* wo = a.ws + idx * DV + 4 * grp;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+        *reinterpret_cast<float4*>(wo + 16 * tt) =
+            make_float4(acc[tt][nb][0], acc[tt][nb][1], acc[tt][nb][2], acc[tt][nb][3]);
+      if (grp == 0) {
+        float* wml = a.ws + (long long)a.B * T * a.hq * a.nsplit * DV + idx * 2;
+        wml[0] = m[nb];
+        wml[1] = lt;
+      }
+    }
+  }
+}
+
+// Per (b, t, h): M = max(sink, m_s), denominator exp2(sink - M) +
+// sum_s exp2(m_s - M) l_s, output sum_s exp2(m_s - M) O_s over it (the sink
+// enters once).  Splits with no visible key carry m = -inf and drop out.
+__global__ __launch_bounds__(64) void decode_multi_combine_kernel(AttnArgs a, int layout) {
+  const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+  const long long rowi = ((long long)b * a.nq + t) * a.hq + h;
+  bf16_t* orow = static_cast<bf16_t*>(a.o) + rowi * DV;
+  long long p0, row0, len;
+  if (!multi_range(a, layout, b, &p0, &row0, &len)) {
+    orow[lane] = 0x7fc0;
+    orow[lane + 64] = 0x7fc0;
+    return;
+  }
+  const int nspl = (int)((len + a.split_keys - 1) / a.split_keys);
+  const long long base = rowi * a.nsplit;
+  const float* wml = a.ws + (long long)a.B * a.nq * a.hq * a.nsplit * DV + base * 2;
+  const float s2 = a.sink ? a.sink[h] * kLog2e : kNegInf;
+  float M = s2;
+  for (int s = 0; s < nspl; ++s) M = fmaxf(M, wml[2 * s]);
+  float den = (s2 > kNegInf) ? fast_exp2(s2 - M) : 0.f;
+  float o0 = 0.f, o1 = 0.f;
+  for (int s = 0; s < nspl; ++s) {
+    if (wml[2 * s] == kNegInf) continue;
+    const float w = fast_exp2(wml[2 * s] - M);
+    den += w * wml[2 * s + 1];
+    const float* wo = a.ws + (base + s) * DV;
+    o0 += w * wo[lane];
+    o1 += w * wo[lane + 64];
+  }
+  const float inv = (den > 0.f) ? 1.f / den : 0.f;
+  orow[lane] = f32_to_bf16_bits(o0 * inv);
+  orow[lane + 64] = f32_to_bf16_bits(o1 * inv);
+}
+
+// Any shape, bf16 or fp32 storage: one wavefront per (sequence, token, head)
+// row, a running (max, sum, output) over the key range seeded with the sink.
+template <typename T>
+__global__ __launch_bounds__(64) void decode_multi_generic_kernel(AttnArgs a, int layout) {
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  const int G = a.hq / a.hkv, g = h / G;
+  const long long rowi = ((long long)b * a.nq + t) * a.hq + h;
+  const T* q = static_cast<const T*>(a.q) + rowi * a.d_qk;
+  const T* kc = static_cast<const T*>(a.k);
+  const T* vc = static_cast<const T*>(a.v);
+  T* orow = static_cast<T*>(a.o) + rowi * a.d_v;
+  auto ld = [](const T* p, long long i) -> float {
+    if constexpr (sizeof(T) == 2) return bf16_to_f32(reinterpret_cast<const bf16_t*>(p)[i]);
+    else return (float)p[i];
+  };
+  auto st = [](T* p, long long i, float x) {
+    if constexpr (sizeof(T) == 2) reinterpret_cast<bf16_t*>(p)[i] = f32_to_bf16_bits(x);
+    else p[i] = x;
+  };
+  long long p0, row0, len;
+  if (!multi_range(a, layout, b, &p0, &row0, &len)) {
+    for (int d = lane; d < a.d_v; d += 64) {
+      if constexpr (sizeof(T) == 2) reinterpret_cast<bf16_t*>(orow)[d] = 0x7fc0;
+      else reinterpret_cast<uint32_t*>(orow)[d] = 0x7fc00000u;
+    }
+    return;
+  }
+  const long long pq = p0 + t;
+  const KeyPos kpos = key_pos(a, layout, p0, row0, layout == 0 ? 0 : a.seq_offsets[b]);
+  const int R = 2 * a.half;
+  float qd[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int d = lane + 64 * u;
+    qd[u] = 0.f;
+    if (d >= a.d_qk) continue;
+    if (d < R) {
+      const int r = (d < a.half) ? d : d - a.half;
+      const double ang = (double)pq * pow(a.rope_theta, -(double)r / (double)a.half);
+      double sd, cd;
+      sincos(ang, &sd, &cd);
+      const float cs = (float)cd, sn = (float)sd;
+      qd[u] = (d < a.half) ? ld(q, d) * cs - ld(q, d + a.half) * sn
+                           : ld(q, d) * cs + ld(q, d - a.half) * sn;
+    } else {
+      qd[u] = ld(q, d);
+    }
+  }
+  float m = a.sink ? a.sink[h] : kNegInf;
+  float l = (m > kNegInf) ? 1.f : 0.f;
+  float od[4] = {0.f, 0.f, 0.f, 0.f};
+  for (long long kk = 0; kk < len; ++kk) {
+    const long long P = kpos(kk);
+    if (P > pq || (a.window > 0 && P <= pq - a.window)) continue;
+    const T* krow = kc + ((row0 + kk) * a.hkv + g) * (long long)a.d_qk;
+    const T* vrow = vc + ((row0 + kk) * a.hkv + g) * (long long)a.d_v;
+    float part = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = lane + 64 * u;
+      if (d < a.d_qk) part += qd[u] * ld(krow, d);
+    }
+    const float sc = wave_sum(part) * a.scale;
+    const float mn = fmaxf(m, sc);
+    const float alpha = expf(m - mn);
+    const float pj = expf(sc - mn);
+    l = l * alpha + pj;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int d = lane + 64 * u;
+      if (d < a.d_v) od[u] = od[u] * alpha + pj * ld(vrow, d);
+    }
+    m = mn;
+  }
+  const float inv = (l > 0.f) ? 1.f / l : 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int d = lane + 64 * u;
+    if (d < a.d_v) st(orow, d, od[u] * inv);
+  }
+}
+
+bool decode_multi_supported(const AttnArgs& a) {
+  const int G = a.hq / a.hkv;
+  return a.d_qk == D && a.d_v == DV && G >= 1 && a.nq * G <= 64 && a.hkv % HG == 0 &&
+         2 * a.half <= D;
+}
+
+hipError_t launch_decode_multi(const AttnArgs& a, int layout, hipStream_t stream) {
+  if (a.B == 0 || a.nq == 0) return hipSuccess;
+  const dim3 rows((unsigned)a.hq, (unsigned)a.nq, (unsigned)a.B);
+  if (a.half > 0) {
+    hipLaunchKernelGGL(decode_multi_rope_q_kernel, rows, dim3(64), 0, stream, a, layout);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int cols = a.nq * (a.hq / a.hkv);
+  const dim3 g1((unsigned)(a.hkv / HG), (unsigned)a.nsplit, (unsigned)a.B);
+  if (cols <= 16)
+    hipLaunchKernelGGL((decode_multi_split_kernel<1, 1>), g1, dim3(256), 0, stream, a, layout);
+  else if (cols <= 32)
+    hipLaunchKernelGGL((decode_multi_split_kernel<2, 1>), g1, dim3(256), 0, stream, a, layout);
+  else
+    hipLaunchKernelGGL((decode_multi_split_kernel<2, 2>), g1, dim3(512), 0, stream, a, layout);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_multi_combine_kernel, rows, dim3(64), 0, stream, a, layout);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_multi_generic(const AttnArgs& a, int layout, bool bf16,
+                                       hipStream_t stream) {
+  if (a.B == 0 || a.nq == 0) return hipSuccess;
+  const dim3 rows((unsigned)a.hq, (unsigned)a.nq, (unsigned)a.B);
+  if (bf16)
+    hipLaunchKernelGGL((decode_multi_generic_kernel<bf16_t>), rows, dim3(64), 0, stream, a, layout);
+  else
+    hipLaunchKernelGGL((decode_multi_generic_kernel<float>), rows, dim3(64), 0, stream, a, layout);
+  return hipGetLastError();
+}
+
+}  // namespace hswa

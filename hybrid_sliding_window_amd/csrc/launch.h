@@ -25,7 +25,9 @@ struct AttnArgs {
   const float* kscale;            // decode FP8 caches: per-kv-head value of one K code unit [hkv]
   const float* vscale;            // the same for V
   int B, n, hq, hkv, d_qk, d_v;   // n: tokens of K/V (and q unless chunked)
-  int nq;                         // prefill: query tokens per sequence (n unless chunked)
+  int nq;                         // prefill: query tokens per sequence (n unless chunked);
+                                  // multi-token decode: queries per sequence
+  int slots;                      // multi-token decode, ring cache: slot count S
   int qoff;                       // prefill: sequence position of query token 0 (n - nq)
   int window;                     // prefill: 0 = full causal; decode: ring size or window
   int half;                       // R / 2 (0 = no RoPE)
@@ -79,6 +81,15 @@ hipError_t launch_decode_bf16(const AttnArgs& a, int layout, hipStream_t stream)
 // (no-op without RoPE) and the combine of the split partials with the sink.
 hipError_t launch_decode_rope_q(const AttnArgs& a, int layout, hipStream_t stream);
 hipError_t launch_decode_combine(const AttnArgs& a, int layout, hipStream_t stream);
+
+// Multi-token decode (nq queries per sequence at pos[b] .. pos[b] + nq - 1):
+// bf16 matrix-core kernels for d_qk = 192, d_v = 128, hkv % 4 == 0 and
+// nq * G <= 64 (workspace as the single-token decode with B * nq rows), and
+// a generic kernel for any shape, bf16 or fp32 (no workspace).
+bool decode_multi_supported(const AttnArgs& a);
+hipError_t launch_decode_multi(const AttnArgs& a, int layout, hipStream_t stream);
+hipError_t launch_decode_multi_generic(const AttnArgs& a, int layout, bool bf16,
+                                       hipStream_t stream);
 
 // Decode over E4M3 caches (same shapes as the bf16 decode kernel).
 bool decode_fp8_supported(const AttnArgs& a);

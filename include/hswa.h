@@ -154,6 +154,41 @@ hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_
                               hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* Bytes of workspace swa_sink_decode_multi needs: as hswa_decode_workspace_size
+ * with batch * q_len query rows and the key range of the longest query. */
+size_t hswa_decode_multi_workspace_size(hswa_kv_layout_t layout, int batch, int q_len, int hq,
+                                        int d_v, int window, int ring_slots, long long max_pos);
+
+/*
+ * Multi-token decode: one verification step of multi-token prediction, the
+ * last accepted token and its drafts checked in one pass ("visual reading:
+ * MiMo MTP/SWA, not MLA" (syt-nju.github.io), MTP section).
+ *   q [batch, q_len, hq, d_qk]: query t of sequence b is the token at
+ *   position pos[b] + t; o [batch, q_len, hq, d_v].  RoPE rotates query t at
+ *   its position in the call; the cache holds keys already rotated.
+ *   pos: int64 [batch] DEVICE array; the caller has written the keys and
+ *   values of positions up to pos[b] + q_len - 1.  max_pos: host-side bound
+ *   on every pos[b] + q_len - 1.
+ * Query t attends to positions max(0, p - window + 1) .. p, p = pos[b] + t
+ * (window == 0: 0 .. p): causal among the drafts too.
+ * HSWA_KV_RING: k_cache [batch, ring_slots, hkv, d_qk], v_cache
+ *   [batch, ring_slots, hkv, d_v], token j in slot j mod ring_slots;
+ *   window > 0 and ring_slots >= window + q_len - 1, so that the drafts have
+ *   not overwritten a key the first query sees.  seq_offsets must be NULL.
+ * HSWA_KV_CONTIGUOUS: as swa_sink_decode (seq_offsets [batch+1]);
+ *   ring_slots must be 0; every pos[b] + q_len - 1 must be below its row count.
+ * A sequence breaking the contract gets NaN outputs; nothing outside the
+ * cache is read.  q_len == 1 with ring_slots == window is swa_sink_decode.
+ */
+hswa_status_t swa_sink_decode_multi(const void* q, const void* k_cache, const void* v_cache,
+                                    hswa_kv_layout_t layout, int ring_slots,
+                                    const long long* seq_offsets, const long long* pos,
+                                    const float* sink, void* o, int batch, int q_len, int hq,
+                                    int hkv, int d_qk, int d_v, int window, long long max_pos,
+                                    float scale, float rope_theta, float rotary_fraction,
+                                    hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /*
  * Single-token decode over an FP8 KV cache: a cache narrowed by the window
  * and stored in FP8 ("MiMo v2.5 inference optimisation" (youngju.dev),

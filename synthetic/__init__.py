@@ -15,6 +15,8 @@ from .workloads import (  # noqa: F401
     ring_decode_inputs,
     contiguous_decode_inputs,
     kv_scales,
+    multi_ring_inputs,
+    multi_contiguous_inputs,
     e4m3_codes,
     ring_decode_inputs_fp8,
     contiguous_decode_inputs_fp8,

@@ -61,6 +61,15 @@ WORKLOADS = {
                               d_qk=192, d_v=128, dtype="bf16",
                               swa=dict(hq=64, hkv=8, window=128, sink_range=(-2.0, 2.0)),
                               ga=dict(hq=64, hkv=4, window=0, sink_range=None)),
+    # Multi-token (MTP verification) decode step: 64 sequences, the last accepted
+    # token plus 3 drafts each ("visual reading: MiMo MTP/SWA, not MLA",
+    # syt-nju.github.io: 3 MTP blocks), first position in [131072, 262140];
+    # the SWA ring holds W + 3 = 131 slots.
+    "mtp_decode_b64_t4": dict(kind="decode_multi", seed=9, B=64, T=4, pos_range=(131072, 262140),
+                              d_qk=192, d_v=128, dtype="bf16",
+                              swa=dict(hq=64, hkv=8, window=128, slots=131,
+                                       sink_range=(-2.0, 2.0)),
+                              ga=dict(hq=64, hkv=4, window=0, sink_range=None)),
     # The same decode step over FP8 (E4M3) caches with per-kv-head scales.
     "hybrid_decode_fp8_b64": dict(kind="decode_fp8", seed=8, B=64, pos_range=(131072, 262143),
                                   d_qk=192, d_v=128, dtype="bf16", scale_range=(0.02, 0.04),
@@ -173,6 +182,29 @@ def contiguous_decode_inputs(B, hq, hkv, d_qk, d_v, dtype, seed, pos, device="cp
     if sink_range is not None:
         sink = uniform((hq,), sink_range[0], sink_range[1], tensor_seed(seed, TID_SINK), device)
     return dict(q=q, k=k, v=v, sink=sink, pos=pos.to(device), seq_offsets=offs.to(device))
+
+
+def multi_ring_inputs(B, T, hq, hkv, slots, d_qk, d_v, dtype, seed, pos, device="cpu",
+                      sink_range=(-2.0, 2.0)):
+    """q [B,T,Hq,d_qk] (T queries per sequence) and a ring k [B,S,Hkv,d_qk],
+    v [B,S,Hkv,d_v] of S slots."""
+    q = normal((B, T, hq, d_qk), tensor_seed(seed, TID_Q), device, dtype)
+    k = normal((B, slots, hkv, d_qk), tensor_seed(seed, TID_K), device, dtype)
+    v = normal((B, slots, hkv, d_v), tensor_seed(seed, TID_V), device, dtype)
+    sink = None
+    if sink_range is not None:
+        sink = uniform((hq,), sink_range[0], sink_range[1], tensor_seed(seed, TID_SINK), device)
+    return dict(q=q, k=k, v=v, sink=sink, pos=pos.to(device))
+
+
+def multi_contiguous_inputs(B, T, hq, hkv, d_qk, d_v, dtype, seed, pos, device="cpu",
+                            sink_range=None, extra_rows=0):
+    """q [B,T,Hq,d_qk] and a packed cache in which sequence b owns
+    pos[b] + T + extra_rows rows (layout as contiguous_decode_inputs)."""
+    d = contiguous_decode_inputs(B, hq, hkv, d_qk, d_v, dtype, seed, pos, device, sink_range,
+                                 extra_rows=extra_rows + T - 1)
+    d["q"] = normal((B, T, hq, d_qk), tensor_seed(seed, TID_Q_GA), device, dtype)
+    return d
 
 
 def kv_scales(hkv, lo, hi, seed, device="cpu"):

@@ -128,6 +128,29 @@ def test_decode_validation(lib):
     assert call(batch=0) == OK
 
 
+def test_decode_multi_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, layout=0, slots=131, offs=None, pos=FAKE, sink=None,
+                 o=FAKE, batch=2, q_len=4, hq=8, hkv=4, d_qk=192, d_v=128, window=128,
+                 max_pos=1000, scale=0.0, theta=1e4, frac=0.0, dtype=1, ws=None, ws_bytes=0,
+                 stream=None)
+        a.update(kw)
+        return lib.swa_sink_decode_multi(*a.values())
+    assert call(slots=130) == INVALID                      # ring too small for 4 queries
+    assert "ring_slots" in lib.hswa_last_error().decode()
+    assert call(window=0) == INVALID                       # a ring serves a window
+    assert call(offs=FAKE) == INVALID
+    assert call(layout=1, slots=0) == INVALID              # contiguous needs offsets
+    assert call(layout=1, slots=5, offs=FAKE) == INVALID   # ... and no slot count
+    assert call(q_len=-1) == INVALID
+    assert call() == INVALID                               # workspace missing
+    assert call(q_len=0, q=None) == OK
+    r256 = lambda x: ((x + 255) // 256) * 256  # noqa: E731
+    # ring of 131 slots: 5 splits of 32 keys per (sequence, token, head)
+    assert hswa.decode_multi_workspace_size(hswa.KV_RING, 64, 4, 64, 128, 128, 131, 262143) == \
+        64 * 4 * 64 * 5 * 128 * 4 + r256(64 * 4 * 64 * 5 * 2 * 4) + 64 * 4 * 64 * 192 * 2
+
+
 def test_decode_fp8_validation(lib):
     def call(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, layout=0, offs=None, pos=FAKE, sink=None,

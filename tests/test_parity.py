@@ -479,6 +479,124 @@ def test_hybrid_decode_full_size(gpu_lib):
 
 
 # ---------------------------------------------------------------------------
+# Multi-token (MTP verification) decode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,slots,hq,hkv,frac", [
+    (4, 131, 64, 8, 0.334),    # the workload's shape: 32 columns, one wavefront per kv head
+    (2, 140, 64, 8, 0.0),      # spare slots
+    (4, 131, 32, 16, 0.334),   # G = 2: 8 columns
+    (3, 130, 128, 8, 0.0),     # G = 16, T = 3: 48 columns, two wavefronts per kv head
+])
+def test_multi_decode_ring(gpu_lib, T, slots, hq, hkv, frac):
+    pos = [0, 1, 5, 124, 125, 126, 127, 300, 131072, 262140]
+    d = synthetic.multi_ring_inputs(len(pos), T, hq, hkv, slots, 192, 128, "bf16", 200 + T,
+                                    torch.tensor(pos), DEV)
+    o = gpu_lib.swa_sink_decode_multi(d["q"], d["k"], d["v"], d["pos"], max(pos) + T - 1,
+                                      layout=gpu_lib.KV_RING, ring_slots=slots, sink=d["sink"],
+                                      window=128, rope_theta=1.0e4, rotary_fraction=frac)
+    ref = oracle.decode_multi_ring(_np(d["q"]), _np(d["k"]), _np(d["v"]), np.array(pos),
+                                   _np(d["sink"]), 128, rope_theta=1.0e4, rotary_fraction=frac)
+    _check(f"multi decode ring T={T} S={slots} {hq}/{hkv}", o, ref)
+
+
+@pytest.mark.parametrize("T,hq,hkv,window,sink,dtype", [
+    (4, 64, 4, 0, None, "bf16"),            # GA layer: 64 columns, two wavefronts per kv head
+    (2, 64, 4, 0, None, "bf16"),            # 32 columns
+    (1, 64, 4, 0, None, "bf16"),            # one query: 16 columns
+    (4, 64, 8, 128, (-2.0, 2.0), "bf16"),   # windowed over the contiguous pool
+    (4, 24, 3, 0, None, "bf16"),            # hkv not a multiple of 4: generic kernel
+    (4, 16, 4, 64, (-1.0, 1.0), "f32"),     # fp32: generic kernel
+])
+def test_multi_decode_contiguous(gpu_lib, T, hq, hkv, window, sink, dtype):
+    pos = [0, 29, 31, 1000, 5000, 777]
+    d = synthetic.multi_contiguous_inputs(len(pos), T, hq, hkv, 192, 128, dtype, 210 + T + hkv,
+                                          torch.tensor(pos), DEV, sink, extra_rows=2)
+    o = gpu_lib.swa_sink_decode_multi(d["q"], d["k"], d["v"], d["pos"], max(pos) + T - 1,
+                                      layout=gpu_lib.KV_CONTIGUOUS, seq_offsets=d["seq_offsets"],
+                                      sink=d["sink"], window=window, rope_theta=1.0e7,
+                                      rotary_fraction=0.334)
+    ref = oracle.decode_multi_contiguous(_np(d["q"]), _np(d["k"]), _np(d["v"]),
+                                         d["seq_offsets"].cpu().numpy(), np.array(pos),
+                                         None if sink is None else _np(d["sink"]), window or None,
+                                         rope_theta=1.0e7, rotary_fraction=0.334)
+    _check(f"multi decode contiguous T={T} {hq}/{hkv} W={window} {dtype}", o, ref,
+           fp32=(dtype == "f32"))
+
+
+def test_multi_decode_one_query_is_decode(gpu_lib):
+    """q_len = 1 over a ring of W slots is the single-token decode."""
+    pos = [0, 5, 127, 128, 1000, 262143]
+    d = _ring_case(pos, seed=220)
+    o1 = gpu_lib.swa_sink_decode(d["q"], d["k"], d["v"], d["pos"], max(pos),
+                                 layout=gpu_lib.KV_RING, sink=d["sink"], window=128)
+    om = gpu_lib.swa_sink_decode_multi(d["q"][:, None].contiguous(), d["k"], d["v"], d["pos"],
+                                       max(pos), layout=gpu_lib.KV_RING, ring_slots=128,
+                                       sink=d["sink"], window=128)
+    _check("multi decode T=1 vs decode", om[:, 0], _np(o1))
+
+
+def test_multi_decode_matches_prefill_rows(gpu_lib):
+    """The verification step over a ring filled from a sequence equals the
+    prefill rows of its last T tokens (both on the GPU)."""
+    L, W, T, S = 300, 128, 4, 131
+    x = _prefill_case(1, L, 64, 8, "bf16", 221)
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=W)
+    p0 = L - T
+    ring_k = torch.zeros(1, S, 8, 192, dtype=torch.bfloat16, device=DEV)
+    ring_v = torch.zeros(1, S, 8, 128, dtype=torch.bfloat16, device=DEV)
+    for j in range(p0 - W + 1, L):
+        ring_k[0, j % S] = x["k"][0, j]
+        ring_v[0, j % S] = x["v"][0, j]
+    om = gpu_lib.swa_sink_decode_multi(x["q"][:, p0:].contiguous(), ring_k, ring_v,
+                                       torch.tensor([p0], device=DEV), L - 1,
+                                       layout=gpu_lib.KV_RING, ring_slots=S, sink=x["sink"],
+                                       window=W)
+    assert (om.float() - o[:, p0:].float()).abs().max().item() <= 2e-2
+
+
+def test_multi_decode_contract_violations_give_nan(gpu_lib):
+    pos = [10, 500]
+    d = synthetic.multi_contiguous_inputs(2, 4, 64, 4, 192, 128, "bf16", 222, torch.tensor(pos), DEV)
+    bad = torch.tensor([10, 501], dtype=torch.int64, device=DEV)   # 501 + 3 >= rows of sequence 1
+    o = gpu_lib.swa_sink_decode_multi(d["q"], d["k"], d["v"], bad, 504,
+                                      layout=gpu_lib.KV_CONTIGUOUS, seq_offsets=d["seq_offsets"],
+                                      window=0)
+    on = _np(o)
+    assert np.isfinite(on[0]).all() and np.isnan(on[1]).all()
+
+
+def test_mtp_decode_full_size(gpu_lib):
+    wl = synthetic.WORKLOADS["mtp_decode_b64_t4"]
+    T = wl["T"]
+    pos = synthetic.decode_positions(wl["B"], *wl["pos_range"], wl["seed"])
+    maxp = wl["pos_range"][1] + T - 1
+    sw, ga = wl["swa"], wl["ga"]
+    d = synthetic.multi_ring_inputs(wl["B"], T, sw["hq"], sw["hkv"], sw["slots"], 192, 128, "bf16",
+                                    wl["seed"], pos, DEV, sw["sink_range"])
+    o = gpu_lib.swa_sink_decode_multi(d["q"], d["k"], d["v"], d["pos"], maxp,
+                                      layout=gpu_lib.KV_RING, ring_slots=sw["slots"],
+                                      sink=d["sink"], window=sw["window"])
+    ref = oracle.decode_multi_ring(_np(d["q"]), _np(d["k"]), _np(d["v"]), pos.numpy(),
+                                   _np(d["sink"]), sw["window"])
+    _check("MTP decode SWA ring (all 64 sequences)", o, ref)
+    del d
+    c = synthetic.multi_contiguous_inputs(wl["B"], T, ga["hq"], ga["hkv"], 192, 128, "bf16",
+                                          wl["seed"], pos, DEV, None)
+    og = gpu_lib.swa_sink_decode_multi(c["q"], c["k"], c["v"], c["pos"], maxp,
+                                       layout=gpu_lib.KV_CONTIGUOUS, seq_offsets=c["seq_offsets"],
+                                       window=0)
+    offs = c["seq_offsets"].cpu().numpy()
+    seqs = [int(pos.argmin()), int(pos.argmax()), 17]
+    for b in seqs:
+        lo, hi = int(offs[b]), int(offs[b + 1])
+        refb = oracle.decode_multi_contiguous(_np(c["q"][b:b + 1]), _np(c["k"][lo:hi]),
+                                              _np(c["v"][lo:hi]), np.array([0, hi - lo]),
+                                              pos.numpy()[b:b + 1])
+        _check(f"MTP decode GA contiguous (sequence {b})", og[b:b + 1], refb)
+
+
+# ---------------------------------------------------------------------------
 # Decode over FP8 (E4M3) caches with per-kv-head scales
 # ---------------------------------------------------------------------------
 
