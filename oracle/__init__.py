@@ -46,6 +46,9 @@ from .attention import (  # noqa: F401
     decode_multi_contiguous,
     e4m3_value,
     dequantise_kv,
+    e4m3_encode,
+    rope_f32_steps,
+    kv_append,
     swa_sink_decode_ring_fp8,
     swa_sink_decode_contiguous_fp8,
     sparse_sink_attn,

@@ -506,3 +506,87 @@ def sparse_rows_fp8(q, k_codes, v_codes, k_scale, v_scale, sel_idx, sel_count, r
                        sel_idx, sel_count, rows, sink, recent=recent, scale=scale,
                        rope_theta=rope_theta, rotary_fraction=rotary_fraction,
                        pos_offset=pos_offset, restricted=restricted)
+
+
+# ----------------------------------------------------------------------------
+# Appending new tokens' keys and values to a decode cache
+# ----------------------------------------------------------------------------
+
+def e4m3_encode(x):
+    """E4M3 code (uint8) nearest to each value of x: ties go to the code with
+    an even mantissa, magnitudes of 448 and above saturate to 448 (reading:
+    a saturating cast, so that no finite value becomes NaN), the sign is
+    kept (a negative value that rounds to zero gives the negative-zero code).
+    By search over the 127 finite non-negative values of e4m3_value."""
+    x = np.asarray(x, dtype=np.float64)
+    finite = e4m3_value(np.arange(127, dtype=np.uint8))          # codes 0x00 .. 0x7E, ascending
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(finite, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo = a - finite[lo]
+    d_hi = finite[hi] - a
+    pick = np.where(d_hi < d_lo, hi, np.where(d_lo < d_hi, lo, np.where(hi % 2 == 0, hi, lo)))
+    pick = np.where(a >= 448.0, 126, pick)
+    return (pick | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def rope_f32_steps(x, pos, theta, rotary_fraction):
+    """The partial RoPE of `rope`, evaluated in float32 the way a quantised
+    cache entry is decided: cos and sin of the float64 angle rounded to
+    float32, then each product and the difference / sum rounded to float32
+    on its own.  x: [..., n, H, d] float32; pos: n positions."""
+    x = np.asarray(x, dtype=np.float32)
+    d = x.shape[-1]
+    rot = rotary_dims(d, rotary_fraction)
+    out = x.copy()
+    if rot == 0:
+        return out
+    half = rot // 2
+    r = np.arange(half, dtype=np.float64)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * theta ** (-(2.0 * r) / rot)   # [n, half]
+    c = np.cos(ang).astype(np.float32)[:, None, :]
+    sn = np.sin(ang).astype(np.float32)[:, None, :]
+    x0, x1 = x[..., :half], x[..., half:rot]
+    out[..., :half] = (x0 * c) - (x1 * sn)
+    out[..., half:rot] = (x1 * c) + (x0 * sn)
+    return out
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, pos, rope_theta, rotary_fraction, ring_slots=None,
+              seq_offsets=None, k_scale=None, v_scale=None, store="same"):
+    """Caches after writing T new tokens per sequence.
+
+    k_new [B, T, Hkv, d_qk], v_new [B, T, Hkv, d_v] (float32 values); token t of
+    sequence b is position pos[b] + t.  Ring (ring_slots = S): cache
+    [B, S, Hkv, d], position j in slot j mod S (youngju.dev: the SWA pool is
+    bounded by the window).  Contiguous (seq_offsets): row seq_offsets[b] + j.
+    Keys are stored rotated (rope_f32_steps); store = "bf16" rounds to
+    bfloat16 (to nearest even), "f32" keeps float32, "e4m3" stores
+    e4m3_encode(value / scale[g]) with the quotient rounded to float32.
+    Returns new (k_cache, v_cache) arrays; the inputs are not modified.
+    """
+    import torch
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    k_new = np.asarray(k_new, dtype=np.float32)
+    v_new = np.asarray(v_new, dtype=np.float32)
+    B, T = k_new.shape[:2]
+    for b in range(B):
+        ps = int(pos[b]) + np.arange(T)
+        kr = rope_f32_steps(k_new[b], ps, rope_theta, rotary_fraction)          # [T, Hkv, d]
+        vr = v_new[b]
+        if ring_slots is not None:
+            rows = (b, np.mod(ps, ring_slots))
+        else:
+            rows = (int(seq_offsets[b]) + ps,)
+        if store == "e4m3":
+            ks = np.asarray(k_scale, dtype=np.float32)[:, None]
+            vs = np.asarray(v_scale, dtype=np.float32)[:, None]
+            kc[rows] = e4m3_encode((kr / ks).astype(np.float32))
+            vc[rows] = e4m3_encode((vr / vs).astype(np.float32))
+        elif store == "bf16":
+            kc[rows] = torch.from_numpy(kr).to(torch.bfloat16).float().numpy()
+            vc[rows] = torch.from_numpy(vr).to(torch.bfloat16).float().numpy()
+        else:
+            kc[rows] = kr
+            vc[rows] = vr
+    return kc, vc

@@ -481,11 +481,64 @@ def pin_p15_multi_token_decode(O):
     assert np.abs(got - ref[:, L - 4:]).max() < 1e-12
 
 
+def pin_p16_kv_append(O):
+    """Cache append: the E4M3 encoder against torch's float8_e4m3fn cast
+    (round to nearest even) on every exact tie and random values in range,
+    saturation at 448; the float32-step RoPE against the float64 one; the
+    ring slot of each position; and decode over a ring filled by appends
+    equal to the scalar brute-force prefill row."""
+    rng = np.random.default_rng(47)
+    finite = O.e4m3_value(np.arange(127, dtype=np.uint8))
+    mids = (finite[:-1] + finite[1:]) / 2                    # every tie between neighbours
+    xs = np.concatenate([finite, mids, rng.uniform(-440, 440, 4000),
+                         rng.standard_normal(4000) * 0.01, -mids]).astype(np.float32)
+    ref = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_encode(xs)
+    assert np.array_equal(got, ref)
+    assert list(O.e4m3_encode(np.array([448.0, 500.0, 1e30, -1e9], dtype=np.float32))) == [0x7E, 0x7E, 0x7E, 0xFE]
+    x = rng.standard_normal((5, 3, 16)).astype(np.float32)
+    p = np.array([0, 1, 7, 1000, 262143])
+    f32 = O.rope_f32_steps(x, p, 1.0e4, 0.5)
+    f64 = O.rope(x.astype(np.float64), p, 1.0e4, 0.5)
+    assert np.abs(f32 - f64).max() < 2e-6 * np.abs(x).max()
+    # appends into a ring of S slots; then decode at the last position
+    L, S, W, hq, hkv, d, dv = 9, 6, 4, 4, 2, 8, 4
+    q = rng.standard_normal((1, L, hq, d))
+    k = rng.standard_normal((1, L, hkv, d)).astype(np.float32)
+    v = rng.standard_normal((1, L, hkv, dv)).astype(np.float32)
+    kc = np.zeros((1, S, hkv, d), dtype=np.float32)
+    vc = np.zeros((1, S, hkv, dv), dtype=np.float32)
+    for j0, T in ((0, 3), (3, 1), (4, 5)):
+        kc2, vc2 = O.kv_append(kc, vc, k[:, j0:j0 + T], v[:, j0:j0 + T], np.array([j0]), 3.0, 0.5,
+                               ring_slots=S, store="f32")
+        changed = sorted(set(np.nonzero((kc2 != kc).any(axis=(0, 2, 3)))[0]))
+        assert set(changed) <= {j % S for j in range(j0, j0 + T)}
+        assert np.array_equal(vc2[0, [j % S for j in range(j0, j0 + T)]], v[0, j0:j0 + T])
+        kc, vc = kc2, vc2
+    sink = np.array([0.5, -1.0, 0.0, 1.0])
+    ref = _brute_prefill(q, k.astype(np.float64), v.astype(np.float64), sink, W, 3.0, 0.5)
+    got = O.swa_sink_decode_ring(q[:, L - 1], kc[:, :, :, :], vc, np.array([L - 1]), sink,
+                                 rope_theta=3.0, rotary_fraction=0.5)
+    # the ring has S = 6 > W = 4 slots: the decode reads the W newest ones
+    got_w = O.decode_multi_ring(q[:, L - 1:], kc, vc, np.array([L - 1]), sink, W, rope_theta=3.0,
+                                rotary_fraction=0.5)
+    assert np.abs(got_w[:, 0] - ref[:, L - 1]).max() < 1e-5
+    assert got.shape == (1, hq, dv)
+    # contiguous pool, E4M3 store: codes decode back to the scaled, rounded values
+    offs = np.array([0, 4])
+    ks, vs = np.array([0.02, 0.05], dtype=np.float32), np.array([0.03, 0.01], dtype=np.float32)
+    kq, vq = O.kv_append(np.zeros((4, hkv, d), np.uint8), np.zeros((4, hkv, dv), np.uint8),
+                         k[:, :4], v[:, :4], np.array([0]), 3.0, 0.5, seq_offsets=offs,
+                         k_scale=ks, v_scale=vs, store="e4m3")
+    back = O.dequantise_kv(vq, vs)
+    assert np.abs(back - v[0, :4]).max() <= np.abs(v[0, :4]).max() * 2 ** -3
+
+
 PINS = [pin_p1_no_sink_is_masked_softmax, pin_p2_wide_window_is_causal, pin_p3_sink_as_extra_key,
         pin_p4_weights_sum, pin_p5_unit_window, pin_p6_zero_query, pin_p7_brute_force,
         pin_p8_rope, pin_p9_gqa, pin_p10_decode_equals_prefill_row, pin_p11_sparse,
         pin_p12_large_sink_is_stable, pin_p13_chunk, pin_p14_fp8_cache,
-        pin_p15_multi_token_decode]
+        pin_p15_multi_token_decode, pin_p16_kv_append]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -519,6 +572,8 @@ MUTANTS = {
     "multi_ring_slot_by_window": ("slots = np.mod(J, S)", "slots = np.mod(J, window)"),
     "multi_query_not_causal_among_drafts": ("            p = int(pos[b]) + t\n            J = window_keys(p, window)\n            qt",
                                             "            p = int(pos[b]) + t\n            J = window_keys(int(pos[b]) + T - 1, window)\n            qt"),
+    "e4m3_encode_ties_up": ("np.where(hi % 2 == 0, hi, lo)", "hi"),
+    "append_slot_by_window": ("rows = (b, np.mod(ps, ring_slots))", "rows = (b, np.mod(ps, ring_slots - 1))"),
     "e4m3_bias_8": ("np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
     "e4m3_subnormal_as_normal": ("np.where(e == 0, m * 2.0 ** -9,", "np.where(e < 0, m * 2.0 ** -9,"),
     "fp8_v_scale_dropped": ("dequantise_kv(v_codes, v_scale), pos, sink, scale=scale,",
