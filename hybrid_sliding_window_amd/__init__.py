@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     decode_multi_workspace_size,
     decode_workspace_size,
     ga_prefill,
+    kv_cache_append,
     lib_path,
     load,
     prefill_workspace_size,

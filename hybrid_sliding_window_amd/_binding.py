@@ -28,6 +28,10 @@ _SIGNATURES = {
     "hswa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i, _ll]),
     "swa_sink_decode": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _ll,
                              _f, _f, _f, _i, _vp, _sz, _vp]),
+    "kv_cache_append": (_i, [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i, _ll, _f, _f,
+                             _i, _vp]),
+    "kv_cache_append_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i,
+                                 _ll, _f, _f, _i, _vp]),
     "hswa_decode_multi_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _ll]),
     "swa_sink_decode_multi": (_i, [_vp, _vp, _vp, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                    _i, _i, _ll, _f, _f, _f, _i, _vp, _sz, _vp]),
@@ -245,6 +249,41 @@ def swa_sink_decode_multi(q, k_cache, v_cache, pos, max_pos, layout=KV_RING, rin
                                    0 if ws is None else ws.numel(), _stream(q))
     _raise(st)
     return o
+
+
+def kv_cache_append(k_new, v_new, k_cache, v_cache, pos, max_pos, layout=KV_RING, ring_slots=0,
+                    seq_offsets=None, rope_theta=10000.0, rotary_fraction=0.0, k_scale=None,
+                    v_scale=None):
+    """Write k_new [B,T,Hkv,d_qk] and v_new [B,T,Hkv,d_v] (token t at pos[b] + t) into
+    a ring or contiguous cache, keys rotated.  An E4M3 cache (uint8 or
+    float8_e4m3fn) needs k_scale and v_scale.  Modifies the caches in place."""
+    lib = load()
+    B, T, hkv, dqk = k_new.shape
+    dv = v_new.shape[-1]
+    if pos.dtype != torch.int64:
+        raise TypeError("pos must be int64")
+    if seq_offsets is not None and seq_offsets.dtype != torch.int64:
+        raise TypeError("seq_offsets must be int64")
+    _check_same(k_new, v_new, k_cache, v_cache, pos, seq_offsets)
+    fp8 = k_cache.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if fp8:
+        for t in (k_scale, v_scale):
+            if t is None or t.dtype != torch.float32 or t.numel() != hkv:
+                raise ValueError("an E4M3 cache needs float32 k_scale and v_scale, one per kv head")
+        _check_same(k_new, k_scale, v_scale)
+        st = lib.kv_cache_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(k_scale), _ptr(v_scale), layout, ring_slots,
+                                     _ptr(seq_offsets), _ptr(pos), B, T, hkv, dqk, dv,
+                                     int(max_pos), rope_theta, rotary_fraction,
+                                     _dtype_code(k_new), _stream(k_new))
+    else:
+        if k_cache.dtype != k_new.dtype or v_cache.dtype != v_new.dtype:
+            raise TypeError("a bf16 / fp32 cache has the type of the new keys and values")
+        st = lib.kv_cache_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), layout,
+                                 ring_slots, _ptr(seq_offsets), _ptr(pos), B, T, hkv, dqk, dv,
+                                 int(max_pos), rope_theta, rotary_fraction, _dtype_code(k_new),
+                                 _stream(k_new))
+    _raise(st)
 
 
 def _fp8_cache(t):

@@ -328,6 +328,55 @@ void multi_split_plan(hswa_kv_layout_t layout, int q_len, int window, int ring_s
     hswa::decode_split_plan(1, window > 0 ? window + q_len - 1 : 0, max_pos, split_keys, nsplit);
 }
 
+// Cache append for bf16 / fp32 caches (e4m3 false) or E4M3 caches with
+// per-kv-head scales (e4m3 true).
+hswa_status_t append_impl(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                          bool e4m3, const float* k_scale, const float* v_scale,
+                          hswa_kv_layout_t layout, int ring_slots, const long long* seq_offsets,
+                          const long long* pos, int batch, int q_len, int hkv, int d_qk, int d_v,
+                          long long max_pos, float rope_theta, float rotary_fraction,
+                          hswa_dtype_t dtype, void* stream) {
+  hswa_status_t st =
+      check_common(batch, hkv, hkv, d_qk, d_v, 0.f, rope_theta, rotary_fraction, dtype);
+  if (st != HSWA_OK) return st;
+  if (layout != HSWA_KV_RING && layout != HSWA_KV_CONTIGUOUS)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "layout must be HSWA_KV_RING or HSWA_KV_CONTIGUOUS");
+  if (q_len < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "q_len must be >= 0");
+  if (layout == HSWA_KV_RING) {
+    if (ring_slots <= 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "a ring cache needs ring_slots > 0");
+    if (seq_offsets) return fail(HSWA_ERR_INVALID_ARGUMENT, "seq_offsets must be NULL for a ring cache");
+  } else {
+    if (ring_slots != 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "ring_slots must be 0 for a contiguous cache");
+    if (!seq_offsets) return fail(HSWA_ERR_INVALID_ARGUMENT, "seq_offsets is required for a contiguous cache");
+  }
+  if (max_pos < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "max_pos must be >= 0");
+  const int half = rotary_half(d_qk, rotary_fraction);
+  if (d_qk % 8 != 0 || d_v % 8 != 0 || half % 8 != 0)
+    return fail(HSWA_ERR_UNSUPPORTED, "head dims and the rotated half-width must be multiples of 8");
+  if (batch == 0 || q_len == 0) return ok();
+  if (!k_new || !v_new || !k_cache || !v_cache || !pos)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "k_new, v_new, caches and pos must be non-null");
+  if (e4m3 && (!k_scale || !v_scale))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "FP8 caches need k_scale and v_scale");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "k_new, v_new and the caches must be 16-byte aligned");
+  AttnArgs a = base_args(batch, 0, hkv, hkv, d_qk, d_v, 0.f, rope_theta, rotary_fraction);
+  a.k = k_new;
+  a.v = v_new;
+  a.kout = k_cache;
+  a.vout = v_cache;
+  a.kscale = k_scale;
+  a.vscale = v_scale;
+  a.seq_offsets = seq_offsets;
+  a.pos = pos;
+  a.max_pos = max_pos;
+  a.nq = q_len;
+  a.slots = ring_slots;
+  return hip_status(hswa::launch_kv_append(a, layout == HSWA_KV_RING ? 0 : 1, dtype == HSWA_BF16,
+                                           e4m3, static_cast<hipStream_t>(stream)),
+                    "cache append launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -470,6 +519,29 @@ hswa_status_t swa_sink_decode_multi(const void* q, const void* k_cache, const vo
   if (!generic_fits(d_qk, d_v)) return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
   return hip_status(hswa::launch_decode_multi_generic(a, lay, dtype == HSWA_BF16, s),
                     "multi-token decode launch");
+}
+
+hswa_status_t kv_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              hswa_kv_layout_t layout, int ring_slots,
+                              const long long* seq_offsets, const long long* pos, int batch,
+                              int q_len, int hkv, int d_qk, int d_v, long long max_pos,
+                              float rope_theta, float rotary_fraction, hswa_dtype_t dtype,
+                              void* stream) {
+  return append_impl(k_new, v_new, k_cache, v_cache, false, nullptr, nullptr, layout, ring_slots,
+                     seq_offsets, pos, batch, q_len, hkv, d_qk, d_v, max_pos, rope_theta,
+                     rotary_fraction, dtype, stream);
+}
+
+hswa_status_t kv_cache_append_fp8(const void* k_new, const void* v_new, void* k_cache,
+                                  void* v_cache, const float* k_scale, const float* v_scale,
+                                  hswa_kv_layout_t layout, int ring_slots,
+                                  const long long* seq_offsets, const long long* pos, int batch,
+                                  int q_len, int hkv, int d_qk, int d_v, long long max_pos,
+                                  float rope_theta, float rotary_fraction, hswa_dtype_t dtype,
+                                  void* stream) {
+  return append_impl(k_new, v_new, k_cache, v_cache, true, k_scale, v_scale, layout, ring_slots,
+                     seq_offsets, pos, batch, q_len, hkv, d_qk, d_v, max_pos, rope_theta,
+                     rotary_fraction, dtype, stream);
 }
 
 hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_cache,

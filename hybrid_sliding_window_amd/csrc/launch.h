@@ -22,6 +22,8 @@ struct AttnArgs {
   const float2* rope;             // prefill / sparse: cos/sin table [n][half]
   const void* krot;               // prefill / sparse bf16: K's first R dims, rotated [B, n, hkv, R]
   void* qrot;                     // decode bf16: q rotated to pos[b] [B, hq, d_qk] (workspace)
+  void* kout;                     // cache append: the K and V caches written
+  void* vout;
   const float* kscale;            // decode FP8 caches: per-kv-head value of one K code unit [hkv]
   const float* vscale;            // the same for V
   int B, n, hq, hkv, d_qk, d_v;   // n: tokens of K/V (and q unless chunked)
@@ -90,6 +92,13 @@ bool decode_multi_supported(const AttnArgs& a);
 hipError_t launch_decode_multi(const AttnArgs& a, int layout, hipStream_t stream);
 hipError_t launch_decode_multi_generic(const AttnArgs& a, int layout, bool bf16,
                                        hipStream_t stream);
+
+// Append nq new tokens per sequence (k, v: [B, nq, hkv, d]) at positions
+// pos[b] .. pos[b] + nq - 1 to a ring (slots) or contiguous cache (kout,
+// vout): RoPE on K at each position, then a copy in the input type or E4M3
+// codes of value / kscale[g] (vscale[g]).  d_qk, d_v and half multiples of 8.
+hipError_t launch_kv_append(const AttnArgs& a, int layout, bool bf16_in, bool e4m3_out,
+                            hipStream_t stream);
 
 // Decode over E4M3 caches (same shapes as the bf16 decode kernel).
 bool decode_fp8_supported(const AttnArgs& a);

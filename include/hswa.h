@@ -154,6 +154,46 @@ hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_
                               hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * Appending q_len new tokens per sequence to a decode cache, ahead of the
+ * decode (or multi-token decode) call that reads them: the ring of an SWA
+ * layer, whose pool is bounded by the window ("MiMo v2.5 inference
+ * optimisation" (youngju.dev): token j in slot j mod ring_slots), or the
+ * contiguous pool of a GA layer (row seq_offsets[b] + j).
+ *   k_new [batch, q_len, hkv, d_qk], v_new [batch, q_len, hkv, d_v] (dtype):
+ *   token t of sequence b is position pos[b] + t (pos: int64 [batch] DEVICE
+ *   array; max_pos: host bound on every pos[b] + q_len - 1).
+ *   Caches: as swa_sink_decode (ring [batch, ring_slots, hkv, d]; contiguous
+ *   [rows, hkv, d] with seq_offsets, ring_slots 0), of type dtype.
+ * Keys are stored rotated: the partial RoPE at the token's position, in
+ * float32 steps (cos/sin of the float64 angle rounded to float32, each
+ * product and the difference / sum rounded on its own), then rounded to the
+ * cache type.  Values are copied.  Tokens whose position is negative, above
+ * max_pos or (contiguous) not below their sequence's row count are not
+ * written.  d_qk, d_v and the rotated half-width R/2 must be multiples of 8.
+ */
+hswa_status_t kv_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              hswa_kv_layout_t layout, int ring_slots,
+                              const long long* seq_offsets, const long long* pos, int batch,
+                              int q_len, int hkv, int d_qk, int d_v, long long max_pos,
+                              float rope_theta, float rotary_fraction, hswa_dtype_t dtype,
+                              void* stream);
+
+/*
+ * The same into E4M3 caches (one byte per element, as swa_sink_decode_fp8):
+ * each stored value is the E4M3 code of the float32 quotient value /
+ * k_scale[g] (rotated key) or value / v_scale[g], rounded to nearest with
+ * ties to the even code and saturated to +-448.  dtype is the type of k_new
+ * and v_new; k_scale, v_scale: fp32 [hkv] DEVICE arrays.
+ */
+hswa_status_t kv_cache_append_fp8(const void* k_new, const void* v_new, void* k_cache,
+                                  void* v_cache, const float* k_scale, const float* v_scale,
+                                  hswa_kv_layout_t layout, int ring_slots,
+                                  const long long* seq_offsets, const long long* pos, int batch,
+                                  int q_len, int hkv, int d_qk, int d_v, long long max_pos,
+                                  float rope_theta, float rotary_fraction, hswa_dtype_t dtype,
+                                  void* stream);
+
 /* Bytes of workspace swa_sink_decode_multi needs: as hswa_decode_workspace_size
  * with batch * q_len query rows and the key range of the longest query. */
 size_t hswa_decode_multi_workspace_size(hswa_kv_layout_t layout, int batch, int q_len, int hq,

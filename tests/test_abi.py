@@ -151,6 +151,28 @@ def test_decode_multi_validation(lib):
         64 * 4 * 64 * 5 * 128 * 4 + r256(64 * 4 * 64 * 5 * 2 * 4) + 64 * 4 * 64 * 192 * 2
 
 
+def test_append_validation(lib):
+    def call(fp8=False, **kw):
+        a = dict(kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, layout=0, slots=131, offs=None, pos=FAKE,
+                 batch=2, q_len=4, hkv=8, d_qk=192, d_v=128, max_pos=1000, theta=1e4, frac=0.334,
+                 dtype=1, stream=None)
+        a.update(kw)
+        if fp8:
+            v = list(a.values())
+            return lib.kv_cache_append_fp8(*v[:4], kw.get("ks", FAKE), kw.get("vs", FAKE), *v[4:])
+        return lib.kv_cache_append(*a.values())
+    assert call(slots=0) == INVALID                        # a ring needs its slot count
+    assert call(offs=FAKE) == INVALID
+    assert call(layout=1, slots=0) == INVALID              # contiguous needs offsets
+    assert call(frac=0.1) == UNSUPPORTED                   # R/2 = 9: not a multiple of 8
+    assert call(d_v=100) == UNSUPPORTED
+    assert call(pos=None) == INVALID
+    assert call(kc=MISALIGNED) == INVALID
+    assert call(q_len=0, kn=None) == OK
+    assert lib.kv_cache_append_fp8(FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, 131, None, FAKE, 2, 4, 8,
+                                   192, 128, 1000, 1e4, 0.334, 1, None) == INVALID   # k_scale missing
+
+
 def test_decode_fp8_validation(lib):
     def call(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, layout=0, offs=None, pos=FAKE, sink=None,

@@ -787,3 +787,100 @@ def test_sparse_fp8_full_size(gpu_lib):
                                  x["sel_count"][:, ridx].cpu().numpy(), rows, _np(x["sink"]),
                                  recent=wl["recent"], restricted=True)
     _check("sparse fp8 full size (sampled rows)", o[:, ridx], ref)
+
+
+# ---------------------------------------------------------------------------
+# Appending new tokens to a decode cache
+# ---------------------------------------------------------------------------
+
+def _append_case(B, T, hkv, rows, dtype, seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kn = torch.randn(B, T, hkv, 192, generator=g).to(tdt).to(DEV)
+    vn = torch.randn(B, T, hkv, 128, generator=g).to(tdt).to(DEV)
+    kc = torch.randn(rows, hkv, 192, generator=g).to(tdt).to(DEV)
+    vc = torch.randn(rows, hkv, 128, generator=g).to(tdt).to(DEV)
+    return kn, vn, kc, vc
+
+
+@pytest.mark.parametrize("dtype,frac", [("bf16", 0.334), ("f32", 0.334), ("bf16", 0.0)])
+def test_append_ring_exact(gpu_lib, dtype, frac):
+    """Every byte of the ring after the append equals the oracle's."""
+    B, T, hkv, S = 5, 4, 8, 131
+    pos = [0, 2, 127, 130, 262140]
+    kn, vn, kc, vc = _append_case(B, T, hkv, B * S, dtype, 230)
+    kc, vc = kc.view(B, S, hkv, 192), vc.view(B, S, hkv, 128)
+    kref, vref = oracle.kv_append(_np(kc), _np(vc), _np(kn), _np(vn), np.array(pos), 1.0e4, frac,
+                                  ring_slots=S, store=dtype)
+    gpu_lib.kv_cache_append(kn, vn, kc, vc, torch.tensor(pos, device=DEV), max(pos) + T - 1,
+                            layout=gpu_lib.KV_RING, ring_slots=S, rope_theta=1.0e4,
+                            rotary_fraction=frac)
+    assert np.array_equal(_np(kc), kref) and np.array_equal(_np(vc), vref)
+
+
+@pytest.mark.parametrize("layout", ["ring", "contiguous"])
+def test_append_e4m3_exact(gpu_lib, layout):
+    """E4M3 codes written by the append are the oracle's codes, bit for bit."""
+    B, T, hkv = 4, 3, 4
+    pos = [0, 9, 500, 131071]
+    kn, vn, _, _ = _append_case(B, T, hkv, 1, "bf16", 231)
+    ks, vs = synthetic.kv_scales(hkv, 0.02, 0.04, 232, DEV)
+    if layout == "ring":
+        S = 130
+        kc = torch.zeros(B, S, hkv, 192, dtype=torch.uint8, device=DEV)
+        vc = torch.zeros(B, S, hkv, 128, dtype=torch.uint8, device=DEV)
+        kw = dict(layout=gpu_lib.KV_RING, ring_slots=S)
+        okw = dict(ring_slots=S)
+    else:
+        lens = torch.tensor(pos) + T + 1
+        offs = torch.zeros(B + 1, dtype=torch.int64)
+        offs[1:] = torch.cumsum(lens, 0)
+        kc = torch.zeros(int(offs[-1]), hkv, 192, dtype=torch.uint8, device=DEV)
+        vc = torch.zeros(int(offs[-1]), hkv, 128, dtype=torch.uint8, device=DEV)
+        kw = dict(layout=gpu_lib.KV_CONTIGUOUS, seq_offsets=offs.to(DEV))
+        okw = dict(seq_offsets=offs.numpy())
+    kref, vref = oracle.kv_append(_codes(kc), _codes(vc), _np(kn), _np(vn), np.array(pos), 1.0e4,
+                                  0.334, k_scale=_np(ks), v_scale=_np(vs), store="e4m3", **okw)
+    gpu_lib.kv_cache_append(kn, vn, kc, vc, torch.tensor(pos, device=DEV), max(pos) + T - 1,
+                            rope_theta=1.0e4, rotary_fraction=0.334, k_scale=ks, v_scale=vs, **kw)
+    assert np.array_equal(_codes(kc), kref) and np.array_equal(_codes(vc), vref)
+
+
+def test_append_contract_violations_write_nothing(gpu_lib):
+    B, T, hkv = 2, 2, 4
+    lens = torch.tensor([10, 10])
+    offs = torch.tensor([0, 10, 20], dtype=torch.int64)
+    kn, vn, kc, vc = _append_case(B, T, hkv, 20, "bf16", 233)
+    k0, v0 = kc.clone(), vc.clone()
+    bad = torch.tensor([9, -1], device=DEV)          # 9 + 1 >= 10 rows; -1 negative
+    gpu_lib.kv_cache_append(kn, vn, kc, vc, bad, 10, layout=gpu_lib.KV_CONTIGUOUS,
+                            seq_offsets=offs.to(DEV), rope_theta=1.0e7, rotary_fraction=0.334)
+    # sequence 0: position 9 is written, position 10 is not; sequence 1:
+    # position -1 is not, position 0 (row 10) is
+    changed = (kc != k0).any(dim=(1, 2)).cpu().numpy()
+    vchanged = (vc != v0).any(dim=(1, 2)).cpu().numpy()
+    assert list(np.nonzero(changed)[0]) == [9, 10] and list(np.nonzero(vchanged)[0]) == [9, 10]
+    assert int(lens.sum()) == 20
+
+
+def test_append_then_multi_decode(gpu_lib):
+    """A verification step end to end on the GPU: append the 4 new tokens, then
+    decode them; the oracle appends and decodes the same way."""
+    B, T, hkv, hq, S, W = 3, 4, 8, 64, 131, 128
+    pos = [5, 126, 70000]
+    kn, vn, kc, vc = _append_case(B, T, hkv, B * S, "bf16", 234)
+    kc, vc = kc.view(B, S, hkv, 192), vc.view(B, S, hkv, 128)
+    q = synthetic.normal((B, T, hq, 192), 235, DEV, "bf16")
+    sink = synthetic.uniform((hq,), -2.0, 2.0, 236, DEV)
+    kref, vref = oracle.kv_append(_np(kc), _np(vc), _np(kn), _np(vn), np.array(pos), 1.0e4, 0.334,
+                                  ring_slots=S, store="bf16")
+    pt = torch.tensor(pos, device=DEV)
+    gpu_lib.kv_cache_append(kn, vn, kc, vc, pt, max(pos) + T - 1, layout=gpu_lib.KV_RING,
+                            ring_slots=S, rope_theta=1.0e4, rotary_fraction=0.334)
+    o = gpu_lib.swa_sink_decode_multi(q, kc, vc, pt, max(pos) + T - 1, layout=gpu_lib.KV_RING,
+                                      ring_slots=S, sink=sink, window=W, rope_theta=1.0e4,
+                                      rotary_fraction=0.334)
+    ref = oracle.decode_multi_ring(_np(q), kref, vref, np.array(pos), _np(sink), W,
+                                   rope_theta=1.0e4, rotary_fraction=0.334)
+    _check("append + multi-token decode", o, ref)
