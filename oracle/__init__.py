@@ -55,4 +55,6 @@ from .attention import (  # noqa: F401
     prefill_rows,
     sparse_rows,
     sparse_rows_fp8,
+    selection_importance,
+    select_tokens,
 )

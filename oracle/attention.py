@@ -590,3 +590,68 @@ def kv_append(k_cache, v_cache, k_new, v_new, pos, rope_theta, rotary_fraction, 
             kc[rows] = kr
             vc[rows] = vr
     return kc, vc
+
+
+# ----------------------------------------------------------------------------
+# Token selection for the sparse layers (HySparse2)
+# ----------------------------------------------------------------------------
+
+def selection_importance(q, k, b, i, g, recent, scale=None, rope_theta=1.0e7,
+                         rotary_fraction=0.0, pos_offset=0):
+    """Importance of every candidate token for query i, kv head g of sequence b.
+
+    "MiMo-V3 HySparse2" (aideepthink.cn), section 4: the sparse layers reuse
+    the token-selection indices of the preceding full-attention layer, with
+    no separately trained retrieval module.  Reading: the importance of token
+    j is the attention the full-attention layer gives it, summed over the
+    group's query heads: I_j = sum_{h in g} exp(a_hij - lse_hi), the softmax
+    over the full causal set 0 .. i (no sink: a GA layer).  Candidates are
+    the tokens outside the recent window, 0 .. i - recent.
+    Returns the float64 importances of tokens 0 .. i - recent (may be empty).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    hq, d = q.shape[2], q.shape[3]
+    hkv = k.shape[2]
+    G = _check_heads(hq, hkv)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    last = i - recent
+    if last < 0:
+        return np.zeros(0)
+    qi = rope(q[b, i][None], np.array([pos_offset + i]), rope_theta, rotary_fraction)[0]
+    kr = rope(k[b, :i + 1], pos_offset + np.arange(i + 1), rope_theta, rotary_fraction)
+    imp = np.zeros(last + 1)
+    for h in range(g * G, (g + 1) * G):
+        a = (kr[:, g] @ qi[h]) * scale                       # a_hij, j = 0 .. i
+        m = a.max()
+        lse = m + math.log(np.exp(a - m).sum())
+        imp += np.exp(a[:last + 1] - lse)
+    return imp
+
+
+def select_tokens(q, k, rows, recent, max_sel, scale=None, rope_theta=1.0e7,
+                  rotary_fraction=0.0, pos_offset=0):
+    """Selected-token lists of the query rows listed in `rows`.
+
+    For each (b, i, g): the min(max_sel, i - recent + 1) candidates of
+    selection_importance with the largest importance, equal importances
+    going to the lower position, listed in ascending order and padded with
+    -1.  Returns idx int32 [B, len(rows), Hkv, max_sel] and count int32
+    [B, len(rows), Hkv] (the layout sparse attention reads).
+    """
+    B, hkv = np.asarray(q).shape[0], np.asarray(k).shape[2]
+    rows = np.asarray(rows, dtype=np.int64)
+    idx = np.full((B, len(rows), hkv, max_sel), -1, dtype=np.int32)
+    cnt = np.zeros((B, len(rows), hkv), dtype=np.int32)
+    for b in range(B):
+        for t, i in enumerate(rows):
+            for g in range(hkv):
+                imp = selection_importance(q, k, b, int(i), g, recent, scale, rope_theta,
+                                           rotary_fraction, pos_offset)
+                take = min(max_sel, imp.size)
+                order = np.lexsort((np.arange(imp.size), -imp))    # importance desc, then position
+                chosen = np.sort(order[:take])
+                idx[b, t, g, :take] = chosen
+                cnt[b, t, g] = take
+    return idx, cnt

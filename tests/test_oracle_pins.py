@@ -534,11 +534,72 @@ def pin_p16_kv_append(O):
     assert np.abs(back - v[0, :4]).max() <= np.abs(v[0, :4]).max() * 2 ** -3
 
 
+def _brute_selection(q, k, b, i, g, recent, K):
+    """Scalar loops: softmax probabilities with math.fsum, then sorted()."""
+    hq, d = q.shape[2], q.shape[3]
+    G = hq // k.shape[2]
+    last = i - recent
+    if last < 0:
+        return []
+    imp = [0.0] * (last + 1)
+    for h in range(g * G, (g + 1) * G):
+        a = [math.fsum(q[b, i, h, t] * k[b, j, g, t] for t in range(d)) / math.sqrt(d)
+             for j in range(i + 1)]
+        m = max(a)
+        z = math.fsum(math.exp(x - m) for x in a)
+        for j in range(last + 1):
+            imp[j] += math.exp(a[j] - m) / z
+    order = sorted(range(last + 1), key=lambda j: (-imp[j], j))
+    return sorted(order[:min(K, last + 1)])
+
+
+def pin_p17_token_selection(O):
+    """Token selection (aideepthink.cn section 4, reading of the importance):
+    against scalar brute force; all candidates when they fit; with one head
+    per group the ranking is the logits' (torch topk); exact ties go to the
+    lower position; and sparse attention over all candidates is full causal
+    attention."""
+    rng = np.random.default_rng(53)
+    n, hq, hkv, d = 14, 4, 2, 8
+    q = rng.standard_normal((1, n, hq, d)) * 2
+    k = rng.standard_normal((1, n, hkv, d)) * 2
+    rows = np.arange(n)
+    for recent, K in ((1, 3), (3, 4), (2, 100)):
+        idx, cnt = O.select_tokens(q, k, rows, recent, K)
+        for i in rows:
+            for g in range(hkv):
+                want = _brute_selection(q, k, 0, int(i), g, recent, K)
+                assert cnt[0, i, g] == len(want)
+                assert list(idx[0, i, g, :len(want)]) == want, (recent, K, i, g)
+                assert (idx[0, i, g, len(want):] == -1).all()
+    # one head per group: the top-K of the probabilities is the top-K of the logits
+    q1 = rng.standard_normal((1, 40, 3, 16))
+    k1 = rng.standard_normal((1, 40, 3, 16))
+    idx, cnt = O.select_tokens(q1, k1, [39], 4, 7)
+    for g in range(3):
+        logits = torch.from_numpy(k1[0, :36, g] @ q1[0, 39, g])
+        want = np.sort(torch.topk(logits, 7).indices.numpy())
+        assert list(idx[0, 0, g, :7]) == list(want)
+    # exact ties: identical keys at positions 0, 2, 5 tie; the lower ones win
+    kt = rng.standard_normal((1, 12, 1, 8))
+    kt[0, [0, 2, 5]] = kt[0, 7]
+    qt = rng.standard_normal((1, 12, 2, 8))
+    qt[0, 11, :] = kt[0, 7, 0] * 3                  # those keys dominate
+    idx, cnt = O.select_tokens(qt, kt, [11], 3, 3)
+    assert list(idx[0, 0, 0, :3]) == [0, 2, 5]
+    # selecting every candidate makes sparse attention the full causal attention
+    v = rng.standard_normal((1, n, hkv, 4))
+    idx, cnt = O.select_tokens(q, k, rows, 2, n)
+    full = O.sparse_sink_attn(q, k, v, idx, cnt, None, recent=2)
+    ga = O.ga_prefill(q, k, v)
+    assert np.abs(full - ga).max() < 1e-12
+
+
 PINS = [pin_p1_no_sink_is_masked_softmax, pin_p2_wide_window_is_causal, pin_p3_sink_as_extra_key,
         pin_p4_weights_sum, pin_p5_unit_window, pin_p6_zero_query, pin_p7_brute_force,
         pin_p8_rope, pin_p9_gqa, pin_p10_decode_equals_prefill_row, pin_p11_sparse,
         pin_p12_large_sink_is_stable, pin_p13_chunk, pin_p14_fp8_cache,
-        pin_p15_multi_token_decode, pin_p16_kv_append]
+        pin_p15_multi_token_decode, pin_p16_kv_append, pin_p17_token_selection]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -574,6 +635,12 @@ MUTANTS = {
                                             "            p = int(pos[b]) + t\n            J = window_keys(int(pos[b]) + T - 1, window)\n            qt"),
     "e4m3_encode_ties_up": ("np.where(hi % 2 == 0, hi, lo)", "hi"),
     "append_slot_by_window": ("rows = (b, np.mod(ps, ring_slots))", "rows = (b, np.mod(ps, ring_slots - 1))"),
+    "selection_ties_to_higher": ("order = np.lexsort((np.arange(imp.size), -imp))",
+                                 "order = np.lexsort((-np.arange(imp.size), -imp))"),
+    "selection_window_inclusive": ("    last = i - recent\n    if last < 0:\n        return np.zeros(0)",
+                                   "    last = i - recent + 1\n    if last < 0:\n        return np.zeros(0)"),
+    "selection_lse_over_candidates": ("lse = m + math.log(np.exp(a - m).sum())",
+                                      "lse = m + math.log(np.exp(a[:last + 1] - m).sum())"),
     "e4m3_bias_8": ("np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
     "e4m3_subnormal_as_normal": ("np.where(e == 0, m * 2.0 ** -9,", "np.where(e < 0, m * 2.0 ** -9,"),
     "fp8_v_scale_dropped": ("dequantise_kv(v_codes, v_scale), pos, sink, scale=scale,",
