@@ -150,12 +150,13 @@ def only(which, steps, warmup):
         return {"copy": copy_calibration(steps, warmup)}
     parts = {"ga": ["ga"], "chunk": ["chunk"], "decode": ["decode"], "decode_mtp": ["decode_mtp"],
              "decode_fp8": ["decode_fp8"],
-             "sparse": ["sparse"], "sparse_fp8": ["sparse_fp8"]}[which]
+             "sparse": ["sparse"], "sparse_fp8": ["sparse_fp8"], "select": ["select"]}[which]
     return secondary(steps, warmup, parts)
 
 
 def secondary(steps, warmup,
-              parts=("ga", "chunk", "decode", "decode_mtp", "decode_fp8", "sparse", "sparse_fp8")):
+              parts=("ga", "chunk", "decode", "decode_mtp", "decode_fp8", "sparse", "sparse_fp8",
+                     "select")):
     out = {}
     dev = "cuda"
     if "ga" in parts:
@@ -172,6 +173,8 @@ def secondary(steps, warmup,
         _sparse(out, dev)
     if "sparse_fp8" in parts:
         _sparse_fp8(out, dev)
+    if "select" in parts:
+        _select(out, dev)
     return out
 
 
@@ -425,6 +428,29 @@ def _sparse_fp8(out, dev):
     _log(f"sparse fp8 {out['sparse_fp8_prefill_n65536']}")
 
 
+def _select(out, dev):
+    # Token selection for the sparse workload: n = 65536, 64 q / 4 kv heads,
+    # the top 1024 of the candidates outside the 128 recent tokens
+    wl = synthetic.WORKLOADS["sparse_prefill_n65536"]
+    x = synthetic.prefill_inputs(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, "bf16", wl["seed"], dev,
+                                 None)
+    idx = torch.empty((1, wl["n"], wl["hkv"], wl["max_sel"]), dtype=torch.int32, device=dev)
+    cnt = torch.empty((1, wl["n"], wl["hkv"]), dtype=torch.int32, device=dev)
+    fn = lambda: hswa.sparse_select_tokens(x["q"], x["k"], max_sel=wl["max_sel"],  # noqa: E731
+                                           recent_window=wl["recent"], out=(idx, cnt))
+    _, per = timed(fn, 3, 1)
+    t = float(np.median(per)) / 1e3
+    i = np.arange(wl["n"], dtype=np.int64)
+    causal = int((i + 1).sum())
+    cand = int(np.maximum(0, i - wl["recent"] + 1).sum())
+    # four passes over the keys: log-sum-exp over 0 .. i, then three over the candidates
+    flops = (causal + 3 * cand) * wl["hq"] * 2 * 192
+    out["select_tokens_n65536"] = {"ms": t * 1e3, "qk_tflops": flops / t / 1e12,
+                                   "rows_per_s": wl["n"] * wl["hkv"] / t,
+                                   "frac_of_bf16_peak": flops / t / 1e12 / BF16_PEAK_TFLOPS}
+    _log(f"select {out['select_tokens_n65536']}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -434,7 +460,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["prefill", "ga", "chunk", "decode", "decode_mtp", "decode_fp8", "sparse",
-                             "sparse_fp8", "copy"], default=None,
+                             "sparse_fp8", "select", "copy"], default=None,
                     help="run one workload only (for profiler runs); prints its figures as JSON")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     load,
     prefill_workspace_size,
     sparse_sink_attn,
+    sparse_select_tokens,
     sparse_sink_attn_fp8,
     sparse_workspace_size,
     swa_sink_decode,

@@ -42,6 +42,9 @@ _SIGNATURES = {
                               _f, _f, _f, _ll, _i, _vp, _sz, _vp]),
     "sparse_sink_attn_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i,
                                   _i, _i, _i, _f, _f, _f, _ll, _i, _vp, _sz, _vp]),
+    "hswa_select_workspace_size": (_sz, [_i, _i, _i, _i, _i, _f]),
+    "sparse_select_tokens": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _f, _f, _ll,
+                                  _i, _vp, _sz, _vp]),
     "hswa_last_error": (ctypes.c_char_p, []),
     "hswa_version": (ctypes.c_char_p, []),
 }
@@ -373,3 +376,27 @@ def sparse_sink_attn_fp8(q, k, v, k_scale, v_scale, sel_idx, sel_count, sink=Non
                                   0 if ws is None else ws.numel(), _stream(q))
     _raise(st)
     return o
+
+
+def sparse_select_tokens(q, k, max_sel=1024, recent_window=128, scale=0.0, rope_theta=1.0e7,
+                         rotary_fraction=0.0, pos_offset=0, out=None, workspace=None):
+    """Selected-token lists for the sparse layers from the full-attention
+    layer's q [B,n,Hq,192] and k [B,n,Hkv,192] (bf16, Hq = 16 Hkv):
+    returns (sel_idx int32 [B,n,Hkv,max_sel], sel_count int32 [B,n,Hkv])."""
+    lib = load()
+    B, n, hq, dqk = q.shape
+    hkv = k.shape[2]
+    if out is not None:
+        idx, cnt = out
+    else:
+        idx = torch.empty((B, n, hkv, max_sel), dtype=torch.int32, device=q.device)
+        cnt = torch.empty((B, n, hkv), dtype=torch.int32, device=q.device)
+    _check_same(q, k, idx, cnt)
+    need = lib.hswa_select_workspace_size(B, n, hq, hkv, dqk, rotary_fraction)
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    st = lib.sparse_select_tokens(_ptr(q), _ptr(k), _ptr(idx), _ptr(cnt), max_sel, recent_window,
+                                  B, n, hq, hkv, dqk, scale, rope_theta, rotary_fraction,
+                                  pos_offset, _dtype_code(q), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(q))
+    _raise(st)
+    return idx, cnt

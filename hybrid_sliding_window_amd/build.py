@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libhswa.so")
 ARCH = os.environ.get("HSWA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.cpp", "rope_prep.hip", "generic.hip", "prefill_bf16.hip", "prefill_persist.hip",
-           "decode_bf16.hip", "decode_fp8.hip", "decode_multi.hip", "kv_append.hip", "sparse_bf16.hip"]
+           "decode_bf16.hip", "decode_fp8.hip", "decode_multi.hip", "kv_append.hip", "select_tokens.hip", "sparse_bf16.hip"]
 
 # Per-source flags.  The persistent prefill runs one wavefront per SIMD and
 # keeps its accumulators in ordinary VGPRs (the VALU rescales them in place);

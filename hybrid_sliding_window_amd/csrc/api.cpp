@@ -569,6 +569,69 @@ hswa_status_t swa_sink_decode_fp8(const void* q, const void* k_cache, const void
                      rotary_fraction, dtype, workspace, workspace_bytes, stream);
 }
 
+size_t hswa_select_workspace_size(int batch, int seqlen, int hq, int hkv, int d_qk,
+                                  float rotary_fraction) {
+  if (batch <= 0 || seqlen <= 0 || hq <= 0 || hkv <= 0 || d_qk <= 0) return 0;
+  if (!(rotary_fraction >= 0.f && rotary_fraction <= 1.f)) return 0;
+  if (rotary_half(d_qk, rotary_fraction) == 0) return 0;
+  const size_t rows = (size_t)batch * seqlen;
+  return round256(rows * hq * (size_t)d_qk * 2) + round256(rows * hkv * (size_t)d_qk * 2);
+}
+
+hswa_status_t sparse_select_tokens(const void* q, const void* k, int* sel_idx, int* sel_count,
+                                   int max_sel, int recent_window, int batch, int seqlen, int hq,
+                                   int hkv, int d_qk, float scale, float rope_theta,
+                                   float rotary_fraction, long long pos_offset,
+                                   hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  hswa_status_t st =
+      check_common(batch, hq, hkv, d_qk, d_qk, scale, rope_theta, rotary_fraction, dtype);
+  if (st != HSWA_OK) return st;
+  if (seqlen < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "seqlen must be >= 0");
+  if (max_sel < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "max_sel must be >= 0");
+  if (recent_window < 1) return fail(HSWA_ERR_INVALID_ARGUMENT, "recent_window must be >= 1");
+  AttnArgs a = base_args(batch, seqlen, hq, hkv, d_qk, d_qk, scale, rope_theta, rotary_fraction);
+  if (dtype != HSWA_BF16 || !hswa::select_tokens_supported(a))
+    return fail(HSWA_ERR_UNSUPPORTED, "token selection takes bf16 q/k with d_qk = 192 and 16 query heads per kv head");
+  if (a.half > 0 && (a.half % 8 != 0 || a.half > 64))
+    return fail(HSWA_ERR_UNSUPPORTED, "the rotated half-width must be a multiple of 8, at most 64");
+  if (batch == 0 || seqlen == 0) return ok();
+  if (!q || !k || !sel_count || (max_sel > 0 && !sel_idx))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "q, k, sel_idx and sel_count must be non-null");
+  if (!aligned16(q) || !aligned16(k)) return fail(HSWA_ERR_INVALID_ARGUMENT, "q and k must be 16-byte aligned");
+  if ((long long)batch * seqlen * hq * (long long)d_qk > (1LL << 56))
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "tensor too large");
+  const size_t need = hswa_select_workspace_size(batch, seqlen, hq, hkv, d_qk, rotary_fraction);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_select_workspace_size()");
+    if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  }
+  a.q = q;
+  a.k = k;
+  a.max_sel = max_sel;
+  a.recent = recent_window;
+  a.pos_offset = pos_offset;
+  a.sel_out = sel_idx;
+  a.cnt_out = sel_count;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.half > 0) {
+    const size_t rows = (size_t)batch * seqlen;
+    uint16_t* qr = static_cast<uint16_t*>(workspace);
+    uint16_t* kr = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
+                                               round256(rows * hq * (size_t)d_qk * 2));
+    hipError_t e = hswa::launch_rope_rows(static_cast<const uint16_t*>(q), qr, batch, seqlen, hq,
+                                          d_qk, a.half, pos_offset, a.rope_theta, s);
+    if (e == hipSuccess)
+      e = hswa::launch_rope_rows(static_cast<const uint16_t*>(k), kr, batch, seqlen, hkv, d_qk,
+                                 a.half, pos_offset, a.rope_theta, s);
+    if (e != hipSuccess) return hip_status(e, "rope preparation launch");
+    a.qrot = qr;
+    a.krot = kr;
+  }
+  return hip_status(hswa::launch_select_tokens(a, s), "token selection launch");
+}
+
 hswa_status_t sparse_sink_attn(const void* q, const void* k, const void* v, const int* sel_idx,
                                const int* sel_count, int max_sel, int recent_window,
                                const float* sink, void* o, int batch, int seqlen, int hq,

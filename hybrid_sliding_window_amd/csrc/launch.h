@@ -22,6 +22,8 @@ struct AttnArgs {
   const float2* rope;             // prefill / sparse: cos/sin table [n][half]
   const void* krot;               // prefill / sparse bf16: K's first R dims, rotated [B, n, hkv, R]
   void* qrot;                     // decode bf16: q rotated to pos[b] [B, hq, d_qk] (workspace)
+  int* sel_out;                   // token selection: lists [B, n, hkv, max_sel]
+  int* cnt_out;                   // and counts [B, n, hkv]
   void* kout;                     // cache append: the K and V caches written
   void* vout;
   const float* kscale;            // decode FP8 caches: per-kv-head value of one K code unit [hkv]
@@ -99,6 +101,19 @@ hipError_t launch_decode_multi_generic(const AttnArgs& a, int layout, bool bf16,
 // codes of value / kscale[g] (vscale[g]).  d_qk, d_v and half multiples of 8.
 hipError_t launch_kv_append(const AttnArgs& a, int layout, bool bf16_in, bool e4m3_out,
                             hipStream_t stream);
+
+// Token selection (bf16, d_qk = 192, 16 query heads per kv head): for every
+// (b, i, g) the max_sel candidates 0 .. i - recent of largest importance into
+// sel_out / cnt_out.  With RoPE (half > 0) q and k are read from qrot / krot,
+// full rotated rows [B, n, hq | hkv, 192] made by launch_rope_rows.
+bool select_tokens_supported(const AttnArgs& a);
+hipError_t launch_select_tokens(const AttnArgs& a, hipStream_t stream);
+
+// dst[row] = src[row] with its first 2 * half dims rotated at position
+// pos0 + (row / heads) % n (cos/sin as launch_rope_k_direct), the rest copied;
+// rows = B * n * heads bf16 rows of d dims.  half <= 64.
+hipError_t launch_rope_rows(const uint16_t* src, uint16_t* dst, int B, int n, int heads, int d,
+                            int half, long long pos0, double theta, hipStream_t stream);
 
 // Decode over E4M3 caches (same shapes as the bf16 decode kernel).
 bool decode_fp8_supported(const AttnArgs& a);

@@ -149,6 +149,60 @@ __global__ void rope_k_direct_kernel(const bf16_t* __restrict__ k, bf16_t* __res
   st16(dst + 8 * c + half, pack8(f1));
 }
 
+// Full rows with their first R dims rotated (the direct cos/sin of
+// rope_k_direct_kernel) and the other dims copied: one thread per 8-dim
+// chunk of the first half (rotated pair) or of the unrotated tail.
+__global__ void rope_rows_kernel(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst,
+                                 long long rows, int n, int heads, int d, int half, long long pos0,
+                                 double theta) {
+  __shared__ double rev[kMaxHalf];
+  if ((int)threadIdx.x < half)
+    rev[threadIdx.x] = pow(theta, -(double)threadIdx.x / (double)half) * 0.15915494309189535;
+  __syncthreads();
+  const int per = (d - half) >> 3;           // chunks: half/8 rotated pairs + (d - 2 half)/8 copies
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * per) return;
+  const long long row = idx / per;
+  const int c = (int)(idx - row * per);
+  const bf16_t* s = src + row * d;
+  bf16_t* o = dst + row * d;
+  if (8 * c < half) {
+    const double pos = (double)(pos0 + (row / heads) % n);
+    float f0[8], f1[8];
+    unpack8(ld16(s + 8 * c), f0);
+    unpack8(ld16(s + 8 * c + half), f1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double turns = pos * rev[8 * c + e];
+      const float f = (float)(turns - floor(turns));
+      const float co = __builtin_amdgcn_cosf(f), si = __builtin_amdgcn_sinf(f);
+      const float y0 = f0[e] * co - f1[e] * si;
+      const float y1 = f1[e] * co + f0[e] * si;
+      f0[e] = y0;
+      f1[e] = y1;
+    }
+    st16(o + 8 * c, pack8(f0));
+    st16(o + 8 * c + half, pack8(f1));
+  } else {
+    const int d0 = 8 * c + half;             // past the rotated 2 * half dims
+    st16(o + d0, ld16(s + d0));
+  }
+}
+
+hipError_t launch_rope_rows(const uint16_t* src, uint16_t* dst, int B, int n, int heads, int d,
+                            int half, long long pos0, double theta, hipStream_t stream) {
+  const long long rows = (long long)B * n * heads;
+  const long long total = rows * ((d - half) >> 3);
+  if (total == 0) return hipSuccess;
+  if (half > kMaxHalf || (half & 7) || (d & 7)) return hipErrorInvalidValue;
+  const int threads = 256;
+  const long long blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(rope_rows_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                     reinterpret_cast<const bf16_t*>(src), reinterpret_cast<bf16_t*>(dst), rows,
+                     n, heads, d, half, pos0, theta);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_table(float2* table, long long pos0, int npos, int half, double theta,
                              hipStream_t stream) {
   const long long total = (long long)npos * half;

@@ -302,6 +302,36 @@ hswa_status_t sparse_sink_attn_fp8(const void* q, const void* k, const void* v,
                                    hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/* Bytes of workspace sparse_select_tokens needs: rotated copies of q and k
+ * (bf16, full rows) when RoPE is on, each rounded up to 256 bytes; else 0. */
+size_t hswa_select_workspace_size(int batch, int seqlen, int hq, int hkv, int d_qk,
+                                  float rotary_fraction);
+
+/*
+ * Token selection for the sparse layers: the selection indices the sparse
+ * layers reuse from the preceding full-attention layer ("MiMo-V3 HySparse2"
+ * (aideepthink.cn), section 4).  For query i (position pos_offset + i) and
+ * kv head g the importance of token j is the full-attention layer's softmax
+ * probability summed over the group's query heads,
+ *     I_j = sum_{h in g} exp(a_hij - lse_hi),   a as swa_sink_prefill, over 0 .. i,
+ * (no sink: a full-attention layer); the candidates are 0 .. i -
+ * recent_window, and the min(max_sel, i - recent_window + 1) of largest
+ * importance are kept, equal importances going to the lower position.
+ * Importances are compared at 22 bits of their fp32 pattern (exponent and 13
+ * mantissa bits): keys that agree to that resolution count as equal.
+ *   q [batch, seqlen, hq, d_qk], k [batch, seqlen, hkv, d_qk] (bf16; d_qk =
+ *   192 and hq = 16 * hkv);  sel_idx int32 [batch, seqlen, hkv, max_sel]
+ *   (ascending, padded with -1), sel_count int32 [batch, seqlen, hkv]: the
+ *   layout sparse_sink_attn reads.  RoPE as swa_sink_prefill (half-width a
+ *   multiple of 8, at most 64); workspace: hswa_select_workspace_size().
+ */
+hswa_status_t sparse_select_tokens(const void* q, const void* k, int* sel_idx, int* sel_count,
+                                   int max_sel, int recent_window, int batch, int seqlen, int hq,
+                                   int hkv, int d_qk, float scale, float rope_theta,
+                                   float rotary_fraction, long long pos_offset,
+                                   hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* Text for the last non-OK status returned on this thread ("" if none). */
 const char* hswa_last_error(void);
 

@@ -173,6 +173,25 @@ def test_append_validation(lib):
                                    192, 128, 1000, 1e4, 0.334, 1, None) == INVALID   # k_scale missing
 
 
+def test_select_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, idx=FAKE, cnt=FAKE, max_sel=64, recent=16, batch=1, seqlen=100,
+                 hq=64, hkv=4, d_qk=192, scale=0.0, theta=1e7, frac=0.0, pos_offset=0, dtype=1,
+                 ws=None, ws_bytes=0, stream=None)
+        a.update(kw)
+        return lib.sparse_select_tokens(*a.values())
+    assert call(hq=32) == UNSUPPORTED                      # 16 query heads per kv head only
+    assert call(dtype=0) == UNSUPPORTED                    # bf16 only
+    assert call(d_qk=128) == UNSUPPORTED
+    assert call(max_sel=-1) == INVALID
+    assert call(recent=0) == INVALID
+    assert call(cnt=None) == INVALID
+    assert call(frac=0.334) == INVALID                     # workspace missing
+    assert call(seqlen=0, q=None) == OK
+    assert hswa._binding.load().hswa_select_workspace_size(1, 100, 64, 4, 192, 0.334) == \
+        100 * 64 * 192 * 2 + 100 * 4 * 192 * 2
+
+
 def test_decode_fp8_validation(lib):
     def call(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, layout=0, offs=None, pos=FAKE, sink=None,

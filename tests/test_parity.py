@@ -884,3 +884,97 @@ def test_append_then_multi_decode(gpu_lib):
     ref = oracle.decode_multi_ring(_np(q), kref, vref, np.array(pos), _np(sink), W,
                                    rope_theta=1.0e4, rotary_fraction=0.334)
     _check("append + multi-token decode", o, ref)
+
+
+# ---------------------------------------------------------------------------
+# Token selection for the sparse layers
+# ---------------------------------------------------------------------------
+
+def _check_selection(name, idx, cnt, q, k, rows, recent, K, frac=0.0, theta=1.0e7, tol=1e-3):
+    """Counts exact; lists ascending, distinct, in range, -1 padded; the selected
+    set valid against the oracle's float64 importances (no unselected candidate
+    above a selected one by more than `tol` relative) and equal to the oracle's
+    selection except where importances tie within `tol`."""
+    idx = idx.cpu().numpy()
+    cnt = cnt.cpu().numpy()
+    B, hkv = idx.shape[0], idx.shape[2]
+    worst, differ, total = 0.0, 0, 0
+    for b in range(B):
+        for t, i in enumerate(rows):
+            for g in range(hkv):
+                ncand = max(0, int(i) - recent + 1)
+                want = min(K, ncand)
+                assert cnt[b, t, g] == want, (name, b, i, g, cnt[b, t, g], want)
+                sel = idx[b, t, g, :want]
+                assert (idx[b, t, g, want:] == -1).all()
+                assert (np.diff(sel) > 0).all() and (sel >= 0).all() and (sel < max(ncand, 1)).all()
+                if want == ncand or want == 0:
+                    continue
+                imp = oracle.selection_importance(q, k, b, int(i), g, recent, rope_theta=theta,
+                                                  rotary_fraction=frac)
+                mask = np.zeros(ncand, bool)
+                mask[sel] = True
+                lo, hi = imp[mask].min(), imp[~mask].max()
+                worst = max(worst, (hi - lo) / max(lo, 1e-300))
+                ref = np.sort(np.lexsort((np.arange(ncand), -imp))[:want])
+                differ += len(np.setdiff1d(sel, ref))
+                total += want
+    print(f"[parity] {name}: worst inversion {worst:.2e}, {differ}/{total} picks differ", flush=True)
+    assert worst <= tol, (name, worst)
+    if total:
+        assert differ <= max(2, 0.01 * total), (name, differ, total)
+
+
+@pytest.mark.parametrize("B,n,hkv,recent,K,frac", [
+    (1, 300, 4, 16, 40, 0.0),       # the workload's heads at a size the oracle covers
+    (2, 211, 2, 32, 64, 0.334),     # ragged rows, RoPE (base 1e7) on both q and k
+    (1, 150, 1, 8, 500, 0.0),       # every candidate fits: no ranking
+    (1, 64, 2, 100, 8, 0.0),        # window wider than most rows: few or no candidates
+])
+def test_select_tokens(gpu_lib, B, n, hkv, recent, K, frac):
+    hq = 16 * hkv
+    x = synthetic.prefill_inputs(B, n, hq, hkv, 192, 128, "bf16", 240 + n, DEV, None)
+    idx, cnt = gpu_lib.sparse_select_tokens(x["q"], x["k"], max_sel=K, recent_window=recent,
+                                            rope_theta=1.0e7, rotary_fraction=frac)
+    _check_selection(f"select B={B} n={n} hkv={hkv} recent={recent} K={K}", idx, cnt, _np(x["q"]),
+                     _np(x["k"]), np.arange(n), recent, K, frac)
+
+
+def test_select_tokens_ties_and_empty(gpu_lib):
+    """Keys equal to each other tie exactly: the lower positions win; max_sel 0
+    keeps nothing."""
+    n, hkv, hq = 48, 1, 16
+    x = synthetic.prefill_inputs(1, n, hq, hkv, 192, 128, "bf16", 250, DEV, None)
+    k = x["k"].clone()
+    for j in (3, 9, 10, 20, 30):
+        k[0, j] = k[0, 40]
+    q = x["q"].clone()
+    q[0, 47] = (k[0, 40] * 2).to(torch.bfloat16).expand(hq, 192)
+    idx, cnt = gpu_lib.sparse_select_tokens(q, k, max_sel=3, recent_window=4)
+    assert cnt[0, 47, 0].item() == 3
+    assert idx[0, 47, 0].tolist() == [3, 9, 10]
+    idx0, cnt0 = gpu_lib.sparse_select_tokens(q, k, max_sel=0, recent_window=4)
+    assert (cnt0 == 0).all() and idx0.numel() == 0
+
+
+def test_select_then_sparse(gpu_lib):
+    """The lists feed sparse attention directly (the reuse of section 4)."""
+    n, hkv, hq, recent, K = 400, 2, 32, 32, 48
+    x = synthetic.prefill_inputs(1, n, hq, hkv, 192, 128, "bf16", 251, DEV)
+    idx, cnt = gpu_lib.sparse_select_tokens(x["q"], x["k"], max_sel=K, recent_window=recent)
+    o = gpu_lib.sparse_sink_attn(x["q"], x["k"], x["v"], idx, cnt, x["sink"], recent_window=recent)
+    q, k, v, s = _host(x)
+    ref = oracle.sparse_sink_attn(q, k, v, idx.cpu().numpy(), cnt.cpu().numpy(), s, recent=recent)
+    _check("sparse attention over selected tokens", o, ref)
+
+
+def test_select_tokens_full_size(gpu_lib):
+    wl = synthetic.WORKLOADS["sparse_prefill_n65536"]
+    x = synthetic.prefill_inputs(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, "bf16", wl["seed"], DEV,
+                                 None)
+    idx, cnt = gpu_lib.sparse_select_tokens(x["q"], x["k"], max_sel=wl["max_sel"],
+                                            recent_window=wl["recent"])
+    rows = np.array([0, 127, 128, 1151, 1152, 1153, 5000, 33333, 65535])
+    ridx = torch.from_numpy(rows).to(DEV)
+    _check_selection("select full size (sampled rows)", idx[:, ridx], cnt[:, ridx], _np(x["q"]),
+                     _np(x["k"]), rows, wl["recent"], wl["max_sel"])
