@@ -50,12 +50,19 @@ constexpr int NBIN = 2048;               // histogram bins per level
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-// Sum over the 16 lanes of a column block (lane bits 0..3).
+// Sum over the 16 lanes of a column block (one DPP row), left in every lane:
+// pairs within quads (quad_perm 1,0,3,2 and 2,3,0,1), then quad with quad
+// (row_half_mirror), then half-row with half-row (row_mirror).  Each step
+// pairs every lane with one partner, so all 16 lanes end with the total.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+  v += dpp<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp<0x141>(v);   // row_half_mirror
+  v += dpp<0x140>(v);   // row_mirror
   return v;
 }
 
