@@ -340,6 +340,18 @@ def _decode_mtp(out, dev):
                                        "tflops": pairs * ga["hq"] * FLOP_PER_PAIR / t / 1e12,
                                        "queries_per_s": wl["B"] * T / t}
     _log(f"MTP decode GA {out['decode_mtp_ga_contiguous']}")
+    # the step's cache append: 64 sequences x 4 new tokens into the GA pool
+    kn = synthetic.normal((wl["B"], T, ga["hkv"], 192), 17, dev, "bf16")
+    vn = synthetic.normal((wl["B"], T, ga["hkv"], 128), 18, dev, "bf16")
+    fa = lambda: hswa.kv_cache_append(kn, vn, c["k"], c["v"], c["pos"], maxp,  # noqa: E731
+                                      layout=hswa.KV_CONTIGUOUS, seq_offsets=c["seq_offsets"],
+                                      rope_theta=1.0e7, rotary_fraction=0.334)
+    _, per = timed(fa, 20, 4)
+    app_bytes = 2 * wl["B"] * T * ga["hkv"] * (192 + 128) * 2
+    t = float(np.median(per)) / 1e3
+    out["kv_append_mtp_ga"] = {"us": t * 1e6, "bytes": app_bytes, "gbps": app_bytes / t / 1e9,
+                               "note": "latency-bound: 64 x 4 tokens, 655 KB read + written"}
+    _log(f"append {out['kv_append_mtp_ga']}")
 
 
 def _decode_fp8(out, dev):

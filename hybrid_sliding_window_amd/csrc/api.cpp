@@ -351,8 +351,9 @@ hswa_status_t append_impl(const void* k_new, const void* v_new, void* k_cache, v
   }
   if (max_pos < 0) return fail(HSWA_ERR_INVALID_ARGUMENT, "max_pos must be >= 0");
   const int half = rotary_half(d_qk, rotary_fraction);
-  if (d_qk % 8 != 0 || d_v % 8 != 0 || half % 8 != 0)
-    return fail(HSWA_ERR_UNSUPPORTED, "head dims and the rotated half-width must be multiples of 8");
+  if (d_qk % 8 != 0 || d_v % 8 != 0 || half % 8 != 0 || half > 64)
+    return fail(HSWA_ERR_UNSUPPORTED,
+                "head dims and the rotated half-width must be multiples of 8 (half-width at most 64)");
   if (batch == 0 || q_len == 0) return ok();
   if (!k_new || !v_new || !k_cache || !v_cache || !pos)
     return fail(HSWA_ERR_INVALID_ARGUMENT, "k_new, v_new, caches and pos must be non-null");

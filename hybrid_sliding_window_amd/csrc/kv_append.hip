@@ -10,8 +10,8 @@
 // value / scale (per kv head) rounded to nearest even and saturated to the
 // largest finite code.
 //
-// One thread per (token, kv head, 8 consecutive dims): fully coalesced 16-
-// or 32-byte reads and writes; the kernel moves each byte once.
+// 16- or 32-byte reads and writes, each byte moved once; the cos/sin of a
+// rotated pair are evaluated once per token, all of a block's in parallel.
 #include <math.h>
 
 #include "common.h"
@@ -93,82 +93,101 @@ __device__ __forceinline__ void store8(void* base, long long elem, const float* 
 
 }  // namespace
 
-// Grid: x over (token, kv head, chunk) work items, 256 threads.  K chunks
-// c < R/16 carry a rotated pair (dims 8c.. and their partners R/2 further
-// on); the others and all V chunks are copied or quantised.
+// A block serves TPB tokens.  First every (token, rotated pair) evaluates
+// its cos/sin once, one per thread, into LDS; then the threads take the
+// (token, kv head, 8-dim chunk) items: K chunks c < R/16 rotate a pair (dims
+// 8c.. and their partners R/2 further on), the other K chunks and all V
+// chunks are copied or quantised.
+constexpr int TPB = 4;
+constexpr int kMaxPairs = 64;
+
 template <typename TIN, int OUT>
 __global__ __launch_bounds__(256) void kv_append_kernel(AttnArgs a, int layout) {
+  __shared__ float2 csn[TPB][kMaxPairs];
   const int half = a.half;
-  const int kch = a.d_qk / 8 - half / 8;           // K work items per row (pairs count once)
+  const long long ntok = (long long)a.B * a.nq;
+  const long long tok0 = (long long)blockIdx.x * TPB;
+  for (int e = threadIdx.x; e < TPB * half; e += blockDim.x) {
+    const int tl = e / half, r = e - tl * half;
+    const long long bt = tok0 + tl;
+    if (bt >= ntok) continue;
+    const long long p = a.pos[bt / a.nq] + bt % a.nq;
+    const double ang = (double)p * pow(a.rope_theta, -(double)r / (double)half);
+    double sd, cd;
+    sincos(ang, &sd, &cd);
+    csn[tl][r] = make_float2((float)cd, (float)sd);
+  }
+  __syncthreads();
+  const int kch = a.d_qk / 8 - half / 8;           // K items per head (pairs count once)
   const int vch = a.d_v / 8;
-  const int per_row = kch + vch;
-  const long long item = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)a.B * a.nq * a.hkv * per_row;
-  if (item >= total) return;
-  const long long rowi = item / per_row;           // (b, t, g)
-  const int w = (int)(item - rowi * per_row);
-  const int g = (int)(rowi % a.hkv);
-  const long long bt = rowi / a.hkv;
-  const int t = (int)(bt % a.nq);
-  const int b = (int)(bt / a.nq);
-  const long long p = a.pos[b] + t;
-  if (p < 0 || p > a.max_pos) return;              // contract broken: nothing is written
-  if (layout == 1 && p >= a.seq_offsets[b + 1] - a.seq_offsets[b]) return;
-  const long long crow = append_row(a, layout, b, p) * a.hkv + g;
-  const TIN* kin = static_cast<const TIN*>(a.k) + rowi * a.d_qk;   // the new keys
-  const TIN* vin = static_cast<const TIN*>(a.v) + rowi * a.d_v;    // and values
-  if (w < kch) {
-    float f0[8], f1[8];
-    if (8 * w < half) {                            // rotated pair: dims 8w.. and 8w + half..
-      const int d0 = 8 * w;
-      load8(kin + d0, f0);
-      load8(kin + d0 + half, f1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double ang = (double)p * pow(a.rope_theta, -(double)(d0 + e) / (double)half);
-        double sd, cd;
-        sincos(ang, &sd, &cd);
-        rotate_pair(f0[e], f1[e], (float)cd, (float)sd);
-      }
-      if (OUT == 1) {
-        const float s = a.kscale[g];
+  const int per_head = kch + vch;
+  const int per_tok = per_head * a.hkv;
+  for (int it = threadIdx.x; it < TPB * per_tok; it += blockDim.x) {
+    const int tl = it / per_tok;
+    const int rem = it - tl * per_tok;
+    const int g = rem / per_head;
+    const int w = rem - g * per_head;
+    const long long bt = tok0 + tl;
+    if (bt >= ntok) continue;
+    const int t = (int)(bt % a.nq);
+    const int b = (int)(bt / a.nq);
+    const long long p = a.pos[b] + t;
+    if (p < 0 || p > a.max_pos) continue;          // contract broken: nothing is written
+    if (layout == 1 && p >= a.seq_offsets[b + 1] - a.seq_offsets[b]) continue;
+    const long long crow = append_row(a, layout, b, p) * a.hkv + g;
+    if (w < kch) {
+      const TIN* kin = static_cast<const TIN*>(a.k) + (bt * a.hkv + g) * a.d_qk;
+      const float s = (OUT == 1) ? a.kscale[g] : 1.f;
+      if (8 * w < half) {                          // rotated pair: dims 8w.. and 8w + half..
+        const int d0 = 8 * w;
+        float f0[8], f1[8];
+        load8(kin + d0, f0);
+        load8(kin + d0 + half, f1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          f0[e] = __fdiv_rn(f0[e], s);
-          f1[e] = __fdiv_rn(f1[e], s);
+          const float2 cs = csn[tl][d0 + e];
+          rotate_pair(f0[e], f1[e], cs.x, cs.y);
         }
+        if (OUT == 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            f0[e] = __fdiv_rn(f0[e], s);
+            f1[e] = __fdiv_rn(f1[e], s);
+          }
+        }
+        store8<TIN, OUT>(a.kout, crow * a.d_qk + d0, f0);
+        store8<TIN, OUT>(a.kout, crow * a.d_qk + d0 + half, f1);
+      } else {                                     // unrotated dims past the first R
+        const int d0 = 8 * w + half;
+        float f0[8];
+        load8(kin + d0, f0);
+        if (OUT == 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f0[e] = __fdiv_rn(f0[e], s);
+        }
+        store8<TIN, OUT>(a.kout, crow * a.d_qk + d0, f0);
       }
-      store8<TIN, OUT>(a.kout, crow * a.d_qk + d0, f0);
-      store8<TIN, OUT>(a.kout, crow * a.d_qk + d0 + half, f1);
-    } else {                                       // unrotated dims
-      const int d0 = 8 * w + half;                 // chunks past the rotated R dims
-      load8(kin + d0, f0);
+    } else {
+      const int d0 = 8 * (w - kch);
+      const TIN* vin = static_cast<const TIN*>(a.v) + (bt * a.hkv + g) * a.d_v;
+      float f[8];
+      load8(vin + d0, f);
       if (OUT == 1) {
-        const float s = a.kscale[g];
+        const float s = a.vscale[g];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f0[e] = __fdiv_rn(f0[e], s);
+        for (int e = 0; e < 8; ++e) f[e] = __fdiv_rn(f[e], s);
       }
-      store8<TIN, OUT>(a.kout, crow * a.d_qk + d0, f0);
+      store8<TIN, OUT>(a.vout, crow * a.d_v + d0, f);
     }
-  } else {
-    const int d0 = 8 * (w - kch);
-    float f[8];
-    load8(vin + d0, f);
-    if (OUT == 1) {
-      const float s = a.vscale[g];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = __fdiv_rn(f[e], s);
-    }
-    store8<TIN, OUT>(a.vout, crow * a.d_v + d0, f);
   }
 }
 
 hipError_t launch_kv_append(const AttnArgs& a, int layout, bool bf16_in, bool e4m3_out,
                             hipStream_t stream) {
-  const long long per_row = a.d_qk / 8 - a.half / 8 + a.d_v / 8;
-  const long long total = (long long)a.B * a.nq * a.hkv * per_row;
-  if (total == 0) return hipSuccess;
-  const long long blocks = (total + 255) / 256;
+  const long long ntok = (long long)a.B * a.nq;
+  if (ntok == 0) return hipSuccess;
+  if (a.half > kMaxPairs) return hipErrorInvalidValue;
+  const long long blocks = (ntok + TPB - 1) / TPB;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(256);
   if (bf16_in) {

@@ -170,7 +170,8 @@ hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_
  * product and the difference / sum rounded on its own), then rounded to the
  * cache type.  Values are copied.  Tokens whose position is negative, above
  * max_pos or (contiguous) not below their sequence's row count are not
- * written.  d_qk, d_v and the rotated half-width R/2 must be multiples of 8.
+ * written.  d_qk, d_v and the rotated half-width R/2 must be multiples of 8,
+ * and R/2 at most 64.
  */
 hswa_status_t kv_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                               hswa_kv_layout_t layout, int ring_slots,

@@ -166,6 +166,7 @@ def test_append_validation(lib):
     assert call(layout=1, slots=0) == INVALID              # contiguous needs offsets
     assert call(frac=0.1) == UNSUPPORTED                   # R/2 = 9: not a multiple of 8
     assert call(d_v=100) == UNSUPPORTED
+    assert call(frac=1.0) == UNSUPPORTED                   # R/2 = 96 > 64
     assert call(pos=None) == INVALID
     assert call(kc=MISALIGNED) == INVALID
     assert call(q_len=0, kn=None) == OK
