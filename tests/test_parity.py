@@ -524,6 +524,29 @@ def test_multi_decode_contiguous(gpu_lib, T, hq, hkv, window, sink, dtype):
            fp32=(dtype == "f32"))
 
 
+def test_multi_decode_wide_falls_back(gpu_lib):
+    """8 queries x 16 heads = 128 columns per kv head: past the matrix-core
+    kernel's 64, the generic kernel serves the step (ring and contiguous)."""
+    T, S, W = 8, 140, 128
+    pos = [0, 3, 130, 5000]
+    d = synthetic.multi_ring_inputs(len(pos), T, 64, 4, S, 192, 128, "bf16", 225,
+                                    torch.tensor(pos), DEV)
+    o = gpu_lib.swa_sink_decode_multi(d["q"], d["k"], d["v"], d["pos"], max(pos) + T - 1,
+                                      layout=gpu_lib.KV_RING, ring_slots=S, sink=d["sink"],
+                                      window=W, rope_theta=1.0e4, rotary_fraction=0.334)
+    ref = oracle.decode_multi_ring(_np(d["q"]), _np(d["k"]), _np(d["v"]), np.array(pos),
+                                   _np(d["sink"]), W, rope_theta=1.0e4, rotary_fraction=0.334)
+    _check("multi decode ring T=8 G=16 (generic)", o, ref)
+    c = synthetic.multi_contiguous_inputs(len(pos), T, 64, 4, 192, 128, "bf16", 226,
+                                          torch.tensor(pos), DEV)
+    oc = gpu_lib.swa_sink_decode_multi(c["q"], c["k"], c["v"], c["pos"], max(pos) + T - 1,
+                                       layout=gpu_lib.KV_CONTIGUOUS, seq_offsets=c["seq_offsets"],
+                                       window=0)
+    refc = oracle.decode_multi_contiguous(_np(c["q"]), _np(c["k"]), _np(c["v"]),
+                                          c["seq_offsets"].cpu().numpy(), np.array(pos))
+    _check("multi decode contiguous T=8 G=16 (generic)", oc, refc)
+
+
 def test_multi_decode_one_query_is_decode(gpu_lib):
     """q_len = 1 over a ring of W slots is the single-token decode."""
     pos = [0, 5, 127, 128, 1000, 262143]
