@@ -10,10 +10,13 @@
 // order: the lists sparse attention reads.
 //
 // A workgroup of eight wavefronts owns 16 consecutive query rows of one
-// (sequence, kv head) with G = 16 query heads: a row is one 16-column block
-// on the N side of 16x16x32 MFMAs (column = head), two rows per wavefront,
-// so every per-row state (softmax totals, histograms, thresholds, output
-// offsets) belongs to one wavefront and needs no synchronisation.  K tiles of
+// (sequence, kv head) with G = 16 query heads, two rows per wavefront, so
+// every per-row state (softmax totals, histograms, thresholds, output
+// offsets) belongs to one wavefront and needs no synchronisation.  A row's
+// scores are S = Q . K^T on 16x16x32 MFMAs with the 16 heads on M and 16
+// keys on N: lane (key c, group q) holds heads 4q .. 4q + 3 of key c, so a
+// key's importance is four exponentials summed in the lane and two
+// exchanges across the lane groups, and lanes 0..15 own the keys in order.  K tiles of
 // 32 keys stream through LDS with global_load_lds, shared by all 16 rows.
 // Four passes over the keys:
 //   1. lse_hi per (row, head): online max / sum in base 2;
@@ -50,19 +53,26 @@ constexpr int NBIN = 2048;               // histogram bins per level
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-// Sum over the 16 lanes of a column block (one DPP row), left in every lane:
-// pairs within quads (quad_perm 1,0,3,2 and 2,3,0,1), then quad with quad
+// Max / sum over the 16 lanes of a DPP row, left in every lane: pairs
+// within quads (quad_perm 1,0,3,2 and 2,3,0,1), then quad with quad
 // (row_half_mirror), then half-row with half-row (row_mirror).  Each step
-// pairs every lane with one partner, so all 16 lanes end with the total.
+// pairs every lane with one partner, so all 16 lanes end with the result.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));    // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp<0x4E>(v));    // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp<0x140>(v));   // row_mirror
+  return v;
+}
 __device__ __forceinline__ float sum16(float v) {
-  v += dpp<0xB1>(v);    // quad_perm [1, 0, 3, 2]
-  v += dpp<0x4E>(v);    // quad_perm [2, 3, 0, 1]
-  v += dpp<0x141>(v);   // row_half_mirror
-  v += dpp<0x140>(v);   // row_mirror
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
   return v;
 }
 
@@ -270,12 +280,16 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
   const float c2 = a.scale * kLog2e;
 
   // ---- pass 1: lse (base 2) of every (row, head) over keys 0 .. i -----------
-  float m[NB], l[NB];
+  // lane (c, q) runs a (max, sum) for heads 4q + r over its keys c of each
+  // 16-key half, reduced over the 16 key lanes at the end
+  float m[NB][4], l[NB][4];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m[nb] = kNegInf;
-    l[nb] = 0.f;
-  }
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m[nb][r] = kNegInf;
+      l[nb][r] = 0.f;
+    }
   if (any_rank) {
     stream(lse_keys, [&](const unsigned char* kc, int k0) {
 #pragma unroll
@@ -288,39 +302,35 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma16(kf[ks], qf[nb][ks], sc[nb]);
+          for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma16(qf[nb][ks], kf[ks], sc[nb]);
+        const int j = k0 + 16 * hf + c;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          float x[4];
-          float mx = kNegInf;
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int j = k0 + 16 * hf + 4 * grp + r;
-            x[r] = (j <= row_i[nb]) ? sc[nb][r] * c2 : kNegInf;
-            mx = fmaxf(mx, x[r]);
+            const float x = (j <= row_i[nb]) ? sc[nb][r] * c2 : kNegInf;
+            const float mn = fmaxf(m[nb][r], x);
+            const float ms = (mn == kNegInf) ? 0.f : mn;
+            l[nb][r] = l[nb][r] * fast_exp2(m[nb][r] - ms) + fast_exp2(x - ms);
+            m[nb][r] = mn;
           }
-          const float mn = fmaxf(m[nb], mx);
-          const float ms = (mn == kNegInf) ? 0.f : mn;
-          float s = 0.f;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) s += fast_exp2(x[r] - ms);
-          l[nb] = l[nb] * fast_exp2(m[nb] - ms) + s;
-          m[nb] = mn;
-        }
       }
     });
   }
-  float lse[NB];
+  float lse[NB][4];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const float M = max_across_groups(m[nb]);
-    const float L = sum_across_groups(l[nb] * ((m[nb] == kNegInf) ? 0.f : fast_exp2(m[nb] - M)));
-    lse[nb] = M + __log2f(L);
-  }
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float M = max16(m[nb][r]);
+      const float L =
+          sum16(l[nb][r] * ((m[nb][r] == kNegInf) ? 0.f : fast_exp2(m[nb][r] - M)));
+      lse[nb][r] = M + __log2f(L);
+    }
 
-  // importance (fp32 bits) of key j of the tile half for row nb, replicated
-  // over the row's 16 head lanes; lanes (c, grp) hold keys 4 grp + r
-  auto importances = [&](const unsigned char* kc, int hf, float (&imp)[NB][4]) {
+  // importance of key c of the tile half for row nb (all four lane groups
+  // of column c end with the sum over the 16 heads)
+  auto importances = [&](const unsigned char* kc, int hf, float (&imp)[NB]) {
     f32x4 sc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -329,20 +339,20 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma16(kf[ks], qf[nb][ks], sc[nb]);
+      for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma16(qf[nb][ks], kf[ks], sc[nb]);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb) {
+      float v = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) imp[nb][r] = sum16(fast_exp2(fmaf(sc[nb][r], c2, -lse[nb])));
+      for (int r = 0; r < 4; ++r) v += fast_exp2(fmaf(sc[nb][r], c2, -lse[nb][r]));
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      imp[nb] = v;
+    }
   };
-  // key owned by this lane (one lane per key: c == r): position and importance
-  auto owned = [&](const float (&imp)[NB][4], int nb) -> float {
-    const float v01 = (c == 0) ? imp[nb][0] : imp[nb][1];
-    const float v23 = (c == 2) ? imp[nb][2] : imp[nb][3];
-    return (c < 2) ? v01 : v23;
-  };
-  const bool owner = c < 4;
-  const int kk_own = 4 * grp + (c & 3);          // key within a 16-key half
+  auto owned = [&](const float (&imp)[NB], int nb) -> float { return imp[nb]; };
+  const bool owner = grp == 0;                   // lanes 0..15 own keys 0..15 of a half
+  const int kk_own = c;
 
   int bin1[NB], t22[NB];
   unsigned above1[NB], quota[NB];
@@ -353,7 +363,7 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
     stream(cand_keys, [&](const unsigned char* kc, int k0) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        float imp[NB][4];
+        float imp[NB];
         importances(kc, hf, imp);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -375,7 +385,7 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
     stream(cand_keys, [&](const unsigned char* kc, int k0) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        float imp[NB][4];
+        float imp[NB];
         importances(kc, hf, imp);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -413,7 +423,7 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
   stream(cand_keys, [&](const unsigned char* kc, int k0) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      float imp[NB][4];
+      float imp[NB];
       if (any_rank) importances(kc, hf, imp);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
