@@ -39,6 +39,7 @@ from .attention import (  # noqa: F401
     attend_row,
     swa_sink_prefill,
     swa_sink_prefill_chunk,
+    swa_sink_prefill_chunk_cached,
     ga_prefill,
     swa_sink_decode_ring,
     swa_sink_decode_contiguous,

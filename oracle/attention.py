@@ -227,6 +227,37 @@ def swa_sink_prefill_chunk(q, k, v, sink, window=128, scale=None, rope_theta=100
                         pos_offset=pos_offset, q_rows=q)
 
 
+def swa_sink_prefill_chunk_cached(q, k_cached, v, sink, window=128, scale=None,
+                                  rope_theta=10000.0, rotary_fraction=0.0, pos_offset=0):
+    """swa_sink_prefill_chunk over a cache whose keys are stored already
+    rotated (the decode caches' convention, written by kv_append): the
+    chunk's queries are rotated at their positions, the keys are used as
+    they are.  k_cached: [B, kv_len, Hkv, d_qk] rotated keys (prefix and
+    chunk, the chunk's appended first)."""
+    q = np.asarray(q)
+    k_cached = np.asarray(k_cached, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, q_len, hq, d = q.shape
+    n, hkv = k_cached.shape[1], k_cached.shape[2]
+    if q_len > n:
+        raise ValueError("a chunk cannot be longer than its sequence")
+    G = _check_heads(hq, hkv)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s_all = _sink_vector(sink, hq)
+    rows = n - q_len + np.arange(q_len)
+    qr = rope(q, pos_offset + rows, rope_theta, rotary_fraction)
+    out = np.zeros((B, q_len, hq, v.shape[-1]), dtype=np.float64)
+    for b in range(B):
+        for t, i in enumerate(rows):
+            J = window_keys(int(i), window)
+            for g in range(hkv):
+                hs = slice(g * G, (g + 1) * G)
+                out[b, t, hs] = attend_row(qr[b, t, hs], k_cached[b, J, g], v[b, J, g], s_all[hs],
+                                           scale)
+    return out
+
+
 def ga_prefill(q, k, v, scale=None, rope_theta=1.0e7, rotary_fraction=0.0, pos_offset=0):
     """GA layer (rslog.cc section 1 and section 5): full causal set, no sink."""
     n = np.asarray(q).shape[1]

@@ -368,6 +368,13 @@ def pin_p13_chunk(O):
                                            rope_theta=3.0, rotary_fraction=0.5)
             assert got.shape == (1, ql, 4, dv)
             assert np.abs(got - ref[:, n - ql:]).max() < 1e-12, (W, ql)
+    # the same chunk over a cache holding the keys already rotated (fp64 here)
+    kc = O.rope(k, np.arange(n), 3.0, 0.5)
+    for W in (1, 3, None):
+        ref = _brute_prefill(q, k, v, sink, W, 3.0, 0.5)
+        got = O.swa_sink_prefill_chunk_cached(q[:, n - 4:], kc, v, sink, window=0 if W is None else W,
+                                              rope_theta=3.0, rotary_fraction=0.5)
+        assert np.abs(got - ref[:, n - 4:]).max() < 1e-12, W
     q, k, v, s = _inputs(2, 40, 8, 2, seed=31)
     ql = 13
     i = np.arange(40 - ql, 40)[:, None]
@@ -629,7 +636,9 @@ MUTANTS = {
     "sparse_drops_selection": ("return np.union1d(sel, rec)", "return rec"),
     "sparse_recent_too_wide": ("lo = max(0, i - recent + 1)", "lo = max(0, i - recent)"),
     "sink_in_numerator": ("out[g] = (e @ vj) / den", "out[g] = (e @ vj + math.exp(min(sink[g] - m[g], 0.0))) / den"),
-    "chunk_rows_from_zero": ("rows = n - q_len + np.arange(q_len)", "rows = np.arange(q_len)"),
+    "chunk_rows_from_zero": ("rows = n - q_len + np.arange(q_len)", "rows = np.arange(q_len)", ),
+    "cached_chunk_query_unrotated": ("qr = rope(q, pos_offset + rows, rope_theta, rotary_fraction)\n    out",
+                                     "qr = np.asarray(q, dtype=np.float64)\n    out"),
     "multi_ring_slot_by_window": ("slots = np.mod(J, S)", "slots = np.mod(J, window)"),
     "multi_query_not_causal_among_drafts": ("            p = int(pos[b]) + t\n            J = window_keys(p, window)\n            qt",
                                             "            p = int(pos[b]) + t\n            J = window_keys(int(pos[b]) + T - 1, window)\n            qt"),
