@@ -231,13 +231,19 @@ def _chunk(out, steps, warmup, dev):
                 x["q"], x["k"], x["v"], x["sink"], window=wl["window"],
                 rope_theta=wl["rope_theta"], rotary_fraction=wl["rotary_fraction"], out=o,
                 workspace=ws)
-            _, per = timed(fn, max(3, steps // 4), 1)
+            # the same chunk over a cache of already-rotated keys (no key preparation)
+            fc = lambda: hswa.swa_sink_prefill_chunk_cached(  # noqa: E731
+                x["q"], x["k"], x["v"], x["sink"], window=wl["window"],
+                rope_theta=wl["rope_theta"], rotary_fraction=wl["rotary_fraction"], out=o,
+                workspace=ws)
             p = np.arange(prefix, kv, dtype=np.int64)
             pairs = int((np.minimum(p + 1, wl["window"]) if wl["window"] > 0 else p + 1).sum())
             flops = pairs * wl["hq"] * FLOP_PER_PAIR
-            t = float(np.median(per)) / 1e3
-            res[f"prefix_{prefix}"] = {"ms_median": t * 1e3, "tflops": flops / t / 1e12,
-                                       "tokens_per_s": wl["q_len"] / t}
+            for key, f in ((f"prefix_{prefix}", fn), (f"prefix_{prefix}_cached_keys", fc)):
+                _, per = timed(f, max(3, steps // 4), 1)
+                t = float(np.median(per)) / 1e3
+                res[key] = {"ms_median": t * 1e3, "tflops": flops / t / 1e12,
+                            "tokens_per_s": wl["q_len"] / t}
             del x, ws, o
         lo, hi = res["prefix_0"], res[f"prefix_{wl['kv_len'] - wl['q_len']}"]
         res["tokens_per_s_ratio_long_vs_empty_prefix"] = hi["tokens_per_s"] / lo["tokens_per_s"]

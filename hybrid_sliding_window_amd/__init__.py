@@ -27,5 +27,6 @@ from ._binding import (  # noqa: F401
     swa_sink_decode_fp8,
     swa_sink_prefill,
     swa_sink_prefill_chunk,
+    swa_sink_prefill_chunk_cached,
     version,
 )

@@ -23,6 +23,8 @@ _SIGNATURES = {
                               _ll, _i, _vp, _sz, _vp]),
     "swa_sink_prefill_chunk": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f,
                                     _f, _f, _ll, _i, _vp, _sz, _vp]),
+    "swa_sink_prefill_chunk_cached": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                                           _f, _f, _f, _ll, _i, _vp, _sz, _vp]),
     "ga_prefill": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _f, _ll, _i, _vp, _sz,
                         _vp]),
     "hswa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i, _ll]),
@@ -176,6 +178,27 @@ def swa_sink_prefill_chunk(q, k, v, sink=None, window=128, scale=0.0, rope_theta
                                     hkv, dqk, dv, window, scale, rope_theta, rotary_fraction,
                                     pos_offset, _dtype_code(q), _ptr(ws),
                                     0 if ws is None else ws.numel(), _stream(q))
+    _raise(st)
+    return o
+
+
+def swa_sink_prefill_chunk_cached(q, k_cache, v_cache, sink=None, window=128, scale=0.0,
+                                  rope_theta=10000.0, rotary_fraction=0.0, pos_offset=0, out=None,
+                                  workspace=None):
+    """swa_sink_prefill_chunk over a cache whose keys are stored already rotated
+    (as kv_cache_append writes them): k_cache [B,kv_len,Hkv,d_qk]."""
+    lib = load()
+    B, nq, hq, dqk = q.shape
+    n, hkv, dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    sink = _sink(sink, q)
+    o = out if out is not None else torch.empty((B, nq, hq, dv), dtype=q.dtype, device=q.device)
+    _check_same(q, k_cache, v_cache, o)
+    need = lib.hswa_prefill_workspace_size(B, n, hkv, dqk, rotary_fraction)
+    ws = workspace if workspace is not None else _workspace(need, q.device)
+    st = lib.swa_sink_prefill_chunk_cached(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sink),
+                                           _ptr(o), B, nq, n, hq, hkv, dqk, dv, window, scale,
+                                           rope_theta, rotary_fraction, pos_offset, _dtype_code(q),
+                                           _ptr(ws), 0 if ws is None else ws.numel(), _stream(q))
     _raise(st)
     return o
 

@@ -108,7 +108,7 @@ size_t rope_workspace_bytes(int batch, int seqlen, int hkv, int d_qk, float rota
 // prefix in a windowed layer).
 hipError_t launch_rope_prep(AttnArgs& a, void* workspace, long long pos_offset, int first,
                             bool rotate_k, bool need_table, hipStream_t s, bool k_e4m3 = false) {
-  if (a.half == 0) return hipSuccess;
+  if (a.half == 0 || (!rotate_k && !need_table)) return hipSuccess;
   float2* table = static_cast<float2*>(workspace);
   const size_t tb = round256((size_t)a.n * a.half * sizeof(float2));
   uint16_t* krot = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + tb);
@@ -135,7 +135,7 @@ hswa_status_t prefill_impl(const void* q, const void* k, const void* v, const fl
                            int batch, int q_len, int kv_len, int hq, int hkv, int d_qk, int d_v,
                            int window, float scale, float rope_theta, float rotary_fraction,
                            long long pos_offset, hswa_dtype_t dtype, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           size_t workspace_bytes, void* stream, bool k_rotated = false) {
   hswa_status_t st =
       check_common(batch, hq, hkv, d_qk, d_v, scale, rope_theta, rotary_fraction, dtype);
   if (st != HSWA_OK) return st;
@@ -165,11 +165,12 @@ hswa_status_t prefill_impl(const void* q, const void* k, const void* v, const fl
   a.sink = sink;
   a.window = (window >= kv_len) ? 0 : window;
   a.pos_offset = pos_offset;
+  a.k_rotated = k_rotated ? 1 : 0;
 
   // the per-block bf16 kernel covers whole sequences only; chunks of the
   // shapes it serves run on the generic kernel
   const bool persist = (dtype == HSWA_BF16) && hswa::prefill_persist_supported(a);
-  const bool per_block = !persist && (dtype == HSWA_BF16) && q_len == kv_len &&
+  const bool per_block = !persist && (dtype == HSWA_BF16) && q_len == kv_len && !k_rotated &&
                          hswa::prefill_bf16_supported(a);
   const bool use_mfma = persist || per_block;
   if (!use_mfma && !generic_fits(d_qk, d_v))
@@ -179,7 +180,8 @@ hswa_status_t prefill_impl(const void* q, const void* k, const void* v, const fl
   {
     // first key position any query of the call reads
     const int first = (a.window > 0 && a.qoff - a.window + 1 > 0) ? a.qoff - a.window + 1 : 0;
-    hipError_t e = launch_rope_prep(a, workspace, pos_offset, first, use_mfma, !persist, s);
+    hipError_t e = launch_rope_prep(a, workspace, pos_offset, first, use_mfma && !k_rotated,
+                                    !persist, s);
     if (e != hipSuccess) return hip_status(e, "rope preparation launch");
   }
   hipError_t e = persist     ? hswa::launch_prefill_persist(a, s)
@@ -416,6 +418,18 @@ hswa_status_t swa_sink_prefill_chunk(const void* q, const void* k, const void* v
   return prefill_impl(q, k, v, sink, o, batch, q_len, kv_len, hq, hkv, d_qk, d_v, window, scale,
                       rope_theta, rotary_fraction, pos_offset, dtype, workspace, workspace_bytes,
                       stream);
+}
+
+hswa_status_t swa_sink_prefill_chunk_cached(const void* q, const void* k_cache, const void* v_cache,
+                                            const float* sink, void* o, int batch, int q_len,
+                                            int kv_len, int hq, int hkv, int d_qk, int d_v,
+                                            int window, float scale, float rope_theta,
+                                            float rotary_fraction, long long pos_offset,
+                                            hswa_dtype_t dtype, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  return prefill_impl(q, k_cache, v_cache, sink, o, batch, q_len, kv_len, hq, hkv, d_qk, d_v,
+                      window, scale, rope_theta, rotary_fraction, pos_offset, dtype, workspace,
+                      workspace_bytes, stream, true);
 }
 
 hswa_status_t ga_prefill(const void* q, const void* k, const void* v, void* o, int batch,

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64) void generic_attn_kernel(AttnArgs a) {
   auto visit = [&](long long j) {
     const TKV* krow = k + ((kbase + j) * a.hkv + g) * (long long)a.d_qk;
     const TKV* vrow = v + ((kbase + j) * a.hkv + g) * (long long)a.d_v;
-    const bool rot_k = (MODE == MODE_PREFILL || MODE == MODE_SPARSE) && R > 0;
+    const bool rot_k = (MODE == MODE_PREFILL || MODE == MODE_SPARSE) && R > 0 && !a.k_rotated;
     float part = 0.f;
 #pragma unroll
     for (int u = 0; u < kGenMaxPerLane; ++u) {

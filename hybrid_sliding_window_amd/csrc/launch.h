@@ -34,6 +34,7 @@ struct AttnArgs {
   int slots;                      // multi-token decode, ring cache: slot count S
   int qoff;                       // prefill: sequence position of query token 0 (n - nq)
   int window;                     // prefill: 0 = full causal; decode: ring size or window
+  int k_rotated;                  // prefill: K rows are stored already rotated (a cache)
   int half;                       // R / 2 (0 = no RoPE)
   int max_sel, recent;            // sparse
   float scale;                    // factor on q.k (natural-log units)

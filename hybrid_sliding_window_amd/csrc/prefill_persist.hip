@@ -315,7 +315,7 @@ __global__ __launch_bounds__(512, 1) void prefill_persist_kernel(AttnArgs a, int
     const int sl = 64 * c + lane;
     const int row = sl / 24, pc = sl - row * 24;
     const int lc = pc ^ ((row >> 1) & 7);
-    krot[u] = lc < (half >> 2);
+    krot[u] = !a.k_rotated && lc < (half >> 2);   // keys stored rotated: every dim from K
     krow[u] = row;
     kcol[u] = 8 * lc;
     kstr[u] = hkv * (krot[u] ? R : D);

@@ -119,6 +119,24 @@ hswa_status_t swa_sink_prefill_chunk(const void* q, const void* k, const void* v
                                      long long pos_offset, hswa_dtype_t dtype, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/*
+ * swa_sink_prefill_chunk over a cache whose keys are stored already rotated
+ * at their positions (the convention of the decode caches and of
+ * kv_cache_append): the prefill chunk of "MiMo v2.5 inference optimisation"
+ * (youngju.dev), KV-cache restructuring and scheduling, reading its cached
+ * prefix where it lives.  k_cache [batch, kv_len, hkv, d_qk] holds the
+ * prefix and the chunk's own keys (appended first), v_cache the values; only
+ * the queries are rotated.  Same operation, arguments, workspace and errors
+ * as swa_sink_prefill_chunk otherwise.
+ */
+hswa_status_t swa_sink_prefill_chunk_cached(const void* q, const void* k_cache, const void* v_cache,
+                                            const float* sink, void* o, int batch, int q_len,
+                                            int kv_len, int hq, int hkv, int d_qk, int d_v,
+                                            int window, float scale, float rope_theta,
+                                            float rotary_fraction, long long pos_offset,
+                                            hswa_dtype_t dtype, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace swa_sink_decode needs for `batch` sequences whose
  * positions are all <= max_pos: split partial results (fp32), then the
  * query rotated to its position (bf16, 192 dims per head). */

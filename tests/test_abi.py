@@ -92,13 +92,14 @@ def test_prefill_validation(lib):
     assert lib.hswa_last_error().decode() == ""
 
 
-def test_prefill_chunk_validation(lib):
+@pytest.mark.parametrize("entry", ["swa_sink_prefill_chunk", "swa_sink_prefill_chunk_cached"])
+def test_prefill_chunk_validation(lib, entry):
     def call(**kw):
         a = dict(q=FAKE, k=FAKE, v=FAKE, sink=None, o=FAKE, batch=1, q_len=16, kv_len=40, hq=4,
                  hkv=2, d_qk=192, d_v=128, window=8, scale=0.0, theta=1e4, frac=0.0,
                  pos_offset=0, dtype=1, ws=None, ws_bytes=0, stream=None)
         a.update(kw)
-        return lib.swa_sink_prefill_chunk(*a.values())
+        return getattr(lib, entry)(*a.values())
     assert call(q_len=41) == INVALID                       # longer than its sequence
     assert "q_len" in lib.hswa_last_error().decode()
     assert call(q_len=-1) == INVALID

@@ -304,6 +304,51 @@ def test_prefill_chunk_is_rows_of_whole_prefill(gpu_lib, hq, hkv, window):
             _check(f"chunk at {start} vs whole prefill {hq}/{hkv}", part, _np(whole[:, start:]))
 
 
+@pytest.mark.parametrize("B,q_len,kv_len,hq,hkv,window,dtype,frac", [
+    (2, 300, 1000, 64, 8, 128, "bf16", 0.334),   # persistent kernel, keys read as stored
+    (1, 250, 900, 64, 4, 0, "bf16", 0.334),      # GA chunk
+    (1, 1, 500, 64, 8, 128, "bf16", 0.334),      # a single query
+    (1, 200, 700, 16, 8, 128, "bf16", 0.334),    # G = 2: generic kernel
+    (1, 130, 600, 4, 2, 64, "f32", 0.334),       # fp32: generic kernel
+])
+def test_prefill_chunk_cached(gpu_lib, B, q_len, kv_len, hq, hkv, window, dtype, frac):
+    """Keys taken as already rotated: any rows serve as the cache."""
+    sink = (-2.0, 2.0) if window > 0 else None
+    x = synthetic.chunk_inputs(B, q_len, kv_len, hq, hkv, 192, 128, dtype, 330 + q_len, DEV, sink)
+    o = gpu_lib.swa_sink_prefill_chunk_cached(x["q"], x["k"], x["v"], x["sink"], window=window,
+                                              rope_theta=1.0e4, rotary_fraction=frac,
+                                              pos_offset=7)
+    q, k, v, s = _host(x)
+    ref = oracle.swa_sink_prefill_chunk_cached(q, k, v, s, window=window, rope_theta=1.0e4,
+                                               rotary_fraction=frac, pos_offset=7)
+    _check(f"cached chunk {dtype} B={B} q={q_len} kv={kv_len} {hq}/{hkv} W={window}", o, ref,
+           fp32=(dtype == "f32"))
+
+
+@pytest.mark.parametrize("window", [128, 0])
+def test_prefill_chunk_cached_after_append(gpu_lib, window):
+    """The serving flow: every token's key and value appended to a contiguous
+    cache (keys rotated there), then the chunk attends over the cache.  The
+    result is the chunk over the unrotated keys."""
+    B, q_len, kv_len, hq, hkv = 2, 260, 800, 64, 8
+    sink = (-2.0, 2.0) if window else None
+    x = synthetic.chunk_inputs(B, q_len, kv_len, hq, hkv, 192, 128, "bf16", 345, DEV, sink)
+    kc = torch.zeros_like(x["k"])
+    vc = torch.zeros_like(x["v"])
+    offs = torch.arange(0, (B + 1) * kv_len, kv_len, dtype=torch.int64, device=DEV)
+    gpu_lib.kv_cache_append(x["k"], x["v"], kc.view(B * kv_len, hkv, 192),
+                            vc.view(B * kv_len, hkv, 128), torch.zeros(B, dtype=torch.int64,
+                                                                       device=DEV),
+                            kv_len - 1, layout=gpu_lib.KV_CONTIGUOUS, seq_offsets=offs,
+                            rope_theta=1.0e4, rotary_fraction=0.334)
+    o = gpu_lib.swa_sink_prefill_chunk_cached(x["q"], kc, vc, x["sink"], window=window,
+                                              rope_theta=1.0e4, rotary_fraction=0.334)
+    q, k, v, s = _host(x)
+    ref = oracle.swa_sink_prefill_chunk(q, k, v, s, window=window, rope_theta=1.0e4,
+                                        rotary_fraction=0.334)
+    _check(f"chunk over an appended cache W={window}", o, ref)
+
+
 def test_prefill_chunk_empty(gpu_lib):
     x = synthetic.chunk_inputs(1, 0, 64, 64, 8, 192, 128, "bf16", 320, DEV)
     o = gpu_lib.swa_sink_prefill_chunk(x["q"], x["k"], x["v"], x["sink"], window=128)
