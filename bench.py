@@ -59,9 +59,29 @@ def window_pairs(n, window):
     return int(np.minimum(i + 1, window).sum()) if window > 0 else int(((i + 1)).sum())
 
 
+CLOCK_SETTLE_S = 0.3
+
+
+def settle_clock(fn, seconds=CLOCK_SETTLE_S):
+    """Back-to-back untimed calls for `seconds`: the shader clock ramps up
+    over the first ~50 ms of sustained work (a 0.5 ms call measured right
+    after idle runs ~16% slower than the same call at steady state)."""
+    t0 = time.perf_counter()
+    batch = 1
+    while True:
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+        batch = min(2 * batch, 64)
+
+
 def timed(fn, steps, warmup):
-    """Warm up, then time `steps` calls with an event pair around each one on
-    the current stream (where the library enqueues its kernels)."""
+    """Settle the clock, warm up, then time `steps` calls with an event pair
+    around each one on the current stream (where the library enqueues its
+    kernels)."""
+    settle_clock(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -472,7 +492,7 @@ def _select(out, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
