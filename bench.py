@@ -553,8 +553,8 @@ def main():
                    "sink": "U(-2,2) per head", "useful_gflop_per_step": flops / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": _traffic("prefill_persist_kernel:swa_prefill_n32768"),
-                     "kernel": "prefill_persist_kernel",
+                     "traffic": _traffic("prefill_seq_kernel:swa_prefill_n32768"),
+                     "kernel": "prefill_seq_kernel",
                      "launch_scope": "one swa_sink_prefill call: RoPE prep kernels + prefill kernel",
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "launch_ms": kern_s * 1e3,

@@ -167,9 +167,11 @@ hswa_status_t prefill_impl(const void* q, const void* k, const void* v, const fl
   a.pos_offset = pos_offset;
   a.k_rotated = k_rotated ? 1 : 0;
 
-  // the per-block bf16 kernel covers whole sequences only; chunks of the
+  // windowed layers: the kernel that keeps the window's K/V tiles resident;
+  // the per-block bf16 kernel covers whole sequences only, chunks of the
   // shapes it serves run on the generic kernel
-  const bool persist = (dtype == HSWA_BF16) && hswa::prefill_persist_supported(a);
+  const bool seq = (dtype == HSWA_BF16) && hswa::prefill_seq_supported(a);
+  const bool persist = (dtype == HSWA_BF16) && (seq || hswa::prefill_persist_supported(a));
   const bool per_block = !persist && (dtype == HSWA_BF16) && q_len == kv_len && !k_rotated &&
                          hswa::prefill_bf16_supported(a);
   const bool use_mfma = persist || per_block;
@@ -184,7 +186,8 @@ hswa_status_t prefill_impl(const void* q, const void* k, const void* v, const fl
                                     !persist, s);
     if (e != hipSuccess) return hip_status(e, "rope preparation launch");
   }
-  hipError_t e = persist     ? hswa::launch_prefill_persist(a, s)
+  hipError_t e = seq         ? hswa::launch_prefill_seq(a, s)
+                 : persist     ? hswa::launch_prefill_persist(a, s)
                  : per_block ? hswa::launch_prefill_bf16(a, s)
                              : hswa::launch_generic(a, hswa::MODE_PREFILL, dtype == HSWA_BF16, false, s);
   return hip_status(e, "prefill launch");

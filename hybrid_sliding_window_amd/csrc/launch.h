@@ -78,6 +78,10 @@ hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
 // streams its items' K/V tiles and next q block while it computes.
 bool prefill_persist_supported(const AttnArgs& a);
 hipError_t launch_prefill_persist(const AttnArgs& a, hipStream_t stream);
+// Windowed layers of the persistent kernel's shapes with W + 2 * (256 / G)
+// small enough for a 7-tile K/V ring (prefill_seq.hip).
+bool prefill_seq_supported(const AttnArgs& a);
+hipError_t launch_prefill_seq(const AttnArgs& a, hipStream_t stream);
 
 bool decode_bf16_supported(const AttnArgs& a);
 void decode_split_plan(int layout, int window, long long max_pos, int* split_keys, int* nsplit);

@@ -349,6 +349,26 @@ def test_prefill_chunk_cached_after_append(gpu_lib, window):
     _check(f"chunk over an appended cache W={window}", o, ref)
 
 
+@pytest.mark.parametrize("q_len,kv_len,hq,hkv,window", [
+    (1000, 2003, 64, 8, 129),   # widest window of the K/V ring at G = 8, query start off the tile grid
+    (1000, 2003, 64, 8, 130),   # one wider: the persistent kernel
+    (700, 1701, 64, 4, 161),    # widest at G = 16
+    (260, 260, 64, 8, 100),     # whole sequence, window off the tile grid
+])
+def test_prefill_window_ring_limits(gpu_lib, q_len, kv_len, hq, hkv, window):
+    """The windowed kernel keeps two consecutive query blocks' key tiles in a
+    7-tile ring; these shapes sit at (and just past) the widest windows it
+    takes, with query blocks not aligned to the 32-key tiles."""
+    x = synthetic.chunk_inputs(2, q_len, kv_len, hq, hkv, 192, 128, "bf16", 360 + window, DEV,
+                               (-2.0, 2.0))
+    o = gpu_lib.swa_sink_prefill_chunk(x["q"], x["k"], x["v"], x["sink"], window=window,
+                                       rope_theta=1.0e4, rotary_fraction=0.334, pos_offset=9)
+    q, k, v, s = _host(x)
+    ref = oracle.swa_sink_prefill_chunk(q, k, v, s, window=window, rope_theta=1.0e4,
+                                        rotary_fraction=0.334, pos_offset=9)
+    _check(f"ring limits q={q_len} kv={kv_len} {hq}/{hkv} W={window}", o, ref)
+
+
 def test_prefill_chunk_empty(gpu_lib):
     x = synthetic.chunk_inputs(1, 0, 64, 64, 8, 192, 128, "bf16", 320, DEV)
     o = gpu_lib.swa_sink_prefill_chunk(x["q"], x["k"], x["v"], x["sink"], window=128)
