@@ -21,9 +21,9 @@
 // copy K, 4..7 V); the item's own tiles were requested one item earlier.  A
 // run that crosses to another sequence or head requests the new item's
 // tiles when it gets there.  Each wavefront loads its q rows of the next
-// item straight into its q registers once the item's last score products
-// have read them (the rows were brought into L2 two tiles earlier), so
-// there is no q staging in LDS and no barrier per tile.
+// item straight into its q registers after storing the item's output (the
+// rows were brought into L2 two tiles earlier), so there is no q staging in
+// LDS and no barrier per tile.
 //
 // Arithmetic per tile is that of the persistent kernel: S^T = K . Q^T on
 // the 32x32x16 MFMA, base-2 online softmax seeded with the sink and a lazily moved
@@ -314,7 +314,6 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
         sc0 = mfma32(__builtin_bit_cast(bf16x8, kf[ks]), __builtin_bit_cast(bf16x8, q0[ks]), sc0);
       // after the item's last score products its q registers take the next
       // item's q rows, which then arrive while this tile finishes
-      if (x == cur.tb && has_next) load_q(nx, q0);
       u32x2 vf[8];
       lds_vhalf<0>(vf, vaddr + vrd[0], vaddr + vrd[1], vaddr + vrd[2], vaddr + vrd[3]);
       uint4 p00, p01;
@@ -356,6 +355,10 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
       }
     };
     store_block(acc0, l0, tok0, head0, b0lo);
+    // the next item's q rows (in L2 since two tiles ago) into the q
+    // registers, issued after the stores so that the stores do not queue
+    // behind them
+    if (has_next) load_q(nx, q0);
 
     mark_cur = mark_next;
     cur = nx;
