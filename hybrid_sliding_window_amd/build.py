@@ -21,14 +21,14 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhswa.so")
 ARCH = os.environ.get("HSWA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "rope_prep.hip", "generic.hip", "prefill_bf16.hip", "prefill_persist.hip", "prefill_seq.hip",
+SOURCES = ["api.cpp", "rope_prep.hip", "generic.hip", "prefill_bf16.hip", "prefill_seq.hip", "prefill_causal.hip",
            "decode_bf16.hip", "decode_fp8.hip", "decode_multi.hip", "kv_append.hip", "select_tokens.hip", "sparse_bf16.hip"]
 
-# Per-source flags.  The persistent prefill runs one wavefront per SIMD and
-# keeps its accumulators in ordinary VGPRs (the VALU rescales them in place);
-# without this the allocator parks them in AGPRs and copies them every tile.
-EXTRA_FLAGS = {"prefill_persist.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-               "prefill_seq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source flags.  The matrix-core prefill kernels keep their accumulators
+# in ordinary VGPRs (the VALU rescales them in place); without this the
+# allocator parks them in AGPRs and copies them every tile.
+EXTRA_FLAGS = {"prefill_seq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+               "prefill_causal.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fno-honor-nans",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

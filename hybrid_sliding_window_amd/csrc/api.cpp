@@ -171,10 +171,11 @@ hswa_status_t prefill_impl(const void* q, const void* k, const void* v, const fl
   // the per-block bf16 kernel covers whole sequences only, chunks of the
   // shapes it serves run on the generic kernel
   const bool seq = (dtype == HSWA_BF16) && hswa::prefill_seq_supported(a);
-  const bool persist = (dtype == HSWA_BF16) && (seq || hswa::prefill_persist_supported(a));
-  const bool per_block = !persist && (dtype == HSWA_BF16) && q_len == kv_len && !k_rotated &&
+  const bool causal = !seq && (dtype == HSWA_BF16) && hswa::prefill_causal_supported(a);
+  const bool own_q = seq || causal;   // kernels that rotate q themselves
+  const bool per_block = !own_q && (dtype == HSWA_BF16) && q_len == kv_len && !k_rotated &&
                          hswa::prefill_bf16_supported(a);
-  const bool use_mfma = persist || per_block;
+  const bool use_mfma = own_q || per_block;
   if (!use_mfma && !generic_fits(d_qk, d_v))
     return fail(HSWA_ERR_UNSUPPORTED, "head dims above 256 are not supported");
 
@@ -183,11 +184,11 @@ hswa_status_t prefill_impl(const void* q, const void* k, const void* v, const fl
     // first key position any query of the call reads
     const int first = (a.window > 0 && a.qoff - a.window + 1 > 0) ? a.qoff - a.window + 1 : 0;
     hipError_t e = launch_rope_prep(a, workspace, pos_offset, first, use_mfma && !k_rotated,
-                                    !persist, s);
+                                    !own_q, s);
     if (e != hipSuccess) return hip_status(e, "rope preparation launch");
   }
   hipError_t e = seq         ? hswa::launch_prefill_seq(a, s)
-                 : persist     ? hswa::launch_prefill_persist(a, s)
+                 : causal      ? hswa::launch_prefill_causal(a, s)
                  : per_block ? hswa::launch_prefill_bf16(a, s)
                              : hswa::launch_generic(a, hswa::MODE_PREFILL, dtype == HSWA_BF16, false, s);
   return hip_status(e, "prefill launch");

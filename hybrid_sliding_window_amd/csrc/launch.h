@@ -73,15 +73,15 @@ hipError_t launch_generic(const AttnArgs& a, int mode, bool bf16, bool kv_fp8, h
 bool prefill_bf16_supported(const AttnArgs& a);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t stream);
 
-// Persistent variant of the bf16 prefill for GQA groups >= 8, rotary
-// half-widths 0, 16 or 32 and at most 256 q heads: one workgroup per CU
-// streams its items' K/V tiles and next q block while it computes.
-bool prefill_persist_supported(const AttnArgs& a);
-hipError_t launch_prefill_persist(const AttnArgs& a, hipStream_t stream);
-// Windowed layers of the persistent kernel's shapes with W + 2 * (256 / G)
-// small enough for a 7-tile K/V ring (prefill_seq.hip).
+// Windowed layers (G >= 8, d 192 / 128, rotary half-width 0, 16 or 32, at
+// most 256 q heads) with W + 2 * (256 / G) small enough for a 7-tile K/V
+// ring (prefill_seq.hip).
 bool prefill_seq_supported(const AttnArgs& a);
 hipError_t launch_prefill_seq(const AttnArgs& a, hipStream_t stream);
+// The same shapes for full causal layers and wider windows, one workgroup
+// barrier per two key tiles (prefill_causal.hip).
+bool prefill_causal_supported(const AttnArgs& a);
+hipError_t launch_prefill_causal(const AttnArgs& a, hipStream_t stream);
 
 bool decode_bf16_supported(const AttnArgs& a);
 void decode_split_plan(int layout, int window, long long max_pos, int* split_keys, int* nsplit);

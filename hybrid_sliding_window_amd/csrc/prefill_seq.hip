@@ -1,9 +1,8 @@
 // Sliding-window bf16 prefill that walks each kv head's query blocks in
-// order and keeps the window's K/V tiles resident in LDS: the same
-// operation as prefill_persist.hip for windowed layers ("MiMo-V2-Flash:
+// order and keeps the window's K/V tiles resident in LDS ("MiMo-V2-Flash:
 // Hybrid Sliding Window Attention Architecture" (rslog.cc) sections 2.1,
-// 2.3, 4.4 and 5), organised for the case where each query block needs only
-// a few key tiles.
+// 2.3, 4.4 and 5), for windowed layers whose query blocks need only a few
+// key tiles; prefill_causal.hip serves full causal layers and wider windows.
 //
 // Why.  With a 128-token window a block of 32 query tokens reads 5 key tiles
 // of 32 keys, 4 of which the previous block of the same head also read.
@@ -25,10 +24,12 @@
 // rows were brought into L2 two tiles earlier), so there is no q staging in
 // LDS and no barrier per tile.
 //
-// Arithmetic per tile is that of the persistent kernel: S^T = K . Q^T on
-// the 32x32x16 MFMA, base-2 online softmax seeded with the sink and a lazily moved
-// reference max, O^T += V^T . P^T with the V^T operand read transposed from
-// LDS so each lane ends up with 16 consecutive output dims.
+// Arithmetic per tile (as in prefill_causal.hip): S^T = K . Q^T on the
+// 32x32x16 MFMA (a lane holds query row i against keys 8j + 4h + r), base-2
+// online softmax seeded with the sink and a lazily moved reference max, l
+// summed from the bf16 P with v_dot2, O^T += V^T . P^T with the V^T operand
+// read transposed from LDS so each lane ends up with 16 consecutive output
+// dims, stored as two 16-byte writes per output tile.
 #include "common.h"
 #include "launch.h"
 #include "tile_ops.h"
@@ -164,18 +165,8 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
     nis += KS;
   };
 
-  // per-lane LDS offsets of the operand reads (see prefill_persist.hip)
-  const int sw = (i >> 1) & 7;
-  const int s1 = sw >> 1, h1 = h ^ (sw & 1);
-  uint32_t krd[4];
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) krd[jj] = i * KROW + 16 * (2 * (jj ^ s1) + h1);
-  const int jv = lane & 15, ihi = (lane >> 4) & 1;
-  uint32_t vrd[4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    vrd[mt] = (4 * h + (jv >> 2)) * VROW + 32 * (jv & 1) + 8 * ((jv >> 1) & 1) + 16 * ihi +
-              64 * (mt ^ (jv >> 2));
+  uint32_t krd[4], vrd[4];   // per-lane LDS offsets of the operand reads
+  operand_offsets(lane, krd, vrd);
   const uint32_t ring0 = lds_addr(ring);
   const float c2 = a.scale * kLog2e;
 
@@ -203,6 +194,10 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
     }
     wait_copy(nis - mark_cur);
     ring_barrier();
+    // this item's q rows (the wavefront's latest loads) have landed: waiting
+    // here, before any new copy is issued, keeps the compiler from waiting
+    // for those copies too at the first use of q
+    __builtin_amdgcn_s_waitcnt(VMCNT(0));
     // tiles the next item adds (same sequence: at most NS with this item's)
     fresh = has_next && nx.bg != req_bg;
     if (has_next && !fresh) {

@@ -172,5 +172,28 @@ __device__ __forceinline__ void rotate_q(u32x4 (&qf)[KS], const double* rev, dou
   }
 }
 
+// Per-lane LDS byte offsets of the MFMA operand reads from a tile, for lane
+// (i = lane & 31, h = lane >> 5).  K (A operand of S^T = K . Q^T): row r of
+// the tile holds logical 16-byte chunk c at physical chunk c ^ ((r >> 1) & 7),
+// and for k-step ks = 4q + j this lane (row i, half h) reads chunk
+// 8q + 2 (j ^ s1) + h1, i.e. krd[j] + 128 q (see lds_ksteps_lo / _hi).
+// V^T (A operand of O^T += V^T . P^T, read transposed): key row 4h + jv/4
+// (+ 16 kk, + 8), 8-byte piece jv % 4 at dim 16 (p & 1) + 4 (p >> 1) + 8 ihi
+// of the 32-dim output tile, so that lane (i, h) receives dims 16h + 0..15
+// of each tile in its 16 outputs; the 64-byte unit of output tile mt in that
+// row is mt ^ (row & 3) = mt ^ (jv / 4).
+__device__ __forceinline__ void operand_offsets(int lane, uint32_t (&krd)[4], uint32_t (&vrd)[4]) {
+  const int i = lane & 31, h = lane >> 5;
+  const int sw = (i >> 1) & 7;
+  const int s1 = sw >> 1, h1 = h ^ (sw & 1);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) krd[j] = i * KROW + 16 * (2 * (j ^ s1) + h1);
+  const int jv = lane & 15, ihi = (lane >> 4) & 1;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    vrd[mt] = (4 * h + (jv >> 2)) * VROW + 32 * (jv & 1) + 8 * ((jv >> 1) & 1) + 16 * ihi +
+              64 * (mt ^ (jv >> 2));
+}
+
 }  // namespace
 }  // namespace hswa

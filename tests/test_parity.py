@@ -112,24 +112,26 @@ def test_ga_prefill_bf16(gpu_lib, B, n, hq, hkv):
     (3, 129, 32, 4, 1, 0.334, True),      # one-token window
     (1, 960, 16, 2, 300, 0.17, False),    # window wider than the 32-key tile stream start
 ])
-def test_persistent_prefill_shapes(gpu_lib, B, n, hq, hkv, window, frac, sink):
-    """Shapes routed to the persistent prefill (G >= 8, R in {0, 32, 64})."""
+def test_matrix_core_prefill_shapes(gpu_lib, B, n, hq, hkv, window, frac, sink):
+    """Shapes routed to the matrix-core prefill kernels (G >= 8, R in {0, 32, 64}):
+    the resident-ring kernel for windows up to its limit, the two-tile-step
+    kernel for wider ones (W = 300 here)."""
     x = _prefill_case(B, n, hq, hkv, "bf16", 90 + n, sink_range=(-2.0, 2.0) if sink else None)
     o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=window,
                                  rope_theta=1.0e4, rotary_fraction=frac, pos_offset=17)
     q, k, v, s = _host(x)
     ref = oracle.swa_sink_prefill(q, k, v, s, window=window, rope_theta=1.0e4,
                                   rotary_fraction=frac, pos_offset=17)
-    _check(f"persistent B={B} n={n} {hq}/{hkv} W={window} R/2={int(frac * 96)}", o, ref)
+    _check(f"matrix-core B={B} n={n} {hq}/{hkv} W={window} R/2={int(frac * 96)}", o, ref)
 
 
 @pytest.mark.parametrize("B,n,hq,hkv", [(3, 250, 64, 8), (1, 515, 128, 4)])
-def test_persistent_ga_shapes(gpu_lib, B, n, hq, hkv):
+def test_matrix_core_ga_shapes(gpu_lib, B, n, hq, hkv):
     x = _prefill_case(B, n, hq, hkv, "bf16", 95 + n, sink_range=None)
     o = gpu_lib.ga_prefill(x["q"], x["k"], x["v"], rope_theta=1.0e7, rotary_fraction=0.334)
     q, k, v, _ = _host(x)
     ref = oracle.ga_prefill(q, k, v, rope_theta=1.0e7, rotary_fraction=0.334)
-    _check(f"persistent ga B={B} n={n} {hq}/{hkv}", o, ref)
+    _check(f"matrix-core ga B={B} n={n} {hq}/{hkv}", o, ref)
 
 
 @pytest.mark.parametrize("frac", [0.0, 2.0 / 3.0, 1.0])
@@ -264,7 +266,7 @@ def test_ga_prefill_full_size(gpu_lib):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("B,q_len,kv_len,hq,hkv,window,dtype,frac", [
-    (2, 300, 1000, 64, 8, 128, "bf16", 0.334),   # persistent kernel, ragged chunk and prefix
+    (2, 300, 1000, 64, 8, 128, "bf16", 0.334),   # ring kernel, ragged chunk and prefix
     (1, 1, 777, 64, 8, 128, "bf16", 0.334),      # a single query behind the prefix
     (1, 100, 150, 64, 8, 128, "bf16", 0.334),    # window reaches back to position 0
     (1, 250, 900, 64, 4, 0, "bf16", 0.334),      # GA chunk (G = 16)
@@ -305,7 +307,7 @@ def test_prefill_chunk_is_rows_of_whole_prefill(gpu_lib, hq, hkv, window):
 
 
 @pytest.mark.parametrize("B,q_len,kv_len,hq,hkv,window,dtype,frac", [
-    (2, 300, 1000, 64, 8, 128, "bf16", 0.334),   # persistent kernel, keys read as stored
+    (2, 300, 1000, 64, 8, 128, "bf16", 0.334),   # ring kernel, keys read as stored
     (1, 250, 900, 64, 4, 0, "bf16", 0.334),      # GA chunk
     (1, 1, 500, 64, 8, 128, "bf16", 0.334),      # a single query
     (1, 200, 700, 16, 8, 128, "bf16", 0.334),    # G = 2: generic kernel
@@ -351,7 +353,7 @@ def test_prefill_chunk_cached_after_append(gpu_lib, window):
 
 @pytest.mark.parametrize("q_len,kv_len,hq,hkv,window", [
     (1000, 2003, 64, 8, 129),   # widest window of the K/V ring at G = 8, query start off the tile grid
-    (1000, 2003, 64, 8, 130),   # one wider: the persistent kernel
+    (1000, 2003, 64, 8, 130),   # one wider: the two-tile-step kernel
     (700, 1701, 64, 4, 161),    # widest at G = 16
     (260, 260, 64, 8, 100),     # whole sequence, window off the tile grid
 ])
