@@ -170,7 +170,7 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
   const uint32_t ring0 = lds_addr(ring);
   const float c2 = a.scale * kLog2e;
 
-  // ---- prologue: the first item's tiles and q, the second item's tiles ----
+  // ---- prologue: the first item's tiles and q rows ------------------------
   SeqItem cur = seq_item(a, j_begin, nblk, T);
   int req_bg = cur.bg, req_hi = cur.tb;   // highest tile requested for sequence req_bg
   for (int x = cur.ta; x <= cur.tb; ++x) request_tile(cur, x);
