@@ -481,8 +481,9 @@ def _select(out, dev):
     i = np.arange(wl["n"], dtype=np.int64)
     causal = int((i + 1).sum())
     cand = int(np.maximum(0, i - wl["recent"] + 1).sum())
-    # four passes over the keys: log-sum-exp over 0 .. i, then three over the candidates
-    flops = (causal + 3 * cand) * wl["hq"] * 2 * 192
+    # two passes of score products: log-sum-exp over keys 0 .. i, then the
+    # importances of the candidates (the two later passes read them back)
+    flops = (causal + cand) * wl["hq"] * 2 * 192
     out["select_tokens_n65536"] = {"ms": t * 1e3, "qk_tflops": flops / t / 1e12,
                                    "rows_per_s": wl["n"] * wl["hkv"] / t,
                                    "frac_of_bf16_peak": flops / t / 1e12 / BF16_PEAK_TFLOPS}

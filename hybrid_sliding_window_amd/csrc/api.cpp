@@ -592,9 +592,10 @@ size_t hswa_select_workspace_size(int batch, int seqlen, int hq, int hkv, int d_
                                   float rotary_fraction) {
   if (batch <= 0 || seqlen <= 0 || hq <= 0 || hkv <= 0 || d_qk <= 0) return 0;
   if (!(rotary_fraction >= 0.f && rotary_fraction <= 1.f)) return 0;
-  if (rotary_half(d_qk, rotary_fraction) == 0) return 0;
+  const size_t scratch = hswa::select_scratch_bytes(seqlen);
+  if (rotary_half(d_qk, rotary_fraction) == 0) return scratch;
   const size_t rows = (size_t)batch * seqlen;
-  return round256(rows * hq * (size_t)d_qk * 2) + round256(rows * hkv * (size_t)d_qk * 2);
+  return round256(rows * hq * (size_t)d_qk * 2) + round256(rows * hkv * (size_t)d_qk * 2) + scratch;
 }
 
 hswa_status_t sparse_select_tokens(const void* q, const void* k, int* sel_idx, int* sel_count,
@@ -621,11 +622,9 @@ hswa_status_t sparse_select_tokens(const void* q, const void* k, int* sel_idx, i
   if ((long long)batch * seqlen * hq * (long long)d_qk > (1LL << 56))
     return fail(HSWA_ERR_INVALID_ARGUMENT, "tensor too large");
   const size_t need = hswa_select_workspace_size(batch, seqlen, hq, hkv, d_qk, rotary_fraction);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need)
-      return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_select_workspace_size()");
-    if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-  }
+  if (!workspace || workspace_bytes < need)
+    return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace smaller than hswa_select_workspace_size()");
+  if (!aligned16(workspace)) return fail(HSWA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   a.q = q;
   a.k = k;
   a.max_sel = max_sel;
@@ -633,6 +632,8 @@ hswa_status_t sparse_select_tokens(const void* q, const void* k, int* sel_idx, i
   a.pos_offset = pos_offset;
   a.sel_out = sel_idx;
   a.cnt_out = sel_count;
+  a.sel_ws = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + need -
+                                         hswa::select_scratch_bytes(seqlen));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.half > 0) {
     const size_t rows = (size_t)batch * seqlen;

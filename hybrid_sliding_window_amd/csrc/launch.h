@@ -24,6 +24,7 @@ struct AttnArgs {
   void* qrot;                     // decode bf16: q rotated to pos[b] [B, hq, d_qk] (workspace)
   int* sel_out;                   // token selection: lists [B, n, hkv, max_sel]
   int* cnt_out;                   // and counts [B, n, hkv]
+  unsigned* sel_ws;               // token selection: importance scratch (select_scratch_bytes)
   void* kout;                     // cache append: the K and V caches written
   void* vout;
   const float* kscale;            // decode FP8 caches: per-kv-head value of one K code unit [hkv]
@@ -111,6 +112,13 @@ hipError_t launch_kv_append(const AttnArgs& a, int layout, bool bf16_in, bool e4
 // (b, i, g) the max_sel candidates 0 .. i - recent of largest importance into
 // sel_out / cnt_out.  With RoPE (half > 0) q and k are read from qrot / krot,
 // full rotated rows [B, n, hq | hkv, 192] made by launch_rope_rows.
+// The kernel runs at most kSelectSlots workgroups, each looping over (row
+// block, kv head) items; workgroup w keeps the importances of its current
+// item's 16 rows in slot w of sel_ws (16 rows of round64(n) words).
+constexpr int kSelectSlots = 256;
+inline size_t select_scratch_bytes(int n) {
+  return (size_t)kSelectSlots * 16 * (((size_t)n + 63) & ~(size_t)63) * 4;
+}
 bool select_tokens_supported(const AttnArgs& a);
 hipError_t launch_select_tokens(const AttnArgs& a, hipStream_t stream);
 

@@ -12,16 +12,18 @@
 // A workgroup of eight wavefronts owns 16 consecutive query rows of one
 // (sequence, kv head) with G = 16 query heads, two rows per wavefront, so
 // every per-row state (softmax totals, histograms, thresholds, output
-// offsets) belongs to one wavefront and needs no synchronisation.  A row's
-// scores are S = Q . K^T on 16x16x32 MFMAs with the 16 heads on M and 16
-// keys on N: lane (key c, group q) holds heads 4q .. 4q + 3 of key c, so a
-// key's importance is four exponentials summed in the lane and two
-// exchanges across the lane groups, and lanes 0..15 own the keys in order.  K tiles of
+// offsets) belongs to one wavefront and needs no synchronisation.  A
+// wavefront's scores are S = Q . K^T on 32x32x16 MFMAs with its two rows'
+// 16 heads each on M and the 32 keys of a tile on N: lane (key c, half h)
+// holds eight heads of each row for key c, so a key's importance is eight
+// exponentials summed in the lane and one exchange across the halves, and
+// lanes 0..31 own the keys in order.  K tiles of
 // 32 keys stream through LDS with global_load_lds, shared by all 16 rows.
 // Four passes over the keys:
-//   1. lse_hi per (row, head): online max / sum in base 2;
-//   2. importance of every candidate (probabilities summed over the 16 head
-//      lanes), a 2048-bin histogram of its bits 31..21 per row in LDS, then
+//   1. lse_hi per (row, head): online max / sum in base 2, one exponential
+//      per score;
+//   2. importance of every candidate (probabilities summed over the 16
+//      heads), a 2048-bin histogram of its bits 31..21 per row in LDS, then
 //      the bin holding the max_sel-th largest;
 //   3. inside that bin, a histogram of bits 20..10: the threshold t of the
 //      22-bit key (importance >> 10, i.e. exponent and 13 mantissa bits) and
@@ -39,16 +41,18 @@ namespace hswa {
 namespace {
 
 constexpr int D = 192;
-constexpr int KS = D / 32;
+constexpr int KS = D / 16;              // k-steps of the 32x32x16 MFMA
 constexpr int GQ = 16;                   // query heads per kv head (one MFMA column block)
 constexpr int NW = 8;                    // wavefronts per workgroup
 constexpr int NB = 2;                    // rows per wavefront
 constexpr int ROWS = NW * NB;            // 16 query rows per workgroup
+static_assert(ROWS == 16, "select_scratch_bytes sizes slots of 16 rows");
 constexpr int BK = 32;                   // keys per LDS tile
 constexpr int KROW = D * 2;              // 384 B per key row
 constexpr int KTILE = BK * KROW;         // 12 KB
 constexpr int KINSTR = KTILE / 1024;     // 12 copies of 1 KB
 constexpr int NBIN = 2048;               // histogram bins per level
+constexpr int UNR = 8;                   // scratch words in flight per lane
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -123,45 +127,54 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// The six K operands of key row r (or r + 16 with HI) at LDS addresses ad[].
-// In asm: for a plain read the compiler would also wait for the next tile's
-// copies in flight; the copies of this tile have been waited for before the
-// barrier.  The block waits for its own reads before it returns.
-template <bool HI>
-__device__ __forceinline__ void lds_k6(bf16x8 (&f)[KS], const uint32_t (&ad)[KS]) {
-  uint4 r0, r1, r2, r3, r4, r5;
-  if (HI)
-    asm volatile(
-        "ds_read_b128 %0, %6 offset:6144\n\t"
-        "ds_read_b128 %1, %7 offset:6144\n\t"
-        "ds_read_b128 %2, %8 offset:6144\n\t"
-        "ds_read_b128 %3, %9 offset:6144\n\t"
-        "ds_read_b128 %4, %10 offset:6144\n\t"
-        "ds_read_b128 %5, %11 offset:6144\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5)
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5])
-        : "memory");
-  else
-    asm volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %7\n\t"
-        "ds_read_b128 %2, %8\n\t"
-        "ds_read_b128 %3, %9\n\t"
-        "ds_read_b128 %4, %10\n\t"
-        "ds_read_b128 %5, %11\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5)
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5])
-        : "memory");
+// Max / sum over the 32 lanes of a wavefront half (two DPP rows).
+__device__ __forceinline__ float max32(float v) {
+  v = max16(v);
+  return fmaxf(v, __shfl_xor(v, 16));
+}
+__device__ __forceinline__ float sum32(float v) {
+  v = sum16(v);
+  return v + __shfl_xor(v, 16);
+}
+
+// The twelve K operands of one key row: k-step 4 u + b sits 128 u bytes on
+// from ad[b].  In asm: for a plain read the compiler would also wait for the
+// next tile's copies in flight; the copies of this tile have been waited for
+// before the barrier.  The block waits for its own reads before it returns.
+__device__ __forceinline__ void lds_k12(bf16x8 (&f)[KS], const uint32_t (&ad)[4]) {
+  uint4 r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11;
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %13\n\t"
+      "ds_read_b128 %2, %14\n\t"
+      "ds_read_b128 %3, %15\n\t"
+      "ds_read_b128 %4, %12 offset:128\n\t"
+      "ds_read_b128 %5, %13 offset:128\n\t"
+      "ds_read_b128 %6, %14 offset:128\n\t"
+      "ds_read_b128 %7, %15 offset:128\n\t"
+      "ds_read_b128 %8, %12 offset:256\n\t"
+      "ds_read_b128 %9, %13 offset:256\n\t"
+      "ds_read_b128 %10, %14 offset:256\n\t"
+      "ds_read_b128 %11, %15 offset:256\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
+        "=&v"(r7), "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11)
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+      : "memory");
   f[0] = as_bf16x8(r0);
   f[1] = as_bf16x8(r1);
   f[2] = as_bf16x8(r2);
   f[3] = as_bf16x8(r3);
   f[4] = as_bf16x8(r4);
   f[5] = as_bf16x8(r5);
+  f[6] = as_bf16x8(r6);
+  f[7] = as_bf16x8(r7);
+  f[8] = as_bf16x8(r8);
+  f[9] = as_bf16x8(r9);
+  f[10] = as_bf16x8(r10);
+  f[11] = as_bf16x8(r11);
 }
-static_assert(16 * KROW == 6144, "the second 16-key half sits 6144 bytes further on");
+static_assert(KS == 12, "twelve k-steps of 16 dims");
 
 // Histogram increment at LDS address addr, in asm for the same reason (a
 // plain atomic would wait for the copies in flight).  No value is returned;
@@ -179,13 +192,22 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
   __shared__ unsigned hist[ROWS][NBIN];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, c = lane & 15, grp = lane >> 4;
+  const int lane = tid & 63, c = lane & 31, hi = lane >> 5;
   const int n = a.n, hkv = a.hkv, K = a.max_sel, recent = a.recent;
   const int nblk = (n + ROWS - 1) / ROWS;
-  // heavy blocks (late rows, long key ranges) first
-  const int item = (int)blockIdx.x;
-  const int bg = item / nblk;
-  const int blk = nblk - 1 - (item - bg * nblk);
+  const int ngrp = a.B * hkv;
+  const int items = ngrp * nblk;
+  const int ncap = (n + 63) & ~63;               // scratch words per row
+  const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
+  unsigned* const scr_wg = a.sel_ws + (size_t)wg * ROWS * ncap;
+  // Items run heaviest first (late row blocks, long key ranges), round r
+  // giving item r * nwg + w to workgroup w, or to nwg - 1 - w in odd rounds,
+  // so that each pair of rounds costs every workgroup about the same.
+  for (int r = 0; r * nwg < items; ++r) {
+  const int item = r * nwg + ((r & 1) ? nwg - 1 - wg : wg);
+  if (item >= items) continue;
+  const int blk = nblk - 1 - item / ngrp;
+  const int bg = item - (item / ngrp) * ngrp;
   const int b = bg / hkv, g = bg - b * hkv;
   const int i0 = blk * ROWS;
   const long long tokbase = (long long)b * n;
@@ -211,13 +233,15 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
   const bf16_t* __restrict__ Qp = static_cast<const bf16_t*>(a.half > 0 ? a.qrot : a.q);
   const bf16_t* __restrict__ Kp = static_cast<const bf16_t*>(a.half > 0 ? a.krot : a.k);
 
-  // q of row nb, head g*16 + c, k-step ks: dims 32 ks + 8 grp .. + 7
-  bf16x8 qf[NB][KS];
+  // q operand: M row c is head g*16 + c % 16 of the wavefront's row c / 16;
+  // k-step ks holds dims 16 ks + 8 hi .. + 7
+  bf16x8 qf[KS];
+  {
+    const int nb = c >> 4;
+    const bf16_t* qrow =
+        Qp + ((tokbase + min(row_i[nb], n - 1)) * a.hq + g * GQ + (c & 15)) * D + 8 * hi;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const bf16_t* qrow = Qp + ((tokbase + min(row_i[nb], n - 1)) * a.hq + g * GQ + c) * D + 8 * grp;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = as_bf16x8(ld16(qrow + 32 * ks));
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 16 * ks));
   }
 
   // ---- K tile copies: instruction ii (12 per tile) fills LDS bytes [1024 ii, +1024):
@@ -247,18 +271,27 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
       }
     }
   };
-  // K operands of key row (16 hf + c), k-step ks: logical chunk 4 ks + grp
-  // (rows c and c + 16 share the swizzle, 6144 bytes apart)
-  uint32_t koff[KS];
+  // K operand of key c, k-step ks = 4 u + b: logical chunk 2 ks + hi =
+  // 8 u + (2 b + hi), so 128 u bytes on from the chunk of k-step b
+  uint32_t koff[4];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = c * KROW + 16 * ((4 * ks + grp) ^ (c & 7));
-  auto kops = [&](const unsigned char* kc, int hf, bf16x8 (&kf)[KS]) {
+  for (int bb = 0; bb < 4; ++bb) koff[bb] = c * KROW + 16 * ((2 * bb + hi) ^ (c & 7));
+  // S = Q . K^T for the tile: element e of the lane is key c against M row
+  // 8 (e / 4) + 4 hi + e % 4, i.e. row e / 8 of the wavefront, head
+  // 8 ((e / 4) % 2) + 4 hi + e % 4
+  auto scores = [&](const unsigned char* kc) {
     const uint32_t base = lds_addr(kc);
-    uint32_t ad[KS];
+    uint32_t ad[4];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ad[ks] = base + koff[ks];
-    if (hf) lds_k6<true>(kf, ad);
-    else lds_k6<false>(kf, ad);
+    for (int bb = 0; bb < 4; ++bb) ad[bb] = base + koff[bb];
+    bf16x8 kf[KS];
+    lds_k12(kf, ad);
+    f32x16 sc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sc = mfma32(qf[ks], kf[ks], sc);
+    return sc;
   };
 
   // Stream keys 0 .. nkeys - 1 in tiles; body(kc, k0) sees each tile in order.
@@ -280,79 +313,57 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
   const float c2 = a.scale * kLog2e;
 
   // ---- pass 1: lse (base 2) of every (row, head) over keys 0 .. i -----------
-  // lane (c, q) runs a (max, sum) for heads 4q + r over its keys c of each
-  // 16-key half, reduced over the 16 key lanes at the end
-  float m[NB][4], l[NB][4];
+  // lane (c, hi) runs a (max, sum) for each of its 16 (row, head) elements
+  // over its key c of every tile, reduced over the 32 key lanes at the end.
+  // One exponential per key: of the two rescaling factors, the one of the
+  // larger operand is exactly 1.  The running max starts finite, so that a
+  // masked key (-inf) leaves the sum unchanged without a special case.
+  float m[16], l[16];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      m[nb][r] = kNegInf;
-      l[nb][r] = 0.f;
-    }
+  for (int e = 0; e < 16; ++e) {
+    m[e] = -__FLT_MAX__;
+    l[e] = 0.f;
+  }
   if (any_rank) {
     stream(lse_keys, [&](const unsigned char* kc, int k0) {
+      const f32x16 sc = scores(kc);
+      const int j = k0 + c;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        f32x4 sc[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 kf[KS];
-        kops(kc, hf, kf);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma16(qf[nb][ks], kf[ks], sc[nb]);
-        const int j = k0 + 16 * hf + c;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float x = (j <= row_i[nb]) ? sc[nb][r] * c2 : kNegInf;
-            const float mn = fmaxf(m[nb][r], x);
-            const float ms = (mn == kNegInf) ? 0.f : mn;
-            l[nb][r] = l[nb][r] * fast_exp2(m[nb][r] - ms) + fast_exp2(x - ms);
-            m[nb][r] = mn;
-          }
+      for (int e = 0; e < 16; ++e) {
+        const float x = (j <= row_i[e >> 3]) ? sc[e] * c2 : kNegInf;
+        const float d = x - m[e];
+        const float f = fast_exp2(-fabsf(d));
+        l[e] = (d > 0.f) ? fmaf(l[e], f, 1.f) : l[e] + f;
+        m[e] = fmaxf(m[e], x);
       }
     });
   }
-  float lse[NB][4];
+  float lse[16];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float M = max16(m[nb][r]);
-      const float L =
-          sum16(l[nb][r] * ((m[nb][r] == kNegInf) ? 0.f : fast_exp2(m[nb][r] - M)));
-      lse[nb][r] = M + __log2f(L);
-    }
+  for (int e = 0; e < 16; ++e) {
+    const float M = max32(m[e]);
+    const float L = sum32(l[e] * fast_exp2(m[e] - M));
+    lse[e] = M + __log2f(L);
+  }
 
-  // importance of key c of the tile half for row nb (all four lane groups
-  // of column c end with the sum over the 16 heads)
-  auto importances = [&](const unsigned char* kc, int hf, float (&imp)[NB]) {
-    f32x4 sc[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 kf[KS];
-    kops(kc, hf, kf);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma16(qf[nb][ks], kf[ks], sc[nb]);
+  // importance of key c of the tile for row nb (both lane halves of column
+  // c end with the sum over the 16 heads)
+  auto importances = [&](const unsigned char* kc, float (&imp)[NB]) {
+    const f32x16 sc = scores(kc);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       float v = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v += fast_exp2(fmaf(sc[nb][r], c2, -lse[nb][r]));
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      imp[nb] = v;
+      for (int r = 0; r < 8; ++r) v += fast_exp2(fmaf(sc[8 * nb + r], c2, -lse[8 * nb + r]));
+      imp[nb] = v + __shfl_xor(v, 32);
     }
   };
-  auto owned = [&](const float (&imp)[NB], int nb) -> float { return imp[nb]; };
-  const bool owner = grp == 0;                   // lanes 0..15 own keys 0..15 of a half
-  const int kk_own = c;
+  const bool owner = hi == 0;                    // lanes 0..31 own keys 0..31 of a tile
+
+  // this wavefront's rows of the workgroup's scratch slot
+  unsigned* scr[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) scr[nb] = scr_wg + (size_t)(NB * wave + nb) * ncap;
 
   int bin1[NB], t22[NB];
   unsigned above1[NB], quota[NB];
@@ -361,17 +372,16 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
     for (int nb = 0; nb < NB; ++nb)
       for (int t = lane; t < NBIN; t += 64) hist[NB * wave + nb][t] = 0u;
     stream(cand_keys, [&](const unsigned char* kc, int k0) {
+      float imp[NB];
+      importances(kc, imp);
+      const int j = k0 + c;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        float imp[NB];
-        importances(kc, hf, imp);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int j = k0 + 16 * hf + kk_own;
-          if (owner && j < ncand[nb] && mode[nb] == 2)
-            lds_inc(lds_addr(&hist[NB * wave + nb][__float_as_uint(owned(imp, nb)) >> 21]));
+      for (int nb = 0; nb < NB; ++nb)
+        if (owner && j < ncand[nb] && mode[nb] == 2) {
+          const unsigned u = __float_as_uint(imp[nb]);
+          scr[nb][j] = u;
+          lds_inc(lds_addr(&hist[NB * wave + nb][u >> 21]));
         }
-      }
     });
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -379,23 +389,33 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
       above1[nb] = 0;
       if (mode[nb] == 2) find_bin(hist[NB * wave + nb], (unsigned)kwant[nb], lane, &bin1[nb], &above1[nb]);
     }
-    // ---- pass 3: level-2 histogram (bits 20..10) inside bin1 ---------------
+    // ---- pass 3: level-2 histogram (bits 20..10) inside bin1, from the
+    // importances pass 2 stored.  The rows are this wavefront's own, on this
+    // compute unit: a workgroup-scope fence (the stores complete) makes them
+    // visible to its loads.
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     for (int nb = 0; nb < NB; ++nb)
       for (int t = lane; t < NBIN; t += 64) hist[NB * wave + nb][t] = 0u;
-    stream(cand_keys, [&](const unsigned char* kc, int k0) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        float imp[NB];
-        importances(kc, hf, imp);
+    for (int nb = 0; nb < NB; ++nb) {
+      if (mode[nb] != 2) continue;
+      const unsigned* row = scr[nb];
+      const int nc = ncand[nb];
+      for (int j0 = 0; j0 < nc; j0 += 64 * UNR) {
+        unsigned u[UNR];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int j = k0 + 16 * hf + kk_own;
-          const unsigned u = __float_as_uint(owned(imp, nb));
-          if (owner && j < ncand[nb] && mode[nb] == 2 && (int)(u >> 21) == bin1[nb])
-            lds_inc(lds_addr(&hist[NB * wave + nb][(u >> 10) & (NBIN - 1)]));
+        for (int t = 0; t < UNR; ++t) {
+          const int j = j0 + 64 * t + lane;
+          u[t] = (j < nc) ? row[j] : 0u;
+        }
+#pragma unroll
+        for (int t = 0; t < UNR; ++t) {
+          const int j = j0 + 64 * t + lane;
+          if (j < nc && (int)(u[t] >> 21) == bin1[nb])
+            lds_inc(lds_addr(&hist[NB * wave + nb][(u[t] >> 10) & (NBIN - 1)]));
         }
       }
-    });
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       t22[nb] = 0;
@@ -410,49 +430,48 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
     }
   }
 
-  // ---- pass 4: emit, ascending ----------------------------------------------
-  int* sel_out[NB];
-  unsigned emitted[NB], ties[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    sel_out[nb] = a.sel_out + ((tokbase + min(row_i[nb], n - 1)) * hkv + g) * (long long)K;
-    emitted[nb] = 0;
-    ties[nb] = 0;
-  }
+  // ---- pass 4: emit, ascending, lanes owning consecutive candidates -------
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  stream(cand_keys, [&](const unsigned char* kc, int k0) {
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      float imp[NB];
-      if (any_rank) importances(kc, hf, imp);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int j = k0 + 16 * hf + kk_own;
-        const bool cand = owner && j < ncand[nb];
-        bool take, tie = false;
-        if (mode[nb] != 2) {
-          take = cand && mode[nb] == 1;           // nothing, or every candidate
-        } else {
-          const int key = (int)(__float_as_uint(owned(imp, nb)) >> 10);
-          tie = cand && key == t22[nb];
-          const unsigned long long tm = __ballot(tie);
-          const unsigned rank = ties[nb] + (unsigned)__builtin_popcountll(tm & below);
-          take = cand && (key > t22[nb] || (tie && rank < quota[nb]));
-          ties[nb] += (unsigned)__builtin_popcountll(tm);
-        }
-        const unsigned long long sm = __ballot(take);
-        const unsigned at = emitted[nb] + (unsigned)__builtin_popcountll(sm & below);
-        if (take && at < (unsigned)kwant[nb]) sel_out[nb][at] = j;
-        emitted[nb] += (unsigned)__builtin_popcountll(sm);
-      }
-    }
-  });
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     if (!row_ok[nb]) continue;
-    for (int t = min((int)emitted[nb], kwant[nb]) + lane; t < K; t += 64) sel_out[nb][t] = -1;
-    if (lane == 0) a.cnt_out[(tokbase + row_i[nb]) * hkv + g] = (int)min(emitted[nb], (unsigned)kwant[nb]);
+    int* out = a.sel_out + ((tokbase + row_i[nb]) * hkv + g) * (long long)K;
+    const int nc = ncand[nb];
+    unsigned emitted = 0;
+    if (mode[nb] == 1) {                       // every candidate
+      for (int t = lane; t < nc; t += 64) out[t] = t;
+      emitted = (unsigned)nc;
+    } else if (mode[nb] == 2) {
+      const unsigned* row = scr[nb];
+      unsigned ties = 0;
+      for (int j0 = 0; j0 < nc; j0 += 64 * UNR) {
+        unsigned u[UNR];
+#pragma unroll
+        for (int t = 0; t < UNR; ++t) {
+          const int j = j0 + 64 * t + lane;
+          u[t] = (j < nc) ? row[j] : 0u;
+        }
+#pragma unroll
+        for (int t = 0; t < UNR; ++t) {
+          const int j = j0 + 64 * t + lane;
+          const bool cand = j < nc;
+          const int key = (int)(u[t] >> 10);
+          const bool tie = cand && key == t22[nb];
+          const unsigned long long tm = __ballot(tie);
+          const unsigned rank = ties + (unsigned)__builtin_popcountll(tm & below);
+          const bool take = cand && (key > t22[nb] || (tie && rank < quota[nb]));
+          ties += (unsigned)__builtin_popcountll(tm);
+          const unsigned long long sm = __ballot(take);
+          const unsigned at = emitted + (unsigned)__builtin_popcountll(sm & below);
+          if (take && at < (unsigned)kwant[nb]) out[at] = j;
+          emitted += (unsigned)__builtin_popcountll(sm);
+        }
+      }
+    }
+    for (int t = min((int)emitted, kwant[nb]) + lane; t < K; t += 64) out[t] = -1;
+    if (lane == 0) a.cnt_out[(tokbase + row_i[nb]) * hkv + g] = (int)min(emitted, (unsigned)kwant[nb]);
   }
+  }  // items
 }
 
 bool select_tokens_supported(const AttnArgs& a) {
@@ -463,7 +482,8 @@ hipError_t launch_select_tokens(const AttnArgs& a, hipStream_t stream) {
   const long long items = (long long)a.B * a.hkv * ((a.n + ROWS - 1) / ROWS);
   if (items == 0) return hipSuccess;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(select_tokens_kernel, dim3((unsigned)items), dim3(NW * 64), 0, stream, a);
+  const unsigned grid = (unsigned)(items < kSelectSlots ? items : kSelectSlots);
+  hipLaunchKernelGGL(select_tokens_kernel, dim3(grid), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -322,7 +322,9 @@ hswa_status_t sparse_sink_attn_fp8(const void* q, const void* k, const void* v,
                                    void* stream);
 
 /* Bytes of workspace sparse_select_tokens needs: rotated copies of q and k
- * (bf16, full rows) when RoPE is on, each rounded up to 256 bytes; else 0. */
+ * (bf16, full rows) when RoPE is on, each rounded up to 256 bytes, followed
+ * by the importance scratch: 256 x 16 x round64(seqlen) 4-byte words (one
+ * 16-row slot per resident workgroup).  0 for invalid arguments. */
 size_t hswa_select_workspace_size(int batch, int seqlen, int hq, int hkv, int d_qk,
                                   float rotary_fraction);
 

@@ -189,9 +189,13 @@ def test_select_validation(lib):
     assert call(recent=0) == INVALID
     assert call(cnt=None) == INVALID
     assert call(frac=0.334) == INVALID                     # workspace missing
+    assert call() == INVALID                               # importance scratch missing
     assert call(seqlen=0, q=None) == OK
-    assert hswa._binding.load().hswa_select_workspace_size(1, 100, 64, 4, 192, 0.334) == \
-        100 * 64 * 192 * 2 + 100 * 4 * 192 * 2
+    scratch = 256 * 16 * 128 * 4                           # 16-row slots of round64(100) words
+    size = hswa._binding.load().hswa_select_workspace_size
+    assert size(1, 100, 64, 4, 192, 0.334) == 100 * 64 * 192 * 2 + 100 * 4 * 192 * 2 + scratch
+    assert size(1, 100, 64, 4, 192, 0.0) == scratch
+    assert call(ws=FAKE, ws_bytes=scratch - 1) == INVALID
 
 
 def test_decode_fp8_validation(lib):
