@@ -52,7 +52,7 @@ constexpr int KROW = D * 2;              // 384 B per key row
 constexpr int KTILE = BK * KROW;         // 12 KB
 constexpr int KINSTR = KTILE / 1024;     // 12 copies of 1 KB
 constexpr int NBIN = 2048;               // histogram bins per level
-constexpr int UNR = 8;                   // scratch words in flight per lane
+constexpr int UNR = 32;                  // scratch words in flight per lane
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
