@@ -52,7 +52,7 @@ constexpr int KROW = D * 2;              // 384 B per key row
 constexpr int KTILE = BK * KROW;         // 12 KB
 constexpr int KINSTR = KTILE / 1024;     // 12 copies of 1 KB
 constexpr int NBIN = 2048;               // histogram bins per level
-constexpr int UNR = 32;                  // scratch words in flight per lane
+constexpr int UNR = 8;                   // 16-byte scratch loads in flight per lane
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -175,6 +175,17 @@ __device__ __forceinline__ void lds_k12(bf16x8 (&f)[KS], const uint32_t (&ad)[4]
   f[11] = as_bf16x8(r11);
 }
 static_assert(KS == 12, "twelve k-steps of 16 dims");
+
+// Sum of x (0 .. 4) over the lanes below this one, from three ballots of
+// its bits; *total = the sum over all 64 lanes.
+__device__ __forceinline__ unsigned prefix_before(unsigned x, unsigned long long below,
+                                                  unsigned* total) {
+  const unsigned long long b0 = __ballot(x & 1u), b1 = __ballot(x & 2u), b2 = __ballot(x & 4u);
+  *total = (unsigned)(__builtin_popcountll(b0) + 2 * __builtin_popcountll(b1) +
+                      4 * __builtin_popcountll(b2));
+  return (unsigned)(__builtin_popcountll(b0 & below) + 2 * __builtin_popcountll(b1 & below) +
+                    4 * __builtin_popcountll(b2 & below));
+}
 
 // Histogram increment at LDS address addr, in asm for the same reason (a
 // plain atomic would wait for the copies in flight).  No value is returned;
@@ -399,20 +410,23 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       if (mode[nb] != 2) continue;
-      const unsigned* row = scr[nb];
-      const int nc = ncand[nb];
-      for (int j0 = 0; j0 < nc; j0 += 64 * UNR) {
-        unsigned u[UNR];
+      const uint4* row = reinterpret_cast<const uint4*>(scr[nb]);
+      const int nc = ncand[nb], nc4 = (nc + 3) >> 2;
+      for (int q0 = 0; q0 < nc4; q0 += 64 * UNR) {
+        uint4 u[UNR];
 #pragma unroll
         for (int t = 0; t < UNR; ++t) {
-          const int j = j0 + 64 * t + lane;
-          u[t] = (j < nc) ? row[j] : 0u;
+          const int q = q0 + 64 * t + lane;
+          u[t] = (q < nc4) ? row[q] : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int t = 0; t < UNR; ++t) {
-          const int j = j0 + 64 * t + lane;
-          if (j < nc && (int)(u[t] >> 21) == bin1[nb])
-            lds_inc(lds_addr(&hist[NB * wave + nb][(u[t] >> 10) & (NBIN - 1)]));
+          const int j = 4 * (q0 + 64 * t + lane);
+          const unsigned w[4] = {u[t].x, u[t].y, u[t].z, u[t].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j + e < nc && (int)(w[e] >> 21) == bin1[nb])
+              lds_inc(lds_addr(&hist[NB * wave + nb][(w[e] >> 10) & (NBIN - 1)]));
         }
       }
     }
@@ -430,7 +444,8 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
     }
   }
 
-  // ---- pass 4: emit, ascending, lanes owning consecutive candidates -------
+  // ---- pass 4: emit, ascending; lane l owns candidates 4 l .. 4 l + 3 of
+  // each 256, ranks from ballots of the per-lane counts ----------------------
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -442,29 +457,50 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
       for (int t = lane; t < nc; t += 64) out[t] = t;
       emitted = (unsigned)nc;
     } else if (mode[nb] == 2) {
-      const unsigned* row = scr[nb];
+      const uint4* row = reinterpret_cast<const uint4*>(scr[nb]);
+      const int nc4 = (nc + 3) >> 2;
       unsigned ties = 0;
-      for (int j0 = 0; j0 < nc; j0 += 64 * UNR) {
-        unsigned u[UNR];
+      for (int q0 = 0; q0 < nc4; q0 += 64 * UNR) {
+        uint4 u[UNR];
 #pragma unroll
         for (int t = 0; t < UNR; ++t) {
-          const int j = j0 + 64 * t + lane;
-          u[t] = (j < nc) ? row[j] : 0u;
+          const int q = q0 + 64 * t + lane;
+          u[t] = (q < nc4) ? row[q] : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int t = 0; t < UNR; ++t) {
-          const int j = j0 + 64 * t + lane;
-          const bool cand = j < nc;
-          const int key = (int)(u[t] >> 10);
-          const bool tie = cand && key == t22[nb];
-          const unsigned long long tm = __ballot(tie);
-          const unsigned rank = ties + (unsigned)__builtin_popcountll(tm & below);
-          const bool take = cand && (key > t22[nb] || (tie && rank < quota[nb]));
-          ties += (unsigned)__builtin_popcountll(tm);
-          const unsigned long long sm = __ballot(take);
-          const unsigned at = emitted + (unsigned)__builtin_popcountll(sm & below);
-          if (take && at < (unsigned)kwant[nb]) out[at] = j;
-          emitted += (unsigned)__builtin_popcountll(sm);
+          // the lane's four consecutive candidates j .. j + 3
+          const int j = 4 * (q0 + 64 * t + lane);
+          const unsigned w[4] = {u[t].x, u[t].y, u[t].z, u[t].w};
+          bool above[4], tie[4];
+          unsigned ntie = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = (int)(w[e] >> 10);
+            above[e] = j + e < nc && key > t22[nb];
+            tie[e] = j + e < nc && key == t22[nb];
+            ntie += tie[e] ? 1u : 0u;
+          }
+          unsigned tie_total;
+          const unsigned tie_at = ties + prefix_before(ntie, below, &tie_total);
+          bool take[4];
+          unsigned ntake = 0, r = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            take[e] = above[e] || (tie[e] && tie_at + r < quota[nb]);
+            r += tie[e] ? 1u : 0u;
+            ntake += take[e] ? 1u : 0u;
+          }
+          unsigned take_total;
+          unsigned at = emitted + prefix_before(ntake, below, &take_total);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (take[e]) {
+              if (at < (unsigned)kwant[nb]) out[at] = j + e;
+              ++at;
+            }
+          ties += tie_total;
+          emitted += take_total;
         }
       }
     }

@@ -1047,6 +1047,23 @@ def test_select_tokens_ties_and_empty(gpu_lib):
     assert (cnt0 == 0).all() and idx0.numel() == 0
 
 
+def test_select_tokens_all_tied(gpu_lib):
+    """q = 0 gives every key of a row the same importance, so every row keeps
+    its lowest candidates: the tie ranks run across lanes and 256-key chunks,
+    and max_sel = 701 cuts the ties inside one lane's group of four."""
+    B, n, hkv, K, recent = 1, 3000, 2, 701, 16
+    x = synthetic.prefill_inputs(B, n, 16 * hkv, hkv, 192, 128, "bf16", 251, DEV, None)
+    q = torch.zeros_like(x["q"])
+    idx, cnt = gpu_lib.sparse_select_tokens(q, x["k"], max_sel=K, recent_window=recent)
+    i = np.arange(n)
+    want_cnt = np.minimum(K, np.maximum(0, i - recent + 1))
+    got_cnt = cnt[0].cpu().numpy()
+    assert (got_cnt == want_cnt[:, None]).all()
+    got = idx[0].cpu().numpy()
+    want = np.where(np.arange(K)[None, :] < want_cnt[:, None], np.arange(K)[None, :], -1)
+    assert (got == want[:, None, :]).all()
+
+
 def test_select_then_sparse(gpu_lib):
     """The lists feed sparse attention directly (the reuse of section 4)."""
     n, hkv, hq, recent, K = 400, 2, 32, 32, 48
