@@ -127,14 +127,31 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// The partner of v across DPP rows: v_permlane16_swap on two copies of v
+// leaves rows (0, 0, 2, 2) in one and (1, 1, 3, 3) in the other;
+// v_permlane32_swap leaves the lower half twice in one and the upper half
+// twice in the other.  Both are VALU moves (no LDS round trip), and both
+// lanes of a pair see the operands in the same order.
+struct Pair {
+  float a, b;
+};
+__device__ __forceinline__ Pair rows16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ Pair halves32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 // Max / sum over the 32 lanes of a wavefront half (two DPP rows).
 __device__ __forceinline__ float max32(float v) {
-  v = max16(v);
-  return fmaxf(v, __shfl_xor(v, 16));
+  const Pair p = rows16(max16(v));
+  return fmaxf(p.a, p.b);
 }
 __device__ __forceinline__ float sum32(float v) {
-  v = sum16(v);
-  return v + __shfl_xor(v, 16);
+  const Pair p = rows16(sum16(v));
+  return p.a + p.b;
 }
 
 // The twelve K operands of one key row: k-step 4 u + b sits 128 u bytes on
@@ -366,7 +383,8 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
       float v = 0.f;
 #pragma unroll
       for (int r = 0; r < 8; ++r) v += fast_exp2(fmaf(sc[8 * nb + r], c2, -lse[8 * nb + r]));
-      imp[nb] = v + __shfl_xor(v, 32);
+      const Pair p = halves32(v);
+      imp[nb] = p.a + p.b;
     }
   };
   const bool owner = hi == 0;                    // lanes 0..31 own keys 0..31 of a tile
