@@ -405,12 +405,14 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
       importances(kc, imp);
       const int j = k0 + c;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        if (owner && j < ncand[nb] && mode[nb] == 2) {
-          const unsigned u = __float_as_uint(imp[nb]);
-          scr[nb][j] = u;
+      for (int nb = 0; nb < NB; ++nb) {
+        const unsigned u = __float_as_uint(imp[nb]);
+        // every lane stores (the two halves write the same word, and words
+        // past the row's candidates, within its round64(n), are never read)
+        scr[nb][j] = u;
+        if (owner && j < ncand[nb] && mode[nb] == 2)
           lds_inc(lds_addr(&hist[NB * wave + nb][u >> 21]));
-        }
+      }
     });
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
