@@ -307,6 +307,37 @@ def pin_p10_decode_equals_prefill_row(O):
         assert np.abs(got_ld - got_ga).max() == 0.0
 
 
+def _brute_sparse(q, k, v, sel_idx, sel_count, rows, sink, recent, theta, frac, off):
+    """Scalar loops for token-level sparse attention: the key set of query i
+    is the recent window plus its listed tokens, each vector rotated by
+    _brute_rope at its own position off + index, sums with math.fsum."""
+    B, n, hq, d = q.shape
+    hkv = k.shape[2]
+    G = hq // hkv
+    R = 2 * int(math.floor(frac * d / 2))
+    out = np.zeros((B, len(rows), hq, v.shape[-1]))
+    for b in range(B):
+        for t, i in enumerate(rows):
+            i = int(i)
+            for g in range(hkv):
+                keys = set(range(max(0, i - recent + 1), i + 1))
+                keys |= {int(j) for j in sel_idx[b, i, g, :sel_count[b, i, g]]}
+                keys = sorted(keys)
+                kr = {j: _brute_rope(list(k[b, j, g]), off + j, theta, R) for j in keys}
+                for h in range(g * G, (g + 1) * G):
+                    qi = _brute_rope(list(q[b, i, h]), off + i, theta, R)
+                    a = {j: math.fsum(qi[c] * kr[j][c] for c in range(d)) / math.sqrt(d)
+                         for j in keys}
+                    sh = NEG_INF if sink is None else float(sink[h])
+                    m = max(max(a.values()), sh)
+                    terms = [math.exp(a[j] - m) for j in keys]
+                    den = math.fsum(terms + ([math.exp(sh - m)] if sh != NEG_INF else []))
+                    for c in range(v.shape[-1]):
+                        out[b, t, h, c] = math.fsum(terms[u] * v[b, j, g, c]
+                                                    for u, j in enumerate(keys)) / den
+    return out
+
+
 def pin_p11_sparse(O):
     """Sparse attention reductions (aideepthink.cn section 4).
 
@@ -337,6 +368,27 @@ def pin_p11_sparse(O):
         ref2 = _sdpa(q[:, :, g * 2:(g + 1) * 2], k[:, :, g:g + 1], v[:, :, g:g + 1], al[None],
                      s[g * 2:(g + 1) * 2], 1 / math.sqrt(192))
         assert np.abs(got2[:, :, g * 2:(g + 1) * 2] - ref2).max() < 1e-12
+    # RoPE on, positions shifted by pos_offset, a subset of rows: against scalar
+    # loops with the real-arithmetic rotation (every key at its own position)
+    rng = np.random.default_rng(24)
+    n, hq, hkv, d, dv, recent, off = 16, 4, 2, 8, 4, 3, 11
+    q = rng.standard_normal((2, n, hq, d)) * 1.5
+    k = rng.standard_normal((2, n, hkv, d)) * 1.5
+    v = rng.standard_normal((2, n, hkv, dv))
+    sink = np.array([-1.0, 0.5, 0.0, 2.0])
+    idx3, cnt3 = synthetic.sparse_selection(2, n, hkv, recent, 4, 25)
+    idx3, cnt3 = idx3.numpy(), cnt3.numpy()
+    rows = np.array([0, 2, 5, 9, 15])
+    for frac, theta in ((0.5, 3.0), (1.0, 7.0)):
+        got3 = O.sparse_rows(q, k, v, idx3, cnt3, rows, sink, recent=recent, rope_theta=theta,
+                             rotary_fraction=frac, pos_offset=off)
+        ref3 = _brute_sparse(q, k, v, idx3, cnt3, rows, sink, recent, theta, frac, off)
+        assert np.abs(got3 - ref3).max() < 1e-12, frac
+        # the same rows handed over alone (restricted) give the same outputs
+        got4 = O.sparse_rows(q[:, rows], k, v, idx3[:, rows], cnt3[:, rows], rows, sink,
+                             recent=recent, rope_theta=theta, rotary_fraction=frac,
+                             pos_offset=off, restricted=True)
+        assert np.abs(got4 - ref3).max() < 1e-12, frac
 
 
 def pin_p12_large_sink_is_stable(O):
@@ -541,16 +593,21 @@ def pin_p16_kv_append(O):
     assert np.abs(back - v[0, :4]).max() <= np.abs(v[0, :4]).max() * 2 ** -3
 
 
-def _brute_selection(q, k, b, i, g, recent, K):
-    """Scalar loops: softmax probabilities with math.fsum, then sorted()."""
+def _brute_selection(q, k, b, i, g, recent, K, theta=1.0e7, frac=0.0, off=0):
+    """Scalar loops: softmax probabilities with math.fsum, then sorted().
+    With frac > 0 every q and k vector is first rotated by _brute_rope at its
+    own position off + index."""
     hq, d = q.shape[2], q.shape[3]
     G = hq // k.shape[2]
+    R = 2 * int(math.floor(frac * d / 2))
     last = i - recent
     if last < 0:
         return []
+    kr = [_brute_rope(list(k[b, j, g]), off + j, theta, R) for j in range(i + 1)]
     imp = [0.0] * (last + 1)
     for h in range(g * G, (g + 1) * G):
-        a = [math.fsum(q[b, i, h, t] * k[b, j, g, t] for t in range(d)) / math.sqrt(d)
+        qi = _brute_rope(list(q[b, i, h]), off + i, theta, R)
+        a = [math.fsum(qi[t] * kr[j][t] for t in range(d)) / math.sqrt(d)
              for j in range(i + 1)]
         m = max(a)
         z = math.fsum(math.exp(x - m) for x in a)
@@ -579,6 +636,24 @@ def pin_p17_token_selection(O):
                 assert cnt[0, i, g] == len(want)
                 assert list(idx[0, i, g, :len(want)]) == want, (recent, K, i, g)
                 assert (idx[0, i, g, len(want):] == -1).all()
+    # RoPE on with a position offset, on a subset of rows of two sequences
+    q2 = rng.standard_normal((2, n, hq, d)) * 2
+    k2 = rng.standard_normal((2, n, hkv, d)) * 2
+    rows2 = np.array([3, 8, 13])
+    for frac, theta, off in ((0.5, 3.0, 9), (1.0, 5.0, 2)):
+        idx, cnt = O.select_tokens(q2, k2, rows2, 2, 4, rope_theta=theta, rotary_fraction=frac,
+                                   pos_offset=off)
+        for b in range(2):
+            for t, i in enumerate(rows2):
+                for g in range(hkv):
+                    want = _brute_selection(q2, k2, b, int(i), g, 2, 4, theta, frac, off)
+                    assert cnt[b, t, g] == len(want)
+                    assert list(idx[b, t, g, :len(want)]) == want, (frac, b, i, g)
+                    imp = O.selection_importance(q2, k2, b, int(i), g, 2, rope_theta=theta,
+                                                 rotary_fraction=frac, pos_offset=off)
+                    # probabilities of one head sum to 1 over 0 .. i; the
+                    # candidates carry at most G of that
+                    assert imp.min() > 0 and imp.sum() < hq // hkv
     # one head per group: the top-K of the probabilities is the top-K of the logits
     q1 = rng.standard_normal((1, 40, 3, 16))
     k1 = rng.standard_normal((1, 40, 3, 16))
@@ -658,17 +733,36 @@ MUTANTS = {
                                    "return sparse_rows(q, e4m3_value(k_codes),"),
     "fp8_scales_swapped": ("return dequantise_kv(kb, k_scale), dequantise_kv(vb, v_scale)",
                            "return dequantise_kv(kb, v_scale), dequantise_kv(vb, k_scale)"),
+    "sparse_query_rotated_at_list_index": ("qr = rope(q_sel, pos_offset + rows, rope_theta, rotary_fraction)",
+                                           "qr = rope(q_sel, pos_offset + np.arange(len(rows)), rope_theta, rotary_fraction)",
+                                           "sparse_rows"),
+    "sparse_keys_rotated_without_offset": ("kr = rope(k, pos_offset + np.arange(n), rope_theta, rotary_fraction)",
+                                           "kr = rope(k, np.arange(n), rope_theta, rotary_fraction)",
+                                           "sparse_rows"),
+    "selection_query_rotated_without_offset": ("qi = rope(q[b, i][None], np.array([pos_offset + i]), rope_theta,",
+                                               "qi = rope(q[b, i][None], np.array([i]), rope_theta,"),
+    "selection_keys_rotated_one_late": ("kr = rope(k[b, :i + 1], pos_offset + np.arange(i + 1), rope_theta,",
+                                        "kr = rope(k[b, :i + 1], pos_offset + np.arange(1, i + 2), rope_theta,"),
     "decode_query_not_rotated": ("qb = rope(q[b][None], np.array([p]), rope_theta, rotary_fraction)[0]\n        slots",
                                  "qb = np.asarray(q[b], dtype=np.float64)\n        slots"),
 }
 
 
 def _mutant(name):
-    old, new = MUTANTS[name]
+    """A copy of the oracle module with one planted mistake.  An entry of
+    MUTANTS is (old, new) or (old, new, function): with a function name only
+    that function's text is changed (the same line may appear elsewhere)."""
+    old, new, *where = MUTANTS[name]
     src = inspect.getsource(OA)
-    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    if where:
+        fsrc = inspect.getsource(getattr(OA, where[0]))
+        assert src.count(fsrc) == 1 and fsrc.count(old) >= 1, f"mutation site for {name} not found"
+        mutated = src.replace(fsrc, fsrc.replace(old, new))
+    else:
+        assert src.count(old) >= 1, f"mutation site for {name} not found"
+        mutated = src.replace(old, new)
     mod = types.ModuleType("oracle_mutant_" + name)
-    exec(compile(src.replace(old, new), "<mutant " + name + ">", "exec"), mod.__dict__)
+    exec(compile(mutated, "<mutant " + name + ">", "exec"), mod.__dict__)
     return mod
 
 

@@ -152,11 +152,13 @@ def test_sink_sensitive_case(gpu_lib, qmul):
     sharpened q: a kernel that dropped or mis-scaled the sink term fails here
     even where the plain workload cannot tell.
 
-    At q x 4 the score perturbation from rounding the rotated q~ and k~ to
-    bf16 grows with |q| (four times the q x 1 case, whose max-abs error is
-    ~8.5e-3), and rows collapse onto single keys with |o| up to ~5; the
-    max-abs bar there is 5e-2, derived from that scaling, with rel-L2 still
-    <= 5e-3."""
+    At q x 4 the rows collapse onto single keys with |o| up to ~5, and
+    rounding the rotated q~ and k~ dims to bf16 (the matrix-core operands)
+    plus the bf16 store already costs 2.9e-2 to 3.2e-2 max-abs against the
+    exact result: the floor measured on the CPU by
+    tests/test_tolerance_floor.py on inputs of this recipe.  The max-abs
+    bar there is 5e-2 (>= 1.4 x that floor), rel-L2 stays <= 5e-3; at
+    q x 2 the floor is 1.4e-2 and the standard bar applies."""
     x = _prefill_case(1, 600, 64, 8, "bf16", 62, sink_range=(2.0, 6.0))
     x["q"] = (x["q"].float() * qmul).to(torch.bfloat16)
     o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=128, rope_theta=1.0e4,
