@@ -98,6 +98,10 @@ def _dtype_code(t):
 
 
 def _check_same(ref, *ts):
+    """Every tensor on ref's device (a GPU: the kernels take device pointers)
+    and dense.  Called after the shape and dtype checks."""
+    if ref.device.type != "cuda":
+        raise ValueError("tensors must live on a GPU device (the library takes device pointers)")
     for t in ts:
         if t is None:
             continue
@@ -105,6 +109,40 @@ def _check_same(ref, *ts):
             raise ValueError("all tensors must live on the same device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+
+
+def _expect(t, name, shape, dtypes=None):
+    """t has exactly `shape` (None entries match anything) and one of `dtypes`."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dim() != len(shape) or any(w is not None and w != g for w, g in zip(shape, t.shape)):
+        want = "[" + ", ".join("*" if w is None else str(w) for w in shape) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
+
+
+def _dims(t, name, ndim):
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {list(t.shape)}")
+    return tuple(t.shape)
+
+
+_FLOAT = (torch.float32, torch.bfloat16)
+_E4M3 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _ws_bytes(ws):
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def _check_workspace(ws, need, ref):
+    if ws is None:
+        return
+    if ws.device != ref.device or not ws.is_contiguous():
+        raise ValueError("workspace must be a dense tensor on the query's device")
+    if _ws_bytes(ws) < need:
+        raise ValueError(f"workspace holds {_ws_bytes(ws)} bytes, the call needs {need}")
 
 
 def _stream(t):
@@ -116,18 +154,40 @@ def _raise(status):
         raise HswaError(status, load().hswa_last_error().decode())
 
 
-def _sink(sink, q):
+def _sink(sink, q, hq):
     if sink is None:
         return None
-    if sink.dtype != torch.float32 or sink.device != q.device or not sink.is_contiguous():
+    _expect(sink, "sink", (hq,), (torch.float32,))
+    if sink.device != q.device or not sink.is_contiguous():
         raise ValueError("sink must be a contiguous float32 tensor on the query's device")
     return sink
+
+
+def _out(out, shape, dtype, device):
+    """The caller's output tensor after a shape / dtype check, or a new one."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _expect(out, "out", shape, (dtype,))
+    return out
 
 
 def _workspace(nbytes, device):
     if nbytes == 0:
         return None
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _positions(pos, B, seq_offsets, contiguous):
+    _expect(pos, "pos", (B,), (torch.int64,))
+    if contiguous:
+        _expect(seq_offsets, "seq_offsets", (B + 1,), (torch.int64,))
+    elif seq_offsets is not None:
+        raise ValueError("seq_offsets must be None for a ring cache")
+
+
+def _scales(k_scale, v_scale, hkv):
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _expect(t, name, (hkv,), (torch.float32,))
 
 
 def prefill_workspace_size(batch, seqlen, hkv, d_qk, rotary_fraction):
@@ -142,20 +202,35 @@ def decode_workspace_size(layout, batch, hq, d_v, window, max_pos):
     return load().hswa_decode_workspace_size(layout, batch, hq, d_v, window, max_pos)
 
 
+def _prefill_operands(q, k, v, sink, out, q_len_may_differ=False):
+    """Shapes of a prefill-type call: q [B,nq,Hq,d_qk], k [B,n,Hkv,d_qk],
+    v [B,n,Hkv,d_v] with nq == n unless q_len_may_differ."""
+    B, nq, hq, dqk = _dims(q, "q", 4)
+    if q.dtype not in _FLOAT:
+        raise TypeError(f"q has dtype {q.dtype}, expected float32 or bfloat16")
+    _, n, hkv, _ = _dims(k, "k", 4)
+    _expect(k, "k", (B, None if q_len_may_differ else nq, hkv, dqk), (q.dtype,))
+    _expect(v, "v", (B, n, hkv, None), (q.dtype,))
+    dv = v.shape[3]
+    if hkv == 0 or hq % hkv != 0:
+        raise ValueError(f"hq ({hq}) must be a positive multiple of hkv ({hkv})")
+    sink = _sink(sink, q, hq)
+    o = _out(out, (B, nq, hq, dv), q.dtype, q.device)
+    return B, nq, n, hq, hkv, dqk, dv, sink, o
+
+
 def swa_sink_prefill(q, k, v, sink=None, window=128, scale=0.0, rope_theta=10000.0,
                      rotary_fraction=0.0, pos_offset=0, out=None, workspace=None):
     """q [B,n,Hq,d_qk], k [B,n,Hkv,d_qk], v [B,n,Hkv,d_v] -> o [B,n,Hq,d_v]."""
     lib = load()
-    B, n, hq, dqk = q.shape
-    hkv, dv = k.shape[2], v.shape[3]
-    sink = _sink(sink, q)
-    o = out if out is not None else torch.empty((B, n, hq, dv), dtype=q.dtype, device=q.device)
-    _check_same(q, k, v, o)
+    B, n, _, hq, hkv, dqk, dv, sink, o = _prefill_operands(q, k, v, sink, out)
     need = lib.hswa_prefill_workspace_size(B, n, hkv, dqk, rotary_fraction)
+    _check_workspace(workspace, need, q)
+    _check_same(q, k, v, o)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     st = lib.swa_sink_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(o), B, n, hq, hkv, dqk,
                               dv, window, scale, rope_theta, rotary_fraction, pos_offset,
-                              _dtype_code(q), _ptr(ws), 0 if ws is None else ws.numel(), _stream(q))
+                              _dtype_code(q), _ptr(ws), _ws_bytes(ws), _stream(q))
     _raise(st)
     return o
 
@@ -167,17 +242,17 @@ def swa_sink_prefill_chunk(q, k, v, sink=None, window=128, scale=0.0, rope_theta
     v [B,kv_len,Hkv,d_v] -> o [B,q_len,Hq,d_v].  window=0 with sink=None is
     the GA layer's chunk."""
     lib = load()
-    B, nq, hq, dqk = q.shape
-    n, hkv, dv = k.shape[1], k.shape[2], v.shape[3]
-    sink = _sink(sink, q)
-    o = out if out is not None else torch.empty((B, nq, hq, dv), dtype=q.dtype, device=q.device)
-    _check_same(q, k, v, o)
+    B, nq, n, hq, hkv, dqk, dv, sink, o = _prefill_operands(q, k, v, sink, out, True)
+    if nq > n:
+        raise ValueError(f"q_len ({nq}) must not exceed kv_len ({n})")
     need = lib.hswa_prefill_workspace_size(B, n, hkv, dqk, rotary_fraction)
+    _check_workspace(workspace, need, q)
+    _check_same(q, k, v, o)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     st = lib.swa_sink_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(sink), _ptr(o), B, nq, n, hq,
                                     hkv, dqk, dv, window, scale, rope_theta, rotary_fraction,
-                                    pos_offset, _dtype_code(q), _ptr(ws),
-                                    0 if ws is None else ws.numel(), _stream(q))
+                                    pos_offset, _dtype_code(q), _ptr(ws), _ws_bytes(ws),
+                                    _stream(q))
     _raise(st)
     return o
 
@@ -188,17 +263,17 @@ def swa_sink_prefill_chunk_cached(q, k_cache, v_cache, sink=None, window=128, sc
     """swa_sink_prefill_chunk over a cache whose keys are stored already rotated
     (as kv_cache_append writes them): k_cache [B,kv_len,Hkv,d_qk]."""
     lib = load()
-    B, nq, hq, dqk = q.shape
-    n, hkv, dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
-    sink = _sink(sink, q)
-    o = out if out is not None else torch.empty((B, nq, hq, dv), dtype=q.dtype, device=q.device)
-    _check_same(q, k_cache, v_cache, o)
+    B, nq, n, hq, hkv, dqk, dv, sink, o = _prefill_operands(q, k_cache, v_cache, sink, out, True)
+    if nq > n:
+        raise ValueError(f"q_len ({nq}) must not exceed kv_len ({n})")
     need = lib.hswa_prefill_workspace_size(B, n, hkv, dqk, rotary_fraction)
+    _check_workspace(workspace, need, q)
+    _check_same(q, k_cache, v_cache, o)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     st = lib.swa_sink_prefill_chunk_cached(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sink),
                                            _ptr(o), B, nq, n, hq, hkv, dqk, dv, window, scale,
                                            rope_theta, rotary_fraction, pos_offset, _dtype_code(q),
-                                           _ptr(ws), 0 if ws is None else ws.numel(), _stream(q))
+                                           _ptr(ws), _ws_bytes(ws), _stream(q))
     _raise(st)
     return o
 
@@ -207,17 +282,33 @@ def ga_prefill(q, k, v, scale=0.0, rope_theta=1.0e7, rotary_fraction=0.0, pos_of
                out=None, workspace=None):
     """Full causal attention without a sink (GA layer)."""
     lib = load()
-    B, n, hq, dqk = q.shape
-    hkv, dv = k.shape[2], v.shape[3]
-    o = out if out is not None else torch.empty((B, n, hq, dv), dtype=q.dtype, device=q.device)
-    _check_same(q, k, v, o)
+    B, n, _, hq, hkv, dqk, dv, _, o = _prefill_operands(q, k, v, None, out)
     need = lib.hswa_prefill_workspace_size(B, n, hkv, dqk, rotary_fraction)
+    _check_workspace(workspace, need, q)
+    _check_same(q, k, v, o)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     st = lib.ga_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, n, hq, hkv, dqk, dv, scale,
                         rope_theta, rotary_fraction, pos_offset, _dtype_code(q), _ptr(ws),
-                        0 if ws is None else ws.numel(), _stream(q))
+                        _ws_bytes(ws), _stream(q))
     _raise(st)
     return o
+
+
+def _decode_caches(k_cache, v_cache, layout, B, rows, dqk, cache_dtypes):
+    """Ring caches [B, rows, Hkv, d]; contiguous caches [total_rows, Hkv, d]."""
+    if layout == KV_RING:
+        _, _, hkv, _ = _dims(k_cache, "k_cache", 4)
+        _expect(k_cache, "k_cache", (B, rows, hkv, dqk), cache_dtypes)
+        _expect(v_cache, "v_cache", (B, rows, hkv, None), cache_dtypes)
+    elif layout == KV_CONTIGUOUS:
+        total, hkv, _ = _dims(k_cache, "k_cache", 3)
+        _expect(k_cache, "k_cache", (total, hkv, dqk), cache_dtypes)
+        _expect(v_cache, "v_cache", (total, hkv, None), cache_dtypes)
+    else:
+        raise ValueError("layout must be KV_RING or KV_CONTIGUOUS")
+    if v_cache.dtype != k_cache.dtype:
+        raise TypeError("k_cache and v_cache must have the same dtype")
+    return hkv, v_cache.shape[-1]
 
 
 def swa_sink_decode(q, k_cache, v_cache, pos, max_pos, layout=KV_RING, seq_offsets=None,
@@ -225,21 +316,21 @@ def swa_sink_decode(q, k_cache, v_cache, pos, max_pos, layout=KV_RING, seq_offse
                     out=None, workspace=None):
     """q [B,Hq,d_qk] against a ring [B,W,Hkv,d] or packed [rows,Hkv,d] cache -> o [B,Hq,d_v]."""
     lib = load()
-    B, hq, dqk = q.shape
-    hkv, dv = k_cache.shape[-2], v_cache.shape[-1]
-    sink = _sink(sink, q)
-    if pos.dtype != torch.int64:
-        raise TypeError("pos must be int64")
-    if seq_offsets is not None and seq_offsets.dtype != torch.int64:
-        raise TypeError("seq_offsets must be int64")
-    o = out if out is not None else torch.empty((B, hq, dv), dtype=q.dtype, device=q.device)
-    _check_same(q, k_cache, v_cache, o, pos, seq_offsets)
+    B, hq, dqk = _dims(q, "q", 3)
+    if q.dtype not in _FLOAT:
+        raise TypeError(f"q has dtype {q.dtype}, expected float32 or bfloat16")
+    hkv, dv = _decode_caches(k_cache, v_cache, layout, B, window, dqk, (q.dtype,))
+    _positions(pos, B, seq_offsets, layout == KV_CONTIGUOUS)
+    sink = _sink(sink, q, hq)
+    o = _out(out, (B, hq, dv), q.dtype, q.device)
     need = lib.hswa_decode_workspace_size(layout, B, hq, dv, window, int(max_pos))
+    _check_workspace(workspace, need, q)
+    _check_same(q, k_cache, v_cache, o, pos, seq_offsets)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     st = lib.swa_sink_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), layout, _ptr(seq_offsets),
                              _ptr(pos), _ptr(sink), _ptr(o), B, hq, hkv, dqk, dv, window,
                              int(max_pos), scale, rope_theta, rotary_fraction, _dtype_code(q),
-                             _ptr(ws), 0 if ws is None else ws.numel(), _stream(q))
+                             _ptr(ws), _ws_bytes(ws), _stream(q))
     _raise(st)
     return o
 
@@ -256,23 +347,23 @@ def swa_sink_decode_multi(q, k_cache, v_cache, pos, max_pos, layout=KV_RING, rin
     ring [B,S,Hkv,d] (S = ring_slots >= window + T - 1) or packed [rows,Hkv,d] cache
     -> o [B,T,Hq,d_v]."""
     lib = load()
-    B, T, hq, dqk = q.shape
-    hkv, dv = k_cache.shape[-2], v_cache.shape[-1]
-    sink = _sink(sink, q)
-    if pos.dtype != torch.int64:
-        raise TypeError("pos must be int64")
-    if seq_offsets is not None and seq_offsets.dtype != torch.int64:
-        raise TypeError("seq_offsets must be int64")
-    o = out if out is not None else torch.empty((B, T, hq, dv), dtype=q.dtype, device=q.device)
-    _check_same(q, k_cache, v_cache, o, pos, seq_offsets)
+    B, T, hq, dqk = _dims(q, "q", 4)
+    if q.dtype not in _FLOAT:
+        raise TypeError(f"q has dtype {q.dtype}, expected float32 or bfloat16")
+    hkv, dv = _decode_caches(k_cache, v_cache, layout, B, ring_slots, dqk, (q.dtype,))
+    _positions(pos, B, seq_offsets, layout == KV_CONTIGUOUS)
+    sink = _sink(sink, q, hq)
+    o = _out(out, (B, T, hq, dv), q.dtype, q.device)
     need = lib.hswa_decode_multi_workspace_size(layout, B, T, hq, dv, window, ring_slots,
                                                 int(max_pos))
+    _check_workspace(workspace, need, q)
+    _check_same(q, k_cache, v_cache, o, pos, seq_offsets)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     st = lib.swa_sink_decode_multi(_ptr(q), _ptr(k_cache), _ptr(v_cache), layout, ring_slots,
                                    _ptr(seq_offsets), _ptr(pos), _ptr(sink), _ptr(o), B, T, hq,
                                    hkv, dqk, dv, window, int(max_pos), scale, rope_theta,
-                                   rotary_fraction, _dtype_code(q), _ptr(ws),
-                                   0 if ws is None else ws.numel(), _stream(q))
+                                   rotary_fraction, _dtype_code(q), _ptr(ws), _ws_bytes(ws),
+                                   _stream(q))
     _raise(st)
     return o
 
@@ -284,18 +375,24 @@ def kv_cache_append(k_new, v_new, k_cache, v_cache, pos, max_pos, layout=KV_RING
     a ring or contiguous cache, keys rotated.  An E4M3 cache (uint8 or
     float8_e4m3fn) needs k_scale and v_scale.  Modifies the caches in place."""
     lib = load()
-    B, T, hkv, dqk = k_new.shape
+    B, T, hkv, dqk = _dims(k_new, "k_new", 4)
+    if k_new.dtype not in _FLOAT:
+        raise TypeError(f"k_new has dtype {k_new.dtype}, expected float32 or bfloat16")
+    _expect(v_new, "v_new", (B, T, hkv, None), (k_new.dtype,))
     dv = v_new.shape[-1]
-    if pos.dtype != torch.int64:
-        raise TypeError("pos must be int64")
-    if seq_offsets is not None and seq_offsets.dtype != torch.int64:
-        raise TypeError("seq_offsets must be int64")
-    _check_same(k_new, v_new, k_cache, v_cache, pos, seq_offsets)
-    fp8 = k_cache.dtype in (torch.uint8, torch.float8_e4m3fn)
+    fp8 = k_cache.dtype in _E4M3
+    cache_dtypes = _E4M3 if fp8 else (k_new.dtype,)
+    if not fp8 and k_cache.dtype != k_new.dtype:
+        raise TypeError("a bf16 / fp32 cache has the type of the new keys and values")
+    chkv, cdv = _decode_caches(k_cache, v_cache, layout, B, ring_slots, dqk, cache_dtypes)
+    if chkv != hkv or cdv != dv:
+        raise ValueError(f"caches hold {chkv} kv heads of {cdv} value dims; the new tokens "
+                         f"{hkv} of {dv}")
+    _positions(pos, B, seq_offsets, layout == KV_CONTIGUOUS)
     if fp8:
-        for t in (k_scale, v_scale):
-            if t is None or t.dtype != torch.float32 or t.numel() != hkv:
-                raise ValueError("an E4M3 cache needs float32 k_scale and v_scale, one per kv head")
+        _scales(k_scale, v_scale, hkv)
+    _check_same(k_new, v_new, k_cache, v_cache, pos, seq_offsets)
+    if fp8:
         _check_same(k_new, k_scale, v_scale)
         st = lib.kv_cache_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                      _ptr(k_scale), _ptr(v_scale), layout, ring_slots,
@@ -303,19 +400,11 @@ def kv_cache_append(k_new, v_new, k_cache, v_cache, pos, max_pos, layout=KV_RING
                                      int(max_pos), rope_theta, rotary_fraction,
                                      _dtype_code(k_new), _stream(k_new))
     else:
-        if k_cache.dtype != k_new.dtype or v_cache.dtype != v_new.dtype:
-            raise TypeError("a bf16 / fp32 cache has the type of the new keys and values")
         st = lib.kv_cache_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), layout,
                                  ring_slots, _ptr(seq_offsets), _ptr(pos), B, T, hkv, dqk, dv,
                                  int(max_pos), rope_theta, rotary_fraction, _dtype_code(k_new),
                                  _stream(k_new))
     _raise(st)
-
-
-def _fp8_cache(t):
-    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
-        raise TypeError("an FP8 cache holds E4M3 codes: uint8 or float8_e4m3fn")
-    return t
 
 
 def swa_sink_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, pos, max_pos, layout=KV_RING,
@@ -324,29 +413,44 @@ def swa_sink_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, pos, max_pos, lay
     """swa_sink_decode over E4M3 caches: the value of a code is e4m3(code) times
     k_scale[g] (K) or v_scale[g] (V) of its kv head g."""
     lib = load()
-    B, hq, dqk = q.shape
-    hkv, dv = k_cache.shape[-2], v_cache.shape[-1]
-    _fp8_cache(k_cache)
-    _fp8_cache(v_cache)
-    for t in (k_scale, v_scale):
-        if t.dtype != torch.float32 or t.numel() != hkv:
-            raise ValueError("k_scale and v_scale must be float32 with one entry per kv head")
-    sink = _sink(sink, q)
-    if pos.dtype != torch.int64:
-        raise TypeError("pos must be int64")
-    if seq_offsets is not None and seq_offsets.dtype != torch.int64:
-        raise TypeError("seq_offsets must be int64")
-    o = out if out is not None else torch.empty((B, hq, dv), dtype=q.dtype, device=q.device)
-    _check_same(q, k_cache, v_cache, o, pos, seq_offsets, k_scale, v_scale)
+    B, hq, dqk = _dims(q, "q", 3)
+    if q.dtype not in _FLOAT:
+        raise TypeError(f"q has dtype {q.dtype}, expected float32 or bfloat16")
+    hkv, dv = _decode_caches(k_cache, v_cache, layout, B, window, dqk, _E4M3)
+    _scales(k_scale, v_scale, hkv)
+    _positions(pos, B, seq_offsets, layout == KV_CONTIGUOUS)
+    sink = _sink(sink, q, hq)
+    o = _out(out, (B, hq, dv), q.dtype, q.device)
     need = lib.hswa_decode_workspace_size(layout, B, hq, dv, window, int(max_pos))
+    _check_workspace(workspace, need, q)
+    _check_same(q, k_cache, v_cache, o, pos, seq_offsets, k_scale, v_scale)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     st = lib.swa_sink_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                  _ptr(v_scale), layout, _ptr(seq_offsets), _ptr(pos), _ptr(sink),
                                  _ptr(o), B, hq, hkv, dqk, dv, window, int(max_pos), scale,
                                  rope_theta, rotary_fraction, _dtype_code(q), _ptr(ws),
-                                 0 if ws is None else ws.numel(), _stream(q))
+                                 _ws_bytes(ws), _stream(q))
     _raise(st)
     return o
+
+
+def _sparse_operands(q, k, v, sel_idx, sel_count, sink, out, kv_dtypes):
+    B, n, hq, dqk = _dims(q, "q", 4)
+    if q.dtype not in _FLOAT:
+        raise TypeError(f"q has dtype {q.dtype}, expected float32 or bfloat16")
+    _, _, hkv, _ = _dims(k, "k", 4)
+    _expect(k, "k", (B, n, hkv, dqk), kv_dtypes)
+    _expect(v, "v", (B, n, hkv, None), kv_dtypes)
+    if v.dtype != k.dtype:
+        raise TypeError("k and v must have the same dtype")
+    if hkv == 0 or hq % hkv != 0:
+        raise ValueError(f"hq ({hq}) must be a positive multiple of hkv ({hkv})")
+    _expect(sel_idx, "sel_idx", (B, n, hkv, None), (torch.int32,))
+    _expect(sel_count, "sel_count", (B, n, hkv), (torch.int32,))
+    dv = v.shape[3]
+    sink = _sink(sink, q, hq)
+    o = _out(out, (B, n, hq, dv), q.dtype, q.device)
+    return B, n, hq, hkv, dqk, dv, sel_idx.shape[-1], sink, o
 
 
 def sparse_sink_attn(q, k, v, sel_idx, sel_count, sink=None, recent_window=128, scale=0.0,
@@ -354,20 +458,16 @@ def sparse_sink_attn(q, k, v, sel_idx, sel_count, sink=None, recent_window=128, 
                      workspace=None):
     """Recent window plus selected tokens per (query, kv head) -> o [B,n,Hq,d_v]."""
     lib = load()
-    B, n, hq, dqk = q.shape
-    hkv, dv = k.shape[2], v.shape[3]
-    max_sel = sel_idx.shape[-1]
-    sink = _sink(sink, q)
-    if sel_idx.dtype != torch.int32 or sel_count.dtype != torch.int32:
-        raise TypeError("sel_idx and sel_count must be int32")
-    o = out if out is not None else torch.empty((B, n, hq, dv), dtype=q.dtype, device=q.device)
-    _check_same(q, k, v, o, sel_idx, sel_count)
+    B, n, hq, hkv, dqk, dv, max_sel, sink, o = _sparse_operands(q, k, v, sel_idx, sel_count, sink,
+                                                                out, (q.dtype,))
     need = lib.hswa_sparse_workspace_size(B, n, hkv, dqk, rotary_fraction)
+    _check_workspace(workspace, need, q)
+    _check_same(q, k, v, o, sel_idx, sel_count)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     st = lib.sparse_sink_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(sel_idx), _ptr(sel_count), max_sel,
                               recent_window, _ptr(sink), _ptr(o), B, n, hq, hkv, dqk, dv, scale,
                               rope_theta, rotary_fraction, pos_offset, _dtype_code(q), _ptr(ws),
-                              0 if ws is None else ws.numel(), _stream(q))
+                              _ws_bytes(ws), _stream(q))
     _raise(st)
     return o
 
@@ -377,26 +477,18 @@ def sparse_sink_attn_fp8(q, k, v, k_scale, v_scale, sel_idx, sel_count, sink=Non
                          pos_offset=0, out=None, workspace=None):
     """sparse_sink_attn over E4M3 K/V codes with per-kv-head scales."""
     lib = load()
-    B, n, hq, dqk = q.shape
-    hkv, dv = k.shape[2], v.shape[3]
-    max_sel = sel_idx.shape[-1]
-    _fp8_cache(k)
-    _fp8_cache(v)
-    for t in (k_scale, v_scale):
-        if t.dtype != torch.float32 or t.numel() != hkv:
-            raise ValueError("k_scale and v_scale must be float32 with one entry per kv head")
-    sink = _sink(sink, q)
-    if sel_idx.dtype != torch.int32 or sel_count.dtype != torch.int32:
-        raise TypeError("sel_idx and sel_count must be int32")
-    o = out if out is not None else torch.empty((B, n, hq, dv), dtype=q.dtype, device=q.device)
-    _check_same(q, k, v, o, sel_idx, sel_count, k_scale, v_scale)
+    B, n, hq, hkv, dqk, dv, max_sel, sink, o = _sparse_operands(q, k, v, sel_idx, sel_count, sink,
+                                                                out, _E4M3)
+    _scales(k_scale, v_scale, hkv)
     need = lib.hswa_sparse_workspace_size(B, n, hkv, dqk, rotary_fraction)
+    _check_workspace(workspace, need, q)
+    _check_same(q, k, v, o, sel_idx, sel_count, k_scale, v_scale)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     st = lib.sparse_sink_attn_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(k_scale), _ptr(v_scale),
                                   _ptr(sel_idx), _ptr(sel_count), max_sel, recent_window,
                                   _ptr(sink), _ptr(o), B, n, hq, hkv, dqk, dv, scale, rope_theta,
                                   rotary_fraction, pos_offset, _dtype_code(q), _ptr(ws),
-                                  0 if ws is None else ws.numel(), _stream(q))
+                                  _ws_bytes(ws), _stream(q))
     _raise(st)
     return o
 
@@ -407,19 +499,24 @@ def sparse_select_tokens(q, k, max_sel=1024, recent_window=128, scale=0.0, rope_
     layer's q [B,n,Hq,192] and k [B,n,Hkv,192] (bf16, Hq = 16 Hkv):
     returns (sel_idx int32 [B,n,Hkv,max_sel], sel_count int32 [B,n,Hkv])."""
     lib = load()
-    B, n, hq, dqk = q.shape
-    hkv = k.shape[2]
+    B, n, hq, dqk = _dims(q, "q", 4)
+    if q.dtype not in _FLOAT:
+        raise TypeError(f"q has dtype {q.dtype}, expected float32 or bfloat16")
+    _, _, hkv, _ = _dims(k, "k", 4)
+    _expect(k, "k", (B, n, hkv, dqk), (q.dtype,))
     if out is not None:
         idx, cnt = out
+        _expect(idx, "sel_idx", (B, n, hkv, max_sel), (torch.int32,))
+        _expect(cnt, "sel_count", (B, n, hkv), (torch.int32,))
     else:
         idx = torch.empty((B, n, hkv, max_sel), dtype=torch.int32, device=q.device)
         cnt = torch.empty((B, n, hkv), dtype=torch.int32, device=q.device)
-    _check_same(q, k, idx, cnt)
     need = lib.hswa_select_workspace_size(B, n, hq, hkv, dqk, rotary_fraction)
+    _check_workspace(workspace, need, q)
+    _check_same(q, k, idx, cnt)
     ws = workspace if workspace is not None else _workspace(need, q.device)
     st = lib.sparse_select_tokens(_ptr(q), _ptr(k), _ptr(idx), _ptr(cnt), max_sel, recent_window,
                                   B, n, hq, hkv, dqk, scale, rope_theta, rotary_fraction,
-                                  pos_offset, _dtype_code(q), _ptr(ws),
-                                  0 if ws is None else ws.numel(), _stream(q))
+                                  pos_offset, _dtype_code(q), _ptr(ws), _ws_bytes(ws), _stream(q))
     _raise(st)
     return idx, cnt

@@ -250,8 +250,10 @@ def test_binding_rejects_bad_tensors(lib):
     q = torch.zeros(1, 4, 2, 192, dtype=torch.float16)
     with pytest.raises(TypeError):
         hswa._binding._dtype_code(q)
-    with pytest.raises(ValueError):
-        hswa._binding._sink(torch.zeros(2, dtype=torch.float64), q)
+    with pytest.raises(TypeError):
+        hswa._binding._sink(torch.zeros(2, dtype=torch.float64), q, 2)
+    with pytest.raises(TypeError, match="q has dtype"):
+        hswa.swa_sink_prefill(q, q[:, :, :1], torch.zeros(1, 4, 1, 128, dtype=torch.float16))
 
 
 def test_product_path_does_not_use_the_oracle():
@@ -263,3 +265,152 @@ def test_product_path_does_not_use_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("the oracle", ""), f
                 assert "scaled_dot_product_attention" not in text, f
+
+
+# ---------------------------------------------------------------------------
+# The Python binding checks shapes and dtypes before any call into the
+# library: mismatches raise on host tensors, so no kernel is ever launched.
+# ---------------------------------------------------------------------------
+
+import torch  # noqa: E402
+
+
+def _t(*shape, dtype=torch.bfloat16):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _prefill_set(B=1, n=40, hq=16, hkv=2, dtype=torch.bfloat16):
+    return _t(B, n, hq, 192, dtype=dtype), _t(B, n, hkv, 192, dtype=dtype), _t(B, n, hkv, 128, dtype=dtype)
+
+
+@pytest.mark.parametrize("case,exc,match", [
+    ("k_dtype", TypeError, "k has dtype"),
+    ("k_len", ValueError, "k has shape"),
+    ("k_dim", ValueError, "k has shape"),
+    ("v_heads", ValueError, "v has shape"),
+    ("v_batch", ValueError, "v has shape"),
+    ("out_shape", ValueError, "out has shape"),
+    ("out_dtype", TypeError, "out has dtype"),
+    ("sink_shape", ValueError, "sink has shape"),
+    ("sink_dtype", TypeError, "sink has dtype"),
+    ("heads", ValueError, "multiple of hkv"),
+    ("q_dims", ValueError, "q must have 4 dims"),
+    ("workspace", ValueError, "workspace holds"),
+    ("host_tensors", ValueError, "GPU device"),
+])
+def test_binding_rejects_prefill_mismatch(lib, case, exc, match):
+    q, k, v = _prefill_set()
+    kw = dict(window=16, rope_theta=1e4, rotary_fraction=0.334)
+    sink = torch.zeros(16, dtype=torch.float32)
+    if case == "k_dtype":
+        q = q.float()
+        v = v.float()
+    elif case == "k_len":
+        k = _t(1, 39, 2, 192)
+    elif case == "k_dim":
+        k = _t(1, 40, 2, 128)
+    elif case == "v_heads":
+        v = _t(1, 40, 4, 128)
+    elif case == "v_batch":
+        v = _t(2, 40, 2, 128)
+    elif case == "out_shape":
+        kw["out"] = _t(1, 40, 16, 192)
+    elif case == "out_dtype":
+        kw["out"] = _t(1, 40, 16, 128, dtype=torch.float32)
+    elif case == "sink_shape":
+        sink = torch.zeros(8, dtype=torch.float32)
+    elif case == "sink_dtype":
+        sink = torch.zeros(16, dtype=torch.float64)
+    elif case == "heads":
+        q = _t(1, 40, 15, 192)
+        sink = torch.zeros(15, dtype=torch.float32)
+    elif case == "q_dims":
+        q = _t(40, 16, 192)
+    elif case == "workspace":
+        kw["workspace"] = torch.zeros(64, dtype=torch.uint8)
+    with pytest.raises(exc, match=match):
+        hswa.swa_sink_prefill(q, k, v, sink, **kw)
+
+
+def test_binding_rejects_other_prefill_mismatches(lib):
+    q, k, v = _prefill_set()
+    with pytest.raises(ValueError, match="must not exceed kv_len"):
+        hswa.swa_sink_prefill_chunk(_t(1, 41, 16, 192), k, v, None, window=16)
+    with pytest.raises(ValueError, match="v has shape"):
+        hswa.swa_sink_prefill_chunk(q[:, :10], k, v[:, :30], None, window=16)
+    with pytest.raises(TypeError, match="k has dtype"):
+        hswa.ga_prefill(q, k.float(), v)
+    with pytest.raises(ValueError, match="k has shape"):
+        hswa.swa_sink_prefill_chunk_cached(q[:, :10], _t(2, 40, 2, 192), v, None)
+
+
+def test_binding_rejects_decode_mismatch(lib):
+    B, hq, hkv, W = 3, 16, 2, 128
+    q = _t(B, hq, 192)
+    kr, vr = _t(B, W, hkv, 192), _t(B, W, hkv, 128)
+    pos = torch.zeros(B, dtype=torch.int64)
+    with pytest.raises(ValueError, match="k_cache has shape"):       # ring shorter than the window
+        hswa.swa_sink_decode(q, _t(B, W - 1, hkv, 192), vr, pos, 10, window=W)
+    with pytest.raises(ValueError, match="v_cache has shape"):
+        hswa.swa_sink_decode(q, kr, _t(B, W, hkv + 1, 128), pos, 10, window=W)
+    with pytest.raises(TypeError, match="pos has dtype"):
+        hswa.swa_sink_decode(q, kr, vr, pos.int(), 10, window=W)
+    with pytest.raises(ValueError, match="pos has shape"):
+        hswa.swa_sink_decode(q, kr, vr, pos[:2], 10, window=W)
+    with pytest.raises(TypeError, match="k_cache has dtype"):
+        hswa.swa_sink_decode(q.float(), kr, vr, pos, 10, window=W)
+    with pytest.raises(ValueError, match="seq_offsets must be None"):
+        hswa.swa_sink_decode(q, kr, vr, pos, 10, window=W, seq_offsets=torch.zeros(B + 1, dtype=torch.int64))
+    kc, vc = _t(100, hkv, 192), _t(100, hkv, 128)
+    with pytest.raises(ValueError, match="seq_offsets is required"):
+        hswa.swa_sink_decode(q, kc, vc, pos, 10, layout=hswa.KV_CONTIGUOUS, window=0)
+    with pytest.raises(ValueError, match="seq_offsets has shape"):
+        hswa.swa_sink_decode(q, kc, vc, pos, 10, layout=hswa.KV_CONTIGUOUS, window=0,
+                             seq_offsets=torch.zeros(B, dtype=torch.int64))
+    with pytest.raises(ValueError, match="out has shape"):
+        hswa.swa_sink_decode(q, kc, vc, pos, 10, layout=hswa.KV_CONTIGUOUS, window=0,
+                             seq_offsets=torch.zeros(B + 1, dtype=torch.int64), out=_t(B, hq, 192))
+    # multi-token: the ring holds ring_slots rows
+    qm = _t(B, 4, hq, 192)
+    with pytest.raises(ValueError, match="k_cache has shape"):
+        hswa.swa_sink_decode_multi(qm, kr, vr, pos, 10, ring_slots=131, window=W)
+    # FP8: codes and per-kv-head scales
+    ks = torch.ones(hkv, dtype=torch.float32)
+    k8, v8 = _t(B, W, hkv, 192, dtype=torch.uint8), _t(B, W, hkv, 128, dtype=torch.uint8)
+    with pytest.raises(TypeError, match="k_cache has dtype"):
+        hswa.swa_sink_decode_fp8(q, kr, vr, ks, ks, pos, 10, window=W)
+    with pytest.raises(ValueError, match="v_scale has shape"):
+        hswa.swa_sink_decode_fp8(q, k8, v8, ks, torch.ones(hkv + 1), pos, 10, window=W)
+
+
+def test_binding_rejects_append_sparse_select_mismatch(lib):
+    B, T, hkv = 2, 3, 2
+    kn, vn = _t(B, T, hkv, 192), _t(B, T, hkv, 128)
+    pos = torch.zeros(B, dtype=torch.int64)
+    with pytest.raises(ValueError, match="v_new has shape"):
+        hswa.kv_cache_append(kn, _t(B, T + 1, hkv, 128), _t(B, 8, hkv, 192), _t(B, 8, hkv, 128), pos,
+                             10, ring_slots=8)
+    with pytest.raises(ValueError, match="v_cache has shape"):
+        hswa.kv_cache_append(kn, vn, _t(B, 8, hkv + 1, 192), _t(B, 8, hkv, 128), pos, 10, ring_slots=8)
+    with pytest.raises(ValueError, match="caches hold 3 kv heads"):
+        hswa.kv_cache_append(kn, vn, _t(B, 8, hkv + 1, 192), _t(B, 8, hkv + 1, 128), pos, 10,
+                             ring_slots=8)
+    with pytest.raises(ValueError, match="k_cache has shape"):
+        hswa.kv_cache_append(kn, vn, _t(B, 7, hkv, 192), _t(B, 7, hkv, 128), pos, 10, ring_slots=8)
+    with pytest.raises(TypeError, match="type of the new keys"):
+        hswa.kv_cache_append(kn, vn, _t(B, 8, hkv, 192, dtype=torch.float32),
+                             _t(B, 8, hkv, 128, dtype=torch.float32), pos, 10, ring_slots=8)
+    with pytest.raises(ValueError, match="k_scale"):
+        hswa.kv_cache_append(kn, vn, _t(B, 8, hkv, 192, dtype=torch.uint8),
+                             _t(B, 8, hkv, 128, dtype=torch.uint8), pos, 10, ring_slots=8)
+    q, k, v = _prefill_set(n=300, hq=64, hkv=4)
+    idx = torch.zeros(1, 300, 4, 16, dtype=torch.int32)
+    cnt = torch.zeros(1, 300, 4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="sel_idx has shape"):
+        hswa.sparse_sink_attn(q, k, v, idx[:, :299], cnt)
+    with pytest.raises(TypeError, match="sel_count has dtype"):
+        hswa.sparse_sink_attn(q, k, v, idx, cnt.long())
+    with pytest.raises(ValueError, match="sel_idx has shape"):
+        hswa.sparse_select_tokens(q, k, max_sel=8, out=(idx, cnt))
+    with pytest.raises(TypeError, match="k has dtype"):
+        hswa.sparse_sink_attn_fp8(q, k, v, torch.ones(4), torch.ones(4), idx, cnt)

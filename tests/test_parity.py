@@ -125,6 +125,65 @@ def test_matrix_core_prefill_shapes(gpu_lib, B, n, hq, hkv, window, frac, sink):
     _check(f"matrix-core B={B} n={n} {hq}/{hkv} W={window} R/2={int(frac * 96)}", o, ref)
 
 
+def _windowed_runs(B, n, hq, hkv):
+    """Item runs of the windowed ring kernel on this device: an item is one kv
+    head and T = 256 / G query tokens, items are ordered (sequence, kv head,
+    block), and each workgroup takes ceil(items / CUs) consecutive items.
+    Returns T, blocks per head, and the items j whose successor j + 1 lies
+    in the same run but belongs to another (sequence, kv head): the point
+    where a run restarts its K/V tile ring."""
+    G = hq // hkv
+    T = 256 // G
+    nblk = -(-n // T)
+    items = B * hkv * nblk
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    run = -(-items // cus)
+    cross = [j for j in range(items - 1) if (j + 1) % run != 0 and j // nblk != (j + 1) // nblk]
+    return T, nblk, cross
+
+
+@pytest.mark.parametrize("B,n,hq,hkv", [(1, 1100, 64, 8), (3, 700, 64, 8), (2, 1000, 64, 4)])
+def test_windowed_run_crosses_heads_and_sequences(gpu_lib, B, n, hq, hkv):
+    """Runs of the windowed kernel that move on to another kv head or sequence
+    (the causal window of rslog.cc section 2.1 over a batch), compared with
+    the oracle over the whole output."""
+    T, nblk, cross = _windowed_runs(B, n, hq, hkv)
+    print(f"[parity] windowed runs: T={T} blocks/head={nblk} crossings after items {cross}",
+          flush=True)
+    assert cross, "the shape no longer makes a run cross a head on this device"
+    x = _prefill_case(B, n, hq, hkv, "bf16", 400 + n)
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=128, rope_theta=1.0e4,
+                                 rotary_fraction=0.334, pos_offset=5)
+    q, k, v, s = _host(x)
+    ref = oracle.swa_sink_prefill(q, k, v, s, window=128, rope_theta=1.0e4, rotary_fraction=0.334,
+                                  pos_offset=5)
+    _check(f"windowed runs B={B} n={n} {hq}/{hkv}", o, ref)
+
+
+def test_windowed_run_crossings_long_sequences(gpu_lib):
+    """Two sequences of 30000 tokens (runs of 59 items on 256 CUs, 938 blocks
+    per kv head): every row of the two items on either side of each crossing
+    against the oracle, element by element."""
+    B, n, hq, hkv = 2, 30000, 64, 8
+    T, nblk, cross = _windowed_runs(B, n, hq, hkv)
+    print(f"[parity] long windowed runs: {len(cross)} crossings", flush=True)
+    assert len(cross) >= 4
+    x = _prefill_case(B, n, hq, hkv, "bf16", 410)
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=128, rope_theta=1.0e4,
+                                 rotary_fraction=0.334)
+    toks = set()
+    for j in cross:
+        for it in (j, j + 1):
+            blk = it % nblk
+            toks.update(range(blk * T, min(n, blk * T + T)))
+    rows = np.array(sorted(toks))
+    ridx = torch.from_numpy(rows).to(DEV)
+    ref = oracle.prefill_rows(None, _np(x["k"]), _np(x["v"]), rows, sink=_np(x["sink"]),
+                              window=128, rope_theta=1.0e4, rotary_fraction=0.334,
+                              q_rows=_np(x["q"][:, ridx]))
+    _check(f"long windowed runs ({len(rows)} rows at crossings)", o[:, ridx], ref)
+
+
 @pytest.mark.parametrize("B,n,hq,hkv", [(3, 250, 64, 8), (1, 515, 128, 4)])
 def test_matrix_core_ga_shapes(gpu_lib, B, n, hq, hkv):
     x = _prefill_case(B, n, hq, hkv, "bf16", 95 + n, sink_range=None)
