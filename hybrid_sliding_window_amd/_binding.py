@@ -30,6 +30,8 @@ _SIGNATURES = {
     "hswa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i, _ll]),
     "swa_sink_decode": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _ll,
                              _f, _f, _f, _i, _vp, _sz, _vp]),
+    "swa_sink_decode_noalloc": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                     _ll, _f, _f, _f, _i, _vp]),
     "kv_cache_append": (_i, [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i, _ll, _f, _f,
                              _i, _vp]),
     "kv_cache_append_fp8": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _i,
@@ -335,6 +337,32 @@ def swa_sink_decode(q, k_cache, v_cache, pos, max_pos, layout=KV_RING, seq_offse
     return o
 
 
+# Bytes of the library's static decode scratch (HSWA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def swa_sink_decode_noalloc(q, k_cache, v_cache, pos, max_pos, layout=KV_RING, seq_offsets=None,
+                            sink=None, window=128, scale=0.0, rope_theta=10000.0,
+                            rotary_fraction=0.0, out=None):
+    """swa_sink_decode with its scratch in the library's static device array
+    (no workspace is allocated; pass `out` to allocate nothing at all)."""
+    lib = load()
+    B, hq, dqk = _dims(q, "q", 3)
+    if q.dtype not in _FLOAT:
+        raise TypeError(f"q has dtype {q.dtype}, expected float32 or bfloat16")
+    hkv, dv = _decode_caches(k_cache, v_cache, layout, B, window, dqk, (q.dtype,))
+    _positions(pos, B, seq_offsets, layout == KV_CONTIGUOUS)
+    sink = _sink(sink, q, hq)
+    o = _out(out, (B, hq, dv), q.dtype, q.device)
+    _check_same(q, k_cache, v_cache, o, pos, seq_offsets)
+    st = lib.swa_sink_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), layout,
+                                     _ptr(seq_offsets), _ptr(pos), _ptr(sink), _ptr(o), B, hq, hkv,
+                                     dqk, dv, window, int(max_pos), scale, rope_theta,
+                                     rotary_fraction, _dtype_code(q), _stream(q))
+    _raise(st)
+    return o
+
+
 def decode_multi_workspace_size(layout, batch, q_len, hq, d_v, window, ring_slots, max_pos):
     return load().hswa_decode_multi_workspace_size(layout, batch, q_len, hq, d_v, window,
                                                    ring_slots, max_pos)
@@ -520,3 +548,4 @@ def sparse_select_tokens(q, k, max_sel=1024, recent_window=128, scale=0.0, rope_
                                   pos_offset, _dtype_code(q), _ptr(ws), _ws_bytes(ws), _stream(q))
     _raise(st)
     return idx, cnt
+

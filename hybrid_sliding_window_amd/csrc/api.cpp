@@ -386,6 +386,11 @@ hswa_status_t append_impl(const void* k_new, const void* v_new, void* k_cache, v
 
 }  // namespace
 
+namespace hswa {
+// Status and message for entry points defined outside this file.
+int api_fail(int status, const char* msg) { return (int)fail((hswa_status_t)status, msg); }
+}  // namespace hswa
+
 extern "C" {
 
 const char* hswa_last_error(void) { return g_last_error.c_str(); }

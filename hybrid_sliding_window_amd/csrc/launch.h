@@ -139,4 +139,7 @@ hipError_t launch_sparse_bf16(const AttnArgs& a, hipStream_t stream);
 bool sparse_fp8_supported(const AttnArgs& a);
 hipError_t launch_sparse_fp8(const AttnArgs& a, hipStream_t stream);
 
+// Records msg as the text of hswa_last_error() and returns status (api.cpp).
+int api_fail(int status, const char* msg);
+
 }  // namespace hswa

@@ -172,6 +172,29 @@ hswa_status_t swa_sink_decode(const void* q, const void* k_cache, const void* v_
                               hswa_dtype_t dtype, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* Bytes of the static device scratch behind swa_sink_decode_noalloc. */
+#define HSWA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * swa_sink_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same operation, arguments, contract and
+ * errors as swa_sink_decode; the scratch it needs comes from a device array
+ * inside the library of HSWA_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held
+ * from the first call on that GPU until the process ends.  A call whose
+ * hswa_decode_workspace_size() exceeds that maximum fails with
+ * HSWA_ERR_INVALID_ARGUMENT before anything is enqueued.  The call allocates
+ * and frees nothing.  All calls on one GPU share its array: calls that may
+ * run at the same time on one GPU (different streams or host threads) race
+ * and must not be issued.
+ */
+hswa_status_t swa_sink_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      hswa_kv_layout_t layout, const long long* seq_offsets,
+                                      const long long* pos, const float* sink, void* o, int batch,
+                                      int hq, int hkv, int d_qk, int d_v, int window,
+                                      long long max_pos, float scale, float rope_theta,
+                                      float rotary_fraction, hswa_dtype_t dtype, void* stream);
+
 /*
  * Appending q_len new tokens per sequence to a decode cache, ahead of the
  * decode (or multi-token decode) call that reads them: the ring of an SWA

@@ -414,3 +414,19 @@ def test_binding_rejects_append_sparse_select_mismatch(lib):
         hswa.sparse_select_tokens(q, k, max_sel=8, out=(idx, cnt))
     with pytest.raises(TypeError, match="k has dtype"):
         hswa.sparse_sink_attn_fp8(q, k, v, torch.ones(4), torch.ones(4), idx, cnt)
+
+
+def test_noalloc_decode_refuses_oversize_on_the_host(lib):
+    """The no-allocation decode refuses a call whose scratch would exceed the
+    static maximum before any HIP call (so this runs without a GPU)."""
+    import ctypes as C
+    text = open(HEADER).read()
+    assert "#define HSWA_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
+    assert hswa.NOALLOC_SCRATCH_BYTES == 64 << 20
+    need = hswa.decode_workspace_size(hswa.KV_CONTIGUOUS, 64, 64, 128, 0, 262143)
+    assert need > hswa.NOALLOC_SCRATCH_BYTES
+    st = lib.swa_sink_decode_noalloc(C.c_void_p(FAKE), C.c_void_p(FAKE), C.c_void_p(FAKE), 1,
+                                     C.c_void_p(FAKE), C.c_void_p(FAKE), None, C.c_void_p(FAKE),
+                                     64, 64, 4, 192, 128, 0, 262143, 0.0, 1e7, 0.0, 1, None)
+    assert st == INVALID
+    assert "static maximum" in lib.hswa_last_error().decode()
