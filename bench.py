@@ -153,6 +153,38 @@ def cpu_baseline(x, wl, budget_s):
                       f"useful FLOPs of the sampled rows over wall time"}
 
 
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    except Exception:  # noqa: BLE001
+        return 1
+
+
+def _oracle_entry(value, unit, seconds, sample, gpu_value):
+    """One oracle baseline: the untuned oracle's rate on a sample of the
+    workload, and the GPU's rate over it."""
+    return {"value": value, "unit": unit, "cores": _oracle_threads(), "kind": "oracle",
+            "seconds": seconds, "sample": sample,
+            "gpu_over_oracle": (gpu_value / value) if value > 0 else None}
+
+
+def _oracle_rows(run_rows, row_cost, n, budget_s, seed, chunk):
+    """Random query rows, `chunk` at a time, until `budget_s` has passed:
+    returns (useful work done, rows done, seconds)."""
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(n)
+    done, work, t0 = 0, 0.0, time.perf_counter()
+    while done < n:
+        rows = np.sort(order[done:done + chunk])
+        run_rows(rows)
+        work += row_cost(rows)
+        done += len(rows)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    return work, done, time.perf_counter() - t0
+
+
 def copy_calibration(steps, warmup):
     """A plain device copy of known size: the reference for scaling the
     profiler's HBM byte counters (FETCH_SIZE / WRITE_SIZE)."""
@@ -168,29 +200,36 @@ def copy_calibration(steps, warmup):
 def only(which, steps, warmup):
     if which == "copy":
         return {"copy": copy_calibration(steps, warmup)}
-    parts = {"ga": ["ga"], "chunk": ["chunk"], "decode": ["decode"], "decode_mtp": ["decode_mtp"],
-             "decode_fp8": ["decode_fp8"],
-             "sparse": ["sparse"], "sparse_fp8": ["sparse_fp8"], "select": ["select"]}[which]
-    return secondary(steps, warmup, parts)
+    parts = {"tiny": ["tiny"], "ga": ["ga"], "chunk": ["chunk"], "decode": ["decode"],
+             "decode_ring": ["decode_ring"], "decode_ga": ["decode_ga"],
+             "decode_mtp": ["decode_mtp"], "decode_fp8": ["decode_fp8"],
+             "sparse": ["sparse"], "sparse_fp8": ["sparse_fp8"], "select": ["select"],
+             "gather": ["gather"]}[which]
+    return secondary(steps, warmup, parts, cpu=False)
 
 
 def secondary(steps, warmup,
-              parts=("ga", "chunk", "decode", "decode_mtp", "decode_fp8", "sparse", "sparse_fp8",
-                     "select")):
+              parts=("tiny", "ga", "chunk", "decode", "decode_mtp", "decode_fp8", "sparse",
+                     "gather", "sparse_fp8", "select"), cpu=True, cpu_seconds=4.0):
     out = {}
     dev = "cuda"
+    budget = cpu_seconds if cpu else 0.0
+    if "tiny" in parts:
+        _tiny(out, steps, warmup, dev, budget)
     if "ga" in parts:
-        _ga(out, steps, warmup, dev)
+        _ga(out, steps, warmup, dev, budget)
     if "chunk" in parts:
         _chunk(out, steps, warmup, dev)
-    if "decode" in parts:
-        _decode(out, dev)
+    if "decode" in parts or "decode_ring" in parts or "decode_ga" in parts:
+        _decode(out, dev, budget, ring="decode_ga" not in parts, ga="decode_ring" not in parts)
     if "decode_mtp" in parts:
         _decode_mtp(out, dev)
     if "decode_fp8" in parts:
         _decode_fp8(out, dev)
     if "sparse" in parts:
-        _sparse(out, dev)
+        _sparse(out, dev, budget)
+    if "gather" in parts:
+        _gather(out, steps, dev)
     if "sparse_fp8" in parts:
         _sparse_fp8(out, dev)
     if "select" in parts:
@@ -214,7 +253,40 @@ def measured_peaks(steps, warmup):
             "spec_bf16_tflops": BF16_PEAK_TFLOPS, "spec_hbm_gbps": HBM_PEAK_GBPS}
 
 
-def _ga(out, steps, warmup, dev):
+def _tiny(out, steps, warmup, dev, cpu_budget):
+    # Tiny fp32 SWA+sink prefill: n = 512, 2 q / 1 kv heads, no RoPE, in its
+    # four variants (sink on / -inf, W = 128 / W = n); launch-latency-bound
+    wl = synthetic.WORKLOADS["tiny_fp32_swa_n512"]
+    res = {}
+    for window in (128, 512):
+        for with_sink in (True, False):
+            x = synthetic.prefill_inputs(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, "f32",
+                                         wl["seed"], dev, wl["sink_range"] if with_sink else None)
+            o = torch.empty(1, wl["n"], wl["hq"], 128, dtype=torch.float32, device=dev)
+            fn = lambda: hswa.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"],  # noqa: E731
+                                               window=window, out=o)
+            _, per = timed(fn, max(20, steps), warmup)
+            t = float(np.median(per)) / 1e3
+            flops = window_pairs(wl["n"], window) * wl["hq"] * FLOP_PER_PAIR
+            key = f"W{window}_{'sink' if with_sink else 'nosink'}"
+            res[key] = {"us_median": t * 1e6, "us_min": float(np.min(per)) * 1e3,
+                        "tflops": flops / t / 1e12}
+            if cpu_budget > 0 and window == 128 and with_sink:
+                import oracle
+                q, k, v = (x[n_].double().cpu().numpy() for n_ in "qkv")
+                sk = x["sink"].double().cpu().numpy()
+                t0 = time.perf_counter()
+                oracle.swa_sink_prefill(q, k, v, sk, window=window)
+                el = time.perf_counter() - t0
+                res["oracle"] = _oracle_entry(flops / el / 1e9, "GFLOP/s", el,
+                                              "the whole workload (512 rows, 2 heads, W = 128, "
+                                              "sink), fp64 NumPy", flops / t / 1e9)
+    res["note"] = "launch-latency-bound: parity only, no roofline claim"
+    out["tiny_fp32_swa_n512"] = res
+    _log(f"tiny {res}")
+
+
+def _ga(out, steps, warmup, dev, cpu_budget=0.0):
     # GA prefill, n = 32768, 64 q / 4 kv heads, full causal
     wl = synthetic.WORKLOADS["ga_prefill_n32768"]
     x = synthetic.prefill_inputs(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, "bf16", wl["seed"], dev,
@@ -230,6 +302,23 @@ def _ga(out, steps, warmup, dev):
     out["ga_prefill_n32768"] = {"tflops": flops / t / 1e12, "ms": t * 1e3,
                                 "ms_median": float(np.median(per)), "ms_min": float(np.min(per)),
                                 "frac_of_bf16_peak": flops / t / 1e12 / BF16_PEAK_TFLOPS}
+    if cpu_budget > 0:
+        import oracle
+        k = x["k"].double().cpu().numpy()
+        v = x["v"].double().cpu().numpy()
+
+        def run(rows):
+            qr = x["q"][:, torch.from_numpy(rows).to(dev)].double().cpu().numpy()
+            oracle.prefill_rows(None, k, v, rows, sink=None, window=None,
+                                rope_theta=wl["rope_theta"], rotary_fraction=wl["rotary_fraction"],
+                                q_rows=qr)
+        work, done, el = _oracle_rows(run, lambda r: float((r + 1).sum()) * wl["hq"] * FLOP_PER_PAIR,
+                                      wl["n"], cpu_budget, 8, 8)
+        out["ga_prefill_n32768"]["oracle"] = _oracle_entry(
+            work / el / 1e9, "GFLOP/s", el,
+            f"{done} random query rows of {wl['n']} (all 64 heads), fp64 NumPy; useful FLOPs of "
+            f"the sampled rows over wall time (extrapolated to the workload by FLOP rate)",
+            flops / t / 1e9)
     _log(f"GA prefill {out['ga_prefill_n32768']}")
 
 
@@ -271,48 +360,83 @@ def _chunk(out, steps, warmup, dev):
         _log(f"{name} {res}")
 
 
-def _decode(out, dev):
+def _decode(out, dev, cpu_budget=0.0, ring=True, ga=True):
     # Hybrid decode: 64 sequences at p ~ U[131072, 262143]
     wl = synthetic.WORKLOADS["hybrid_decode_b64"]
     pos = synthetic.decode_positions(wl["B"], *wl["pos_range"], wl["seed"])
     maxp = wl["pos_range"][1]
-    sw, ga = wl["swa"], wl["ga"]
-    # ring: rotate over 8 buffer sets (> 256 MB) so the cache is not served from the MALL
-    sets = [synthetic.ring_decode_inputs(wl["B"], sw["hq"], sw["hkv"], sw["window"], 192, 128, "bf16",
-                                         wl["seed"] + 100 * r, pos, dev, sw["sink_range"])
-            for r in range(8)]
-    wsr = torch.empty(hswa.decode_workspace_size(hswa.KV_RING, wl["B"], sw["hq"], 128, sw["window"],
-                                                 maxp), dtype=torch.uint8, device=dev)
-    orr = torch.empty(wl["B"], sw["hq"], 128, dtype=torch.bfloat16, device=dev)
-    it = [0]
+    sw, ga_cfg = wl["swa"], wl["ga"]
+    if ring:
+        # ring: rotate over 8 buffer sets (> 256 MB) so the cache is not served from the MALL
+        sets = [synthetic.ring_decode_inputs(wl["B"], sw["hq"], sw["hkv"], sw["window"], 192, 128,
+                                             "bf16", wl["seed"] + 100 * r, pos, dev,
+                                             sw["sink_range"])
+                for r in range(8)]
+        wsr = torch.empty(hswa.decode_workspace_size(hswa.KV_RING, wl["B"], sw["hq"], 128,
+                                                     sw["window"], maxp),
+                          dtype=torch.uint8, device=dev)
+        orr = torch.empty(wl["B"], sw["hq"], 128, dtype=torch.bfloat16, device=dev)
+        it = [0]
 
-    def ring_step():
-        d = sets[it[0] % len(sets)]
-        it[0] += 1
-        hswa.swa_sink_decode(d["q"], d["k"], d["v"], d["pos"], maxp, layout=hswa.KV_RING,
-                             sink=d["sink"], window=sw["window"], out=orr, workspace=wsr)
-    _, per = timed(ring_step, 40, 8)
-    ring_bytes = wl["B"] * sw["window"] * sw["hkv"] * (192 + 128) * 2 + wl["B"] * sw["hq"] * (192 + 128) * 2
-    t = float(np.mean(per)) / 1e3
-    out["decode_swa_ring"] = {"gbps": ring_bytes / t / 1e9, "us": t * 1e6, "bytes": ring_bytes,
-                              "frac_of_hbm_peak": ring_bytes / t / 1e9 / HBM_PEAK_GBPS,
-                              "note": "8 rotated buffer sets (353 MB) to defeat MALL residency"}
-    _log(f"decode ring {out['decode_swa_ring']}")
-    del sets
-    c = synthetic.contiguous_decode_inputs(wl["B"], ga["hq"], ga["hkv"], 192, 128, "bf16",
+        def ring_step():
+            d = sets[it[0] % len(sets)]
+            it[0] += 1
+            hswa.swa_sink_decode(d["q"], d["k"], d["v"], d["pos"], maxp, layout=hswa.KV_RING,
+                                 sink=d["sink"], window=sw["window"], out=orr, workspace=wsr)
+        _, per = timed(ring_step, 40, 8)
+        ring_bytes = (wl["B"] * sw["window"] * sw["hkv"] * (192 + 128) * 2 +
+                      wl["B"] * sw["hq"] * (192 + 128) * 2)
+        t = float(np.mean(per)) / 1e3
+        out["decode_swa_ring"] = {"gbps": ring_bytes / t / 1e9, "us": t * 1e6, "bytes": ring_bytes,
+                                  "frac_of_hbm_peak": ring_bytes / t / 1e9 / HBM_PEAK_GBPS,
+                                  "note": "8 rotated buffer sets (353 MB) to defeat MALL residency"}
+        if cpu_budget > 0:
+            import oracle
+            d = sets[0]
+            q, k, v = (d[n_].double().cpu().numpy() for n_ in "qkv")
+            sk = d["sink"].double().cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.swa_sink_decode_ring(q, k, v, pos.numpy(), sk)
+            el = time.perf_counter() - t0
+            out["decode_swa_ring"]["oracle"] = _oracle_entry(
+                ring_bytes / el / 1e9, "GB/s", el,
+                "the whole step (64 sequences, all heads), fp64 NumPy; algorithmic bytes over "
+                "wall time", ring_bytes / t / 1e9)
+        _log(f"decode ring {out['decode_swa_ring']}")
+        del sets
+    if not ga:
+        return
+    c = synthetic.contiguous_decode_inputs(wl["B"], ga_cfg["hq"], ga_cfg["hkv"], 192, 128, "bf16",
                                            wl["seed"], pos, dev, None)
-    wsc = torch.empty(hswa.decode_workspace_size(hswa.KV_CONTIGUOUS, wl["B"], ga["hq"], 128, 0, maxp),
+    wsc = torch.empty(hswa.decode_workspace_size(hswa.KV_CONTIGUOUS, wl["B"], ga_cfg["hq"], 128, 0,
+                                                 maxp),
                       dtype=torch.uint8, device=dev)
-    oc = torch.empty(wl["B"], ga["hq"], 128, dtype=torch.bfloat16, device=dev)
+    oc = torch.empty(wl["B"], ga_cfg["hq"], 128, dtype=torch.bfloat16, device=dev)
     fn = lambda: hswa.swa_sink_decode(c["q"], c["k"], c["v"], c["pos"], maxp,  # noqa: E731
                                       layout=hswa.KV_CONTIGUOUS, seq_offsets=c["seq_offsets"],
                                       window=0, out=oc, workspace=wsc)
     _, per = timed(fn, 10, 2)
     keys = int((pos + 1).sum())
-    ga_bytes = keys * ga["hkv"] * (192 + 128) * 2 + wl["B"] * ga["hq"] * (192 + 128) * 2
+    ga_bytes = keys * ga_cfg["hkv"] * (192 + 128) * 2 + wl["B"] * ga_cfg["hq"] * (192 + 128) * 2
     t = float(np.mean(per)) / 1e3
     out["decode_ga_contiguous"] = {"gbps": ga_bytes / t / 1e9, "ms": t * 1e3, "bytes": ga_bytes,
                                    "frac_of_hbm_peak": ga_bytes / t / 1e9 / HBM_PEAK_GBPS}
+    if cpu_budget > 0:
+        import oracle
+        offs = c["seq_offsets"].cpu().numpy()
+        b = int(pos.argmin())   # the shortest sequence: 1 of the 64
+        lo, hi = int(offs[b]), int(offs[b + 1])
+        kb, vb = c["k"][lo:hi].double().cpu().numpy(), c["v"][lo:hi].double().cpu().numpy()
+        q = c["q"].double().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.swa_sink_decode_contiguous(q, None, None, offs, pos.numpy(), None, None,
+                                          seqs=np.array([b]), kv_loader=lambda _b: (kb, vb))
+        el = time.perf_counter() - t0
+        sb = (int(pos[b]) + 1) * ga_cfg["hkv"] * (192 + 128) * 2
+        out["decode_ga_contiguous"]["oracle"] = _oracle_entry(
+            sb / el / 1e9, "GB/s", el,
+            f"1 of the 64 sequences (the shortest, {int(pos[b]) + 1} keys, all 64 heads), fp64 "
+            f"NumPy; its algorithmic bytes over wall time", ga_bytes / t / 1e9)
     _log(f"decode GA {out['decode_ga_contiguous']}")
 
 
@@ -427,7 +551,7 @@ def _decode_fp8(out, dev):
     _log(f"decode fp8 GA {out['decode_fp8_ga_contiguous']}")
 
 
-def _sparse(out, dev):
+def _sparse(out, dev, cpu_budget=0.0):
     # Sparse prefill, n = 65536, 128 recent + <= 1024 selected
     wl = synthetic.WORKLOADS["sparse_prefill_n65536"]
     x = synthetic.sparse_inputs(1, wl["n"], wl["hq"], wl["hkv"], 192, 128, "bf16", wl["seed"],
@@ -443,7 +567,115 @@ def _sparse(out, dev):
     t = float(np.mean(per)) / 1e3
     out["sparse_prefill_n65536"] = {"tflops": flops / t / 1e12, "ms": t * 1e3,
                                     "gathered_kv_gbps": gathered / t / 1e9}
+    # The bound of this kernel: its own gathers without its arithmetic.  The
+    # probe reads each (query, kv head) list as the kernel does (selected
+    # rows, then the recent window; 36 tiles of 32 rows, lists shorter than
+    # 1152 padded with repeats of their last row) with the lists handed to
+    # workgroups in the kernel's order (consecutive queries of a kv head on
+    # one XCD).
+    lists = _sparse_lists(x, wl, dev)
+    tiles = (wl["max_sel"] + 128) // 32
+    o = torch.empty(lists.shape[0] // (tiles * 32), dtype=torch.int32, device=dev)
+    kf = x["k"].view(-1, 192)
+    vf = x["v"].view(-1, 128)
+    _, per = timed(lambda: hswa.gather_probe(kf, vf, lists, tiles, out=o), 5, 1)
+    tp = float(np.median(per)) / 1e3
+    out["sparse_prefill_n65536"]["gather_bound"] = {
+        "probe_ms": tp * 1e3, "probe_gbps": gathered / tp / 1e9,
+        "note": "hswa_gather_probe over the workload's own lists in the kernel's workgroup order"}
+    out["sparse_prefill_n65536"]["frac_of_measured_gather_peak"] = tp / t
+    del lists, o
+    if cpu_budget > 0:
+        import oracle
+        k = x["k"].double().cpu().numpy()
+        v = x["v"].double().cpu().numpy()
+        sk = x["sink"].double().cpu().numpy()
+        G = wl["hq"] // wl["hkv"]
+
+        def run(rows):
+            ri = torch.from_numpy(rows).to(dev)
+            oracle.sparse_rows(x["q"][:, ri].double().cpu().numpy(), k, v,
+                               x["sel_idx"][:, ri].cpu().numpy(), x["sel_count"][:, ri].cpu().numpy(),
+                               rows, sk, recent=wl["recent"], restricted=True)
+
+        def cost(rows):
+            return float((np.minimum(1024, np.maximum(0, rows - 128)) +
+                          np.minimum(rows + 1, 128)).sum()) * wl["hkv"] * G * FLOP_PER_PAIR
+        work, done, el = _oracle_rows(run, cost, wl["n"], cpu_budget, 9, 64)
+        out["sparse_prefill_n65536"]["oracle"] = _oracle_entry(
+            work / el / 1e9, "GFLOP/s", el,
+            f"{done} random query rows of {wl['n']} (all 64 heads), fp64 NumPy; useful FLOPs of "
+            f"the sampled rows over wall time (extrapolated to the workload by FLOP rate)",
+            flops / t / 1e9)
     _log(f"sparse {out['sparse_prefill_n65536']}")
+
+
+def _sparse_lists(x, wl, dev):
+    """Row numbers (token * hkv + g) of every (query, kv head) list of the
+    sparse workload (max_sel + 128 entries, padded with repeats of the
+    list's last row), lists in the order the sparse kernel's workgroups take
+    them: physical workgroup b serves logical list xcd_remap(b) = (g, i) with
+    logical index g * n + i."""
+    n, hkv = wl["n"], wl["hkv"]
+    sel = x["sel_idx"][0].long()                                  # [n, hkv, ms], -1 padded
+    cnt = x["sel_count"][0].long()                                # [n, hkv]
+    ms = sel.shape[-1]
+    width = ms + 128
+    i = torch.arange(n, device=dev)
+    rec = (i[:, None] - 127 + torch.arange(128, device=dev)[None, :])   # [n, 128]
+    full = torch.cat([sel, rec[:, None, :].expand(n, hkv, 128)], dim=2)  # [n, hkv, width]
+    # entry t of a list is sel[t] for t < cnt, else the recent window's t - cnt
+    t = torch.arange(width, device=dev)[None, None, :]
+    src = torch.where(t < cnt[..., None], t, ms + (t - cnt[..., None]))
+    lst = torch.gather(full, 2, src.clamp(max=width - 1))
+    rec_len = torch.minimum(i + 1, torch.tensor(128, device=dev))
+    length = cnt + rec_len[:, None]                                # [n, hkv]
+    # the recent window of query i starts at max(0, i - 127)
+    first_rec = (i - 127).clamp(min=0)[:, None, None]
+    lst = torch.where((t >= cnt[..., None]) & (t < length[..., None]),
+                      first_rec + (t - cnt[..., None]), lst)
+    last = torch.gather(lst, 2, (length - 1).clamp(min=0)[..., None])
+    lst = torch.where(t < length[..., None], lst, last).clamp(min=0)
+    rows = lst * hkv + torch.arange(hkv, device=dev)[None, :, None]              # [n, hkv, width]
+    logical = rows.permute(1, 0, 2).reshape(hkv * n, width)                       # index g * n + i
+    nwg = hkv * n
+    b = torch.arange(nwg, device=dev)
+    q, rem = nwg >> 3, nwg & 7
+    xx, slot = b & 7, b >> 3
+    lg = torch.where(xx < rem, xx * (q + 1) + slot, rem * (q + 1) + (xx - rem) * q + slot)
+    return logical[lg].reshape(-1).to(torch.int32).contiguous()
+
+
+def _gather(out, steps, dev):
+    # Random-row gather bandwidth with the sparse kernel's access pattern:
+    # K rows of 384 B and V rows of 256 B picked uniformly from the sparse
+    # workload's cache (65536 tokens x 4 kv heads: 168 MB, resident in the
+    # 256 MB last-level cache) and from a cache 16 times larger (2.7 GB, so
+    # nearly every row comes from HBM); 36 tiles of 32 rows per wavefront,
+    # 32768 wavefronts (37.7 M rows, 24.2 GB per call).
+    wl = synthetic.WORKLOADS["sparse_prefill_n65536"]
+    nwaves, tiles = 32768, 36
+    res = {}
+    for label, mult in (("cache_168MB", 1), ("cache_2.7GB", 16)):
+        rows = wl["n"] * wl["hkv"] * mult
+        k = synthetic.normal((rows, 192), 31, dev, "bf16")
+        v = synthetic.normal((rows, 128), 32, dev, "bf16")
+        g = torch.Generator(device=dev)
+        g.manual_seed(33)
+        idx = torch.randint(0, rows, (nwaves * tiles * 32,), generator=g, device=dev,
+                            dtype=torch.int32)
+        o = torch.empty(nwaves, dtype=torch.int32, device=dev)
+        fn = lambda: hswa.gather_probe(k, v, idx, tiles, out=o)  # noqa: E731
+        _, per = timed(fn, max(5, steps // 10), 1)
+        t = float(np.median(per)) / 1e3
+        nbytes = nwaves * tiles * 32 * (192 + 128) * 2
+        res[label] = {"gbps": nbytes / t / 1e9, "us": t * 1e6, "bytes": nbytes,
+                      "cache_bytes": rows * (192 + 128) * 2}
+        del k, v, idx, o
+    res["note"] = ("hswa_gather_probe: the sparse kernel's loads (16-byte pieces, 32-row tiles, one "
+                   "wavefront per list) of uniformly random rows, no arithmetic")
+    out["gather_probe"] = res
+    _log(f"gather {res}")
 
 
 def _sparse_fp8(out, dev):
@@ -498,8 +730,9 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["prefill", "ga", "chunk", "decode", "decode_mtp", "decode_fp8", "sparse",
-                             "sparse_fp8", "select", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "tiny", "ga", "chunk", "decode", "decode_ring",
+                                       "decode_ga", "decode_mtp", "decode_fp8", "sparse", "gather",
+                                       "sparse_fp8", "select", "copy"], default=None,
                     help="run one workload only (for profiler runs); prints its figures as JSON")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -572,7 +805,7 @@ def main():
     del x, o, ws
     torch.cuda.empty_cache()
     if not args.no_secondary:
-        rec["secondary"] = secondary(args.steps, args.warmup)
+        rec["secondary"] = secondary(args.steps, args.warmup, cpu=not args.no_cpu)
         rec["measured_peaks"] = measured_peaks(args.steps, args.warmup)
         _log(f"measured peaks {rec['measured_peaks']}")
     print(json.dumps(rec), flush=True)

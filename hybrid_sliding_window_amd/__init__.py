@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     decode_multi_workspace_size,
     decode_workspace_size,
     ga_prefill,
+    gather_probe,
     kv_cache_append,
     lib_path,
     load,

@@ -16,7 +16,8 @@ _STATUS = {0: "HSWA_OK", 1: "HSWA_ERR_INVALID_ARGUMENT", 2: "HSWA_ERR_UNSUPPORTE
 
 _vp, _i, _ll, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_size_t
 
-# Every symbol include/hswa.h declares, with (restype, argtypes).
+# Every symbol include/hswa.h and include/hswa_measure.h declare, with
+# (restype, argtypes).
 _SIGNATURES = {
     "hswa_prefill_workspace_size": (_sz, [_i, _i, _i, _i, _f]),
     "swa_sink_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _f, _f,
@@ -49,6 +50,7 @@ _SIGNATURES = {
     "hswa_select_workspace_size": (_sz, [_i, _i, _i, _i, _i, _f]),
     "sparse_select_tokens": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _f, _f, _ll,
                                   _i, _vp, _sz, _vp]),
+    "hswa_gather_probe": (_i, [_vp, _vp, _i, _vp, _i, _i, _vp, _vp]),
     "hswa_last_error": (ctypes.c_char_p, []),
     "hswa_version": (ctypes.c_char_p, []),
 }
@@ -549,3 +551,21 @@ def sparse_select_tokens(q, k, max_sel=1024, recent_window=128, scale=0.0, rope_
     _raise(st)
     return idx, cnt
 
+
+def gather_probe(k, v, idx, tiles_per_wave, out=None):
+    """Random-row gather probe (include/hswa_measure.h): k bf16 [rows, 192],
+    v bf16 [rows, 128], idx int32 [nwaves * tiles_per_wave * 32] -> one
+    uint32 checksum (as int32) per wavefront."""
+    lib = load()
+    rows = _dims(k, "k", 2)[0]
+    _expect(k, "k", (rows, 192), (torch.bfloat16,))
+    _expect(v, "v", (rows, 128), (torch.bfloat16,))
+    n_idx = _dims(idx, "idx", 1)[0]
+    if idx.dtype != torch.int32 or n_idx % (32 * tiles_per_wave) != 0 or n_idx == 0:
+        raise ValueError("idx must be int32 with a positive multiple of 32 * tiles_per_wave entries")
+    nwaves = n_idx // (32 * tiles_per_wave)
+    o = _out(out, (nwaves,), torch.int32, k.device)
+    _check_same(k, v, idx, o)
+    _raise(lib.hswa_gather_probe(_ptr(k), _ptr(v), rows, _ptr(idx), nwaves, tiles_per_wave, _ptr(o),
+                                 _stream(k)))
+    return o

@@ -27,7 +27,8 @@ def lib():
 
 
 def _declared():
-    text = open(HEADER).read()
+    inc = os.path.dirname(HEADER)
+    text = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)
     return sorted(set(names))
