@@ -12,9 +12,9 @@
 // share their K/V tiles in that XCD's L2, the order reversed every other
 // round so that long and short causal rows even out per workgroup.  The key tiles of its
 // items form one stream; tile number x of the stream lives in stage x % 6
-// of a ring of 20 KB K/V tiles.  A step consumes two tiles: after the
-// step's barrier every wavefront issues its five of the 40 copies of the
-// step two ahead, whose stages the previous step has just released.  q
+// of a ring of 20 KB K/V tiles.  A step consumes two tiles behind one
+// barrier; between them wavefronts 0..3 issue the 40 copies of the step two
+// ahead, into the stages the previous step has just released.  q
 // goes straight from memory into each wavefront's registers when an item
 // starts (long items: the load is paid once per item).
 #include "common.h"
@@ -89,38 +89,16 @@ __global__ __launch_bounds__(512, 1) void prefill_causal_kernel(AttnArgs a, int 
   bf16_t* __restrict__ Op = static_cast<bf16_t*>(a.o);
 
   // ---- copies: a step is 2 tiles x (12 K + 8 V copies of 1 KB) ------------
-  // copy c = wave + 8u (u < 5) of a step: tile c / 20, copy c % 20 of that
-  // tile (below 12: K copy, slot s = 64 cc + lane, row s / 24, physical
-  // chunk s % 24 holding logical chunk pc ^ ((row >> 1) & 7), chunks below
-  // R/8 from the rotated copy unless K is stored rotated; else V copy
-  // cc - 12, row s / 16, 64-byte unit (pc / 4) ^ (row & 3)).
-  int ctile[5], crow[5], ccol[5], cstr[5], coff[5];
-  bool cisk[5], crot[5];
-#pragma unroll
-  for (int u = 0; u < 5; ++u) {
-    const int c = wave + 8 * u;
-    ctile[u] = c / 20;
-    const int cc = c - 20 * ctile[u];
-    cisk[u] = cc < 12;
-    if (cisk[u]) {
-      const int sl = 64 * cc + lane;
-      const int row = sl / 24, pc = sl - row * 24;
-      const int lc = pc ^ ((row >> 1) & 7);
-      crot[u] = !a.k_rotated && lc < (half >> 2);
-      crow[u] = row;
-      ccol[u] = 8 * lc;
-      cstr[u] = hkv * (crot[u] ? R : D);
-      coff[u] = 1024 * cc;
-    } else {
-      const int sl = 64 * (cc - 12) + lane;
-      const int row = sl >> 4, pc = sl & 15;
-      crot[u] = false;
-      crow[u] = row;
-      ccol[u] = 8 * (4 * ((pc >> 2) ^ (row & 3)) + (pc & 3));
-      cstr[u] = hkv * DV;
-      coff[u] = KTILE + 1024 * (cc - 12);
-    }
-  }
+  // Only wavefronts 0..3 issue copies, ten each: copy c = wave + 4u (u < 10)
+  // of a step is tile c / 20, copy cc = c % 20 of that tile (below 12: K
+  // copy, slot s = 64 cc + lane, row s / 24, physical chunk s % 24 holding
+  // logical chunk pc ^ ((row >> 1) & 7), chunks below R/8 from the rotated
+  // copy unless K is stored rotated; else V copy cc - 12, row s / 16, 64-byte
+  // unit (pc / 4) ^ (row & 3)).  Issuing a copy stalls the wavefront until
+  // the vector-memory path accepts it (about 1700 cycles for a step's 40
+  // copies when every wavefront issued five right after the barrier, and no
+  // wavefront computed meanwhile); with the copies on one wavefront of each
+  // SIMD, the other one keeps the SIMD busy while its partner waits.
 
   // request cursor: round rj, tile rt of item rc; past the last item the last
   // tile is requested again (finite data, never read)
@@ -128,14 +106,18 @@ __global__ __launch_bounds__(512, 1) void prefill_causal_kernel(AttnArgs a, int 
   CItem rc = citem(a, citem_of(0, pos, P), nblk, T);
   int put = 0;   // stream number of the next tile requested
   int nis = 0;   // vector-memory operations issued by this wavefront so far
+  const bool producer = wave < 4;
   auto request_step = [&]() {
-    long long rb[2];
+    uintptr_t bk[2], br[2], bv[2];
     int lim[2], st[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int j0 = rc.kstart + rt * BK;
       lim[k] = rc.kend - 1 - j0;
-      rb[k] = (rc.kbase + j0) * hkv + rc.g;
+      const long long rb = (rc.kbase + j0) * hkv + rc.g;
+      bk[k] = reinterpret_cast<uintptr_t>(Kp + rb * D);
+      br[k] = reinterpret_cast<uintptr_t>(Kr + rb * R);
+      bv[k] = reinterpret_cast<uintptr_t>(Vp + rb * DV);
       st[k] = put % CA_NS;
       ++put;
       if (rt + 1 < rc.ntiles) {
@@ -146,15 +128,44 @@ __global__ __launch_bounds__(512, 1) void prefill_causal_kernel(AttnArgs a, int 
         rc = citem(a, citem_of(rj, pos, P), nblk, T);
       }
     }
+    if (producer) {
+      // the per-lane offsets are recomputed here (an opaque copy of the lane
+      // index keeps the compiler from hoisting them into registers held for
+      // the whole kernel)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int u = 0; u < 5; ++u) {
-      const int k = ctile[u];
-      const int row = min(crow[u], lim[k]) * cstr[u] + ccol[u];
-      const bf16_t* src = cisk[u] ? (crot[u] ? Kr + rb[k] * R : Kp + rb[k] * D) : Vp + rb[k] * DV;
-      g2lds16(src + row, ring + st[k] * CA_SLOT + coff[u]);
+      for (int u = 0; u < 10; ++u) {
+        const int c = wave + 4 * u;
+        const int k = c / 20;
+        const int cc = c - 20 * k;
+        uint32_t off;
+        uintptr_t base;
+        int dst;
+        if (cc < 12) {
+          const int sl = 64 * cc + ln;
+          const int row = sl / 24, pc = sl - row * 24;
+          const int lc = pc ^ ((row >> 1) & 7);
+          const bool rot = !a.k_rotated && lc < (half >> 2);
+          off = (uint32_t)(min(row, lim[k]) * (hkv * (rot ? R : D)) + 8 * lc) * 2u;
+          // the K rows or their rotated copy, chosen by arithmetic: a select
+          // here was lowered to a lookup in scratch memory, whose load then
+          // waited for every copy in flight
+          base = bk[k] + ((br[k] - bk[k]) & (uintptr_t)(0 - (uintptr_t)rot));
+          dst = 1024 * cc;
+        } else {
+          const int sl = 64 * (cc - 12) + ln;
+          const int row = sl >> 4, pc = sl & 15;
+          off = (uint32_t)(min(row, lim[k]) * (hkv * DV) + 8 * (4 * ((pc >> 2) ^ (row & 3)) + (pc & 3))) *
+                2u;
+          base = bv[k];
+          dst = KTILE + 1024 * (cc - 12);
+        }
+        g2lds16(reinterpret_cast<const void*>(base + off), ring + st[k] * CA_SLOT + dst);
+      }
+      nis += 10;
     }
     asm volatile("" ::: "memory");
-    nis += 5;
   };
   request_step();
   int ma = nis;   // nis after the copies of the step about to be consumed
@@ -320,14 +331,16 @@ __global__ __launch_bounds__(512, 1) void prefill_causal_kernel(AttnArgs a, int 
 
   // Step: wait for this step's two tiles (copied by the request two steps
   // back); the barrier also releases the two stages the previous step read,
-  // into which the request of the step two ahead goes.
+  // into which the request of the step two ahead goes, issued between the
+  // step's two tiles (measured faster than right after the barrier).
   while (!done) {
     wait_copy(nis - ma);
     ring_barrier();
-    request_step();
-    ma = mb;
-    mb = nis;
+    const int mnext = mb;
     consume();
+    request_step();
+    ma = mnext;
+    mb = nis;
     if (!done) consume();
   }
   __builtin_amdgcn_s_waitcnt(VMCNT(0));   // no copy into LDS outlives the workgroup
