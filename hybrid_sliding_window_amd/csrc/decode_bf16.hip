@@ -275,6 +275,182 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(AttnArgs a, int layo
   orow[lane + 64] = f32_to_bf16_bits(o1 * inv);
 }
 
+// ---- ring caches of at most 128 slots: one launch -------------------------
+// The SWA layer's ring is small (W = 128 keys per sequence and kv head), so
+// the split-K form above spends its time in launches and in waits, not in
+// bytes.  Here a workgroup owns (sequence b, kv head g) and its 4
+// wavefronts take 32 ring slots each: every wavefront issues all copies of
+// its slots into its own LDS region at once (one memory latency, no
+// barrier before the products), computes S^T = K . Q^T and O^T += V^T P^T
+// over its two 16-key tiles as the split kernel does, and the four partial
+// (m, l, O) are merged through LDS with the sink added once (the output
+// rule of rslog.cc section 4.4), written as o directly: no workspace
+// partials and no second launch.
+constexpr int RG_ROWS = 32;                 // ring slots per wavefront
+constexpr int RG_KREG = RG_ROWS * D * 2;    // 12 KB: 32 rows of 384 B
+constexpr int RG_VREG = RG_ROWS * DV * 2;   // 8 KB: 32 rows of 256 B
+
+__global__ __launch_bounds__(256, 2) void decode_ring_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char kreg_all[4 * RG_KREG];
+  __shared__ __attribute__((aligned(16))) unsigned char vreg_all[4 * RG_VREG];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, c = lane & 15, grp = lane >> 4;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int G = a.hq / a.hkv;
+  unsigned char* kreg = kreg_all + wave * RG_KREG;
+  unsigned char* vreg = vreg_all + wave * RG_VREG;
+
+  long long p, row0, len;
+  if (!key_range(a, 0, b, &p, &row0, &len)) {   // uniform over the workgroup
+    if (c < G) {   // a broken contract: NaN outputs
+      bf16_t* orow = static_cast<bf16_t*>(a.o) + ((long long)b * a.hq + g * G + c) * DV + 32 * wave + 8 * grp;
+      st16(orow, make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u));
+    }
+    return;
+  }
+  const int key0 = RG_ROWS * wave;             // this wavefront's first slot
+  const int nk = (int)min((long long)RG_ROWS, max(0LL, len - key0));   // its valid slots
+
+  // ---- copies: K slot s = 64 ii + lane (ii < 12) is row s / 24, physical
+  // chunk s % 24 holding logical chunk pc ^ ((row >> 1) & 7); V slot s =
+  // 64 jj + lane (jj < 8) is row s / 16, 16-byte chunk s % 16 of physical
+  // 32-byte unit u holding logical unit u ^ (row & 7).  Rows past the last
+  // valid slot reload the last one (finite data, masked).
+  if (nk > 0) {
+    const unsigned char* kb = static_cast<const unsigned char*>(a.k) + (row0 * a.hkv + g) * (long long)(D * 2);
+    const unsigned char* vb = static_cast<const unsigned char*>(a.v) + (row0 * a.hkv + g) * (long long)(DV * 2);
+    const int kstr = a.hkv * D * 2, vstr = a.hkv * DV * 2;
+#pragma unroll
+    for (int ii = 0; ii < 12; ++ii) {
+      const int sl = 64 * ii + lane;
+      const int row = sl / 24, pc = sl - row * 24;
+      const int lc = pc ^ ((row >> 1) & 7);
+      const int key = key0 + min(row, nk - 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(kb + (__umul24(key, kstr) + 16 * lc)),
+                                       (lds_void_t*)(kreg + 1024 * ii), 16, 0, 0);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int sl = 64 * jj + lane;
+      const int row = sl >> 4, pc = sl & 15;
+      const int lc = 2 * ((pc >> 1) ^ (row & 7)) + (pc & 1);
+      const int key = key0 + min(row, nk - 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (__umul24(key, vstr) + 16 * lc)),
+                                       (lds_void_t*)(vreg + 1024 * jj), 16, 0, 0);
+    }
+  }
+
+  // q of head g*G + c (rotated to position p by the preparation kernel when
+  // RoPE is on); columns c >= G are padding
+  bf16x8 qf[KS];
+  {
+    const bf16_t* qsrc = static_cast<const bf16_t*>(a.half > 0 ? a.qrot : a.q);
+    const bf16_t* qrow = qsrc + ((long long)b * a.hq + g * G + min(c, G - 1)) * D + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = as_bf16x8(c < G ? ld16(qrow + 32 * ks) : make_uint4(0, 0, 0, 0));
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): q and this wavefront's slots have landed
+
+  const float c2 = a.scale * kLog2e;
+  float m = kNegInf, l = 0.f;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int t = 0; t < RG_ROWS / BK; ++t) {
+    if (t * BK >= nk) break;   // uniform
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int kr = BK * t + c;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int pcq = (4 * ks + grp) ^ ((kr >> 1) & 7);
+      sc = mfma16(as_bf16x8(ld16(kreg + kr * (D * 2) + 16 * pcq)), qf[ks], sc);
+    }
+    // branch-free masking (see the split kernel)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = (BK * t + 4 * grp + r < nk) ? sc[r] : kNegInf;
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = max_across_groups(mx) * c2;
+    const float mn = fmaxf(m, mx);
+    const float ms = (mn == kNegInf) ? 0.f : mn;
+    const float alpha = fast_exp2(m - ms);
+    float pv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(fmaf(sc[r], c2, -ms));
+    const uint2 pk = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
+    l = l * alpha + add_bf16_pair(pk.y, add_bf16_pair(pk.x, 0.f));
+    m = mn;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] *= alpha;
+    const v4i16 pb = __builtin_bit_cast(v4i16, pk);
+    const int vr = BK * t + 4 * grp + (c >> 2);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const uint2 vt = lds_tr4(vreg + vr * (DV * 2) + 32 * (tt ^ (vr & 7)) + 8 * (c & 3));
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, vt), pb,
+                                                         acc[tt], 0, 0, 0);
+    }
+  }
+  l = sum_across_groups(l);
+
+  // ---- merge the four wavefronts' partials -----------------------------------
+  // each wavefront leaves O [16 columns][128 dims], m and l [16] (fp32, base
+  // 2) in its own K region; then wavefront w writes dims 32w .. 32w + 31
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  float* po = reinterpret_cast<float*>(kreg);
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt)
+    *reinterpret_cast<float4*>(po + c * DV + 16 * tt + 4 * grp) =
+        make_float4(acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]);
+  if (grp == 0) {
+    po[16 * DV + c] = m;
+    po[16 * DV + 16 + c] = l;
+  }
+  __syncthreads();
+  const float s2 = (c < G && a.sink) ? a.sink[g * G + c] * kLog2e : kNegInf;
+  float mw[4], lw[4];
+  float M = s2;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float* pw = reinterpret_cast<const float*>(kreg_all + w * RG_KREG);
+    mw[w] = pw[16 * DV + c];
+    lw[w] = pw[16 * DV + 16 + c];
+    M = fmaxf(M, mw[w]);
+  }
+  float den = (s2 > kNegInf) ? fast_exp2(s2 - M) : 0.f;
+  float o8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o8[e] = 0.f;
+  const int d0 = 32 * wave + 8 * grp;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float sw = (mw[w] > kNegInf) ? fast_exp2(mw[w] - M) : 0.f;
+    den += sw * lw[w];
+    const float* pw = reinterpret_cast<const float*>(kreg_all + w * RG_KREG) + c * DV + d0;
+    const float4 x0 = *reinterpret_cast<const float4*>(pw);
+    const float4 x1 = *reinterpret_cast<const float4*>(pw + 4);
+    o8[0] += sw * x0.x; o8[1] += sw * x0.y; o8[2] += sw * x0.z; o8[3] += sw * x0.w;
+    o8[4] += sw * x1.x; o8[5] += sw * x1.y; o8[6] += sw * x1.z; o8[7] += sw * x1.w;
+  }
+  if (c < G) {
+    const float inv = (den > 0.f) ? 1.f / den : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o8[e] *= inv;
+    bf16_t* orow = static_cast<bf16_t*>(a.o) + ((long long)b * a.hq + g * G + c) * DV + d0;
+    st16(orow, pack8(o8));
+  }
+}
+
+bool decode_ring_supported(const AttnArgs& a, int layout) {
+  const int G = a.hq / a.hkv;
+  return layout == 0 && a.window > 0 && a.window <= 4 * RG_ROWS && a.d_qk == D && a.d_v == DV &&
+         G >= 1 && G <= 16 && 2 * a.half <= D;
+}
+
 bool decode_bf16_supported(const AttnArgs& a) {
   const int G = a.hq / a.hkv;
   return a.d_qk == D && a.d_v == DV && G >= 1 && G <= 16 && a.hkv % HG == 0 && 2 * a.half <= D;
@@ -324,6 +500,11 @@ hipError_t launch_decode_bf16(const AttnArgs& a, int layout, hipStream_t stream)
   if (a.B == 0) return hipSuccess;
   hipError_t e = launch_decode_rope_q(a, layout, stream);
   if (e != hipSuccess) return e;
+  if (decode_ring_supported(a, layout)) {
+    hipLaunchKernelGGL(decode_ring_kernel, dim3((unsigned)a.hkv, (unsigned)a.B), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
   dim3 g1((unsigned)(a.hkv / HG), (unsigned)a.nsplit, (unsigned)a.B);
   hipLaunchKernelGGL(decode_split_kernel, g1, dim3(256), 0, stream, a, layout);
   e = hipGetLastError();
