@@ -597,10 +597,13 @@ size_t hswa_select_workspace_size(int batch, int seqlen, int hq, int hkv, int d_
                                   float rotary_fraction) {
   if (batch <= 0 || seqlen <= 0 || hq <= 0 || hkv <= 0 || d_qk <= 0) return 0;
   if (!(rotary_fraction >= 0.f && rotary_fraction <= 1.f)) return 0;
-  const size_t scratch = hswa::select_scratch_bytes(seqlen);
-  if (rotary_half(d_qk, rotary_fraction) == 0) return scratch;
+  // [rotated q][rotated k] (RoPE only), then the log-sum-exp rows, then the
+  // importance scratch
+  const size_t tail = round256(hswa::select_lse_bytes(batch, seqlen, hq)) +
+                      hswa::select_scratch_bytes(seqlen);
+  if (rotary_half(d_qk, rotary_fraction) == 0) return tail;
   const size_t rows = (size_t)batch * seqlen;
-  return round256(rows * hq * (size_t)d_qk * 2) + round256(rows * hkv * (size_t)d_qk * 2) + scratch;
+  return round256(rows * hq * (size_t)d_qk * 2) + round256(rows * hkv * (size_t)d_qk * 2) + tail;
 }
 
 hswa_status_t sparse_select_tokens(const void* q, const void* k, int* sel_idx, int* sel_count,
@@ -639,6 +642,8 @@ hswa_status_t sparse_select_tokens(const void* q, const void* k, int* sel_idx, i
   a.cnt_out = sel_count;
   a.sel_ws = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) + need -
                                          hswa::select_scratch_bytes(seqlen));
+  a.sel_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(a.sel_ws) -
+                                       round256(hswa::select_lse_bytes(batch, seqlen, hq)));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.half > 0) {
     const size_t rows = (size_t)batch * seqlen;

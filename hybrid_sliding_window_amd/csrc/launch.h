@@ -25,6 +25,7 @@ struct AttnArgs {
   int* sel_out;                   // token selection: lists [B, n, hkv, max_sel]
   int* cnt_out;                   // and counts [B, n, hkv]
   unsigned* sel_ws;               // token selection: importance scratch (select_scratch_bytes)
+  float* sel_lse;                 // token selection: log2-sum-exp2 per (b, i, query head)
   void* kout;                     // cache append: the K and V caches written
   void* vout;
   const float* kscale;            // decode FP8 caches: per-kv-head value of one K code unit [hkv]
@@ -112,13 +113,20 @@ hipError_t launch_kv_append(const AttnArgs& a, int layout, bool bf16_in, bool e4
 // (b, i, g) the max_sel candidates 0 .. i - recent of largest importance into
 // sel_out / cnt_out.  With RoPE (half > 0) q and k are read from qrot / krot,
 // full rotated rows [B, n, hq | hkv, 192] made by launch_rope_rows.
-// The kernel runs at most kSelectSlots workgroups, each looping over (row
-// block, kv head) items; workgroup w keeps the importances of its current
-// item's 16 rows in slot w of sel_ws (16 rows of round64(n) words).
+// A first kernel writes sel_lse [B, n, hq] (fp32, base 2) for the rows that
+// rank their candidates; the selection kernel runs at most kSelectSlots
+// workgroups, each looping over (row block, kv head) items; workgroup w keeps
+// the importances of its current item's kSelectRows rows in slot w of sel_ws
+// (kSelectRows rows of round64(n) words), then, after all slots, a list of
+// kSelectListCap (position, key) pairs per row and slot.
 constexpr int kSelectSlots = 256;
+constexpr int kSelectRows = 32;
+constexpr int kSelectListCap = 4096;
 inline size_t select_scratch_bytes(int n) {
-  return (size_t)kSelectSlots * 16 * (((size_t)n + 63) & ~(size_t)63) * 4;
+  return (size_t)kSelectSlots * kSelectRows *
+         ((((size_t)n + 63) & ~(size_t)63) * 4 + (size_t)kSelectListCap * 8);
 }
+inline size_t select_lse_bytes(int B, int n, int hq) { return (size_t)B * n * hq * 4; }
 bool select_tokens_supported(const AttnArgs& a);
 hipError_t launch_select_tokens(const AttnArgs& a, hipStream_t stream);
 

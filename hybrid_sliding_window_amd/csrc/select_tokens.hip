@@ -9,19 +9,19 @@
 // importance, equal importances going to the lower position, in ascending
 // order: the lists sparse attention reads.
 //
-// A workgroup of eight wavefronts owns 16 consecutive query rows of one
+// Two kernels.  The first, select_lse_kernel, writes lse_hi (base 2) for
+// every (row, head) of the rows that rank their candidates.  In the second,
+// a workgroup of eight wavefronts owns 16 consecutive query rows of one
 // (sequence, kv head) with G = 16 query heads, two rows per wavefront, so
-// every per-row state (softmax totals, histograms, thresholds, output
-// offsets) belongs to one wavefront and needs no synchronisation.  A
-// wavefront's scores are S = Q . K^T on 32x32x16 MFMAs with its two rows'
-// 16 heads each on M and the 32 keys of a tile on N: lane (key c, half h)
-// holds eight heads of each row for key c, so a key's importance is eight
-// exponentials summed in the lane and one exchange across the halves, and
-// lanes 0..31 own the keys in order.  K tiles of
-// 32 keys stream through LDS with global_load_lds, shared by all 16 rows.
-// Four passes over the keys:
-//   1. lse_hi per (row, head): online max / sum in base 2, one exponential
-//      per score;
+// every per-row state (histograms, thresholds, output offsets) belongs to
+// one wavefront and needs no synchronisation.  A wavefront's scores are
+// S = Q . K^T on 32x32x16 MFMAs with its two rows' 16 heads each on M and
+// the 32 keys of a tile on N: lane (key c, half h) holds eight heads of each
+// row for key c, so a key's importance is eight exponentials summed in the
+// lane and one exchange across the halves, and lanes 0..31 own the keys in
+// order.  K tiles of 32 keys stream through LDS with global_load_lds, shared
+// by all 16 rows.  Passes:
+//   1. (first kernel) lse_hi per (row, head), online max / sum in base 2;
 //   2. importance of every candidate (probabilities summed over the 16
 //      heads), a 2048-bin histogram of its bits 31..21 per row in LDS, then
 //      the bin holding the max_sel-th largest;
@@ -44,15 +44,17 @@ constexpr int D = 192;
 constexpr int KS = D / 16;              // k-steps of the 32x32x16 MFMA
 constexpr int GQ = 16;                   // query heads per kv head (one MFMA column block)
 constexpr int NW = 8;                    // wavefronts per workgroup
-constexpr int NB = 2;                    // rows per wavefront
-constexpr int ROWS = NW * NB;            // 16 query rows per workgroup
-static_assert(ROWS == 16, "select_scratch_bytes sizes slots of 16 rows");
+constexpr int RW = 4;                    // rows per wavefront: two blocks of 2 rows x 16 heads
+constexpr int ROWS = NW * RW;            // 32 query rows per workgroup
+static_assert(ROWS == kSelectRows, "select_scratch_bytes sizes slots of kSelectRows rows");
 constexpr int BK = 32;                   // keys per LDS tile
 constexpr int KROW = D * 2;              // 384 B per key row
 constexpr int KTILE = BK * KROW;         // 12 KB
 constexpr int KINSTR = KTILE / 1024;     // 12 copies of 1 KB
-constexpr int NBIN = 2048;               // histogram bins per level
+constexpr int NBIN1 = 1024;              // level-1 bins: bits 30..21 (importances are >= 0)
+constexpr int NBIN2 = 2048;              // level-2 bins: bits 20..10
 constexpr int UNR = 8;                   // 16-byte scratch loads in flight per lane
+constexpr int LCAP = kSelectListCap;     // compact-list entries per row
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -93,9 +95,10 @@ __device__ __forceinline__ unsigned suffix_sum(unsigned v, int lane) {
 // Largest bin b of the histogram h[0 .. NBIN) with (count above b) < need
 // <= (count above b) + h[b], scanning from the top.  Returns b and the
 // count strictly above it (uniform over the wavefront).
+template <int NBIN>
 __device__ __forceinline__ void find_bin(const unsigned* h, unsigned need, int lane, int* bin,
                                          unsigned* above) {
-  constexpr int PER = NBIN / 64;          // 32 bins per lane
+  constexpr int PER = NBIN / 64;          // bins per lane
   unsigned mine = 0;
 #pragma unroll 8
   for (int t = 0; t < PER; ++t) mine += h[PER * lane + t];
@@ -193,6 +196,49 @@ __device__ __forceinline__ void lds_k12(bf16x8 (&f)[KS], const uint32_t (&ad)[4]
 }
 static_assert(KS == 12, "twelve k-steps of 16 dims");
 
+// The same operands in two halves of six k-steps (0..5, then 6..11), so that
+// only half of them is live at a time.
+__device__ __forceinline__ void lds_k6_lo(bf16x8 (&f)[KS], const uint32_t (&ad)[4]) {
+  uint4 r0, r1, r2, r3, r4, r5;
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b128 %2, %8\n\t"
+      "ds_read_b128 %3, %9\n\t"
+      "ds_read_b128 %4, %6 offset:128\n\t"
+      "ds_read_b128 %5, %7 offset:128\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5)
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+      : "memory");
+  f[0] = as_bf16x8(r0);
+  f[1] = as_bf16x8(r1);
+  f[2] = as_bf16x8(r2);
+  f[3] = as_bf16x8(r3);
+  f[4] = as_bf16x8(r4);
+  f[5] = as_bf16x8(r5);
+}
+__device__ __forceinline__ void lds_k6_hi(bf16x8 (&f)[KS], const uint32_t (&ad)[4]) {
+  uint4 r6, r7, r8, r9, r10, r11;
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:128\n\t"
+      "ds_read_b128 %1, %9 offset:128\n\t"
+      "ds_read_b128 %2, %6 offset:256\n\t"
+      "ds_read_b128 %3, %7 offset:256\n\t"
+      "ds_read_b128 %4, %8 offset:256\n\t"
+      "ds_read_b128 %5, %9 offset:256\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r6), "=&v"(r7), "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11)
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+      : "memory");
+  f[6] = as_bf16x8(r6);
+  f[7] = as_bf16x8(r7);
+  f[8] = as_bf16x8(r8);
+  f[9] = as_bf16x8(r9);
+  f[10] = as_bf16x8(r10);
+  f[11] = as_bf16x8(r11);
+}
+
 // Sum of x (0 .. 4) over the lanes below this one, from three ballots of
 // its bits; *total = the sum over all 64 lanes.
 __device__ __forceinline__ unsigned prefix_before(unsigned x, unsigned long long below,
@@ -202,6 +248,20 @@ __device__ __forceinline__ unsigned prefix_before(unsigned x, unsigned long long
                       4 * __builtin_popcountll(b2));
   return (unsigned)(__builtin_popcountll(b0 & below) + 2 * __builtin_popcountll(b1 & below) +
                     4 * __builtin_popcountll(b2 & below));
+}
+
+// The same for x in 0 .. 32 (six ballots).
+__device__ __forceinline__ unsigned prefix_before6(unsigned x, unsigned long long below,
+                                                   unsigned* total) {
+  unsigned t = 0, p = 0;
+#pragma unroll
+  for (int bit = 0; bit < 6; ++bit) {
+    const unsigned long long bb = __ballot((x >> bit) & 1u);
+    t += (unsigned)__builtin_popcountll(bb) << bit;
+    p += (unsigned)__builtin_popcountll(bb & below) << bit;
+  }
+  *total = t;
+  return p;
 }
 
 // Histogram increment at LDS address addr, in asm for the same reason (a
@@ -217,7 +277,11 @@ __device__ __forceinline__ void lds_inc(uint32_t addr) {
 __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char kst0[KTILE];
   __shared__ __attribute__((aligned(16))) unsigned char kst1[KTILE];
-  __shared__ unsigned hist[ROWS][NBIN];
+  // level-1 histograms of the 32 rows; once a wavefront has found its four
+  // rows' level-1 bins, it reuses their 16 KB for the level-2 histogram of
+  // one row at a time
+  __shared__ __attribute__((aligned(16))) unsigned hist[ROWS][NBIN1];
+  static_assert(RW * NBIN1 >= NBIN2, "a wavefront's level-1 rows hold one level-2 histogram");
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, c = lane & 31, hi = lane >> 5;
@@ -228,6 +292,36 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
   const int ncap = (n + 63) & ~63;               // scratch words per row
   const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
   unsigned* const scr_wg = a.sel_ws + (size_t)wg * ROWS * ncap;
+  uint2* const lst_wg = reinterpret_cast<uint2*>(a.sel_ws + (size_t)nwg * ROWS * ncap) +
+                        (size_t)wg * ROWS * LCAP;
+  const float c2 = a.scale * kLog2e;
+  const bf16_t* __restrict__ Qp = static_cast<const bf16_t*>(a.half > 0 ? a.qrot : a.q);
+  const bf16_t* __restrict__ Kp = static_cast<const bf16_t*>(a.half > 0 ? a.krot : a.k);
+  const int kstride = hkv * KROW;
+
+  // ---- K tile copies: instruction ii (12 per tile) fills LDS bytes [1024 ii, +1024):
+  // slot s = 64 ii + lane, key row s / 24, physical chunk pc = s % 24 holding
+  // logical chunk pc ^ ((row >> 1) & 7) (within its aligned 128 B): rows lie
+  // 384 B apart, so rows r and r + 1 start half a 256-byte bank line apart,
+  // and the sixteen lanes that read one line each cycle (rows c .. c + 15,
+  // same logical chunk) hit sixteen different 16-byte bank groups.
+  // Wavefront w issues ii = w and, for w < 4, ii = w + 8.
+  int drow[2], doff[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ii = wave + NW * u;
+    const int sl = 64 * ii + lane;
+    const int row = sl / 24, pc = sl - row * 24;
+    drow[u] = row;
+    doff[u] = 16 * (pc ^ ((row >> 1) & 7));
+  }
+  // K operand of key c, k-step ks = 4 u + b: logical chunk 2 ks + hi =
+  // 8 u + (2 b + hi), so 128 u bytes on from the chunk of k-step b
+  uint32_t koff[4];
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) koff[bb] = c * KROW + 16 * ((2 * bb + hi) ^ ((c >> 1) & 7));
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
   // Items run heaviest first (late row blocks, long key ranges), round r
   // giving item r * nwg + w to workgroup w, or to nwg - 1 - w in odd rounds,
   // so that each pair of rounds costs every workgroup about the same.
@@ -240,294 +334,479 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
   const int i0 = blk * ROWS;
   const long long tokbase = (long long)b * n;
 
-  // this wavefront's rows
+  // this wavefront's rows i0 + 4 w + rr
   // mode: 0 keeps nothing, 1 keeps every candidate, 2 ranks them
-  int row_i[NB], ncand[NB], kwant[NB], mode[NB];
-  bool row_ok[NB];
+  int row_i[RW], ncand[RW], kwant[RW], mode[RW];
+  bool row_ok[RW];
+  bool mine = false;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    row_i[nb] = i0 + NB * wave + nb;
-    row_ok[nb] = row_i[nb] < n;
-    ncand[nb] = row_ok[nb] ? max(0, row_i[nb] - recent + 1) : 0;
-    kwant[nb] = min(K, ncand[nb]);
-    mode[nb] = (kwant[nb] == 0) ? 0 : (ncand[nb] <= kwant[nb]) ? 1 : 2;
+  for (int rr = 0; rr < RW; ++rr) {
+    row_i[rr] = i0 + RW * wave + rr;
+    row_ok[rr] = row_i[rr] < n;
+    ncand[rr] = row_ok[rr] ? max(0, row_i[rr] - recent + 1) : 0;
+    kwant[rr] = min(K, ncand[rr]);
+    mode[rr] = (kwant[rr] == 0) ? 0 : (ncand[rr] <= kwant[rr]) ? 1 : 2;
+    mine = mine || mode[rr] == 2;
   }
   const int ilast = min(n - 1, i0 + ROWS - 1);       // last row of the workgroup
-  const int lse_keys = ilast + 1;                     // pass 1 covers keys 0 .. ilast
   const int cand_keys = max(0, ilast - recent + 1);   // passes 2-4 cover 0 .. ilast - recent
   // the selection needs importances only where a row has more candidates than it keeps
-  const bool any_rank = __syncthreads_or((lane == 0) && (mode[0] == 2 || mode[1] == 2));
+  const bool any_rank = __syncthreads_or((lane == 0) && mine);
 
-  const bf16_t* __restrict__ Qp = static_cast<const bf16_t*>(a.half > 0 ? a.qrot : a.q);
-  const bf16_t* __restrict__ Kp = static_cast<const bf16_t*>(a.half > 0 ? a.krot : a.k);
-
-  // q operand: M row c is head g*16 + c % 16 of the wavefront's row c / 16;
-  // k-step ks holds dims 16 ks + 8 hi .. + 7
-  bf16x8 qf[KS];
-  {
-    const int nb = c >> 4;
-    const bf16_t* qrow =
-        Qp + ((tokbase + min(row_i[nb], n - 1)) * a.hq + g * GQ + (c & 15)) * D + 8 * hi;
+  // this wavefront's rows of the workgroup's scratch slot
+  unsigned* scr[RW];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 16 * ks));
+  for (int rr = 0; rr < RW; ++rr) scr[rr] = scr_wg + (size_t)(RW * wave + rr) * ncap;
+
+  int bin1[RW];
+  unsigned above1[RW], cnt1[RW];
+#pragma unroll
+  for (int rr = 0; rr < RW; ++rr) {
+    bin1[rr] = 0;
+    above1[rr] = 0;
+    cnt1[rr] = 0;
   }
-
-  // ---- K tile copies: instruction ii (12 per tile) fills LDS bytes [1024 ii, +1024):
-  // slot s = 64 ii + lane, key row s / 24, physical chunk pc = s % 24 holding
-  // logical chunk pc ^ (row & 7) (within its aligned 128 B).  Wavefront w
-  // issues ii = w and, for w < 4, ii = w + 8.
-  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(Kp + (tokbase * hkv + g) * D);
-  const int kstride = hkv * KROW;
-  int drow[2], doff[2];
+  if (any_rank) {
+    // q operand of block nb: M row c is head g*16 + c % 16 of the
+    // wavefront's row 2 nb + c / 16; k-step ks holds dims 16 ks + 8 hi .. + 7
+    bf16x8 qf[2][KS];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int ii = wave + NW * u;
-    const int sl = 64 * ii + lane;
-    const int row = sl / 24, pc = sl - row * 24;
-    drow[u] = row;
-    doff[u] = 16 * (pc ^ (row & 7));
-  }
-  auto issue = [&](int k0, int kend, unsigned char* kd) {
+    for (int nb = 0; nb < 2; ++nb) {
+      const bf16_t* qrow =
+          Qp + ((tokbase + min(row_i[2 * nb + (c >> 4)], n - 1)) * a.hq + g * GQ + (c & 15)) * D +
+          8 * hi;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int ii = wave + NW * u;
-      if (ii < KINSTR) {
-        const int key = min(k0 + drow[u], kend - 1);
-        __builtin_amdgcn_global_load_lds(
-            (glb_void_t*)(kbase + ((long long)key * kstride + doff[u])),
-            (lds_void_t*)(kd + 1024 * ii), 16, 0, 0);
-      }
+      for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = as_bf16x8(ld16(qrow + 16 * ks));
     }
-  };
-  // K operand of key c, k-step ks = 4 u + b: logical chunk 2 ks + hi =
-  // 8 u + (2 b + hi), so 128 u bytes on from the chunk of k-step b
-  uint32_t koff[4];
+    // lse_hi (base 2) of element e of block nb, from the first kernel: row
+    // 2 nb + e / 8, head 8 ((e / 4) % 2) + 4 hi + e % 4
+    float lse[2][16];
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) koff[bb] = c * KROW + 16 * ((2 * bb + hi) ^ (c & 7));
-  // S = Q . K^T for the tile: element e of the lane is key c against M row
-  // 8 (e / 4) + 4 hi + e % 4, i.e. row e / 8 of the wavefront, head
-  // 8 ((e / 4) % 2) + 4 hi + e % 4
-  auto scores = [&](const unsigned char* kc) {
-    const uint32_t base = lds_addr(kc);
-    uint32_t ad[4];
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) ad[bb] = base + koff[bb];
-    bf16x8 kf[KS];
-    lds_k12(kf, ad);
-    f32x16 sc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sc[e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sc = mfma32(qf[ks], kf[ks], sc);
-    return sc;
-  };
+      for (int e = 0; e < 16; ++e) {
+        const int rr = 2 * nb + (e >> 3);
+        lse[nb][e] = (mode[rr] == 2)
+                         ? a.sel_lse[(tokbase + row_i[rr]) * a.hq + g * GQ + 8 * ((e >> 2) & 1) +
+                                     4 * hi + (e & 3)]
+                         : 0.f;
+      }
 
-  // Stream keys 0 .. nkeys - 1 in tiles; body(kc, k0) sees each tile in order.
-  auto stream = [&](int nkeys, auto&& body) {
-    if (nkeys <= 0) return;
-    const int ntile = (nkeys + BK - 1) / BK;
-    __syncthreads();                       // the previous stream's tiles are consumed
-    issue(0, nkeys, kst0);
+    const unsigned char* kbase =
+        reinterpret_cast<const unsigned char*>(Kp + (tokbase * hkv + g) * D);
+    auto issue = [&](int k0, int kend, unsigned char* kd) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int ii = wave + NW * u;
+        if (ii < KINSTR) {
+          const int key = min(k0 + drow[u], kend - 1);
+          __builtin_amdgcn_global_load_lds(
+              (glb_void_t*)(kbase + ((long long)key * kstride + doff[u])),
+              (lds_void_t*)(kd + 1024 * ii), 16, 0, 0);
+        }
+      }
+    };
+
+    // ---- pass 2: importances of the candidates, stored to the scratch
+    // rows, and the level-1 histogram (bits 30..21) of each ranking row.
+    // S = Q . K^T per block: element e of the lane is key c against M row
+    // 8 (e / 4) + 4 hi + e % 4, i.e. block row e / 8, head
+    // 8 ((e / 4) % 2) + 4 hi + e % 4.  A key's importance for a row is the
+    // lane's eight exponentials summed plus the other half's eight, so both
+    // halves end with all four rows' importances of key c; lane (c, h)
+    // stores and counts rows h and 2 + h.
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) {
+      uint4* hrow = reinterpret_cast<uint4*>(hist[RW * wave + rr]);
+      for (int t = lane; t < NBIN1 / 4; t += 64) hrow[t] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int ntile = (cand_keys + BK - 1) / BK;
+    __syncthreads();                       // the previous item's tiles are consumed
+    if (ntile > 0) issue(0, cand_keys, kst0);
     for (int t = 0; t < ntile; ++t) {
       unsigned char* cur = (t & 1) ? kst1 : kst0;
       unsigned char* nxt = (t & 1) ? kst0 : kst1;
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's copies of tile t
       __syncthreads();                     // everyone's copies landed; tile t - 1 consumed
-      if (t + 1 < ntile) issue((t + 1) * BK, nkeys, nxt);
-      body(cur, t * BK);
-    }
-  };
-
-  const float c2 = a.scale * kLog2e;
-
-  // ---- pass 1: lse (base 2) of every (row, head) over keys 0 .. i -----------
-  // lane (c, hi) runs a (max, sum) for each of its 16 (row, head) elements
-  // over its key c of every tile, reduced over the 32 key lanes at the end.
-  // One exponential per key: of the two rescaling factors, the one of the
-  // larger operand is exactly 1.  The running max starts finite, so that a
-  // masked key (-inf) leaves the sum unchanged without a special case.
-  float m[16], l[16];
+      if (t + 1 < ntile) issue((t + 1) * BK, cand_keys, nxt);
+      const uint32_t base = lds_addr(cur);
+      uint32_t ad[4];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    m[e] = -__FLT_MAX__;
-    l[e] = 0.f;
-  }
-  if (any_rank) {
-    stream(lse_keys, [&](const unsigned char* kc, int k0) {
-      const f32x16 sc = scores(kc);
-      const int j = k0 + c;
+      for (int bb = 0; bb < 4; ++bb) ad[bb] = base + koff[bb];
+      bf16x8 kf[KS];
+      f32x16 sc[2];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float x = (j <= row_i[e >> 3]) ? sc[e] * c2 : kNegInf;
-        const float d = x - m[e];
-        const float f = fast_exp2(-fabsf(d));
-        l[e] = (d > 0.f) ? fmaf(l[e], f, 1.f) : l[e] + f;
-        m[e] = fmaxf(m[e], x);
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[nb][e] = 0.f;
+      lds_k6_lo(kf, ad);
+#pragma unroll
+      for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) sc[nb] = mfma32(qf[nb][ks], kf[ks], sc[nb]);
+      lds_k6_hi(kf, ad);
+#pragma unroll
+      for (int ks = KS / 2; ks < KS; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) sc[nb] = mfma32(qf[nb][ks], kf[ks], sc[nb]);
+      const int j = t * BK + c;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float imp2[2];
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) {
+          float v = 0.f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            v += fast_exp2(fmaf(sc[nb][8 * r2 + q], c2, -lse[nb][8 * r2 + q]));
+          const Pair p = halves32(v);
+          imp2[r2] = p.a + p.b;
+        }
+        const int rr = 2 * nb + hi;          // the row this lane stores and counts
+        const unsigned u = __float_as_uint(hi ? imp2[1] : imp2[0]);
+        const int nc = hi ? ncand[2 * nb + 1] : ncand[2 * nb];
+        const bool rank = hi ? mode[2 * nb + 1] == 2 : mode[2 * nb] == 2;
+        // words past the row's candidates, within its round64(n), are never read
+        (hi ? scr[2 * nb + 1] : scr[2 * nb])[j] = u;
+        if (j < nc && rank) lds_inc(lds_addr(&hist[RW * wave + rr][u >> 21]));
       }
-    });
-  }
-  float lse[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const float M = max32(m[e]);
-    const float L = sum32(l[e] * fast_exp2(m[e] - M));
-    lse[e] = M + __log2f(L);
-  }
-
-  // importance of key c of the tile for row nb (both lane halves of column
-  // c end with the sum over the 16 heads)
-  auto importances = [&](const unsigned char* kc, float (&imp)[NB]) {
-    const f32x16 sc = scores(kc);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float v = 0.f;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) v += fast_exp2(fmaf(sc[8 * nb + r], c2, -lse[8 * nb + r]));
-      const Pair p = halves32(v);
-      imp[nb] = p.a + p.b;
     }
-  };
-  const bool owner = hi == 0;                    // lanes 0..31 own keys 0..31 of a tile
 
-  // this wavefront's rows of the workgroup's scratch slot
-  unsigned* scr[NB];
+    // ---- level-1 bin of each ranking row, and how many candidates are in it
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) scr[nb] = scr_wg + (size_t)(NB * wave + nb) * ncap;
-
-  int bin1[NB], t22[NB];
-  unsigned above1[NB], quota[NB];
-  if (any_rank) {
-    // ---- pass 2: level-1 histogram (bits 31..21) ---------------------------
-    for (int nb = 0; nb < NB; ++nb)
-      for (int t = lane; t < NBIN; t += 64) hist[NB * wave + nb][t] = 0u;
-    stream(cand_keys, [&](const unsigned char* kc, int k0) {
-      float imp[NB];
-      importances(kc, imp);
-      const int j = k0 + c;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const unsigned u = __float_as_uint(imp[nb]);
-        // every lane stores (the two halves write the same word, and words
-        // past the row's candidates, within its round64(n), are never read)
-        scr[nb][j] = u;
-        if (owner && j < ncand[nb] && mode[nb] == 2)
-          lds_inc(lds_addr(&hist[NB * wave + nb][u >> 21]));
+    for (int rr = 0; rr < RW; ++rr) {
+      bin1[rr] = 0;
+      above1[rr] = 0;
+      cnt1[rr] = 0;
+      if (mode[rr] == 2) {
+        find_bin<NBIN1>(hist[RW * wave + rr], (unsigned)kwant[rr], lane, &bin1[rr], &above1[rr]);
+        cnt1[rr] = hist[RW * wave + rr][bin1[rr]];
       }
-    });
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      bin1[nb] = 0;
-      above1[nb] = 0;
-      if (mode[nb] == 2) find_bin(hist[NB * wave + nb], (unsigned)kwant[nb], lane, &bin1[nb], &above1[nb]);
     }
-    // ---- pass 3: level-2 histogram (bits 20..10) inside bin1, from the
-    // importances pass 2 stored.  The rows are this wavefront's own, on this
-    // compute unit: a workgroup-scope fence (the stores complete) makes them
-    // visible to its loads.
+    // The scratch rows are this wavefront's own, on this compute unit: a
+    // workgroup-scope fence (the stores complete) makes them visible to its
+    // loads.
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-    for (int nb = 0; nb < NB; ++nb)
-      for (int t = lane; t < NBIN; t += 64) hist[NB * wave + nb][t] = 0u;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      if (mode[nb] != 2) continue;
-      const uint4* row = reinterpret_cast<const uint4*>(scr[nb]);
-      const int nc = ncand[nb], nc4 = (nc + 3) >> 2;
-      for (int q0 = 0; q0 < nc4; q0 += 64 * UNR) {
-        uint4 u[UNR];
-#pragma unroll
-        for (int t = 0; t < UNR; ++t) {
-          const int q = q0 + 64 * t + lane;
-          u[t] = (q < nc4) ? row[q] : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int t = 0; t < UNR; ++t) {
-          const int j = 4 * (q0 + 64 * t + lane);
-          const unsigned w[4] = {u[t].x, u[t].y, u[t].z, u[t].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (j + e < nc && (int)(w[e] >> 21) == bin1[nb])
-              lds_inc(lds_addr(&hist[NB * wave + nb][(w[e] >> 10) & (NBIN - 1)]));
-        }
-      }
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      t22[nb] = 0;
-      quota[nb] = 0;
-      if (mode[nb] == 2) {
-        int bin2;
-        unsigned above2;
-        find_bin(hist[NB * wave + nb], (unsigned)kwant[nb] - above1[nb], lane, &bin2, &above2);
-        t22[nb] = (bin1[nb] << 11) | bin2;
-        quota[nb] = (unsigned)kwant[nb] - above1[nb] - above2;   // ties at t22 to take
-      }
-    }
   }
 
-  // ---- pass 4: emit, ascending; lane l owns candidates 4 l .. 4 l + 3 of
-  // each 256, ranks from ballots of the per-lane counts ----------------------
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    if (!row_ok[nb]) continue;
-    int* out = a.sel_out + ((tokbase + row_i[nb]) * hkv + g) * (long long)K;
-    const int nc = ncand[nb];
+  // ---- per row: the threshold inside bin1 (level 2, bits 20..10) and the
+  // lists, ascending.  A row whose candidates at or above bin1 fit in LCAP
+  // is read once: the candidates above bin1 and those in it go, in position
+  // order, to a compact list (position, 22-bit key) while the level-2
+  // histogram of bin1 builds; the list is then ranked.  Otherwise the
+  // importances are read twice, for the histogram and then to emit.  The
+  // level-2 histogram lives in the wavefront's own level-1 rows.
+  unsigned* const h2 = hist[RW * wave];
+  for (int rr = 0; rr < RW; ++rr) {
+    if (!row_ok[rr]) continue;
+    int* out = a.sel_out + ((tokbase + row_i[rr]) * hkv + g) * (long long)K;
+    const int nc = ncand[rr];
     unsigned emitted = 0;
-    if (mode[nb] == 1) {                       // every candidate
+    if (mode[rr] == 1) {                       // every candidate
       for (int t = lane; t < nc; t += 64) out[t] = t;
       emitted = (unsigned)nc;
-    } else if (mode[nb] == 2) {
-      const uint4* row = reinterpret_cast<const uint4*>(scr[nb]);
+    } else if (mode[rr] == 2) {
+      const int want = kwant[rr], b1 = bin1[rr];
+      for (int t = lane; t < NBIN2 / 4; t += 64)
+        reinterpret_cast<uint4*>(h2)[t] = make_uint4(0u, 0u, 0u, 0u);
+      const uint4* row = reinterpret_cast<const uint4*>(scr[rr]);
       const int nc4 = (nc + 3) >> 2;
-      unsigned ties = 0;
-      for (int q0 = 0; q0 < nc4; q0 += 64 * UNR) {
-        uint4 u[UNR];
+      if (above1[rr] + cnt1[rr] <= (unsigned)LCAP) {
+        // one read: lane l scans the 32 consecutive candidates
+        // 32 l .. 32 l + 31 of each 2048, so that one prefix over the lanes
+        // orders the kept ones
+        uint2* lst = lst_wg + (size_t)(RW * wave + rr) * LCAP;
+        unsigned count = 0;
+        for (int q0 = 0; q0 < nc4; q0 += 64 * UNR) {
+          uint4 u[UNR];
 #pragma unroll
-        for (int t = 0; t < UNR; ++t) {
-          const int q = q0 + 64 * t + lane;
-          u[t] = (q < nc4) ? row[q] : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int t = 0; t < UNR; ++t) {
-          // the lane's four consecutive candidates j .. j + 3
-          const int j = 4 * (q0 + 64 * t + lane);
-          const unsigned w[4] = {u[t].x, u[t].y, u[t].z, u[t].w};
-          bool above[4], tie[4];
-          unsigned ntie = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = (int)(w[e] >> 10);
-            above[e] = j + e < nc && key > t22[nb];
-            tie[e] = j + e < nc && key == t22[nb];
-            ntie += tie[e] ? 1u : 0u;
+          for (int t = 0; t < UNR; ++t) {
+            const int q = q0 + UNR * lane + t;
+            u[t] = (q < nc4) ? row[q] : make_uint4(0u, 0u, 0u, 0u);
           }
-          unsigned tie_total;
-          const unsigned tie_at = ties + prefix_before(ntie, below, &tie_total);
-          bool take[4];
-          unsigned ntake = 0, r = 0;
+          const int j0 = 4 * (q0 + UNR * lane);
+          unsigned nk = 0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            take[e] = above[e] || (tie[e] && tie_at + r < quota[nb]);
-            r += tie[e] ? 1u : 0u;
-            ntake += take[e] ? 1u : 0u;
-          }
-          unsigned take_total;
-          unsigned at = emitted + prefix_before(ntake, below, &take_total);
+          for (int t = 0; t < UNR; ++t) {
+            const unsigned w[4] = {u[t].x, u[t].y, u[t].z, u[t].w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (take[e]) {
-              if (at < (unsigned)kwant[nb]) out[at] = j + e;
-              ++at;
+            for (int e = 0; e < 4; ++e) {
+              const bool in = j0 + 4 * t + e < nc;
+              const int bin = (int)(w[e] >> 21);
+              if (in && bin == b1) lds_inc(lds_addr(&h2[(w[e] >> 10) & (NBIN2 - 1)]));
+              nk += (in && bin >= b1) ? 1u : 0u;
             }
-          ties += tie_total;
-          emitted += take_total;
+          }
+          unsigned total;
+          unsigned at = count + prefix_before6(nk, below, &total);
+          if (nk) {
+#pragma unroll
+            for (int t = 0; t < UNR; ++t) {
+              const unsigned w[4] = {u[t].x, u[t].y, u[t].z, u[t].w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int j = j0 + 4 * t + e;
+                if (j < nc && (int)(w[e] >> 21) >= b1) lst[at++] = make_uint2((unsigned)j, w[e] >> 10);
+              }
+            }
+          }
+          count += total;
+        }
+        int bin2;
+        unsigned above2;
+        find_bin<NBIN2>(h2, (unsigned)want - above1[rr], lane, &bin2, &above2);
+        const unsigned t22 = ((unsigned)b1 << 11) | (unsigned)bin2;
+        const unsigned quota = (unsigned)want - above1[rr] - above2;   // ties at t22 to take
+        // the list is this wavefront's own stores: visible after a fence
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        unsigned ties = 0;
+        for (int q0 = 0; q0 < (int)count; q0 += 64) {
+          const int q = q0 + lane;
+          const uint2 en = (q < (int)count) ? lst[q] : make_uint2(0u, 0u);
+          const bool in = q < (int)count;
+          const bool tie = in && en.y == t22;
+          const unsigned long long bt = __ballot(tie);
+          const bool take = in && (en.y > t22 || (tie && ties + (unsigned)__builtin_popcountll(bt & below) < quota));
+          const unsigned long long bk = __ballot(take);
+          const unsigned at = emitted + (unsigned)__builtin_popcountll(bk & below);
+          if (take && at < (unsigned)want) out[at] = (int)en.x;
+          ties += (unsigned)__builtin_popcountll(bt);
+          emitted += (unsigned)__builtin_popcountll(bk);
+        }
+      } else {
+        // level 2 over the whole row, then a second read to emit; lane l
+        // owns candidates 4 l .. 4 l + 3 of each 256, ranks from ballots of
+        // the per-lane counts
+        for (int q0 = 0; q0 < nc4; q0 += 64 * UNR) {
+          uint4 u[UNR];
+#pragma unroll
+          for (int t = 0; t < UNR; ++t) {
+            const int q = q0 + 64 * t + lane;
+            u[t] = (q < nc4) ? row[q] : make_uint4(0u, 0u, 0u, 0u);
+          }
+#pragma unroll
+          for (int t = 0; t < UNR; ++t) {
+            const int j = 4 * (q0 + 64 * t + lane);
+            const unsigned w[4] = {u[t].x, u[t].y, u[t].z, u[t].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (j + e < nc && (int)(w[e] >> 21) == b1)
+                lds_inc(lds_addr(&h2[(w[e] >> 10) & (NBIN2 - 1)]));
+          }
+        }
+        int bin2;
+        unsigned above2;
+        find_bin<NBIN2>(h2, (unsigned)want - above1[rr], lane, &bin2, &above2);
+        const int t22 = (b1 << 11) | bin2;
+        const unsigned quota = (unsigned)want - above1[rr] - above2;
+        unsigned ties = 0;
+        for (int q0 = 0; q0 < nc4; q0 += 64 * UNR) {
+          uint4 u[UNR];
+#pragma unroll
+          for (int t = 0; t < UNR; ++t) {
+            const int q = q0 + 64 * t + lane;
+            u[t] = (q < nc4) ? row[q] : make_uint4(0u, 0u, 0u, 0u);
+          }
+#pragma unroll
+          for (int t = 0; t < UNR; ++t) {
+            // the lane's four consecutive candidates j .. j + 3
+            const int j = 4 * (q0 + 64 * t + lane);
+            const unsigned w[4] = {u[t].x, u[t].y, u[t].z, u[t].w};
+            bool above[4], tie[4];
+            unsigned ntie = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int key = (int)(w[e] >> 10);
+              above[e] = j + e < nc && key > t22;
+              tie[e] = j + e < nc && key == t22;
+              ntie += tie[e] ? 1u : 0u;
+            }
+            unsigned tie_total;
+            const unsigned tie_at = ties + prefix_before(ntie, below, &tie_total);
+            bool take[4];
+            unsigned ntake = 0, rk = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              take[e] = above[e] || (tie[e] && tie_at + rk < quota);
+              rk += tie[e] ? 1u : 0u;
+              ntake += take[e] ? 1u : 0u;
+            }
+            unsigned take_total;
+            unsigned at = emitted + prefix_before(ntake, below, &take_total);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (take[e]) {
+                if (at < (unsigned)want) out[at] = j + e;
+                ++at;
+              }
+            ties += tie_total;
+            emitted += take_total;
+          }
         }
       }
     }
-    for (int t = min((int)emitted, kwant[nb]) + lane; t < K; t += 64) out[t] = -1;
-    if (lane == 0) a.cnt_out[(tokbase + row_i[nb]) * hkv + g] = (int)min(emitted, (unsigned)kwant[nb]);
+    for (int t = min((int)emitted, kwant[rr]) + lane; t < K; t += 64) out[t] = -1;
+    if (lane == 0) a.cnt_out[(tokbase + row_i[rr]) * hkv + g] = (int)min(emitted, (unsigned)kwant[rr]);
   }
   }  // items
+}
+
+// lse_hi = log2 sum_{j <= i} 2^(c2 s_hij) for every (row, head) of the rows
+// that rank their candidates (i - recent + 1 > max_sel > 0).  A workgroup of
+// four wavefronts owns 16 consecutive rows of one (sequence, kv head), four
+// rows per wavefront: two blocks of 32 (row, head) columns, row 2 nb + c / 16
+// of the wavefront and head c % 16 in column c of block nb.  Each block's
+// product is K . Q^T with the 32 keys of a tile on M, so lane (column c,
+// half h) holds 16 keys of one (row, head): the running max moves once per
+// tile and each score costs one exponential and an add.  The two lane halves
+// hold different keys of the same column and are merged at the end.  Two
+// workgroups share a compute unit, one wavefront of each per SIMD, so that
+// the matrix products of one overlap the exponentials of the other.
+constexpr int LNW = 4;                           // wavefronts per workgroup
+constexpr int LRW = 4;                           // rows per wavefront
+constexpr int LROWS = LNW * LRW;                 // 16 rows per workgroup
+constexpr int LCP = KINSTR / LNW;                // 1 KB tile copies per wavefront
+static_assert(KINSTR % LNW == 0, "copies split evenly over the wavefronts");
+constexpr int LNS = 4;                           // K tile stages: copies run three tiles ahead
+static_assert(LCP == 3, "the waits below count three copies per tile");
+__global__ __launch_bounds__(LNW * 64, 2) void select_lse_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char kst[LNS][KTILE];
+  constexpr int RW = LRW;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, c = lane & 31, hi = lane >> 5;
+  const int n = a.n, hkv = a.hkv, K = a.max_sel, recent = a.recent;
+  const int nblk = (n + LROWS - 1) / LROWS;
+  const int ngrp = a.B * hkv;
+  const int items = ngrp * nblk;
+  const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
+  const float c2 = a.scale * kLog2e;
+  const bf16_t* __restrict__ Qp = static_cast<const bf16_t*>(a.half > 0 ? a.qrot : a.q);
+  const bf16_t* __restrict__ Kp = static_cast<const bf16_t*>(a.half > 0 ? a.krot : a.k);
+  const int kstride = hkv * KROW;
+
+  // K tile copies (layout as in the selection kernel; wavefront w issues
+  // copies w, w + 4, w + 8) and operand addresses
+  int drow[LCP], doff[LCP];
+#pragma unroll
+  for (int u = 0; u < LCP; ++u) {
+    const int sl = 64 * (wave + LNW * u) + lane;
+    const int row = sl / 24, pc = sl - row * 24;
+    drow[u] = row;
+    doff[u] = 16 * (pc ^ ((row >> 1) & 7));
+  }
+  uint32_t koff[4];
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) koff[bb] = c * KROW + 16 * ((2 * bb + hi) ^ ((c >> 1) & 7));
+
+  // heaviest items first, alternating direction per round (as the selection kernel)
+  for (int r = 0; r * nwg < items; ++r) {
+    const int item = r * nwg + ((r & 1) ? nwg - 1 - wg : wg);
+    if (item >= items) continue;
+    const int blk = nblk - 1 - item / ngrp;
+    const int bg = item - (item / ngrp) * ngrp;
+    const int b = bg / hkv, g = bg - b * hkv;
+    const int i0 = blk * LROWS;
+    const int ilast = min(n - 1, i0 + LROWS - 1);
+    // the block's last row has the most candidates: nothing to rank if it keeps them all
+    if (K <= 0 || ilast - recent + 1 <= K) continue;
+    const long long tokbase = (long long)b * n;
+    const int r0 = i0 + RW * wave;               // the wavefront's first row
+
+    int myrow[2];
+    bf16x8 qf[2][KS];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      myrow[nb] = r0 + 2 * nb + (c >> 4);
+      const bf16_t* qrow =
+          Qp + ((tokbase + min(myrow[nb], n - 1)) * a.hq + g * GQ + (c & 15)) * D + 8 * hi;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = as_bf16x8(ld16(qrow + 16 * ks));
+    }
+    const unsigned char* kbase =
+        reinterpret_cast<const unsigned char*>(Kp + (tokbase * hkv + g) * D);
+    auto issue = [&](int k0, int kend, unsigned char* kd) {
+#pragma unroll
+      for (int u = 0; u < LCP; ++u) {
+        const int key = min(k0 + drow[u], kend - 1);
+        __builtin_amdgcn_global_load_lds(
+            (glb_void_t*)(kbase + ((long long)key * kstride + doff[u])),
+            (lds_void_t*)(kd + 1024 * (wave + LNW * u)), 16, 0, 0);
+      }
+    };
+
+    // running (max, sum) of the lane's column in each block over its keys;
+    // the max starts finite, so a masked key (-inf) needs no special case
+    float m[2] = {-__FLT_MAX__, -__FLT_MAX__}, l[2] = {0.f, 0.f};
+    const int nkeys = ilast + 1;
+    const int ntile = (nkeys + BK - 1) / BK;
+    __syncthreads();                             // the previous item's tiles are consumed
+    for (int t = 0; t < LNS - 1 && t < ntile; ++t) issue(t * BK, nkeys, kst[t]);
+    for (int t = 0; t < ntile; ++t) {
+      unsigned char* cur = kst[t % LNS];
+      // this wavefront's copies of tile t have landed once at most those of
+      // the (up to two) tiles issued after it are outstanding
+      const int ahead = min(ntile - 1 - t, LNS - 2);
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F76);        // vmcnt(6)
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F73);   // vmcnt(3)
+      else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
+      __syncthreads();                           // everyone's copies landed; tile t - 1 consumed
+      if (t + LNS - 1 < ntile) issue((t + LNS - 1) * BK, nkeys, kst[(t + LNS - 1) % LNS]);
+      const int k0 = t * BK;
+      if (k0 > r0 + RW - 1) continue;            // keys past all of the wavefront's rows
+      const uint32_t base = lds_addr(cur);
+      uint32_t ad[4];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) ad[bb] = base + koff[bb];
+      bf16x8 kf[KS];
+      lds_k12(kf, ad);
+      f32x16 sc[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[nb][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) sc[nb] = mfma32(kf[ks], qf[nb][ks], sc[nb]);
+      // element e is key k0 + 8 (e / 4) + 4 hi + e % 4
+      const bool diag = k0 + BK - 1 > r0;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        f32x16 x = sc[nb];
+        if (diag) {
+          // key k0 + kk (kk = 8 (e / 4) + 4 hi + e % 4) is visible iff kk <= dhi
+          const int dhi = myrow[nb] - (k0 + 4 * hi);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int kk = 8 * (e >> 2) + (e & 3);
+            x[e] = (kk > dhi) ? kNegInf : x[e];
+          }
+        }
+        float mx = fmaxf(x[0], x[1]);
+#pragma unroll
+        for (int e = 2; e < 16; ++e) mx = fmaxf(mx, x[e]);
+        const float mn = fmaxf(m[nb], mx * c2);
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) part[e & 3] += fast_exp2(fmaf(x[e], c2, -mn));
+        l[nb] = fmaf(l[nb], fast_exp2(m[nb] - mn), (part[0] + part[1]) + (part[2] + part[3]));
+        m[nb] = mn;
+      }
+    }
+    // merge the two halves' keys; lane (c, h) writes column c of block h
+    float out[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const Pair pm = halves32(m[nb]), pl = halves32(l[nb]);
+      const float M = fmaxf(pm.a, pm.b);
+      const float L = pl.a * fast_exp2(pm.a - M) + pl.b * fast_exp2(pm.b - M);
+      out[nb] = M + __log2f(L);
+    }
+    const int row = r0 + 2 * hi + (c >> 4);
+    if (row < n) a.sel_lse[(tokbase + row) * a.hq + g * GQ + (c & 15)] = hi ? out[1] : out[0];
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);            // no copy into LDS outlives the workgroup
 }
 
 bool select_tokens_supported(const AttnArgs& a) {
@@ -538,6 +817,16 @@ hipError_t launch_select_tokens(const AttnArgs& a, hipStream_t stream) {
   const long long items = (long long)a.B * a.hkv * ((a.n + ROWS - 1) / ROWS);
   if (items == 0) return hipSuccess;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const long long lse_items = (long long)a.B * a.hkv * ((a.n + LROWS - 1) / LROWS);
+  const unsigned lse_grid = (unsigned)(lse_items < 2 * cus ? lse_items : 2 * cus);
+  hipLaunchKernelGGL(select_lse_kernel, dim3(lse_grid), dim3(LNW * 64), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(items < kSelectSlots ? items : kSelectSlots);
   hipLaunchKernelGGL(select_tokens_kernel, dim3(grid), dim3(NW * 64), 0, stream, a);
   return hipGetLastError();

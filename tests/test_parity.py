@@ -1111,8 +1111,10 @@ def test_select_tokens_ties_and_empty(gpu_lib):
 def test_select_tokens_all_tied(gpu_lib):
     """q = 0 gives every key of a row the same importance, so every row keeps
     its lowest candidates: the tie ranks run across lanes and 256-key chunks,
-    and max_sel = 701 cuts the ties inside one lane's group of four."""
-    B, n, hkv, K, recent = 1, 3000, 2, 701, 16
+    and max_sel = 701 cuts the ties inside one lane's group of four.  Rows
+    with up to 4096 candidates rank a compact list; longer rows (all tied in
+    one bin) take the two-read path."""
+    B, n, hkv, K, recent = 1, 6000, 2, 701, 16
     x = synthetic.prefill_inputs(B, n, 16 * hkv, hkv, 192, 128, "bf16", 251, DEV, None)
     q = torch.zeros_like(x["q"])
     idx, cnt = gpu_lib.sparse_select_tokens(q, x["k"], max_sel=K, recent_window=recent)
