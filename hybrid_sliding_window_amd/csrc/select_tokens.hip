@@ -492,8 +492,8 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
   // ---- per row: the threshold inside bin1 (level 2, bits 20..10) and the
   // lists, ascending.  A row whose candidates at or above bin1 fit in LCAP
   // is read once: the candidates above bin1 and those in it go, in position
-  // order, to a compact list (position, 22-bit key) while the level-2
-  // histogram of bin1 builds; the list is then ranked.  Otherwise the
+  // order, to a compact list (position, 22-bit key), from which the level-2
+  // histogram of bin1 and then the ranking are taken.  Otherwise the
   // importances are read twice, for the histogram and then to emit.  The
   // level-2 histogram lives in the wavefront's own level-1 rows.
   unsigned* const h2 = hist[RW * wave];
@@ -517,12 +517,22 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
         // orders the kept ones
         uint2* lst = lst_wg + (size_t)(RW * wave + rr) * LCAP;
         unsigned count = 0;
-        for (int q0 = 0; q0 < nc4; q0 += 64 * UNR) {
-          uint4 u[UNR];
+        // the next round's loads are issued before this round is counted
+        uint4 u[UNR], un[UNR];
 #pragma unroll
-          for (int t = 0; t < UNR; ++t) {
-            const int q = q0 + UNR * lane + t;
-            u[t] = (q < nc4) ? row[q] : make_uint4(0u, 0u, 0u, 0u);
+        for (int t = 0; t < UNR; ++t) {
+          const int q = UNR * lane + t;
+          un[t] = (q < nc4) ? row[q] : make_uint4(0u, 0u, 0u, 0u);
+        }
+        for (int q0 = 0; q0 < nc4; q0 += 64 * UNR) {
+#pragma unroll
+          for (int t = 0; t < UNR; ++t) u[t] = un[t];
+          if (q0 + 64 * UNR < nc4) {
+#pragma unroll
+            for (int t = 0; t < UNR; ++t) {
+              const int q = q0 + 64 * UNR + UNR * lane + t;
+              un[t] = (q < nc4) ? row[q] : make_uint4(0u, 0u, 0u, 0u);
+            }
           }
           const int j0 = 4 * (q0 + UNR * lane);
           unsigned nk = 0;
@@ -530,12 +540,8 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
           for (int t = 0; t < UNR; ++t) {
             const unsigned w[4] = {u[t].x, u[t].y, u[t].z, u[t].w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bool in = j0 + 4 * t + e < nc;
-              const int bin = (int)(w[e] >> 21);
-              if (in && bin == b1) lds_inc(lds_addr(&h2[(w[e] >> 10) & (NBIN2 - 1)]));
-              nk += (in && bin >= b1) ? 1u : 0u;
-            }
+            for (int e = 0; e < 4; ++e)
+              nk += (j0 + 4 * t + e < nc && (int)(w[e] >> 21) >= b1) ? 1u : 0u;
           }
           unsigned total;
           unsigned at = count + prefix_before6(nk, below, &total);
@@ -552,13 +558,18 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
           }
           count += total;
         }
+        // the list is this wavefront's own stores: visible after a fence;
+        // the level-2 histogram of its bin1 entries
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        for (int q = lane; q < (int)count; q += 64) {
+          const unsigned key = lst[q].y;
+          if ((int)(key >> 11) == b1) lds_inc(lds_addr(&h2[key & (NBIN2 - 1)]));
+        }
         int bin2;
         unsigned above2;
         find_bin<NBIN2>(h2, (unsigned)want - above1[rr], lane, &bin2, &above2);
         const unsigned t22 = ((unsigned)b1 << 11) | (unsigned)bin2;
         const unsigned quota = (unsigned)want - above1[rr] - above2;   // ties at t22 to take
-        // the list is this wavefront's own stores: visible after a fence
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
         unsigned ties = 0;
         for (int q0 = 0; q0 < (int)count; q0 += 64) {
           const int q = q0 + lane;
