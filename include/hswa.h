@@ -345,9 +345,12 @@ hswa_status_t sparse_sink_attn_fp8(const void* q, const void* k, const void* v,
                                    void* stream);
 
 /* Bytes of workspace sparse_select_tokens needs: rotated copies of q and k
- * (bf16, full rows) when RoPE is on, each rounded up to 256 bytes, followed
- * by the importance scratch: 256 x 16 x round64(seqlen) 4-byte words (one
- * 16-row slot per resident workgroup).  0 for invalid arguments. */
+ * (bf16, full rows) when RoPE is on, each rounded up to 256 bytes, then the
+ * log-sum-exp rows (fp32 [batch, seqlen, hq], rounded up to 256 bytes), then
+ * the importance scratch: 256 slots (one per resident workgroup) of 32 rows,
+ * each row round64(seqlen) 4-byte words plus a 4096-entry list of 8 bytes.
+ * The scratch grows linearly in seqlen and not with batch: about 2.4 GB at
+ * seqlen = 65536.  0 for invalid arguments. */
 size_t hswa_select_workspace_size(int batch, int seqlen, int hq, int hkv, int d_qk,
                                   float rotary_fraction);
 

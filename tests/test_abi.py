@@ -192,7 +192,10 @@ def test_select_validation(lib):
     assert call(frac=0.334) == INVALID                     # workspace missing
     assert call() == INVALID                               # importance scratch missing
     assert call(seqlen=0, q=None) == OK
-    scratch = 256 * 16 * 128 * 4                           # 16-row slots of round64(100) words
+    # log-sum-exp rows (fp32, rounded up to 256 bytes), then 256 slots of 32
+    # rows: round64(100) words and a 4096-entry list of 8 bytes per row
+    lse = (100 * 64 * 4 + 255) // 256 * 256
+    scratch = lse + 256 * 32 * (128 * 4 + 4096 * 8)
     size = hswa._binding.load().hswa_select_workspace_size
     assert size(1, 100, 64, 4, 192, 0.334) == 100 * 64 * 192 * 2 + 100 * 4 * 192 * 2 + scratch
     assert size(1, 100, 64, 4, 192, 0.0) == scratch
