@@ -105,6 +105,83 @@ __device__ __forceinline__ uint2 lds_tr4(const void* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// Decode lazy-rescaling threshold (log2 units): a running max moves only when
+// a tile's max passes it by more than this, so the probabilities stay
+// below 2^kDecLazy.
+constexpr float kDecLazy = 8.f;
+
+// Workgroup barrier without the release fence of __syncthreads(), which
+// would wait for every copy in flight; the caller waits with an explicit
+// vmcnt for the copies it needs, and its LDS writes that other wavefronts
+// read must be complete (lgkmcnt) before it.  The empty asm statements keep
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS reads of global_load_lds targets, written as inline asm with their own
+// lgkmcnt(0) wait.  The compiler's wait analysis would otherwise see a plain
+// read as one of memory that copies in flight may write and wait for every
+// copy (vmcnt(0)), also those issued for later tiles; the caller waits for
+// the copies of the tile it reads (s_waitcnt vmcnt) and a barrier.
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_b128x2(uint4& r0, uint4& r1, uint32_t a0, uint32_t a1) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1)
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+__device__ __forceinline__ void lds_b64x6(uint2 (&r)[6], const uint32_t (&a)[6]) {
+  asm volatile(
+      "ds_read_b64 %0, %6\n\t"
+      "ds_read_b64 %1, %7\n\t"
+      "ds_read_b64 %2, %8\n\t"
+      "ds_read_b64 %3, %9\n\t"
+      "ds_read_b64 %4, %10\n\t"
+      "ds_read_b64 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+      : "memory");
+}
+__device__ __forceinline__ void lds_b128x6(uint4 (&r)[6], const uint32_t (&a)[6]) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b128 %2, %8\n\t"
+      "ds_read_b128 %3, %9\n\t"
+      "ds_read_b128 %4, %10\n\t"
+      "ds_read_b128 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+      : "memory");
+}
+// Eight transposed 4 x 16-bit reads (as lds_tr4).
+__device__ __forceinline__ void lds_tr4x8(uint2 (&r)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
 // Codes 2w, 2w + 1 of the 4 E4M3 codes in v (w = 0 or 1) as a packed bf16
 // pair.  The hardware conversion to fp32 is exact, and every E4M3 value is a
 // bf16 value, so keeping the upper halves is exact too.

@@ -199,18 +199,26 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(AttnArgs a, int la
     for (int r = 0; r < 4; ++r) sc[r] = (k0 + 4 * grp + r < nkeys) ? sc[r] : kNegInf;
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = max_across_groups(mx) * c2;   // base-2 units
-    const float mn = fmaxf(m, mx);
-    const float ms = (mn == kNegInf) ? 0.f : mn;
-    const float alpha = fast_exp2(m - ms);
+    // Lazy rescaling: the reference m moves only when a column's tile max
+    // passes it by more than kDecLazy, so P = exp2(s - m) <= 2^kDecLazy
+    // (exact in fp32 and bf16's range); (m, l, O) stay consistent for the
+    // combine, which only needs them to share one reference.
+    if (__any(mx > m + kDecLazy)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - ((mn == kNegInf) ? 0.f : mn));
+      l *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) acc[tt] *= alpha;
+      m = mn;
+      asm volatile("s_nop 4" ::: "memory");   // the PV products read acc below
+    }
+    const float ms = (m == kNegInf) ? 0.f : m;
     float pv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(fmaf(sc[r], c2, -ms));
     const uint2 pk = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
     // l sums the bf16 P that weight V
-    l = l * alpha + add_bf16_pair(pk.y, add_bf16_pair(pk.x, 0.f));
-    m = mn;
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) acc[tt] *= alpha;
+    l += add_bf16_pair(pk.y, add_bf16_pair(pk.x, 0.f));
     const v4i16 pb = __builtin_bit_cast(v4i16, pk);
     // -- O^T += V^T . P^T: lane (c, grp) holds keys 4 grp + r, the k-index of
     //    the 16x16x16 form; the transposed read gives V[4 grp + r][16 tt + c]

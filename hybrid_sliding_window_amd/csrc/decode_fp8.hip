@@ -35,6 +35,7 @@ namespace {
 constexpr int D = 192;
 constexpr int DV = 128;
 constexpr int KS = D / 32;
+static_assert(KS == 6, "six k-steps of 32 dims");
 constexpr int NT = DV / 16;
 constexpr int BK = 16;                      // keys per tile
 constexpr int HG = 4;                       // kv heads per workgroup (one per wavefront)
@@ -54,11 +55,13 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 
 }  // namespace
 
+// Three LDS stages: tile t + 2 is requested while tile t is computed, so a
+// workgroup keeps two tiles (40 KB) of loads in flight, as the bf16 decode
+// does with its twice-as-large tiles; two workgroups share a compute unit.
+constexpr int NST = 3;
 __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, int layout) {
-  __shared__ __attribute__((aligned(16))) unsigned char kst0[KTILE8];
-  __shared__ __attribute__((aligned(16))) unsigned char vst0[VTILE8];
-  __shared__ __attribute__((aligned(16))) unsigned char kst1[KTILE8];
-  __shared__ __attribute__((aligned(16))) unsigned char vst1[VTILE8];
+  __shared__ __attribute__((aligned(16))) unsigned char kst[NST][KTILE8];
+  __shared__ __attribute__((aligned(16))) unsigned char vst[NST][VTILE8];
   __shared__ __attribute__((aligned(16))) unsigned char vwide[VTILEB];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
@@ -119,8 +122,6 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, in
   };
   static_assert(KINSTR / HG == 3, "the K/V split of a wavefront's loads");
 
-  issue(0, kst0, vst0);
-
   // q of head g*G + c (rotated to position p by the preparation kernel when
   // RoPE is on); columns c >= G are padding.
   bf16x8 qf[KS];
@@ -132,7 +133,11 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, in
       qf[ks] = as_bf16x8(c < G ? ld16(qrow + 32 * ks) : make_uint4(0, 0, 0, 0));
   }
   const float kscale = a.kscale[g], vscale = a.vscale[g];
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): q and tile 0 have landed
+  // q has landed before the first copies go out (a wait the compiler sees,
+  // so that it adds none of its own inside the tile loop)
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  issue(0, kst[0], vst[0]);
+  if (ntile > 1) issue(BK, kst[1], vst[1]);
 
   const float c2 = a.scale * kLog2e * kscale;   // raw code score -> base-2 units
   float m = kNegInf, l = 0.f;
@@ -150,46 +155,57 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, in
 
   auto tile = [&](int t, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
                   unsigned char* vn) __attribute__((always_inline)) {
-    // Tile t's loads are this wavefront's only ones in flight.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __syncthreads();   // every wavefront's share of tile t has landed; tile t-1 is consumed
-    if (t + 1 < ntile) issue((t + 1) * BK, kn, vn);
+    // This wavefront's loads in flight: tile t's, then (if it exists) tile
+    // t + 1's five.
+    if (t + 1 < ntile) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
+    ring_barrier();   // every wavefront's share of tile t has landed; tile t-1 is consumed
+    if (t + 2 < ntile) issue((t + 2) * BK, kn, vn);
     // widen this wavefront's V stripe; LDS operations of a wavefront complete
     // in order, so its transposed reads below see these writes
+    const int u0 = 8 * wave + 2 * grp;
+    uint4 codes[2];
+    lds_b128x2(codes[0], codes[1], lds_off(vc + c * VROW8 + 16 * (u0 ^ (c & 7))),
+               lds_off(vc + c * VROW8 + 16 * ((u0 + 1) ^ (c & 7))));
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int unit = 8 * wave + 2 * grp + j;
-      const uint4 codes = ld16(vc + c * VROW8 + 16 * (unit ^ (c & 7)));
-      unsigned char* dst = vwide + c * VROWB + 32 * (unit ^ (c & 7));
-      st16(dst, widen8(make_uint2(codes.x, codes.y)));
-      st16(dst + 16, widen8(make_uint2(codes.z, codes.w)));
+      unsigned char* dst = vwide + c * VROWB + 32 * ((u0 + j) ^ (c & 7));
+      st16(dst, widen8(make_uint2(codes[j].x, codes[j].y)));
+      st16(dst + 16, widen8(make_uint2(codes[j].z, codes[j].w)));
     }
     const int k0 = t * BK;
+    // dims 32 ks + 8 grp .. + 7: logical 16-byte chunk 12 wave + 2 ks + grp/2, half grp%2
+    uint32_t kad[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kad[ks] = lds_off(kc + krow + 16 * ((12 * wave + 2 * ks + (grp >> 1)) ^ c) + 8 * (grp & 1));
+    uint2 kw[KS];
+    lds_b64x6(kw, kad);
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      // dims 32 ks + 8 grp .. + 7: logical 16-byte chunk 12 wave + 2 ks + grp/2, half grp%2
-      const int lc = 12 * wave + 2 * ks + (grp >> 1);
-      const uint2 w = *reinterpret_cast<const uint2*>(kc + krow + 16 * (lc ^ c) + 8 * (grp & 1));
-      sc = mfma16(as_bf16x8(widen8(w)), qf[ks], sc);
-    }
+    for (int ks = 0; ks < KS; ++ks) sc = mfma16(as_bf16x8(widen8(kw[ks])), qf[ks], sc);
     // Branch-free on purpose (MFMA result read by the VALU right after).
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[r] = (k0 + 4 * grp + r < nkeys) ? sc[r] : kNegInf;
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = max_across_groups(mx) * c2;   // base-2 units
-    const float mn = fmaxf(m, mx);
-    const float ms = (mn == kNegInf) ? 0.f : mn;
-    const float alpha = fast_exp2(m - ms);
+    // lazy rescaling, as the bf16 decode
+    if (__any(mx > m + kDecLazy)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - ((mn == kNegInf) ? 0.f : mn));
+      l *= alpha;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) acc[tt] *= alpha;
+      m = mn;
+      asm volatile("s_nop 4" ::: "memory");   // the PV products read acc below
+    }
+    const float ms = (m == kNegInf) ? 0.f : m;
     float pv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(fmaf(sc[r], c2, -ms));
     const uint2 pk = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
     // l sums the bf16 P that weight V
-    l = l * alpha + add_bf16_pair(pk.y, add_bf16_pair(pk.x, 0.f));
-    m = mn;
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) acc[tt] *= alpha;
+    l += add_bf16_pair(pk.y, add_bf16_pair(pk.x, 0.f));
     const v4i16_t pb = __builtin_bit_cast(v4i16_t, pk);
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
@@ -199,12 +215,15 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, in
     }
   };
 
-  int t = 0;
-  for (; t + 2 <= ntile; t += 2) {
-    tile(t, kst0, vst0, kst1, vst1);
-    tile(t + 1, kst1, vst1, kst0, vst0);
+  // tile t sits in stage t % 3; tile t + 2 goes to stage (t + 2) % 3, the
+  // one tile t - 1 used
+  static_assert(DMA_PER_WAVE == 5, "the waits count five loads per tile");
+  int st = 0;
+  for (int t = 0; t < ntile; ++t) {
+    const int sn = (st == 0) ? 2 : st - 1;
+    tile(t, kst[st], vst[st], kst[sn], vst[sn]);
+    st = (st == NST - 1) ? 0 : st + 1;
   }
-  if (t < ntile) tile(t, kst0, vst0, kst1, vst1);
 
   l = sum_across_groups(l);
   if (g < a.hkv && c < G) {

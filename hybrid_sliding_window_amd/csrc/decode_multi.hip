@@ -30,7 +30,9 @@ namespace {
 constexpr int D = 192;
 constexpr int DV = 128;
 constexpr int KS = D / 32;
+static_assert(KS == 6, "six k-steps of 32 dims");
 constexpr int NT = DV / 16;
+static_assert(NT == 8, "eight 16-dim output tiles");
 constexpr int BK = 16;                    // keys per tile
 constexpr int HG = 4;                     // kv heads per workgroup
 constexpr int KROW = HG * D * 2;          // 1536 B: the group's K of one cache row
@@ -120,18 +122,25 @@ __global__ __launch_bounds__(64) void decode_multi_rope_q_kernel(AttnArgs a, int
   }
 }
 
+// s_waitcnt operand with vmcnt n (0..63) and the other counters open.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 // NB: 16-column blocks per wavefront; CW: wavefronts per kv head (each with
-// NB * 16 of the T * G columns).
-template <int NB, int CW>
-__global__ __launch_bounds__(256 * CW, 3 - CW) void decode_multi_split_kernel(AttnArgs a,
-                                                                                int layout) {
+// NB * 16 of the T * G columns); NST: LDS stages of 40 KB.  Long splits take
+// four stages, which fill the compute unit's 160 KB: tiles t + 1 .. t + 3
+// are in flight while tile t is computed (120 KB of loads per compute unit,
+// one workgroup each).  Short splits (a ring of a few tiles) take two, so
+// that two workgroups of four wavefronts share a compute unit.
+template <int NB, int CW, int NST>
+__global__ __launch_bounds__(256 * CW, (NST == 2 && CW == 1) ? 2 : 1) void decode_multi_split_kernel(
+    AttnArgs a, int layout) {
   constexpr int NWAVE = HG * CW;
   constexpr int DMA_PER_WAVE = (KINSTR + VINSTR) / NWAVE;
   static_assert((KINSTR + VINSTR) % NWAVE == 0 && KINSTR % NWAVE == 0, "even split of the loads");
-  __shared__ __attribute__((aligned(16))) unsigned char kst0[KTILE];
-  __shared__ __attribute__((aligned(16))) unsigned char vst0[VTILE];
-  __shared__ __attribute__((aligned(16))) unsigned char kst1[KTILE];
-  __shared__ __attribute__((aligned(16))) unsigned char vst1[VTILE];
+  static_assert(DMA_PER_WAVE * (NST - 2) <= 63, "the vmcnt field holds the loads in flight");
+  static_assert(NST == 2 || NST == 4, "stage arithmetic below");
+  __shared__ __attribute__((aligned(16))) unsigned char kst[NST][KTILE];
+  __shared__ __attribute__((aligned(16))) unsigned char vst[NST][VTILE];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
   const int hw = wave % HG, ch = wave / HG;                     // kv head in group, column half
@@ -187,8 +196,6 @@ __global__ __launch_bounds__(256 * CW, 3 - CW) void decode_multi_split_kernel(At
     }
   };
 
-  issue(0, kst0, vst0);
-
   // ---- this lane's query columns: n = 16 (NB ch + nb) + c -------------------
   bf16x8 qf[NB][KS];
   int ctok[NB];
@@ -208,7 +215,10 @@ __global__ __launch_bounds__(256 * CW, 3 - CW) void decode_multi_split_kernel(At
         qf[nb][ks] = as_bf16x8(cval[nb] ? ld16(qrow + 32 * ks) : make_uint4(0, 0, 0, 0));
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): q and tile 0 have landed
+  // q has landed before the first copies go out (a wait the compiler sees,
+  // so that it adds none of its own inside the tile loop)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  for (int t = 0; t < NST - 1 && t < ntile; ++t) issue(t * BK, kst[t], vst[t]);
 
   const float c2 = a.scale * kLog2e;
   const int W = a.window;
@@ -228,9 +238,14 @@ __global__ __launch_bounds__(256 * CW, 3 - CW) void decode_multi_split_kernel(At
 
   auto tile = [&](int t, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
                   unsigned char* vn) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile t's loads are this wavefront's only ones
-    __syncthreads();   // every wavefront's share of tile t has landed; tile t-1 is consumed
-    if (t + 1 < ntile) issue((t + 1) * BK, kn, vn);
+    // this wavefront's loads issued after tile t's: those of the (up to
+    // NST - 2) tiles after it
+    const int ahead = min(ntile - 1 - t, NST - 2);
+    if (NST == 4 && ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_WAVE));
+    else if (NST == 4 && ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMA_PER_WAVE));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    ring_barrier();   // every wavefront's share of tile t has landed; tile t-1 is consumed
+    if (t + NST - 1 < ntile) issue((t + NST - 1) * BK, kn, vn);
     const int k0 = t * BK;
     // key 4 grp + r of the tile is visible to column token tn iff it exists
     // and its position lies in [p0 + tn - W + 1, p0 + tn].  Decided before the
@@ -249,13 +264,15 @@ __global__ __launch_bounds__(256 * CW, 3 - CW) void decode_multi_split_kernel(At
     f32x4 sc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint32_t kad[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int q = 24 * hw + 4 * ks + grp;
-      const bf16x8 kf = as_bf16x8(ld16(kc + krow + 16 * (q ^ c)));
+    for (int ks = 0; ks < KS; ++ks) kad[ks] = lds_off(kc + krow + 16 * ((24 * hw + 4 * ks + grp) ^ c));
+    uint4 kf[KS];
+    lds_b128x6(kf, kad);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma16(kf, qf[nb][ks], sc[nb]);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma16(as_bf16x8(kf[ks]), qf[nb][ks], sc[nb]);
     uint2 pk[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -263,35 +280,43 @@ __global__ __launch_bounds__(256 * CW, 3 - CW) void decode_multi_split_kernel(At
       for (int r = 0; r < 4; ++r) sc[nb][r] = vis[nb][r] ? sc[nb][r] : kNegInf;
       float mx = fmaxf(fmaxf(sc[nb][0], sc[nb][1]), fmaxf(sc[nb][2], sc[nb][3]));
       mx = max_across_groups(mx) * c2;
-      const float mn = fmaxf(m[nb], mx);
-      const float ms = (mn == kNegInf) ? 0.f : mn;
-      const float alpha = fast_exp2(m[nb] - ms);
+      // lazy rescaling, as the single-token decode
+      if (__any(mx > m[nb] + kDecLazy)) {
+        const float mn = fmaxf(m[nb], mx);
+        const float alpha = fast_exp2(m[nb] - ((mn == kNegInf) ? 0.f : mn));
+        l[nb] *= alpha;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) acc[tt][nb] *= alpha;
+        m[nb] = mn;
+        asm volatile("s_nop 4" ::: "memory");   // the PV products read acc below
+      }
+      const float ms = (m[nb] == kNegInf) ? 0.f : m[nb];
       float pv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(fmaf(sc[nb][r], c2, -ms));
       pk[nb] = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
-      l[nb] = l[nb] * alpha + add_bf16_pair(pk[nb].y, add_bf16_pair(pk[nb].x, 0.f));
-      m[nb] = mn;
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) acc[tt][nb] *= alpha;
+      l[nb] += add_bf16_pair(pk[nb].y, add_bf16_pair(pk[nb].x, 0.f));
     }
+    uint32_t vad[NT];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      const uint2 vt = lds_tr4(vc + vrow + 32 * ((8 * hw + tt) ^ (vr & 7)));
+    for (int tt = 0; tt < NT; ++tt) vad[tt] = lds_off(vc + vrow + 32 * ((8 * hw + tt) ^ (vr & 7)));
+    uint2 vt[NT];
+    lds_tr4x8(vt, vad);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         acc[tt][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            __builtin_bit_cast(v4i16_t, vt), __builtin_bit_cast(v4i16_t, pk[nb]), acc[tt][nb], 0,
-            0, 0);
-    }
+            __builtin_bit_cast(v4i16_t, vt[tt]), __builtin_bit_cast(v4i16_t, pk[nb]), acc[tt][nb],
+            0, 0, 0);
   };
 
-  int t = 0;
-  for (; t + 2 <= ntile; t += 2) {
-    tile(t, kst0, vst0, kst1, vst1);
-    tile(t + 1, kst1, vst1, kst0, vst0);
+  // tile t sits in stage t % NST; tile t + NST - 1 goes to the stage tile
+  // t - 1 used
+  for (int t = 0; t < ntile; ++t) {
+    const int st = t & (NST - 1), sn = (t + NST - 1) & (NST - 1);
+    tile(t, kst[st], vst[st], kst[sn], vst[sn]);
   }
-  if (t < ntile) tile(t, kst0, vst0, kst1, vst1);
 
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -448,14 +473,22 @@ hipError_t launch_decode_multi(const AttnArgs& a, int layout, hipStream_t stream
   }
   const int cols = a.nq * (a.hq / a.hkv);
   const dim3 g1((unsigned)(a.hkv / HG), (unsigned)a.nsplit, (unsigned)a.B);
-  if (cols <= 16)
-    hipLaunchKernelGGL((decode_multi_split_kernel<1, 1>), g1, dim3(256), 0, stream, a, layout);
-  else if (cols <= 32)
-    hipLaunchKernelGGL((decode_multi_split_kernel<2, 1>), g1, dim3(256), 0, stream, a, layout);
-  else
-    hipLaunchKernelGGL((decode_multi_split_kernel<2, 2>), g1, dim3(512), 0, stream, a, layout);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // four stages once a split spans at least 32 tiles
+  const bool deep = a.split_keys >= 32 * BK;
+  if (cols <= 16) {
+    if (deep) hipLaunchKernelGGL((decode_multi_split_kernel<1, 1, 4>), g1, dim3(256), 0, stream, a, layout);
+    else hipLaunchKernelGGL((decode_multi_split_kernel<1, 1, 2>), g1, dim3(256), 0, stream, a, layout);
+  } else if (cols <= 32) {
+    if (deep) hipLaunchKernelGGL((decode_multi_split_kernel<2, 1, 4>), g1, dim3(256), 0, stream, a, layout);
+    else hipLaunchKernelGGL((decode_multi_split_kernel<2, 1, 2>), g1, dim3(256), 0, stream, a, layout);
+  } else {
+    if (deep) hipLaunchKernelGGL((decode_multi_split_kernel<2, 2, 4>), g1, dim3(512), 0, stream, a, layout);
+    else hipLaunchKernelGGL((decode_multi_split_kernel<2, 2, 2>), g1, dim3(512), 0, stream, a, layout);
+  }
+  {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(decode_multi_combine_kernel, rows, dim3(64), 0, stream, a, layout);
   return hipGetLastError();
 }

@@ -40,16 +40,6 @@ __device__ __forceinline__ void g2lds16_nt(const void* src, void* lds_base) {
 }
 
 
-// Workgroup barrier without the release fence of __syncthreads(), which
-// would wait for every copy in flight; the caller waits with an explicit
-// vmcnt for the copies it needs.  The empty asm statements keep the
-// compiler from moving LDS accesses across it.
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 constexpr float kLazy = 8.f;
 
 // vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt bits

@@ -717,6 +717,25 @@ def test_multi_decode_contract_violations_give_nan(gpu_lib):
     assert np.isfinite(on[0]).all() and np.isnan(on[1]).all()
 
 
+@pytest.mark.parametrize("T,hq,hkv", [(2, 32, 4), (4, 32, 4)])
+def test_multi_decode_long_splits(gpu_lib, T, hq, hkv):
+    """Splits of at least 32 tiles run the four-stage kernels: 16 and 32
+    query columns per kv head (the 64-column one is the full-size case)."""
+    pos = torch.tensor([33001, 40006])
+    c = synthetic.multi_contiguous_inputs(2, T, hq, hkv, 192, 128, "bf16", 231, pos, DEV, None)
+    maxp = int(pos.max()) + T - 1
+    o = gpu_lib.swa_sink_decode_multi(c["q"], c["k"], c["v"], c["pos"], maxp,
+                                      layout=gpu_lib.KV_CONTIGUOUS, seq_offsets=c["seq_offsets"],
+                                      window=0)
+    offs = c["seq_offsets"].cpu().numpy()
+    for b in range(2):
+        lo, hi = int(offs[b]), int(offs[b + 1])
+        refb = oracle.decode_multi_contiguous(_np(c["q"][b:b + 1]), _np(c["k"][lo:hi]),
+                                              _np(c["v"][lo:hi]), np.array([0, hi - lo]),
+                                              pos.numpy()[b:b + 1])
+        _check(f"multi decode long splits T={T} hq={hq} (sequence {b})", o[b:b + 1], refb)
+
+
 def test_mtp_decode_full_size(gpu_lib):
     wl = synthetic.WORKLOADS["mtp_decode_b64_t4"]
     T = wl["T"]
