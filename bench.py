@@ -736,8 +736,8 @@ def _select(out, dev):
     i = np.arange(wl["n"], dtype=np.int64)
     causal = int((i + 1).sum())
     cand = int(np.maximum(0, i - wl["recent"] + 1).sum())
-    # two passes of score products: log-sum-exp over keys 0 .. i, then the
-    # importances of the candidates (the two later passes read them back)
+    # two passes of score products: log-sum-exp over keys 0 .. i (its own
+    # kernel), then the importances of the candidates (read back once)
     flops = (causal + cand) * wl["hq"] * 2 * 192
     out["select_tokens_n65536"] = {"ms": t * 1e3, "qk_tflops": flops / t / 1e12,
                                    "rows_per_s": wl["n"] * wl["hkv"] / t,
