@@ -1106,8 +1106,10 @@ def test_select_tokens(gpu_lib, B, n, hkv, recent, K, frac):
     x = synthetic.prefill_inputs(B, n, hq, hkv, 192, 128, "bf16", 240 + n, DEV, None)
     idx, cnt = gpu_lib.sparse_select_tokens(x["q"], x["k"], max_sel=K, recent_window=recent,
                                             rope_theta=1.0e7, rotary_fraction=frac)
+    # with RoPE the rotated dims enter the products as bf16: the floor that
+    # alone causes (tests/test_tolerance_floor.py) sets the bar
     _check_selection(f"select B={B} n={n} hkv={hkv} recent={recent} K={K}", idx, cnt, _np(x["q"]),
-                     _np(x["k"]), np.arange(n), recent, K, frac)
+                     _np(x["k"]), np.arange(n), recent, K, frac, tol=3e-3 if frac > 0 else 1e-3)
 
 
 def test_select_tokens_ties_and_empty(gpu_lib):

@@ -14,6 +14,8 @@ and 5) takes its bars from this measurement:
     |o| ~ 4, where a score error of 2^-9 relative moves o visibly), so the
     case is held to 5e-2 max-abs, at least 1.4 times the floor measured
     here, and to the standard 5e-3 rel-L2.
+The token-selection parity check with RoPE takes its inversion bar the same
+way (the last test below).
 """
 
 import numpy as np
@@ -62,3 +64,59 @@ def test_sink_case_floor_sets_the_bars():
         # ... and the bar used instead leaves room above the floor
         assert SINK_CASE_MAXABS_Q4 >= 1.4 * mx4
         assert rl2_4 < BF16_RL2
+
+
+# ---------------------------------------------------------------------------
+# Token selection with RoPE: the inversion bf16 rotated operands cause
+# ---------------------------------------------------------------------------
+
+# the bars tests/test_parity.py's _check_selection applies: without RoPE the
+# kernel's operands are the exact bf16 inputs (no floor), with RoPE the
+# rotated dims are rounded to bf16
+SELECTION_INVERSION_BAR = 1e-3
+SELECTION_INVERSION_BAR_ROPE = 3e-3
+
+
+def _selection_floor(seed, B=2, n=211, hkv=2, recent=32, K=64, frac=0.334, theta=1.0e7):
+    """Worst relative inversion of a selection made from importances whose
+    rotated q and k dims were rounded to bf16 (what a kernel feeding bf16
+    matrix products must do), judged by the exact importances ("MiMo-V3
+    HySparse2" (aideepthink.cn), section 4, under the summed-probability
+    reading of the importance)."""
+    hq = 16 * hkv
+    x = synthetic.prefill_inputs(B, n, hq, hkv, 192, 128, "bf16", seed, "cpu", None)
+    q, k = x["q"].double().numpy(), x["k"].double().numpy()
+    R = oracle.rotary_dims(192, frac)
+    pos = np.arange(n)
+    qr = np.stack([oracle.rope(q[b], pos, theta, frac) for b in range(B)])
+    kr = np.stack([oracle.rope(k[b], pos, theta, frac) for b in range(B)])
+    qr[..., :R] = _bf16(qr[..., :R])
+    kr[..., :R] = _bf16(kr[..., :R])
+    worst = 0.0
+    for b in range(B):
+        for i in range(n):
+            for g in range(hkv):
+                ncand = max(0, i - recent + 1)
+                if ncand <= K:
+                    continue
+                exact = oracle.selection_importance(q, k, b, i, g, recent, rope_theta=theta,
+                                                    rotary_fraction=frac)
+                emu = oracle.selection_importance(qr, kr, b, i, g, recent, rotary_fraction=0.0)
+                chosen = np.lexsort((np.arange(ncand), -emu))[:K]
+                mask = np.zeros(ncand, bool)
+                mask[chosen] = True
+                lo, hi = exact[mask].min(), exact[~mask].max()
+                worst = max(worst, (hi - lo) / lo)
+    return worst
+
+
+def test_selection_rope_floor_sets_the_bar():
+    """With RoPE, rounding the rotated q and k dims to bf16 alone reorders
+    candidates by up to ~1.3e-3 relative (12 seeds of this shape: 4.8e-4 ..
+    1.3e-3), above the 1e-3 bar of the cases without RoPE, which a
+    bf16-operand kernel therefore cannot be held to.  The RoPE cases take
+    3e-3, at least twice the floor measured here."""
+    floors = [_selection_floor(seed) for seed in range(451, 459)]
+    print(f"[floor] selection with RoPE: worst inversions {['%.2e' % f for f in floors]}", flush=True)
+    assert max(floors) > SELECTION_INVERSION_BAR          # the no-RoPE bar is out of reach ...
+    assert SELECTION_INVERSION_BAR_ROPE >= 2.0 * max(floors)   # ... the RoPE bar leaves room
