@@ -242,12 +242,200 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, in
   }
 }
 
+// Rings of at most 128 slots in one launch (as the bf16 decode's
+// decode_ring_kernel): a workgroup per (sequence, kv head), wavefront w on
+// slots 32 w .. 32 w + 31.  Every copy of a wavefront's slots goes out at
+// once into its own LDS region (6 KB of K codes, rows of 192 B; 4 KB of V
+// codes, rows of 128 B); the wavefront widens its V codes into a bf16 copy
+// laid out like the bf16 ring kernel's V (rows of 256 B, 32-byte unit u at
+// u ^ (row & 7)) for the transposed reads, computes its two 16-key tiles,
+// and the four partials (m, l, O) are merged in LDS with the sink added
+// once.  k_scale folds into the base-2 score factor, v_scale multiplies the
+// merged output.
+constexpr int RG_ROWS = 32;                  // ring slots per wavefront
+constexpr int RG_K8 = RG_ROWS * D;           // 6 KB of K codes
+constexpr int RG_V8 = RG_ROWS * DV;          // 4 KB of V codes
+constexpr int RG_VB = RG_ROWS * DV * 2;      // 8 KB of widened V
+constexpr int RG_REG = RG_K8 + RG_V8 + RG_VB;
+static_assert(RG_REG >= 16 * DV * 4 + 32 * 4, "a region holds a wavefront's partial for the merge");
+
+__global__ __launch_bounds__(256, 2) void decode_ring_fp8_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char reg_all[4 * RG_REG];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, c = lane & 15, grp = lane >> 4;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int G = a.hq / a.hkv;
+  unsigned char* kreg = reg_all + wave * RG_REG;
+  unsigned char* vreg = kreg + RG_K8;
+  unsigned char* vwb = vreg + RG_V8;
+
+  long long p, row0, len;
+  if (!key_range(a, 0, b, &p, &row0, &len)) {   // uniform over the workgroup
+    if (c < G) {   // a broken contract: NaN outputs
+      bf16_t* orow = static_cast<bf16_t*>(a.o) + ((long long)b * a.hq + g * G + c) * DV + 32 * wave + 8 * grp;
+      st16(orow, make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u));
+    }
+    return;
+  }
+  const int key0 = RG_ROWS * wave;             // this wavefront's first slot
+  const int nk = (int)min((long long)RG_ROWS, max(0LL, len - key0));   // its valid slots
+
+  // ---- copies: K slot s = 64 ii + lane (ii < 6) is row s / 12, 16-byte
+  // chunk s % 12; V slot s = 64 jj + lane (jj < 4) is row s / 8, chunk s % 8.
+  // Rows past the last valid slot reload the last one (finite data, masked).
+  if (nk > 0) {
+    const unsigned char* kb = static_cast<const unsigned char*>(a.k) + (row0 * a.hkv + g) * (long long)D;
+    const unsigned char* vb = static_cast<const unsigned char*>(a.v) + (row0 * a.hkv + g) * (long long)DV;
+    const int kstr = a.hkv * D, vstr = a.hkv * DV;
+#pragma unroll
+    for (int ii = 0; ii < RG_K8 / 1024; ++ii) {
+      const int sl = 64 * ii + lane;
+      const int row = sl / 12, pc = sl - row * 12;
+      const int key = key0 + min(row, nk - 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(kb + (__umul24(key, kstr) + 16 * pc)),
+                                       (lds_void_t*)(kreg + 1024 * ii), 16, 0, 0);
+    }
+#pragma unroll
+    for (int jj = 0; jj < RG_V8 / 1024; ++jj) {
+      const int sl = 64 * jj + lane;
+      const int row = sl >> 3, pc = sl & 7;
+      const int key = key0 + min(row, nk - 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (__umul24(key, vstr) + 16 * pc)),
+                                       (lds_void_t*)(vreg + 1024 * jj), 16, 0, 0);
+    }
+  }
+
+  // q of head g*G + c (rotated to position p by the preparation kernel when
+  // RoPE is on); columns c >= G are padding
+  bf16x8 qf[KS];
+  {
+    const bf16_t* qsrc = static_cast<const bf16_t*>(a.half > 0 ? a.qrot : a.q);
+    const bf16_t* qrow = qsrc + ((long long)b * a.hq + g * G + min(c, G - 1)) * D + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = as_bf16x8(c < G ? ld16(qrow + 32 * ks) : make_uint4(0, 0, 0, 0));
+  }
+  const float kscale = a.kscale[g], vscale = a.vscale[g];
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): q and this wavefront's slots have landed
+
+  // widen the V codes: lane handles (row, 16-code chunk) items lane + 64 j
+  if (nk > 0) {
+#pragma unroll
+    for (int j = 0; j < RG_ROWS * DV / 16 / 64; ++j) {
+      const int it = lane + 64 * j;
+      const int row = it >> 3, cc = it & 7;
+      const uint4 codes = ld16(vreg + row * DV + 16 * cc);
+      unsigned char* dst = vwb + row * (DV * 2) + 32 * (cc ^ (row & 7));
+      st16(dst, widen8(make_uint2(codes.x, codes.y)));
+      st16(dst + 16, widen8(make_uint2(codes.z, codes.w)));
+    }
+  }
+
+  const float c2 = a.scale * kLog2e * kscale;   // raw code score -> base-2 units
+  float m = kNegInf, l = 0.f;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int t = 0; t < RG_ROWS / BK; ++t) {
+    if (t * BK >= nk) break;   // uniform
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int kr = BK * t + c;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      // dims 32 ks + 8 grp .. + 7 of key row kr: 8 codes
+      const uint2 w = *reinterpret_cast<const uint2*>(kreg + kr * D + 32 * ks + 8 * grp);
+      sc = mfma16(as_bf16x8(widen8(w)), qf[ks], sc);
+    }
+    // branch-free masking (see the split kernels)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = (BK * t + 4 * grp + r < nk) ? sc[r] : kNegInf;
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = max_across_groups(mx) * c2;
+    const float mn = fmaxf(m, mx);
+    const float ms = (mn == kNegInf) ? 0.f : mn;
+    const float alpha = fast_exp2(m - ms);
+    float pv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(fmaf(sc[r], c2, -ms));
+    const uint2 pk = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
+    l = l * alpha + add_bf16_pair(pk.y, add_bf16_pair(pk.x, 0.f));
+    m = mn;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] *= alpha;
+    const v4i16_t pb = __builtin_bit_cast(v4i16_t, pk);
+    const int vr = BK * t + 4 * grp + (c >> 2);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const uint2 vt = lds_tr4(vwb + vr * (DV * 2) + 32 * (tt ^ (vr & 7)) + 8 * (c & 3));
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16_t, vt), pb,
+                                                         acc[tt], 0, 0, 0);
+    }
+  }
+  l = sum_across_groups(l);
+
+  // ---- merge the four wavefronts' partials (O [16 columns][128 dims], m and
+  // l [16], fp32, base 2, in each wavefront's own region); then wavefront w
+  // writes dims 32 w .. 32 w + 31
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  float* po = reinterpret_cast<float*>(kreg);
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt)
+    *reinterpret_cast<float4*>(po + c * DV + 16 * tt + 4 * grp) =
+        make_float4(acc[tt][0], acc[tt][1], acc[tt][2], acc[tt][3]);
+  if (grp == 0) {
+    po[16 * DV + c] = m;
+    po[16 * DV + 16 + c] = l;
+  }
+  __syncthreads();
+  const float s2 = (c < G && a.sink) ? a.sink[g * G + c] * kLog2e : kNegInf;
+  float mw[4], lw[4];
+  float M = s2;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float* pw = reinterpret_cast<const float*>(reg_all + w * RG_REG);
+    mw[w] = pw[16 * DV + c];
+    lw[w] = pw[16 * DV + 16 + c];
+    M = fmaxf(M, mw[w]);
+  }
+  float den = (s2 > kNegInf) ? fast_exp2(s2 - M) : 0.f;
+  float o8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o8[e] = 0.f;
+  const int d0 = 32 * wave + 8 * grp;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float sw = (mw[w] > kNegInf) ? fast_exp2(mw[w] - M) : 0.f;
+    den += sw * lw[w];
+    const float* pw = reinterpret_cast<const float*>(reg_all + w * RG_REG) + c * DV + d0;
+    const float4 x0 = *reinterpret_cast<const float4*>(pw);
+    const float4 x1 = *reinterpret_cast<const float4*>(pw + 4);
+    o8[0] += sw * x0.x; o8[1] += sw * x0.y; o8[2] += sw * x0.z; o8[3] += sw * x0.w;
+    o8[4] += sw * x1.x; o8[5] += sw * x1.y; o8[6] += sw * x1.z; o8[7] += sw * x1.w;
+  }
+  if (c < G) {
+    const float inv = (den > 0.f) ? vscale / den : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o8[e] *= inv;
+    bf16_t* orow = static_cast<bf16_t*>(a.o) + ((long long)b * a.hq + g * G + c) * DV + d0;
+    st16(orow, pack8(o8));
+  }
+}
+
 bool decode_fp8_supported(const AttnArgs& a) { return decode_bf16_supported(a); }
 
 hipError_t launch_decode_fp8(const AttnArgs& a, int layout, hipStream_t stream) {
   if (a.B == 0) return hipSuccess;
   hipError_t e = launch_decode_rope_q(a, layout, stream);
   if (e != hipSuccess) return e;
+  if (decode_ring_supported(a, layout)) {
+    hipLaunchKernelGGL(decode_ring_fp8_kernel, dim3((unsigned)a.hkv, (unsigned)a.B), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
   dim3 g1((unsigned)(a.hkv / HG), (unsigned)a.nsplit, (unsigned)a.B);
   hipLaunchKernelGGL(decode_fp8_split_kernel, g1, dim3(256), 0, stream, a, layout);
   e = hipGetLastError();

@@ -88,6 +88,9 @@ hipError_t launch_prefill_causal(const AttnArgs& a, hipStream_t stream);
 bool decode_bf16_supported(const AttnArgs& a);
 void decode_split_plan(int layout, int window, long long max_pos, int* split_keys, int* nsplit);
 hipError_t launch_decode_bf16(const AttnArgs& a, int layout, hipStream_t stream);
+// Rings of at most 128 slots (and head shapes the matrix-core decode takes)
+// run in one launch, without split partials.
+bool decode_ring_supported(const AttnArgs& a, int layout);
 // The two kernels around a decode split kernel: q rotated to its position
 // (no-op without RoPE) and the combine of the split partials with the sink.
 hipError_t launch_decode_rope_q(const AttnArgs& a, int layout, hipStream_t stream);
