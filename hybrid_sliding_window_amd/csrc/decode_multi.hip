@@ -457,6 +457,228 @@ __global__ __launch_bounds__(64) void decode_multi_generic_kernel(AttnArgs a, in
   }
 }
 
+// Ring caches of at most 160 slots in one launch: a workgroup per
+// (sequence, kv head), wavefront w on slots 32 w .. 32 w + 31 (five
+// wavefronts).  Every copy of a wavefront's slots goes out at once into its
+// own LDS region (the single-token ring kernel's layout: K rows of 384 B
+// with 16-byte chunk c at c ^ ((row >> 1) & 7), V rows of 256 B with 32-byte
+// unit u at u ^ (row & 7)); the wavefront runs its (at most two) 16-key
+// tiles over all T * G query columns of the kv head (NB blocks of 16) with
+// the split kernel's visibility rule; the five partials (m, l, O) per
+// column are merged in LDS with the sink added once, as the combine does.
+constexpr int MR_ROWS = 32;                  // ring slots per wavefront
+constexpr int MR_NW = 5;                     // wavefronts per workgroup
+constexpr int MR_K = MR_ROWS * D * 2;        // 12 KB
+constexpr int MR_V = MR_ROWS * DV * 2;       // 8 KB
+constexpr int MR_REG = MR_K + MR_V;
+static_assert(MR_REG >= 32 * DV * 4 + 64 * 4, "a region holds a wavefront's partial for the merge");
+
+template <int NB>
+__global__ __launch_bounds__(64 * MR_NW, 1) void decode_multi_ring_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char reg_all[MR_NW * MR_REG];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, c = lane & 15, grp = lane >> 4;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int G = a.hq / a.hkv, T = a.nq, W = a.window;
+  unsigned char* kreg = reg_all + wave * MR_REG;
+  unsigned char* vreg = kreg + MR_K;
+
+  long long p0, row0, len;
+  if (!multi_range(a, 0, b, &p0, &row0, &len)) {   // uniform over the workgroup
+    // a broken contract: NaN outputs (wavefronts 0..3 own 32 dims each)
+    if (wave < 4) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int n = 16 * nb + c;
+        if (n < T * G) {
+          const int tn = n / G, hn = n - tn * G;
+          bf16_t* orow = static_cast<bf16_t*>(a.o) +
+                         (((long long)b * T + tn) * a.hq + g * G + hn) * DV + 32 * wave + 8 * grp;
+          st16(orow, make_uint4(0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u));
+        }
+      }
+    }
+    return;
+  }
+  const int key0 = MR_ROWS * wave;             // this wavefront's first slot
+  const int nk = (int)min((long long)MR_ROWS, max(0LL, len - key0));   // its valid slots
+
+  if (nk > 0) {
+    const unsigned char* kb = static_cast<const unsigned char*>(a.k) + (row0 * a.hkv + g) * (long long)(D * 2);
+    const unsigned char* vb = static_cast<const unsigned char*>(a.v) + (row0 * a.hkv + g) * (long long)(DV * 2);
+    const int kstr = a.hkv * D * 2, vstr = a.hkv * DV * 2;
+#pragma unroll
+    for (int ii = 0; ii < MR_K / 1024; ++ii) {
+      const int sl = 64 * ii + lane;
+      const int row = sl / 24, pc = sl - row * 24;
+      const int lc = pc ^ ((row >> 1) & 7);
+      const int key = key0 + min(row, nk - 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(kb + (__umul24(key, kstr) + 16 * lc)),
+                                       (lds_void_t*)(kreg + 1024 * ii), 16, 0, 0);
+    }
+#pragma unroll
+    for (int jj = 0; jj < MR_V / 1024; ++jj) {
+      const int sl = 64 * jj + lane;
+      const int row = sl >> 4, pc = sl & 15;
+      const int lc = 2 * ((pc >> 1) ^ (row & 7)) + (pc & 1);
+      const int key = key0 + min(row, nk - 1);
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (__umul24(key, vstr) + 16 * lc)),
+                                       (lds_void_t*)(vreg + 1024 * jj), 16, 0, 0);
+    }
+  }
+
+  // this lane's query columns: n = 16 nb + c (token n / G, head n % G)
+  bf16x8 qf[NB][KS];
+  int ctok[NB];
+  bool cval[NB];
+  {
+    const bf16_t* qsrc = static_cast<const bf16_t*>(a.half > 0 ? a.qrot : a.q);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = 16 * nb + c;
+      cval[nb] = n < T * G;
+      const int tn = cval[nb] ? n / G : 0, hn = cval[nb] ? n - tn * G : 0;
+      ctok[nb] = tn;
+      const bf16_t* qrow = qsrc + (((long long)b * T + tn) * a.hq + g * G + hn) * D + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[nb][ks] = as_bf16x8(cval[nb] ? ld16(qrow + 32 * ks) : make_uint4(0, 0, 0, 0));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // q and this wavefront's slots have landed
+
+  const KeyPos kpos = key_pos(a, 0, p0, row0, 0);
+  const float c2 = a.scale * kLog2e;
+  float m[NB], l[NB];
+  f32x4 acc[NT][NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m[nb] = kNegInf;
+    l[nb] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+#pragma unroll
+  for (int t = 0; t < MR_ROWS / BK; ++t) {
+    if (t * BK >= nk) break;   // uniform
+    // visibility of slot key0 + 16 t + 4 grp + r to column token tn, decided
+    // before the score products (see the split kernel)
+    bool vis[NB][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int kk = BK * t + 4 * grp + r;
+      const int rel = (int)(kpos(key0 + kk) - p0);
+      const bool here = kk < nk;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        vis[nb][r] = here & (rel <= ctok[nb]) & ((W == 0) | (rel > ctok[nb] - W));
+    }
+    f32x4 sc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int kr = BK * t + c;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int pcq = (4 * ks + grp) ^ ((kr >> 1) & 7);
+      const bf16x8 kf = as_bf16x8(ld16(kreg + kr * (D * 2) + 16 * pcq));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma16(kf, qf[nb][ks], sc[nb]);
+    }
+    uint2 pk[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[nb][r] = vis[nb][r] ? sc[nb][r] : kNegInf;
+      float mx = fmaxf(fmaxf(sc[nb][0], sc[nb][1]), fmaxf(sc[nb][2], sc[nb][3]));
+      mx = max_across_groups(mx) * c2;
+      const float mn = fmaxf(m[nb], mx);
+      const float ms = (mn == kNegInf) ? 0.f : mn;
+      const float alpha = fast_exp2(m[nb] - ms);
+      float pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(fmaf(sc[nb][r], c2, -ms));
+      pk[nb] = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
+      l[nb] = l[nb] * alpha + add_bf16_pair(pk[nb].y, add_bf16_pair(pk[nb].x, 0.f));
+      m[nb] = mn;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) acc[tt][nb] *= alpha;
+    }
+    const int vr = BK * t + 4 * grp + (c >> 2);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      const uint2 vt = lds_tr4(vreg + vr * (DV * 2) + 32 * (tt ^ (vr & 7)) + 8 * (c & 3));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[tt][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            __builtin_bit_cast(v4i16_t, vt), __builtin_bit_cast(v4i16_t, pk[nb]), acc[tt][nb], 0,
+            0, 0);
+    }
+  }
+
+  // ---- merge: each wavefront leaves O [16 NB columns][128 dims], m and l
+  // [16 NB] (fp32, base 2) in its own region; wavefronts 0..3 then write
+  // dims 32 w .. 32 w + 31 of every column
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  float* po = reinterpret_cast<float*>(kreg);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float lt = sum_across_groups(l[nb]);
+    const int n = 16 * nb + c;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+      *reinterpret_cast<float4*>(po + n * DV + 16 * tt + 4 * grp) =
+          make_float4(acc[tt][nb][0], acc[tt][nb][1], acc[tt][nb][2], acc[tt][nb][3]);
+    if (grp == 0) {
+      po[32 * DV + n] = m[nb];
+      po[32 * DV + 32 + n] = lt;
+    }
+  }
+  __syncthreads();
+  if (wave < 4) {
+    const int d0 = 32 * wave + 8 * grp;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = 16 * nb + c;
+      const int hn = n - ctok[nb] * G;
+      const float s2 = (cval[nb] && a.sink) ? a.sink[g * G + hn] * kLog2e : kNegInf;
+      float mw[MR_NW], lw[MR_NW];
+      float M = s2;
+#pragma unroll
+      for (int w = 0; w < MR_NW; ++w) {
+        const float* pw = reinterpret_cast<const float*>(reg_all + w * MR_REG);
+        mw[w] = pw[32 * DV + n];
+        lw[w] = pw[32 * DV + 32 + n];
+        M = fmaxf(M, mw[w]);
+      }
+      float den = (s2 > kNegInf) ? fast_exp2(s2 - M) : 0.f;
+      float o8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o8[e] = 0.f;
+#pragma unroll
+      for (int w = 0; w < MR_NW; ++w) {
+        const float sw = (mw[w] > kNegInf) ? fast_exp2(mw[w] - M) : 0.f;
+        den += sw * lw[w];
+        const float* pw = reinterpret_cast<const float*>(reg_all + w * MR_REG) + n * DV + d0;
+        const float4 x0 = *reinterpret_cast<const float4*>(pw);
+        const float4 x1 = *reinterpret_cast<const float4*>(pw + 4);
+        o8[0] += sw * x0.x; o8[1] += sw * x0.y; o8[2] += sw * x0.z; o8[3] += sw * x0.w;
+        o8[4] += sw * x1.x; o8[5] += sw * x1.y; o8[6] += sw * x1.z; o8[7] += sw * x1.w;
+      }
+      if (cval[nb]) {
+        const float inv = (den > 0.f) ? 1.f / den : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o8[e] *= inv;
+        bf16_t* orow = static_cast<bf16_t*>(a.o) +
+                       (((long long)b * T + ctok[nb]) * a.hq + g * G + hn) * DV + d0;
+        st16(orow, pack8(o8));
+      }
+    }
+  }
+}
+
 bool decode_multi_supported(const AttnArgs& a) {
   const int G = a.hq / a.hkv;
   return a.d_qk == D && a.d_v == DV && G >= 1 && a.nq * G <= 64 && a.hkv % HG == 0 &&
@@ -472,6 +694,15 @@ hipError_t launch_decode_multi(const AttnArgs& a, int layout, hipStream_t stream
     if (e != hipSuccess) return e;
   }
   const int cols = a.nq * (a.hq / a.hkv);
+  // a ring of at most 160 slots and at most 32 columns per kv head: one launch
+  if (layout == 0 && a.slots <= MR_NW * MR_ROWS && cols <= 32) {
+    const dim3 gr((unsigned)a.hkv, (unsigned)a.B);
+    if (cols <= 16)
+      hipLaunchKernelGGL((decode_multi_ring_kernel<1>), gr, dim3(64 * MR_NW), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_multi_ring_kernel<2>), gr, dim3(64 * MR_NW), 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 g1((unsigned)(a.hkv / HG), (unsigned)a.nsplit, (unsigned)a.B);
   // four stages once a split spans at least 32 tiles
   const bool deep = a.split_keys >= 32 * BK;

@@ -611,10 +611,11 @@ def test_hybrid_decode_full_size(gpu_lib):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,slots,hq,hkv,frac", [
-    (4, 131, 64, 8, 0.334),    # the workload's shape: 32 columns, one wavefront per kv head
-    (2, 140, 64, 8, 0.0),      # spare slots
-    (4, 131, 32, 16, 0.334),   # G = 2: 8 columns
-    (3, 130, 128, 8, 0.0),     # G = 16, T = 3: 48 columns, two wavefronts per kv head
+    (4, 131, 64, 8, 0.334),    # the workload's shape: 32 columns, one-launch ring kernel
+    (2, 140, 64, 8, 0.0),      # spare slots, 16 columns (one-launch)
+    (4, 131, 32, 16, 0.334),   # G = 2: 8 columns (one-launch)
+    (3, 130, 128, 8, 0.0),     # G = 16, T = 3: 48 columns: split kernel, two wavefronts per kv head
+    (2, 170, 64, 8, 0.0),      # more than 160 slots: split kernel
 ])
 def test_multi_decode_ring(gpu_lib, T, slots, hq, hkv, frac):
     pos = [0, 1, 5, 124, 125, 126, 127, 300, 131072, 262140]
@@ -704,6 +705,18 @@ def test_multi_decode_matches_prefill_rows(gpu_lib):
                                        layout=gpu_lib.KV_RING, ring_slots=S, sink=x["sink"],
                                        window=W)
     assert (om.float() - o[:, p0:].float()).abs().max().item() <= 2e-2
+
+
+def test_multi_decode_ring_contract_violation_gives_nan(gpu_lib):
+    """A sequence whose last draft position passes max_pos: NaN rows from the
+    one-launch ring kernel, the other sequence untouched."""
+    pos = [10, 500]
+    d = synthetic.multi_ring_inputs(2, 4, 64, 8, 131, 192, 128, "bf16", 223, torch.tensor(pos), DEV)
+    bad = torch.tensor([10, 501], dtype=torch.int64, device=DEV)   # 501 + 3 > max_pos
+    o = gpu_lib.swa_sink_decode_multi(d["q"], d["k"], d["v"], bad, 503, layout=gpu_lib.KV_RING,
+                                      ring_slots=131, sink=d["sink"], window=128)
+    on = _np(o)
+    assert np.isfinite(on[0]).all() and np.isnan(on[1]).all()
 
 
 def test_multi_decode_contract_violations_give_nan(gpu_lib):
