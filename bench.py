@@ -212,6 +212,29 @@ def copy_calibration(steps, warmup):
             "us": t * 1e6}
 
 
+def stream_bound(read_bytes, write_bytes, steps=10, warmup=2):
+    """The rate at which the chip moves read_bytes in and write_bytes out
+    with no arithmetic: hswa_stream_probe (16-byte coalesced accesses, each
+    wavefront interleaving its reads and writes in proportion) at 4, 8, 16
+    and 32 wavefronts per CU, the best median kept."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    src = torch.empty(read_bytes, dtype=torch.uint8, device="cuda") if read_bytes else None
+    dst = torch.empty(write_bytes, dtype=torch.uint8, device="cuda") if write_bytes else None
+    total = read_bytes + write_bytes
+    by_shape, best = {}, None
+    for per_cu in (1, 2, 4, 8):
+        blocks = per_cu * cus
+        o = torch.empty(4 * blocks, dtype=torch.int32, device="cuda")
+        _, per = timed(lambda: hswa.stream_probe(src, dst, blocks, out=o), steps, warmup)
+        t = float(np.median(per)) / 1e3
+        by_shape[f"{4 * per_cu}_waves_per_cu"] = total / t / 1e9
+        if best is None or t < best[0]:
+            best = (t, 4 * per_cu)
+    del src, dst
+    return {"ms": best[0] * 1e3, "gbps": total / best[0] / 1e9, "waves_per_cu": best[1],
+            "read_bytes": read_bytes, "write_bytes": write_bytes, "gbps_by_shape": by_shape}
+
+
 def only(which, steps, warmup):
     if which == "copy":
         return {"copy": copy_calibration(steps, warmup)}
@@ -264,7 +287,9 @@ def measured_peaks(steps, warmup):
     gemm = 2 * 8192 ** 3 / t / 1e12
     del a, b, c
     copy = copy_calibration(steps, warmup)
+    read_only = stream_bound(4 << 30, 0)
     return {"bf16_gemm_8192_tflops": gemm, "copy_1gib_gbps_read_plus_write": copy["gbps_read_plus_write"],
+            "stream_probe_read_4gib_gbps": read_only["gbps"],
             "spec_bf16_tflops": BF16_PEAK_TFLOPS, "spec_hbm_gbps": HBM_PEAK_GBPS}
 
 
@@ -819,6 +844,14 @@ def main():
                      "launch_ms_min": float(np.min(per)),
                      "frac_of_bf16_mfma_peak": value / BF16_PEAK_TFLOPS},
     }
+    # the same bytes moved with no arithmetic: the rate this traffic mix allows
+    out_bytes = n * hq * 128 * 2
+    sb = stream_bound(alg_bytes - out_bytes, out_bytes)
+    sb["frac"] = sb["ms"] / (kern_s * 1e3)
+    sb["note"] = ("hswa_stream_probe moving the call's algorithmic read and write bytes; frac = "
+                  "probe time / prefill call time")
+    rec["roofline"]["measured_stream_bound"] = sb
+    _log(f"stream bound {sb}")
     if args.only:
         print(json.dumps(rec), flush=True)
         return

@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     sparse_select_tokens,
     sparse_sink_attn_fp8,
     sparse_workspace_size,
+    stream_probe,
     swa_sink_decode,
     swa_sink_decode_multi,
     swa_sink_decode_noalloc,

@@ -51,6 +51,7 @@ _SIGNATURES = {
     "sparse_select_tokens": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _f, _f, _ll,
                                   _i, _vp, _sz, _vp]),
     "hswa_gather_probe": (_i, [_vp, _vp, _i, _vp, _i, _i, _vp, _vp]),
+    "hswa_stream_probe": (_i, [_vp, _ll, _vp, _ll, _i, _vp, _vp]),
     "hswa_last_error": (ctypes.c_char_p, []),
     "hswa_version": (ctypes.c_char_p, []),
 }
@@ -568,4 +569,30 @@ def gather_probe(k, v, idx, tiles_per_wave, out=None):
     _check_same(k, v, idx, o)
     _raise(lib.hswa_gather_probe(_ptr(k), _ptr(v), rows, _ptr(idx), nwaves, tiles_per_wave, _ptr(o),
                                  _stream(k)))
+    return o
+
+
+def stream_probe(src, dst, blocks, out=None):
+    """Streaming probe (include/hswa_measure.h): reads every byte of src,
+    overwrites every byte of dst (either may be None), each wavefront of
+    blocks * 4 walking its shares of both together -> one uint32 checksum
+    (as int32) per wavefront."""
+    lib = load()
+    ref = src if src is not None else dst
+    if ref is None:
+        raise ValueError("stream_probe needs a source or a destination")
+    nr = 0 if src is None else src.numel() * src.element_size()
+    nw = 0 if dst is None else dst.numel() * dst.element_size()
+    for t, name in ((src, "src"), (dst, "dst")):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if nr % 1024 or nw % 1024:
+        raise ValueError("src and dst sizes must be multiples of 1024 bytes")
+    if blocks <= 0:
+        raise ValueError("blocks must be positive")
+    o = _out(out, (4 * blocks,), torch.int32, ref.device)
+    _check_same(*[t for t in (src, dst) if t is not None], o)
+    _raise(lib.hswa_stream_probe(None if src is None else _ptr(src), nr,
+                                 None if dst is None else _ptr(dst), nw, blocks, _ptr(o),
+                                 _stream(ref)))
     return o

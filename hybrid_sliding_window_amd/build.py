@@ -23,7 +23,7 @@ ARCH = os.environ.get("HSWA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.cpp", "rope_prep.hip", "generic.hip", "prefill_bf16.hip", "prefill_seq.hip", "prefill_causal.hip",
            "decode_bf16.hip", "decode_fp8.hip", "decode_multi.hip", "kv_append.hip", "select_tokens.hip", "sparse_bf16.hip",
-           "decode_noalloc.hip", "gather_probe.hip"]
+           "decode_noalloc.hip", "gather_probe.hip", "stream_probe.hip"]
 
 # Per-source flags.  The matrix-core prefill kernels keep their accumulators
 # in ordinary VGPRs (the VALU rescales them in place); without this the

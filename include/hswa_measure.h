@@ -27,6 +27,26 @@ extern "C" {
 int hswa_gather_probe(const void* k, const void* v, int rows, const int* idx, int nwaves,
                       int tiles_per_wave, unsigned* out, void* stream);
 
+/*
+ * Streaming probe: the traffic of the windowed prefill ("MiMo-V2-Flash:
+ * Hybrid Sliding Window Attention Architecture" (rslog.cc) sections 2.1 and
+ * 4.4: q, K and V read once, the output written once) without its
+ * arithmetic, to measure the rate at which the chip moves a given mix of
+ * read and written bytes.
+ *   src: DEVICE array of read_bytes bytes, read once; dst: DEVICE array of
+ *   write_bytes bytes, overwritten with a pattern; both 16-byte aligned,
+ *   both counts multiples of 1024 (either may be 0, not both).
+ *   blocks: workgroups of 4 wavefronts; out: uint32 [blocks * 4] DEVICE
+ *   array receiving one checksum of the read words per wavefront.
+ * Each wavefront reads and writes a contiguous share of each array,
+ * interleaving its reads and writes in proportion.  Returns 0 (HSWA_OK),
+ * 1 (invalid argument, nothing enqueued) or 3 (launch error);
+ * hswa_last_error() describes a failure.  Asynchronous on stream (a
+ * hipStream_t as void*).
+ */
+int hswa_stream_probe(const void* src, long long read_bytes, void* dst, long long write_bytes,
+                      int blocks, unsigned* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -434,3 +434,25 @@ def test_noalloc_decode_refuses_oversize_on_the_host(lib):
                                      64, 64, 4, 192, 128, 0, 262143, 0.0, 1e7, 0.0, 1, None)
     assert st == INVALID
     assert "static maximum" in lib.hswa_last_error().decode()
+
+
+def test_probes_reject_bad_arguments(lib):
+    gp = lambda **kw: lib.hswa_gather_probe(*[kw.get(k_, d) for k_, d in (  # noqa: E731
+        ("k", FAKE), ("v", FAKE), ("rows", 10), ("idx", FAKE), ("nwaves", 2), ("tiles", 1),
+        ("out", FAKE), ("stream", None))])
+    assert gp(k=None) == INVALID
+    assert gp(rows=0) == INVALID
+    assert gp(v=MISALIGNED) == INVALID
+    assert gp(nwaves=1 << 26, tiles=1 << 4) == INVALID      # index list past 2^31 entries
+    sp = lambda **kw: lib.hswa_stream_probe(*[kw.get(k_, d) for k_, d in (  # noqa: E731
+        ("src", FAKE), ("nr", 4096), ("dst", FAKE), ("nw", 2048), ("blocks", 4), ("out", FAKE),
+        ("stream", None))])
+    assert sp(out=None) == INVALID
+    assert sp(blocks=0) == INVALID
+    assert sp(nr=0, nw=0) == INVALID
+    assert sp(nr=-1024) == INVALID
+    assert sp(nr=1000) == INVALID                            # not a multiple of 1024
+    assert sp(src=None) == INVALID
+    assert sp(dst=None) == INVALID
+    assert sp(dst=MISALIGNED) == INVALID
+    assert sp(blocks=1 << 30) == INVALID
