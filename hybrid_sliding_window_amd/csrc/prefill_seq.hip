@@ -42,6 +42,11 @@ constexpr int SW_ROWS = 256;               // query rows per item
 constexpr int SLOT = KTILE + VTILE;        // 20 KB: K tile then V tile
 constexpr int NS = 7;                      // ring slots
 
+template <bool B>
+struct GroupTag {
+  static constexpr bool value = B;
+};
+
 // Item k of the (sequence, kv head, query block) order.
 struct SeqItem {
   long long kbase;   // b * n
@@ -106,6 +111,10 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
   // R/8 come from the rotated copy (row pitch R) unless K is stored rotated.
   // V copy c = cw + 4u (u < 2): row s / 16, 64-byte unit (pc / 4) ^ (row & 3).
   const bool kwave = wave < SW_NW / 2;
+  // The two wavefronts of a SIMD work out of phase: the early one (0..3)
+  // stores an item's output and loads the next item's q at the end of the
+  // item, the late one (4..7) does both at the start of the next item, so
+  // that each one's memory traffic overlaps the other's products.
   const int cw = kwave ? wave : wave - SW_NW / 2;
   int krow[3], kcol[3], kstr[3], vrow[2], vcol[2];
   bool krot[3];
@@ -165,19 +174,61 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
     nis += KS;
   };
 
+  // The output rows of an item as a buffer resource (token i0, head 0 at
+  // offset 0; the sequence's tokens from i0 on in range): stores of rows
+  // past the sequence's last token fall outside it and are dropped by the
+  // hardware, so every wavefront issues the same 8 stores and the explicit
+  // vector-memory waits can count them.
+  auto out_rsrc = [&](const SeqItem& c) __attribute__((always_inline)) {
+    const int rows = max(0, min(T, n - c.i0));
+    return __builtin_amdgcn_make_buffer_rsrc(Op + (c.qbase + c.i0) * hq * DV, 0, rows * hq * DV * 2,
+                                             0x00020000);
+  };
+  // o = O / l in bf16, 16 consecutive dims per lane per output tile
+  auto store_block = [&](const f32x16 (&acc)[MT], float l, int row, __amdgpu_buffer_rsrc_t rs)
+      __attribute__((always_inline)) {
+    const float lt = l + __shfl_xor(l, 32);
+    const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+    const int off = row * (DV * 2) + 32 * h;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float f[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) f[v] = acc[mt][v] * inv;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pack8(f)), rs, off + 64 * mt, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pack8(f + 8)), rs,
+                                             off + 64 * mt + 16, 0, 0);
+    }
+    asm volatile("" ::: "memory");
+    nis += 2 * MT;
+  };
+
   uint32_t krd[4], vrd[4];   // per-lane LDS offsets of the operand reads
   operand_offsets(lane, krd, vrd);
   const uint32_t ring0 = lds_addr(ring);
   const float c2 = a.scale * kLog2e;
 
+  // The item loop, generated once per group so that each group's stores,
+  // loads and waits form straight-line code the compiler's wait analysis
+  // can follow.
+  auto run_items = [&](auto group) __attribute__((always_inline)) {
+  constexpr bool late = decltype(group)::value;
   // ---- prologue: the first item's tiles and q rows ------------------------
   SeqItem cur = seq_item(a, j_begin, nblk, T);
   int req_bg = cur.bg, req_hi = cur.tb;   // highest tile requested for sequence req_bg
   for (int x = cur.ta; x <= cur.tb; ++x) request_tile(cur, x);
   int mark_cur = nis;                     // nis after the copies the current item reads
   u32x4 q0[KS];                           // q of the current item (then of the next)
-  load_q(cur, q0);
+  if (!late) load_q(cur, q0);
   bool fresh = false;                     // the current item's tiles are still to request
+
+  // O, l of the item being finished; the late group keeps them (and the
+  // item's output coordinates) across the barrier and stores them at the
+  // start of the next item
+  f32x16 acc0[MT];
+  float l0 = 0.f;
+  int prow = 0;                                                    // (token - i0) hq + head
+  __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(Op, 0, 0, 0x00020000);   // no rows
 
   for (int j = j_begin; j < j_end; ++j) {
     const bool has_next = j + 1 < j_end;
@@ -194,10 +245,17 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
     }
     wait_copy(nis - mark_cur);
     ring_barrier();
-    // this item's q rows (the wavefront's latest loads) have landed: waiting
-    // here, before any new copy is issued, keeps the compiler from waiting
-    // for those copies too at the first use of q
-    __builtin_amdgcn_s_waitcnt(VMCNT(0));
+    // this item's q rows have landed (the late group first loads them and
+    // then stores the previous item's output, whose 8 stores it does not
+    // wait for); waiting here, before any new copy is issued, keeps the
+    // compiler from waiting for those copies too at the first use of q
+    if (late) {
+      load_q(cur, q0);
+      store_block(acc0, l0, prow, prs);   // nothing in range before the first item
+      __builtin_amdgcn_s_waitcnt(VMCNT(2 * MT));
+    } else {
+      __builtin_amdgcn_s_waitcnt(VMCNT(0));
+    }
     // tiles the next item adds (same sequence: at most NS with this item's)
     fresh = has_next && nx.bg != req_bg;
     if (has_next && !fresh) {
@@ -218,8 +276,7 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
     const int b0hi = min(n - 1, cur.i0 + ((32 * wave + 31) >> log2g));
 
     float m0 = sinkbuf[head0];
-    float l0 = (h == 0 && m0 > kNegInf) ? 1.f : 0.f;
-    f32x16 acc0[MT];
+    l0 = (h == 0 && m0 > kNegInf) ? 1.f : 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -279,7 +336,7 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
       // L2 (one dword per 128-byte line of this wavefront's 32 rows, copied
       // into a scratch area nobody reads), so that the loads into the q
       // registers after the last score products hit L2.
-      if (has_next && x == max(cur.ta, cur.tb - 2)) {
+      if (has_next && x == max(cur.ta, cur.tb - (late ? 0 : 2))) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int ln = 64 * u + lane;
@@ -326,38 +383,25 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
                           as_bf16x8(p01), acc0[mt]);
     }
 
-    // ---- output: o = O / l in bf16, 16 consecutive dims per lane per tile --
+    // ---- output (early group): o = O / l, then the next item's q --------
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-    auto store_block = [&](const f32x16 (&acc)[MT], float l, int tok, int head, int lo)
-        __attribute__((always_inline)) {
-      const float lt = l + __shfl_xor(l, 32);
-      const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-      if (lo < n) {   // the block's first row is a real token: 8 stores issued
-        if (tok < n) {
-          bf16_t* orow = Op + ((cur.qbase + tok) * hq + head) * DV + 16 * h;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            float f[16];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) f[v] = acc[mt][v] * inv;
-            st16(orow + 32 * mt, pack8(f));
-            st16(orow + 32 * mt + 8, pack8(f + 8));
-          }
-        }
-        asm volatile("" ::: "memory");
-        nis += 2 * MT;
-      }
-    };
-    store_block(acc0, l0, tok0, head0, b0lo);
-    // the next item's q rows (in L2 since two tiles ago) into the q
-    // registers, issued after the stores so that the stores do not queue
-    // behind them
-    if (has_next) load_q(nx, q0);
+    const int row0 = (tok0 - cur.i0) * hq + head0;
+    if (!late) {
+      store_block(acc0, l0, row0, out_rsrc(cur));
+      if (has_next) load_q(nx, q0);
+    } else {
+      prow = row0;
+      prs = out_rsrc(cur);
+    }
 
     mark_cur = mark_next;
     cur = nx;
   }
+  if (late) store_block(acc0, l0, prow, prs);   // the run's last item
+  };
+  if (kwave) run_items(GroupTag<false>{});
+  else run_items(GroupTag<true>{});
   __builtin_amdgcn_s_waitcnt(VMCNT(0));   // no copy into LDS outlives the workgroup
 }
 
