@@ -272,6 +272,16 @@ def secondary(steps, warmup,
         _sparse_fp8(out, dev)
     if "select" in parts:
         _select(out, dev)
+    ga_decodes = [k for k in ("decode_ga_contiguous", "decode_mtp_ga_contiguous",
+                              "decode_fp8_ga_contiguous") if k in out]
+    if ga_decodes:
+        # the rate the chip reads a large buffer at (no writes, no arithmetic):
+        # the measured bound of the HBM-bound decode kernels
+        rb = stream_bound(4 << 30, 0)
+        for k in ga_decodes:
+            out[k]["frac_of_stream_read_bound"] = out[k]["gbps"] / rb["gbps"]
+            out[k]["stream_read_bound_gbps"] = rb["gbps"]
+        _log(f"stream read bound {rb['gbps']:.0f} GB/s")
     return out
 
 
