@@ -847,7 +847,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": _traffic("prefill_seq_kernel:swa_prefill_n32768"),
                      "kernel": "prefill_seq_kernel",
-                     "launch_scope": "one swa_sink_prefill call: RoPE prep kernels + prefill kernel",
+                     "launch_scope": "one swa_sink_prefill call (one kernel: q and K rotated inside it)",
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "launch_ms": kern_s * 1e3,
                      "launch_ms_median": float(np.median(per)),

@@ -183,7 +183,8 @@ hswa_status_t prefill_impl(const void* q, const void* k, const void* v, const fl
   {
     // first key position any query of the call reads
     const int first = (a.window > 0 && a.qoff - a.window + 1 > 0) ? a.qoff - a.window + 1 : 0;
-    hipError_t e = launch_rope_prep(a, workspace, pos_offset, first, use_mfma && !k_rotated,
+    // (the windowed kernel rotates its K tiles in LDS itself)
+    hipError_t e = launch_rope_prep(a, workspace, pos_offset, first, use_mfma && !k_rotated && !seq,
                                     !own_q, s);
     if (e != hipSuccess) return hip_status(e, "rope preparation launch");
   }

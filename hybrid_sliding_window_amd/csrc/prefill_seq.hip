@@ -89,7 +89,6 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
   const int n = a.n, hkv = a.hkv, hq = a.hq;
   const int W = a.window;
   const int half = a.half;
-  const int R = 2 * half;
 
   const int j_begin = blockIdx.x * run;
   const int j_end = min(items, j_begin + run);
@@ -101,14 +100,14 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
 
   const bf16_t* __restrict__ Qp = static_cast<const bf16_t*>(a.q);
   const bf16_t* __restrict__ Kp = static_cast<const bf16_t*>(a.k);
-  const bf16_t* __restrict__ Kr = static_cast<const bf16_t*>(a.krot);
   const bf16_t* __restrict__ Vp = static_cast<const bf16_t*>(a.v);
   bf16_t* __restrict__ Op = static_cast<bf16_t*>(a.o);
 
   // ---- tile copies: 12 K copies of 1 KB by wavefronts 0..3, 8 V by 4..7 --
-  // K copy c = cw + 4u (u < 3): slot s = 64 c + lane, row s / 24, physical
-  // chunk s % 24 holding logical chunk pc ^ ((row >> 1) & 7); chunks below
-  // R/8 come from the rotated copy (row pitch R) unless K is stored rotated.
+  // K copy c = 3 cw + u (u < 3): slot s = 64 c + lane, row s / 24, physical
+  // chunk s % 24 holding logical chunk pc ^ ((row >> 1) & 7), so wavefront
+  // cw copies whole rows 8 cw .. 8 cw + 7 (and rotates their rotary dims
+  // once they have landed, see rotate_k_rows).
   // V copy c = cw + 4u (u < 2): row s / 16, 64-byte unit (pc / 4) ^ (row & 3).
   const bool kwave = wave < SW_NW / 2;
   // The two wavefronts of a SIMD work out of phase: the early one (0..3)
@@ -116,17 +115,13 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
   // item, the late one (4..7) does both at the start of the next item, so
   // that each one's memory traffic overlaps the other's products.
   const int cw = kwave ? wave : wave - SW_NW / 2;
-  int krow[3], kcol[3], kstr[3], vrow[2], vcol[2];
-  bool krot[3];
+  int krow[3], kcol[3], vrow[2], vcol[2];
 #pragma unroll
   for (int u = 0; u < 3; ++u) {
-    const int sl = 64 * (cw + 4 * u) + lane;
+    const int sl = 64 * (3 * cw + u) + lane;
     const int row = sl / 24, pc = sl - row * 24;
-    const int lc = pc ^ ((row >> 1) & 7);
-    krot[u] = !a.k_rotated && lc < (half >> 2);
     krow[u] = row;
-    kcol[u] = 8 * lc;
-    kstr[u] = hkv * (krot[u] ? R : D);
+    kcol[u] = 8 * (pc ^ ((row >> 1) & 7));
   }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -143,14 +138,13 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
     const int lim = n - 1 - j0;
     const long long rb = (c.kbase + j0) * hkv + c.g;
     const bf16_t* kb = Kp + rb * D;
-    const bf16_t* rbp = Kr + rb * R;
     const bf16_t* vb = Vp + rb * DV;
     unsigned char* kd = ring + (x % NS) * SLOT;
     unsigned char* vd = kd + KTILE;
     if (kwave) {
 #pragma unroll
       for (int u = 0; u < 3; ++u)
-        g2lds16((krot[u] ? rbp : kb) + (min(krow[u], lim) * kstr[u] + kcol[u]), kd + 1024 * (cw + 4 * u));
+        g2lds16(kb + (min(krow[u], lim) * (hkv * D) + kcol[u]), kd + 1024 * (3 * cw + u));
       asm volatile("" ::: "memory");
       nis += 3;
     } else {
@@ -206,6 +200,52 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
   uint32_t krd[4], vrd[4];   // per-lane LDS offsets of the operand reads
   operand_offsets(lane, krd, vrd);
   const uint32_t ring0 = lds_addr(ring);
+
+  // RoPE of the keys in LDS (K stored unrotated): an early wavefront turns
+  // the rotary dims of the rows it copied (rows 8 cw .. 8 cw + 7 of tile x,
+  // keys x * 32 + row at positions pos_offset + key) once its copies have
+  // landed and before the barrier that publishes the tile.  Lane (row
+  // lane / 8, chunk pair (lane / 2) % 4, elements 4 (lane % 2) .. + 3):
+  // dims 8 p + e and their partners half further on, with the angle formed
+  // in fp64 revolutions and evaluated by the hardware sine and cosine, as the
+  // rotated-K preparation does.
+  const bool rot_k = half > 0 && !a.k_rotated;
+  auto rotate_k_rows = [&](int x) __attribute__((always_inline)) {
+    const int r = 8 * cw + (lane >> 3);
+    const int pr = (lane >> 1) & 3;
+    const int e0 = 4 * (lane & 1);
+    if (pr < (half >> 3)) {
+      const int sw = (r >> 1) & 7;
+      const uint32_t rowa = ring0 + (x % NS) * SLOT + r * KROW + 2 * e0;
+      const uint32_t a0 = rowa + 16 * (pr ^ sw);
+      const uint32_t a1 = rowa + 16 * ((pr + (half >> 3)) ^ sw);
+      u32x2 w0, w1;
+      asm volatile("ds_read_b64 %0, %2\n\tds_read_b64 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                   : "=&v"(w0), "=&v"(w1) : "v"(a0), "v"(a1) : "memory");
+      float f0[4], f1[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u0 = w0[e >> 1], u1 = w1[e >> 1];
+        f0[e] = __uint_as_float((e & 1) ? (u0 & 0xffff0000u) : (u0 << 16));
+        f1[e] = __uint_as_float((e & 1) ? (u1 & 0xffff0000u) : (u1 << 16));
+      }
+      const double pos = (double)(a.pos_offset + (long long)x * BK + r);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double turns = pos * revbuf[8 * pr + e0 + e];
+        const float f = (float)(turns - floor(turns));
+        const float co = __builtin_amdgcn_cosf(f), si = __builtin_amdgcn_sinf(f);
+        const float y0 = f0[e] * co - f1[e] * si;
+        const float y1 = f1[e] * co + f0[e] * si;
+        f0[e] = y0;
+        f1[e] = y1;
+      }
+      const u32x2 o0 = {pack_bf16x2(f0[0], f0[1]), pack_bf16x2(f0[2], f0[3])};
+      const u32x2 o1 = {pack_bf16x2(f1[0], f1[1]), pack_bf16x2(f1[2], f1[3])};
+      asm volatile("ds_write_b64 %0, %1\n\tds_write_b64 %2, %3\n\ts_waitcnt lgkmcnt(0)"
+                   :: "v"(a0), "v"(o0), "v"(a1), "v"(o1) : "memory");
+    }
+  };
   const float c2 = a.scale * kLog2e;
 
   // The item loop, generated once per group so that each group's stores,
@@ -216,6 +256,7 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
   // ---- prologue: the first item's tiles and q rows ------------------------
   SeqItem cur = seq_item(a, j_begin, nblk, T);
   int req_bg = cur.bg, req_hi = cur.tb;   // highest tile requested for sequence req_bg
+  int rot_bg = -1, rot_hi = 0;            // highest tile rotated for sequence rot_bg
   for (int x = cur.ta; x <= cur.tb; ++x) request_tile(cur, x);
   int mark_cur = nis;                     // nis after the copies the current item reads
   u32x4 q0[KS];                           // q of the current item (then of the next)
@@ -244,6 +285,12 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
       mark_cur = nis;
     }
     wait_copy(nis - mark_cur);
+    if (!late && rot_k) {   // the tiles this item adds, now landed
+      for (int x = (cur.bg == rot_bg) ? max(rot_hi + 1, cur.ta) : cur.ta; x <= cur.tb; ++x)
+        rotate_k_rows(x);
+      rot_bg = cur.bg;
+      rot_hi = cur.tb;
+    }
     ring_barrier();
     // this item's q rows have landed (the late group first loads them and
     // then stores the previous item's output, whose 8 stores it does not
