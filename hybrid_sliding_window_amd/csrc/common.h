@@ -183,12 +183,13 @@ __device__ __forceinline__ void lds_tr4x8(uint2 (&r)[8], const uint32_t (&a)[8])
 }
 
 // Codes 2w, 2w + 1 of the 4 E4M3 codes in v (w = 0 or 1) as a packed bf16
-// pair.  The hardware conversion to fp32 is exact, and every E4M3 value is a
-// bf16 value, so keeping the upper halves is exact too.
+// pair, by gfx950's direct E4M3 -> bf16 conversion with a unit scale: every
+// E4M3 value is a bf16 value, so the conversion is exact (the same bits as
+// the exact conversion to fp32 with the lower halves dropped).
+typedef __bf16 bf16x2_hw_t __attribute__((ext_vector_type(2)));
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3_pair(uint32_t v) {
-  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(v, HI);
-  return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, HI));
 }
 
 // 8 E4M3 codes -> 8 bf16 (element e from byte e).
