@@ -198,16 +198,23 @@ __device__ __forceinline__ uint4 widen8(uint2 w) {
                     e4m3_pair<true>(w.y));
 }
 
-// Max / sum across the four lanes l, l^16, l^32, l^48 (same column c).
+// Max / sum across the four lanes l, l^16, l^32, l^48 (same column c), with
+// gfx950's row-swapping moves instead of LDS-routed lane shuffles:
+// v_permlane16_swap on two copies of v leaves rows (0, 0, 2, 2) in one and
+// (1, 1, 3, 3) in the other, v_permlane32_swap the lower half twice in one
+// and the upper half twice in the other; both lanes of a pair combine the
+// same two operands in the same order.
 __device__ __forceinline__ float max_across_groups(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_across_groups(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
