@@ -135,8 +135,8 @@ template <int NB, int CW, int NST>
 __global__ __launch_bounds__(256 * CW, (NST == 2 && CW == 1) ? 2 : 1) void decode_multi_split_kernel(
     AttnArgs a, int layout) {
   constexpr int NWAVE = HG * CW;
-  constexpr int DMA_PER_WAVE = (KINSTR + VINSTR) / NWAVE;
-  static_assert((KINSTR + VINSTR) % NWAVE == 0 && KINSTR % NWAVE == 0, "even split of the loads");
+  constexpr int DMA_PER_WAVE = (KINSTR + VINSTR) / HG;   // producers: the wavefronts of column half 0
+  static_assert((KINSTR + VINSTR) % HG == 0 && KINSTR % HG == 0, "even split of the loads");
   static_assert(DMA_PER_WAVE * (NST - 2) <= 63, "the vmcnt field holds the loads in flight");
   static_assert(NST == 2 || NST == 4, "stage arithmetic below");
   __shared__ __attribute__((aligned(16))) unsigned char kst[NST][KTILE];
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256 * CW, (NST == 2 && CW == 1) ? 2 : 1) void decod
   int drow[DMA_PER_WAVE], doff[DMA_PER_WAVE];
 #pragma unroll
   for (int u = 0; u < DMA_PER_WAVE; ++u) {
-    const int ii = wave + NWAVE * u;
+    const int ii = hw + HG * u;
     if (ii < KINSTR) {
       const int sl = 64 * ii + lane;
       const int row = sl / 96, pc = sl - row * 96;
@@ -182,12 +182,17 @@ __global__ __launch_bounds__(256 * CW, (NST == 2 && CW == 1) ? 2 : 1) void decod
       doff[u] = 32 * ((pc >> 1) ^ (row & 7)) + 16 * (pc & 1);
     }
   }
+  // Only the wavefronts of column half 0 (one per SIMD when CW = 2) issue
+  // the copies: issuing stalls a wavefront until the vector-memory path
+  // accepts each copy, and the SIMD's other wavefront computes meanwhile.
+  const bool producer = ch == 0;
   auto issue = [&](int k0, unsigned char* kd, unsigned char* vd) {
+    if (!producer) return;
 #pragma unroll
     for (int u = 0; u < DMA_PER_WAVE; ++u) {
-      const int ii = wave + NWAVE * u;
+      const int ii = hw + HG * u;
       const int key = min(k0 + drow[u], nkeys - 1);
-      if (u < KINSTR / NWAVE)   // wave-uniform: K instructions first, then V
+      if (u < KINSTR / HG)   // wave-uniform: K instructions first, then V
         __builtin_amdgcn_global_load_lds((glb_void_t*)(kbase + (__umul24(key, kstride) + doff[u])),
                                          (lds_void_t*)(kd + 1024 * ii), 16, 0, 0);
       else
