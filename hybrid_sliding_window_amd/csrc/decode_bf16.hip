@@ -267,16 +267,39 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(AttnArgs a, int layo
   const long long base = ((long long)b * a.hq + h) * a.nsplit;
   const float* wml = a.ws + (long long)a.B * a.hq * a.nsplit * DV + base * 2;
   const float s2 = a.sink ? a.sink[h] * kLog2e : kNegInf;
+  // Splits in batches of eight whose loads are all issued before any is
+  // used (one memory round trip per batch, not per split); the sums run in
+  // split order.  Indices past the last split re-read it and are ignored.
   float M = s2;
-  for (int s = 0; s < nspl; ++s) M = fmaxf(M, wml[2 * s]);
+  for (int s0 = 0; s0 < nspl; s0 += 8) {
+    float mv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mv[j] = wml[2 * min(s0 + j, nspl - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) M = fmaxf(M, mv[j]);
+  }
   float den = (s2 > kNegInf) ? fast_exp2(s2 - M) : 0.f;
   float o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < nspl; ++s) {
-    const float w = fast_exp2(wml[2 * s] - M);
-    den += w * wml[2 * s + 1];
-    const float* wo = a.ws + (base + s) * DV;
-    o0 += w * wo[lane];
-    o1 += w * wo[lane + 64];
+  for (int s0 = 0; s0 < nspl; s0 += 8) {
+    float mv[8], lv[8], x0[8], x1[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int sj = min(s0 + j, nspl - 1);
+      mv[j] = wml[2 * sj];
+      lv[j] = wml[2 * sj + 1];
+      const float* wo = a.ws + (base + sj) * DV;
+      x0[j] = wo[lane];
+      x1[j] = wo[lane + 64];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j < nspl) {   // uniform
+        const float w = fast_exp2(mv[j] - M);
+        den += w * lv[j];
+        o0 += w * x0[j];
+        o1 += w * x1[j];
+      }
+    }
   }
   const float inv = (den > 0.f) ? 1.f / den : 0.f;
   orow[lane] = f32_to_bf16_bits(o0 * inv);
