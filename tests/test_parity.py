@@ -205,6 +205,23 @@ def test_prefill_rotary_widths(gpu_lib, frac):
     _check(f"rotary fraction {frac:.3f}", o, ref)
 
 
+@pytest.mark.parametrize("hq,hkv,frac", [(64, 8, 0.334), (32, 2, 0.17)])
+def test_windowed_prefill_far_positions(gpu_lib, hq, hkv, frac):
+    """The windowed kernel turns q in registers and K in LDS at the tokens'
+    positions: behind a position offset of 2^20 + 123 the angles reach
+    ~1e6 rad, where only an fp64 angle keeps them right; 700 tokens leave a
+    ragged last block (rows past the end dropped by the range-checked
+    stores)."""
+    x = _prefill_case(1, 700, hq, hkv, "bf16", 77 + hq)
+    off = (1 << 20) + 123
+    o = gpu_lib.swa_sink_prefill(x["q"], x["k"], x["v"], x["sink"], window=128, rope_theta=1.0e4,
+                                 rotary_fraction=frac, pos_offset=off)
+    q, k, v, s = _host(x)
+    ref = oracle.swa_sink_prefill(q, k, v, s, window=128, rope_theta=1.0e4, rotary_fraction=frac,
+                                  pos_offset=off)
+    _check(f"windowed prefill at positions {off}.. {hq}/{hkv} frac {frac}", o, ref)
+
+
 @pytest.mark.parametrize("qmul", [2.0, 4.0])
 def test_sink_sensitive_case(gpu_lib, qmul):
     """Large sinks U(2, 6) (the sink absorbs a large share of each row) and a
