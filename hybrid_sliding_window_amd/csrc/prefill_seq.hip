@@ -19,17 +19,20 @@
 // never needs more than NS tiles together with this one; wavefronts 0..3
 // copy K, 4..7 V); the item's own tiles were requested one item earlier.  A
 // run that crosses to another sequence or head requests the new item's
-// tiles when it gets there.  Each wavefront loads its q rows of the next
-// item straight into its q registers after storing the item's output (the
-// rows were brought into L2 two tiles earlier), so there is no q staging in
-// LDS and no barrier per tile.
+// tiles when it gets there.  K is copied unrotated; each K-copying
+// wavefront turns the rotary dims of the rows it copied in LDS once they
+// have landed, before the barrier that publishes the tile.  q goes straight
+// into registers (no q staging in LDS, no barrier per tile): the two
+// wavefronts of a SIMD work out of phase, one storing its output and
+// loading the next item's q at the end of an item, the other at the start
+// of the next, after touching the rows into L2 during its last tile.
 //
 // Arithmetic per tile (as in prefill_causal.hip): S^T = K . Q^T on the
 // 32x32x16 MFMA (a lane holds query row i against keys 8j + 4h + r), base-2
 // online softmax seeded with the sink and a lazily moved reference max, l
 // summed from the bf16 P with v_dot2, O^T += V^T . P^T with the V^T operand
 // read transposed from LDS so each lane ends up with 16 consecutive output
-// dims, stored as two 16-byte writes per output tile.
+// dims, stored as two 16-byte range-checked buffer writes per output tile.
 #include "common.h"
 #include "launch.h"
 #include "tile_ops.h"
@@ -379,10 +382,11 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
       const uint32_t kaddr = ring0 + (x % NS) * SLOT;
       const uint32_t vaddr = kaddr + KTILE;
       const int j0 = x * BK;
-      // Two tiles before the item's end, bring the next item's q rows into
-      // L2 (one dword per 128-byte line of this wavefront's 32 rows, copied
-      // into a scratch area nobody reads), so that the loads into the q
-      // registers after the last score products hit L2.
+      // Bring the next item's q rows into L2 (one dword per 128-byte line
+      // of this wavefront's 32 rows, copied into a scratch area nobody
+      // reads) two tiles before the item's end (early group) or in its last
+      // tile (late group), so that the q loads hit L2 (earlier touches
+      // measured slower: the lines leave L2 again).
       if (has_next && x == max(cur.ta, cur.tb - (late ? 0 : 2))) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -411,8 +415,6 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
 #pragma unroll
       for (int ks = 6; ks < KS; ++ks)
         sc0 = mfma32(__builtin_bit_cast(bf16x8, kf[ks]), __builtin_bit_cast(bf16x8, q0[ks]), sc0);
-      // after the item's last score products its q registers take the next
-      // item's q rows, which then arrive while this tile finishes
       u32x2 vf[8];
       lds_vhalf<0>(vf, vaddr + vrd[0], vaddr + vrd[1], vaddr + vrd[2], vaddr + vrd[3]);
       uint4 p00, p01;
