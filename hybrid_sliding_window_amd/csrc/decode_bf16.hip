@@ -342,47 +342,52 @@ __global__ __launch_bounds__(256, 2) void decode_ring_kernel(AttnArgs a) {
   }
   const int key0 = RG_ROWS * wave;             // this wavefront's first slot
   const int nk = (int)min((long long)RG_ROWS, max(0LL, len - key0));   // its valid slots
-
-  // ---- copies: K slot s = 64 ii + lane (ii < 12) is row s / 24, physical
-  // chunk s % 24 holding logical chunk pc ^ ((row >> 1) & 7); V slot s =
-  // 64 jj + lane (jj < 8) is row s / 16, 16-byte chunk s % 16 of physical
-  // 32-byte unit u holding logical unit u ^ (row & 7).  Rows past the last
-  // valid slot reload the last one (finite data, masked).
-  if (nk > 0) {
-    const unsigned char* kb = static_cast<const unsigned char*>(a.k) + (row0 * a.hkv + g) * (long long)(D * 2);
-    const unsigned char* vb = static_cast<const unsigned char*>(a.v) + (row0 * a.hkv + g) * (long long)(DV * 2);
-    const int kstr = a.hkv * D * 2, vstr = a.hkv * DV * 2;
-#pragma unroll
-    for (int ii = 0; ii < 12; ++ii) {
-      const int sl = 64 * ii + lane;
-      const int row = sl / 24, pc = sl - row * 24;
-      const int lc = pc ^ ((row >> 1) & 7);
-      const int key = key0 + min(row, nk - 1);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(kb + (__umul24(key, kstr) + 16 * lc)),
-                                       (lds_void_t*)(kreg + 1024 * ii), 16, 0, 0);
-    }
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int sl = 64 * jj + lane;
-      const int row = sl >> 4, pc = sl & 15;
-      const int lc = 2 * ((pc >> 1) ^ (row & 7)) + (pc & 1);
-      const int key = key0 + min(row, nk - 1);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (__umul24(key, vstr) + 16 * lc)),
-                                       (lds_void_t*)(vreg + 1024 * jj), 16, 0, 0);
-    }
-  }
+  const int klast = (int)len - 1;              // len >= 1 here
 
   // q of head g*G + c (rotated to position p by the preparation kernel when
-  // RoPE is on); columns c >= G are padding
+  // RoPE is on); columns c >= G repeat head G - 1 (their results are never
+  // stored).  Issued first, so that it lands with tile 0.
   bf16x8 qf[KS];
   {
     const bf16_t* qsrc = static_cast<const bf16_t*>(a.half > 0 ? a.qrot : a.q);
     const bf16_t* qrow = qsrc + ((long long)b * a.hq + g * G + min(c, G - 1)) * D + 8 * grp;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = as_bf16x8(c < G ? ld16(qrow + 32 * ks) : make_uint4(0, 0, 0, 0));
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 32 * ks));
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): q and this wavefront's slots have landed
+
+  // ---- copies, tile by tile (keys 0..15, then 16..31 of the wavefront's
+  // slots): K slot s = 64 ii + lane (ii < 12) is row s / 24, physical chunk
+  // s % 24 holding logical chunk pc ^ ((row >> 1) & 7); V slot s = 64 jj +
+  // lane (jj < 8) is row s / 16, 16-byte chunk s % 16 of physical 32-byte
+  // unit u holding logical unit u ^ (row & 7).  Rows past the last valid
+  // slot reload the last one (finite data, masked); a wavefront with no
+  // valid slot reloads the ring's last written slot, so every wavefront
+  // issues the same 20 copies and the waits below count exactly.
+  {
+    const unsigned char* kb = static_cast<const unsigned char*>(a.k) + (row0 * a.hkv + g) * (long long)(D * 2);
+    const unsigned char* vb = static_cast<const unsigned char*>(a.v) + (row0 * a.hkv + g) * (long long)(DV * 2);
+    const int kstr = a.hkv * D * 2, vstr = a.hkv * DV * 2;
+    auto slot = [&](int row) { return min(key0 + min(row, nk - 1), klast); };
+#pragma unroll
+    for (int half16 = 0; half16 < 2; ++half16) {
+#pragma unroll
+      for (int ii = 6 * half16; ii < 6 * half16 + 6; ++ii) {
+        const int sl = 64 * ii + lane;
+        const int row = sl / 24, pc = sl - row * 24;
+        const int lc = pc ^ ((row >> 1) & 7);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(kb + (__umul24(slot(row), kstr) + 16 * lc)),
+                                         (lds_void_t*)(kreg + 1024 * ii), 16, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 4 * half16; jj < 4 * half16 + 4; ++jj) {
+        const int sl = 64 * jj + lane;
+        const int row = sl >> 4, pc = sl & 15;
+        const int lc = 2 * ((pc >> 1) ^ (row & 7)) + (pc & 1);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (__umul24(slot(row), vstr) + 16 * lc)),
+                                         (lds_void_t*)(vreg + 1024 * jj), 16, 0, 0);
+      }
+    }
+  }
 
   const float c2 = a.scale * kLog2e;
   float m = kNegInf, l = 0.f;
@@ -390,16 +395,20 @@ __global__ __launch_bounds__(256, 2) void decode_ring_kernel(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int t = 0; t < RG_ROWS / BK; ++t) {
-    if (t * BK >= nk) break;   // uniform
-    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // one 16-key tile from the wavefront's region; its LDS reads are inline
+  // asm that wait for their own data, so the compiler's wait analysis does
+  // not add a wait for the copies still in flight
+  auto tile = [&](int t) __attribute__((always_inline)) {
     const int kr = BK * t + c;
+    uint32_t kad[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int pcq = (4 * ks + grp) ^ ((kr >> 1) & 7);
-      sc = mfma16(as_bf16x8(ld16(kreg + kr * (D * 2) + 16 * pcq)), qf[ks], sc);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      kad[ks] = lds_off(kreg + kr * (D * 2) + 16 * ((4 * ks + grp) ^ ((kr >> 1) & 7)));
+    uint4 kw[KS];
+    lds_b128x6(kw, kad);
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sc = mfma16(as_bf16x8(kw[ks]), qf[ks], sc);
     // branch-free masking (see the split kernel)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[r] = (BK * t + 4 * grp + r < nk) ? sc[r] : kNegInf;
@@ -418,13 +427,25 @@ __global__ __launch_bounds__(256, 2) void decode_ring_kernel(AttnArgs a) {
     for (int tt = 0; tt < NT; ++tt) acc[tt] *= alpha;
     const v4i16 pb = __builtin_bit_cast(v4i16, pk);
     const int vr = BK * t + 4 * grp + (c >> 2);
+    uint32_t vad[NT];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      const uint2 vt = lds_tr4(vreg + vr * (DV * 2) + 32 * (tt ^ (vr & 7)) + 8 * (c & 3));
-      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, vt), pb,
+    for (int tt = 0; tt < NT; ++tt)
+      vad[tt] = lds_off(vreg + vr * (DV * 2) + 32 * (tt ^ (vr & 7)) + 8 * (c & 3));
+    uint2 vt[NT];
+    lds_tr4x8(vt, vad);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, vt[tt]), pb,
                                                          acc[tt], 0, 0, 0);
-    }
-  }
+  };
+  static_assert(NT == 8 && KS == 6, "the read helpers take six K and eight V pieces");
+
+  // q and tile 0's ten copies have landed once at most tile 1's ten are in
+  // flight; tile 1 is computed after everything has landed
+  __builtin_amdgcn_s_waitcnt(0x0F7A);   // vmcnt(10)
+  if (nk > 0) tile(0);                  // uniform
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  if (nk > BK) tile(1);                 // uniform
   l = sum_across_groups(l);
 
   // ---- merge the four wavefronts' partials -----------------------------------

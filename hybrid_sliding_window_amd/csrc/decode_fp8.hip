@@ -242,6 +242,8 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, in
   }
 }
 
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
 // Rings of at most 128 slots in one launch (as the bf16 decode's
 // decode_ring_kernel): a workgroup per (sequence, kv head), wavefront w on
 // slots 32 w .. 32 w + 31.  Every copy of a wavefront's slots goes out at
@@ -280,57 +282,51 @@ __global__ __launch_bounds__(256, 2) void decode_ring_fp8_kernel(AttnArgs a) {
   }
   const int key0 = RG_ROWS * wave;             // this wavefront's first slot
   const int nk = (int)min((long long)RG_ROWS, max(0LL, len - key0));   // its valid slots
+  const int klast = (int)len - 1;              // len >= 1 here
 
-  // ---- copies: K slot s = 64 ii + lane (ii < 6) is row s / 12, 16-byte
-  // chunk s % 12; V slot s = 64 jj + lane (jj < 4) is row s / 8, chunk s % 8.
-  // Rows past the last valid slot reload the last one (finite data, masked).
-  if (nk > 0) {
-    const unsigned char* kb = static_cast<const unsigned char*>(a.k) + (row0 * a.hkv + g) * (long long)D;
-    const unsigned char* vb = static_cast<const unsigned char*>(a.v) + (row0 * a.hkv + g) * (long long)DV;
-    const int kstr = a.hkv * D, vstr = a.hkv * DV;
-#pragma unroll
-    for (int ii = 0; ii < RG_K8 / 1024; ++ii) {
-      const int sl = 64 * ii + lane;
-      const int row = sl / 12, pc = sl - row * 12;
-      const int key = key0 + min(row, nk - 1);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(kb + (__umul24(key, kstr) + 16 * pc)),
-                                       (lds_void_t*)(kreg + 1024 * ii), 16, 0, 0);
-    }
-#pragma unroll
-    for (int jj = 0; jj < RG_V8 / 1024; ++jj) {
-      const int sl = 64 * jj + lane;
-      const int row = sl >> 3, pc = sl & 7;
-      const int key = key0 + min(row, nk - 1);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (__umul24(key, vstr) + 16 * pc)),
-                                       (lds_void_t*)(vreg + 1024 * jj), 16, 0, 0);
-    }
-  }
-
+  const float kscale = a.kscale[g], vscale = a.vscale[g];
   // q of head g*G + c (rotated to position p by the preparation kernel when
-  // RoPE is on); columns c >= G are padding
+  // RoPE is on); columns c >= G repeat head G - 1 (their results are never
+  // stored).  Issued before the copies, so that it lands with tile 0.
   bf16x8 qf[KS];
   {
     const bf16_t* qsrc = static_cast<const bf16_t*>(a.half > 0 ? a.qrot : a.q);
     const bf16_t* qrow = qsrc + ((long long)b * a.hq + g * G + min(c, G - 1)) * D + 8 * grp;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = as_bf16x8(c < G ? ld16(qrow + 32 * ks) : make_uint4(0, 0, 0, 0));
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 32 * ks));
   }
-  const float kscale = a.kscale[g], vscale = a.vscale[g];
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): q and this wavefront's slots have landed
 
-  // widen the V codes: lane handles (row, 16-code chunk) items lane + 64 j
-  if (nk > 0) {
+  // ---- copies, tile by tile (keys 0..15, then 16..31 of the wavefront's
+  // slots): K slot s = 64 ii + lane (ii < 6) is row s / 12, 16-byte chunk
+  // s % 12; V slot s = 64 jj + lane (jj < 4) is row s / 8, chunk s % 8.
+  // Rows past the last valid slot reload the last one (finite data,
+  // masked); a wavefront with no valid slot reloads the ring's last written
+  // slot, so every wavefront issues the same 10 copies and the waits below
+  // count exactly.
+  {
+    const unsigned char* kb = static_cast<const unsigned char*>(a.k) + (row0 * a.hkv + g) * (long long)D;
+    const unsigned char* vb = static_cast<const unsigned char*>(a.v) + (row0 * a.hkv + g) * (long long)DV;
+    const int kstr = a.hkv * D, vstr = a.hkv * DV;
+    auto slot = [&](int row) { return min(key0 + min(row, nk - 1), klast); };
 #pragma unroll
-    for (int j = 0; j < RG_ROWS * DV / 16 / 64; ++j) {
-      const int it = lane + 64 * j;
-      const int row = it >> 3, cc = it & 7;
-      const uint4 codes = ld16(vreg + row * DV + 16 * cc);
-      unsigned char* dst = vwb + row * (DV * 2) + 32 * (cc ^ (row & 7));
-      st16(dst, widen8(make_uint2(codes.x, codes.y)));
-      st16(dst + 16, widen8(make_uint2(codes.z, codes.w)));
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int ii = 3 * t; ii < 3 * t + 3; ++ii) {
+        const int sl = 64 * ii + lane;
+        const int row = sl / 12, pc = sl - row * 12;
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(kb + (__umul24(slot(row), kstr) + 16 * pc)),
+                                         (lds_void_t*)(kreg + 1024 * ii), 16, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 2 * t; jj < 2 * t + 2; ++jj) {
+        const int sl = 64 * jj + lane;
+        const int row = sl >> 3, pc = sl & 7;
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (__umul24(slot(row), vstr) + 16 * pc)),
+                                         (lds_void_t*)(vreg + 1024 * jj), 16, 0, 0);
+      }
     }
   }
+  static_assert(RG_K8 == 6 * 1024 && RG_V8 == 4 * 1024, "three K and two V copies per tile");
 
   const float c2 = a.scale * kLog2e * kscale;   // raw code score -> base-2 units
   float m = kNegInf, l = 0.f;
@@ -338,17 +334,50 @@ __global__ __launch_bounds__(256, 2) void decode_ring_fp8_kernel(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // one 16-key tile: widen its V codes (lane handles the (row, 16-code
+  // chunk) items 128 t + lane and 128 t + 64 + lane) into the bf16 copy,
+  // then the products.  Reads of the copy targets are inline asm that wait
+  // for their own data, so the compiler's wait analysis does not add a
+  // wait for the copies still in flight; the wavefront's LDS operations
+  // complete in order, so its transposed reads see its widening writes.
+  auto tile = [&](int t) __attribute__((always_inline)) {
+    uint32_t wad[2];
 #pragma unroll
-  for (int t = 0; t < RG_ROWS / BK; ++t) {
-    if (t * BK >= nk) break;   // uniform
-    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int kr = BK * t + c;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      // dims 32 ks + 8 grp .. + 7 of key row kr: 8 codes
-      const uint2 w = *reinterpret_cast<const uint2*>(kreg + kr * D + 32 * ks + 8 * grp);
-      sc = mfma16(as_bf16x8(widen8(w)), qf[ks], sc);
+    for (int j = 0; j < 2; ++j) {
+      const int it = 128 * t + 64 * j + lane;
+      wad[j] = lds_off(vreg + (it >> 3) * DV + 16 * (it & 7));
     }
+    uint4 codes[2];
+    lds_b128x2(codes[0], codes[1], wad[0], wad[1]);
+    uint32_t dad[2];
+    u32x4_t wide[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int it = 128 * t + 64 * j + lane;
+      const int row = it >> 3, cc = it & 7;
+      dad[j] = lds_off(vwb + row * (DV * 2) + 32 * (cc ^ (row & 7)));
+      wide[2 * j] = __builtin_bit_cast(u32x4_t, widen8(make_uint2(codes[j].x, codes[j].y)));
+      wide[2 * j + 1] = __builtin_bit_cast(u32x4_t, widen8(make_uint2(codes[j].z, codes[j].w)));
+    }
+    // written in asm too: a plain LDS store would also wait for every copy
+    // in flight (the compiler orders it after all pending LDS writes)
+    asm volatile(
+        "ds_write_b128 %0, %2\n\t"
+        "ds_write_b128 %0, %3 offset:16\n\t"
+        "ds_write_b128 %1, %4\n\t"
+        "ds_write_b128 %1, %5 offset:16"
+        :
+        : "v"(dad[0]), "v"(dad[1]), "v"(wide[0]), "v"(wide[1]), "v"(wide[2]), "v"(wide[3])
+        : "memory");
+    const int kr = BK * t + c;
+    uint32_t kad[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kad[ks] = lds_off(kreg + kr * D + 32 * ks + 8 * grp);
+    uint2 kw[KS];
+    lds_b64x6(kw, kad);   // dims 32 ks + 8 grp .. + 7 of key row kr: 8 codes each
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sc = mfma16(as_bf16x8(widen8(kw[ks])), qf[ks], sc);
     // branch-free masking (see the split kernels)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sc[r] = (BK * t + 4 * grp + r < nk) ? sc[r] : kNegInf;
@@ -367,13 +396,25 @@ __global__ __launch_bounds__(256, 2) void decode_ring_fp8_kernel(AttnArgs a) {
     for (int tt = 0; tt < NT; ++tt) acc[tt] *= alpha;
     const v4i16_t pb = __builtin_bit_cast(v4i16_t, pk);
     const int vr = BK * t + 4 * grp + (c >> 2);
+    uint32_t vad[NT];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      const uint2 vt = lds_tr4(vwb + vr * (DV * 2) + 32 * (tt ^ (vr & 7)) + 8 * (c & 3));
-      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16_t, vt), pb,
+    for (int tt = 0; tt < NT; ++tt)
+      vad[tt] = lds_off(vwb + vr * (DV * 2) + 32 * (tt ^ (vr & 7)) + 8 * (c & 3));
+    uint2 vt[NT];
+    lds_tr4x8(vt, vad);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16_t, vt[tt]), pb,
                                                          acc[tt], 0, 0, 0);
-    }
-  }
+  };
+  static_assert(NT == 8 && KS == 6 && RG_ROWS == 2 * BK, "two tiles; six K and eight V pieces");
+
+  // q and tile 0's five copies have landed once at most tile 1's five are
+  // in flight; tile 1 is computed after everything has landed
+  __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
+  if (nk > 0) tile(0);                  // uniform
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  if (nk > BK) tile(1);                 // uniform
   l = sum_across_groups(l);
 
   // ---- merge the four wavefronts' partials (O [16 columns][128 dims], m and

@@ -525,6 +525,28 @@ def test_ring_decode_rope_large_positions(gpu_lib):
     _check("ring decode rope", o, ref)
 
 
+@pytest.mark.parametrize("hq,hkv,W", [(64, 4, 64), (16, 4, 100), (32, 8, 33), (8, 8, 128)])
+def test_ring_decode_other_windows_and_groups(gpu_lib, hq, hkv, W):
+    """The one-launch ring kernels (bf16 and E4M3 caches) at windows below 128,
+    where whole wavefronts of slots are empty, and at GQA groups 16, 4 and 1
+    (padded MFMA columns), warm-up positions included (rslog.cc section 2.1:
+    the window holds the last W tokens, fewer before the W-th)."""
+    pos = [0, 3, W - 2, W - 1, W, 5000, 131071]
+    d = _ring_case(pos, hq=hq, hkv=hkv, W=W, seed=95)
+    o = gpu_lib.swa_sink_decode(d["q"], d["k"], d["v"], d["pos"], max(pos), layout=gpu_lib.KV_RING,
+                                sink=d["sink"], window=W)
+    ref = oracle.swa_sink_decode_ring(_np(d["q"]), _np(d["k"]), _np(d["v"]), np.array(pos),
+                                      _np(d["sink"]))
+    _check(f"ring decode hq {hq} hkv {hkv} W {W}", o, ref)
+    f = synthetic.ring_decode_inputs_fp8(len(pos), hq, hkv, W, 192, 128, 96, torch.tensor(pos), DEV)
+    o8 = gpu_lib.swa_sink_decode_fp8(f["q"], f["k"], f["v"], f["k_scale"], f["v_scale"], f["pos"],
+                                     max(pos), layout=gpu_lib.KV_RING, sink=f["sink"], window=W)
+    ref8 = oracle.swa_sink_decode_ring_fp8(_np(f["q"]), f["k"].cpu().numpy(), f["v"].cpu().numpy(),
+                                           _np(f["k_scale"]), _np(f["v_scale"]), np.array(pos),
+                                           _np(f["sink"]))
+    _check(f"ring decode fp8 hq {hq} hkv {hkv} W {W}", o8, ref8)
+
+
 def _contig_case(pos, hq=64, hkv=4, seed=90, dtype="bf16", sink=None, extra=0):
     pos = torch.as_tensor(pos, dtype=torch.int64)
     return synthetic.contiguous_decode_inputs(len(pos), hq, hkv, 192, 128, dtype, seed, pos, DEV,
