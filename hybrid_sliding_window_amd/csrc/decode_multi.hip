@@ -530,32 +530,11 @@ __global__ __launch_bounds__(64 * MR_NW, 1) void decode_multi_ring_kernel(AttnAr
   }
   const int key0 = MR_ROWS * wave;             // this wavefront's first slot
   const int nk = (int)min((long long)MR_ROWS, max(0LL, len - key0));   // its valid slots
+  const int klast = (int)len - 1;              // len >= 1 here
 
-  if (nk > 0) {
-    const unsigned char* kb = static_cast<const unsigned char*>(a.k) + (row0 * a.hkv + g) * (long long)(D * 2);
-    const unsigned char* vb = static_cast<const unsigned char*>(a.v) + (row0 * a.hkv + g) * (long long)(DV * 2);
-    const int kstr = a.hkv * D * 2, vstr = a.hkv * DV * 2;
-#pragma unroll
-    for (int ii = 0; ii < MR_K / 1024; ++ii) {
-      const int sl = 64 * ii + lane;
-      const int row = sl / 24, pc = sl - row * 24;
-      const int lc = pc ^ ((row >> 1) & 7);
-      const int key = key0 + min(row, nk - 1);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(kb + (__umul24(key, kstr) + 16 * lc)),
-                                       (lds_void_t*)(kreg + 1024 * ii), 16, 0, 0);
-    }
-#pragma unroll
-    for (int jj = 0; jj < MR_V / 1024; ++jj) {
-      const int sl = 64 * jj + lane;
-      const int row = sl >> 4, pc = sl & 15;
-      const int lc = 2 * ((pc >> 1) ^ (row & 7)) + (pc & 1);
-      const int key = key0 + min(row, nk - 1);
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (__umul24(key, vstr) + 16 * lc)),
-                                       (lds_void_t*)(vreg + 1024 * jj), 16, 0, 0);
-    }
-  }
-
-  // this lane's query columns: n = 16 nb + c (token n / G, head n % G)
+  // this lane's query columns: n = 16 nb + c (token n / G, head n % G);
+  // columns n >= T * G repeat column 0 (their results are never stored).
+  // Issued before the copies, so that q lands with tile 0.
   bf16x8 qf[NB][KS];
   int ctok[NB];
   bool cval[NB];
@@ -569,11 +548,41 @@ __global__ __launch_bounds__(64 * MR_NW, 1) void decode_multi_ring_kernel(AttnAr
       ctok[nb] = tn;
       const bf16_t* qrow = qsrc + (((long long)b * T + tn) * a.hq + g * G + hn) * D + 8 * grp;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qf[nb][ks] = as_bf16x8(cval[nb] ? ld16(qrow + 32 * ks) : make_uint4(0, 0, 0, 0));
+      for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = as_bf16x8(ld16(qrow + 32 * ks));
     }
   }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // q and this wavefront's slots have landed
+
+  // copies, tile by tile (slots 0..15, then 16..31 of the wavefront's
+  // range); rows past the last valid slot reload the last one (finite data,
+  // masked), and a wavefront with no valid slot reloads the ring's last
+  // written slot, so every wavefront issues the same 20 copies and the waits
+  // below count exactly
+  {
+    const unsigned char* kb = static_cast<const unsigned char*>(a.k) + (row0 * a.hkv + g) * (long long)(D * 2);
+    const unsigned char* vb = static_cast<const unsigned char*>(a.v) + (row0 * a.hkv + g) * (long long)(DV * 2);
+    const int kstr = a.hkv * D * 2, vstr = a.hkv * DV * 2;
+    auto slot = [&](int row) { return min(key0 + min(row, nk - 1), klast); };
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int ii = 6 * t; ii < 6 * t + 6; ++ii) {
+        const int sl = 64 * ii + lane;
+        const int row = sl / 24, pc = sl - row * 24;
+        const int lc = pc ^ ((row >> 1) & 7);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(kb + (__umul24(slot(row), kstr) + 16 * lc)),
+                                         (lds_void_t*)(kreg + 1024 * ii), 16, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 4 * t; jj < 4 * t + 4; ++jj) {
+        const int sl = 64 * jj + lane;
+        const int row = sl >> 4, pc = sl & 15;
+        const int lc = 2 * ((pc >> 1) ^ (row & 7)) + (pc & 1);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(vb + (__umul24(slot(row), vstr) + 16 * lc)),
+                                         (lds_void_t*)(vreg + 1024 * jj), 16, 0, 0);
+      }
+    }
+  }
+  static_assert(MR_K == 12 * 1024 && MR_V == 8 * 1024 && MR_ROWS == 2 * BK, "two tiles of 10 copies");
 
   const KeyPos kpos = key_pos(a, 0, p0, row0, 0);
   const float c2 = a.scale * kLog2e;
@@ -587,9 +596,10 @@ __global__ __launch_bounds__(64 * MR_NW, 1) void decode_multi_ring_kernel(AttnAr
     for (int t = 0; t < NT; ++t) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-#pragma unroll
-  for (int t = 0; t < MR_ROWS / BK; ++t) {
-    if (t * BK >= nk) break;   // uniform
+  // one 16-key tile from the wavefront's region; its LDS reads are inline
+  // asm that wait for their own data, so the compiler's wait analysis does
+  // not add a wait for the copies still in flight
+  auto tile = [&](int t) __attribute__((always_inline)) {
     // visibility of slot key0 + 16 t + 4 grp + r to column token tn, decided
     // before the score products (see the split kernel)
     bool vis[NB][4];
@@ -606,12 +616,16 @@ __global__ __launch_bounds__(64 * MR_NW, 1) void decode_multi_ring_kernel(AttnAr
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) sc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int kr = BK * t + c;
+    uint32_t kad[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kad[ks] = lds_off(kreg + kr * (D * 2) + 16 * ((4 * ks + grp) ^ ((kr >> 1) & 7)));
+    uint4 kw[KS];
+    lds_b128x6(kw, kad);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int pcq = (4 * ks + grp) ^ ((kr >> 1) & 7);
-      const bf16x8 kf = as_bf16x8(ld16(kreg + kr * (D * 2) + 16 * pcq));
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma16(kf, qf[nb][ks], sc[nb]);
+      for (int nb = 0; nb < NB; ++nb) sc[nb] = mfma16(as_bf16x8(kw[ks]), qf[nb][ks], sc[nb]);
     }
     uint2 pk[NB];
 #pragma unroll
@@ -633,16 +647,29 @@ __global__ __launch_bounds__(64 * MR_NW, 1) void decode_multi_ring_kernel(AttnAr
       for (int tt = 0; tt < NT; ++tt) acc[tt][nb] *= alpha;
     }
     const int vr = BK * t + 4 * grp + (c >> 2);
+    uint32_t vad[NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+      vad[tt] = lds_off(vreg + vr * (DV * 2) + 32 * (tt ^ (vr & 7)) + 8 * (c & 3));
+    uint2 vt[NT];
+    lds_tr4x8(vt, vad);
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
-      const uint2 vt = lds_tr4(vreg + vr * (DV * 2) + 32 * (tt ^ (vr & 7)) + 8 * (c & 3));
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         acc[tt][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            __builtin_bit_cast(v4i16_t, vt), __builtin_bit_cast(v4i16_t, pk[nb]), acc[tt][nb], 0,
-            0, 0);
+            __builtin_bit_cast(v4i16_t, vt[tt]), __builtin_bit_cast(v4i16_t, pk[nb]), acc[tt][nb],
+            0, 0, 0);
     }
-  }
+  };
+  static_assert(NT == 8 && KS == 6, "the read helpers take six K and eight V pieces");
+
+  // q and tile 0's ten copies have landed once at most tile 1's ten are in
+  // flight; tile 1 is computed after everything has landed
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(10));
+  if (nk > 0) tile(0);                  // uniform
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if (nk > BK) tile(1);                 // uniform
 
   // ---- merge: each wavefront leaves O [16 NB columns][128 dims], m and l
   // [16 NB] (fp32, base 2) in its own region; wavefronts 0..3 then write
