@@ -113,6 +113,76 @@ def batched_us(fn, calls=200):
     return a.elapsed_time(b) * 1e3 / calls
 
 
+def graph_us(fn, calls=64, replays=20):
+    """Device time per call with the host out of the loop: `calls` calls
+    captured in one HIP graph (torch.cuda.CUDAGraph on torch's current
+    device), replayed `replays` times between one event pair.  For calls of
+    ~10 us the host-side argument checks of each call take longer than the
+    kernel, so back-to-back eager calls measure the host (us_batched); a
+    serving loop replays such steps as a graph."""
+    settle_clock(fn)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) * 1e3 / (replays * calls)
+
+
+def small_stream_bound_us(read_bytes, write_bytes):
+    """Device time per call of hswa_stream_probe moving read_bytes in (from
+    rotated sources, over 400 MB in all, so that the reads are not served
+    from the 256 MB last-level cache) and write_bytes out, timed as graph_us:
+    the bound for a one-launch step of that many bytes, launch ramp
+    included.  Best of 1, 2 and 4 workgroups of 4 wavefronts per CU."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rb = (read_bytes + 1023) // 1024 * 1024
+    wb = max(1024, (write_bytes + 1023) // 1024 * 1024)
+    sets = max(8, -(-400_000_000 // rb))
+    srcs = [torch.empty(rb, dtype=torch.uint8, device="cuda") for _ in range(sets)]
+    dst = torch.empty(wb, dtype=torch.uint8, device="cuda")
+    best = None
+    for per_cu in (1, 2, 4):
+        blocks = per_cu * cus
+        o = torch.empty(4 * blocks, dtype=torch.int32, device="cuda")
+        it = [0]
+
+        def step():
+            src = srcs[it[0] % sets]
+            it[0] += 1
+            hswa.stream_probe(src, dst, blocks, out=o)
+        us = graph_us(step)
+        if best is None or us < best[0]:
+            best = (us, 4 * per_cu)
+    del srcs, dst
+    return {"us": best[0], "waves_per_cu": best[1], "read_bytes": rb, "write_bytes": wb}
+
+
+def _graph_entry(step, nbytes, read_bytes, write_bytes):
+    us = graph_us(step)
+    bound = small_stream_bound_us(read_bytes, write_bytes)
+    return {"us": us, "gbps": nbytes / us / 1e3, "frac_of_hbm_peak": nbytes / us / 1e3 / HBM_PEAK_GBPS,
+            "stream_bound_us": bound["us"], "frac_of_stream_bound": bound["us"] / us,
+            "note": "64 calls (rotated buffer sets) captured in one HIP graph and replayed: device "
+                    "time per call; stream bound: hswa_stream_probe moving the same read and "
+                    "written bytes in one launch, timed the same way"}
+
+
 def _traffic(kernel_key):
     """HBM bytes per launch from the committed rocprofv3 counter summary.
 
@@ -438,9 +508,11 @@ def _decode(out, dev, cpu_budget=0.0, ring=True, ga=True):
                       wl["B"] * sw["hq"] * (192 + 128) * 2)
         t = float(np.mean(per)) / 1e3
         tb = batched_us(ring_step) / 1e6
+        out_bytes = wl["B"] * sw["hq"] * 128 * 2
         out["decode_swa_ring"] = {"gbps": ring_bytes / t / 1e9, "us": t * 1e6, "bytes": ring_bytes,
                                   "frac_of_hbm_peak": ring_bytes / t / 1e9 / HBM_PEAK_GBPS,
                                   "us_batched": tb * 1e6, "gbps_batched": ring_bytes / tb / 1e9,
+                                  "graph": _graph_entry(ring_step, ring_bytes, ring_bytes, out_bytes),
                                   "note": "8 rotated buffer sets (353 MB) to defeat MALL residency; "
                                           "us: one event pair per call; us_batched: 200 calls "
                                           "between one event pair"}
@@ -523,7 +595,9 @@ def _decode_mtp(out, dev):
     tb = batched_us(ring_step) / 1e6
     out["decode_mtp_swa_ring"] = {"gbps": ring_bytes / t / 1e9, "us": t * 1e6, "bytes": ring_bytes,
                                   "queries_per_s": wl["B"] * T / t, "us_batched": tb * 1e6,
-                                  "gbps_batched": ring_bytes / tb / 1e9}
+                                  "gbps_batched": ring_bytes / tb / 1e9,
+                                  "graph": _graph_entry(ring_step, ring_bytes, ring_bytes,
+                                                        wl["B"] * T * sw["hq"] * 128 * 2)}
     _log(f"MTP decode ring {out['decode_mtp_swa_ring']}")
     del sets
     c = synthetic.multi_contiguous_inputs(wl["B"], T, ga["hq"], ga["hkv"], 192, 128, "bf16",
@@ -588,7 +662,9 @@ def _decode_fp8(out, dev):
     tb = batched_us(ring_step) / 1e6
     out["decode_fp8_swa_ring"] = {"gbps": ring_bytes / t / 1e9, "us": t * 1e6, "bytes": ring_bytes,
                                   "frac_of_hbm_peak": ring_bytes / t / 1e9 / HBM_PEAK_GBPS,
-                                  "us_batched": tb * 1e6, "gbps_batched": ring_bytes / tb / 1e9}
+                                  "us_batched": tb * 1e6, "gbps_batched": ring_bytes / tb / 1e9,
+                                  "graph": _graph_entry(ring_step, ring_bytes, ring_bytes,
+                                                        wl["B"] * sw["hq"] * 128 * 2)}
     _log(f"decode fp8 ring {out['decode_fp8_swa_ring']}")
     del sets
     c = synthetic.contiguous_decode_inputs_fp8(wl["B"], ga["hq"], ga["hkv"], 192, 128, wl["seed"],
