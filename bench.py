@@ -1,6 +1,6 @@
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu] [--no-graph]
 
 A step is one sliding-window+sink prefill of the SWA-layer workload
 (n = 32768 tokens, 64 query / 8 kv heads, d_qk 192, d_v 128, W = 128,
@@ -173,7 +173,12 @@ def small_stream_bound_us(read_bytes, write_bytes):
     return {"us": best[0], "waves_per_cu": best[1], "read_bytes": rb, "write_bytes": wb}
 
 
+GRAPH_TIMING = True   # cleared by --no-graph (profiler runs)
+
+
 def _graph_entry(step, nbytes, read_bytes, write_bytes):
+    if not GRAPH_TIMING:
+        return None
     us = graph_us(step)
     bound = small_stream_bound_us(read_bytes, write_bytes)
     return {"us": us, "gbps": nbytes / us / 1e3, "frac_of_hbm_peak": nbytes / us / 1e3 / HBM_PEAK_GBPS,
@@ -863,6 +868,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replayed decode timings (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["prefill", "tiny", "ga", "chunk", "decode", "decode_ring",
                                        "decode_ga", "decode_mtp", "decode_fp8", "sparse", "gather",
@@ -874,6 +881,8 @@ def main():
               "(the sharding plan is design only).", file=sys.stderr)
         sys.exit(2)
     _ensure_built()
+    global GRAPH_TIMING
+    GRAPH_TIMING = not args.no_graph
     dev = "cuda"
     if args.only and args.only != "prefill":
         print(json.dumps(only(args.only, args.steps, args.warmup)), flush=True)
