@@ -55,41 +55,82 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 
 }  // namespace
 
-// Three LDS stages: tile t + 2 is requested while tile t is computed, so a
-// workgroup keeps two tiles (40 KB) of loads in flight, as the bf16 decode
-// does with its twice-as-large tiles; two workgroups share a compute unit.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// The widened V codes of two 16-code chunks (32 bytes each at a[0], a[1])
+// written to LDS in asm: a plain LDS store makes the compiler wait for every
+// copy in flight first (it orders the store after all pending LDS writes).
+__device__ __forceinline__ void lds_st_wide(const uint32_t (&a)[2], const u32x4_t (&w)[4]) {
+  asm volatile(
+      "ds_write_b128 %0, %2\n\t"
+      "ds_write_b128 %0, %3 offset:16\n\t"
+      "ds_write_b128 %1, %4\n\t"
+      "ds_write_b128 %1, %5 offset:16"
+      :
+      : "v"(a[0]), "v"(a[1]), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3])
+      : "memory");
+}
+
+// A workgroup of 8 wavefronts takes two consecutive splits s = 2 sp and
+// 2 sp + 1 of one (sequence, group of four kv heads): wavefront w computes
+// head w % 4 of split 2 sp + w / 4.  Only wavefronts 0..3 (one per SIMD)
+// issue copies, those of both splits (ten per tile): a wavefront stalls
+// while the vector-memory path accepts its copies, and the other wavefront
+// of its SIMD, which issues none, computes meanwhile.  Three LDS stages per
+// split: tile t + 2 is requested while tile t is computed, so two tiles
+// (40 KB per split) of loads stay in flight.
 constexpr int NST = 3;
-__global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, int layout) {
-  __shared__ __attribute__((aligned(16))) unsigned char kst[NST][KTILE8];
-  __shared__ __attribute__((aligned(16))) unsigned char vst[NST][VTILE8];
-  __shared__ __attribute__((aligned(16))) unsigned char vwide[VTILEB];
+constexpr int SPW = 2;   // splits per workgroup
+__global__ __launch_bounds__(64 * HG * SPW, 1) void decode_fp8_split_kernel(AttnArgs a, int layout) {
+  __shared__ __attribute__((aligned(16))) unsigned char kst[SPW][NST][KTILE8];
+  __shared__ __attribute__((aligned(16))) unsigned char vst[SPW][NST][VTILE8];
+  __shared__ __attribute__((aligned(16))) unsigned char vwide_all[SPW][VTILEB];
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
-  const int gx = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
+  const int wave = wv & (HG - 1);                            // head within the group
+  const int half = wv / HG;                                  // which of the two splits
+  const bool producer = half == 0;
+  const int gx = blockIdx.x, b = blockIdx.z;
   const int g = HG * gx + wave;
   const int lane = tid & 63, c = lane & 15, grp = lane >> 4;
   const int G = a.hq / a.hkv;
+  unsigned char* vwide = vwide_all[half];
 
   long long p, row0, len;
   if (!key_range(a, layout, b, &p, &row0, &len)) return;   // uniform over the workgroup
-  const long long ks0 = (long long)s * a.split_keys;
-  if (ks0 >= len) return;
-  const long long ks1 = (ks0 + a.split_keys < len) ? ks0 + a.split_keys : len;
-  const int nkeys = (int)(ks1 - ks0);
-  const int ntile = (nkeys + BK - 1) / BK;
+  // keys of split 2 sp + h: [ks0[h], ks0[h] + nk[h]); the second may be empty
+  long long ks0[SPW];
+  int nk[SPW];
+#pragma unroll
+  for (int h = 0; h < SPW; ++h) {
+    ks0[h] = (long long)(SPW * blockIdx.y + h) * a.split_keys;
+    const long long e = (ks0[h] + a.split_keys < len) ? ks0[h] + a.split_keys : len;
+    nk[h] = (e > ks0[h]) ? (int)(e - ks0[h]) : 0;
+  }
+  if (nk[0] == 0) return;   // uniform: the second split starts later still
+  const int ntile = (nk[0] + BK - 1) / BK;                 // steps of the loop (the longer split)
+  const int my_nk = nk[half];
+  const int my_ntile = (my_nk + BK - 1) / BK;
 
-  // ---- this lane's 16-byte slots of a tile ------------------------------------
+  // ---- the 16-byte slots of a tile a producer copies ------------------------
   // Load instruction ii = wave + 4u fills LDS bytes [1024 ii', +1024) of the
   // K stage (ii < 12, ii' = ii) or the V stage (ii' = ii - 12).  K slot s is
   // row s / 48, physical chunk pc = s % 48 holding logical chunk pc ^ row%16
   // (XOR on the low four bits: within its aligned 256 B); V slot s is row
   // s / 32, physical chunk pc = s % 32 holding logical chunk pc ^ row%8
-  // (within its head's aligned 128 B).  Rows past the split reload its last
-  // key (masked later).
-  const unsigned char* kbase = static_cast<const unsigned char*>(a.k) +
-                               ((row0 + ks0) * a.hkv + HG * gx) * (long long)D;
-  const unsigned char* vbase = static_cast<const unsigned char*>(a.v) +
-                               ((row0 + ks0) * a.hkv + HG * gx) * (long long)DV;
+  // (within its head's aligned 128 B).  Rows past a split reload its last
+  // key (masked later); an empty second split reloads the first one's rows
+  // (never read).
+  const unsigned char* kbase[SPW];
+  const unsigned char* vbase[SPW];
+  int lastkey[SPW];
+#pragma unroll
+  for (int h = 0; h < SPW; ++h) {
+    const int hh = (nk[h] > 0) ? h : 0;
+    kbase[h] = static_cast<const unsigned char*>(a.k) + ((row0 + ks0[hh]) * a.hkv + HG * gx) * (long long)D;
+    vbase[h] = static_cast<const unsigned char*>(a.v) + ((row0 + ks0[hh]) * a.hkv + HG * gx) * (long long)DV;
+    lastkey[h] = nk[hh] - 1;
+  }
   const int kstride = a.hkv * D, vstride = a.hkv * DV;   // bytes per cache row
   int drow[DMA_PER_WAVE], doff[DMA_PER_WAVE];
 #pragma unroll
@@ -107,17 +148,23 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, in
       doff[u] = 16 * (pc ^ (row & 7));
     }
   }
-  auto issue = [&](int k0, unsigned char* kd, unsigned char* vd) {
+  // the copies of tile t of both splits into stage st (producers only)
+  auto issue = [&](int t, int st) {
 #pragma unroll
-    for (int u = 0; u < DMA_PER_WAVE; ++u) {
-      const int ii = wave + HG * u;
-      const int key = min(k0 + drow[u], nkeys - 1);
-      if (u < KINSTR / HG)   // wave-uniform: the first three instructions are K, the rest V
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(kbase + (__umul24(key, kstride) + doff[u])),
-                                         (lds_void_t*)(kd + 1024 * ii), 16, 0, 0);
-      else
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(vbase + (__umul24(key, vstride) + doff[u])),
-                                         (lds_void_t*)(vd + 1024 * (ii - KINSTR)), 16, 0, 0);
+    for (int h = 0; h < SPW; ++h) {
+#pragma unroll
+      for (int u = 0; u < DMA_PER_WAVE; ++u) {
+        const int ii = wave + HG * u;
+        const int key = min(t * BK + drow[u], lastkey[h]);
+        if (u < KINSTR / HG)   // wave-uniform: the first three instructions are K, the rest V
+          __builtin_amdgcn_global_load_lds(
+              (glb_void_t*)(kbase[h] + (__umul24(key, kstride) + doff[u])),
+              (lds_void_t*)(kst[h][st] + 1024 * ii), 16, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds(
+              (glb_void_t*)(vbase[h] + (__umul24(key, vstride) + doff[u])),
+              (lds_void_t*)(vst[h][st] + 1024 * (ii - KINSTR)), 16, 0, 0);
+      }
     }
   };
   static_assert(KINSTR / HG == 3, "the K/V split of a wavefront's loads");
@@ -136,8 +183,10 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, in
   // q has landed before the first copies go out (a wait the compiler sees,
   // so that it adds none of its own inside the tile loop)
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  issue(0, kst[0], vst[0]);
-  if (ntile > 1) issue(BK, kst[1], vst[1]);
+  if (producer) {
+    issue(0, 0);
+    if (ntile > 1) issue(1, 1);
+  }
 
   const float c2 = a.scale * kLog2e * kscale;   // raw code score -> base-2 units
   float m = kNegInf, l = 0.f;
@@ -153,26 +202,22 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, in
   const int vr = 4 * grp + (c >> 2);
   const int vrow = vr * VROWB + 8 * (c & 3);
 
-  auto tile = [&](int t, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
-                  unsigned char* vn) __attribute__((always_inline)) {
-    // This wavefront's loads in flight: tile t's, then (if it exists) tile
-    // t + 1's five.
-    if (t + 1 < ntile) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
-    ring_barrier();   // every wavefront's share of tile t has landed; tile t-1 is consumed
-    if (t + 2 < ntile) issue((t + 2) * BK, kn, vn);
+  auto tile = [&](int t, const unsigned char* kc, const unsigned char* vc) __attribute__((always_inline)) {
     // widen this wavefront's V stripe; LDS operations of a wavefront complete
     // in order, so its transposed reads below see these writes
     const int u0 = 8 * wave + 2 * grp;
     uint4 codes[2];
     lds_b128x2(codes[0], codes[1], lds_off(vc + c * VROW8 + 16 * (u0 ^ (c & 7))),
                lds_off(vc + c * VROW8 + 16 * ((u0 + 1) ^ (c & 7))));
+    uint32_t dad[2];
+    u32x4_t wide[4];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      unsigned char* dst = vwide + c * VROWB + 32 * ((u0 + j) ^ (c & 7));
-      st16(dst, widen8(make_uint2(codes[j].x, codes[j].y)));
-      st16(dst + 16, widen8(make_uint2(codes[j].z, codes[j].w)));
+      dad[j] = lds_off(vwide + c * VROWB + 32 * ((u0 + j) ^ (c & 7)));
+      wide[2 * j] = __builtin_bit_cast(u32x4_t, widen8(make_uint2(codes[j].x, codes[j].y)));
+      wide[2 * j + 1] = __builtin_bit_cast(u32x4_t, widen8(make_uint2(codes[j].z, codes[j].w)));
     }
+    lds_st_wide(dad, wide);
     const int k0 = t * BK;
     // dims 32 ks + 8 grp .. + 7: logical 16-byte chunk 12 wave + 2 ks + grp/2, half grp%2
     uint32_t kad[KS];
@@ -186,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, in
     for (int ks = 0; ks < KS; ++ks) sc = mfma16(as_bf16x8(widen8(kw[ks])), qf[ks], sc);
     // Branch-free on purpose (MFMA result read by the VALU right after).
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = (k0 + 4 * grp + r < nkeys) ? sc[r] : kNegInf;
+    for (int r = 0; r < 4; ++r) sc[r] = (k0 + 4 * grp + r < my_nk) ? sc[r] : kNegInf;
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = max_across_groups(mx) * c2;   // base-2 units
     // lazy rescaling, as the bf16 decode
@@ -207,26 +252,37 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, in
     // l sums the bf16 P that weight V
     l += add_bf16_pair(pk.y, add_bf16_pair(pk.x, 0.f));
     const v4i16_t pb = __builtin_bit_cast(v4i16_t, pk);
+    uint32_t vad[NT];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      const uint2 vt = lds_tr4(vwide + vrow + 32 * ((8 * wave + tt) ^ (vr & 7)));
-      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16_t, vt), pb,
+    for (int tt = 0; tt < NT; ++tt) vad[tt] = lds_off(vwide + vrow + 32 * ((8 * wave + tt) ^ (vr & 7)));
+    uint2 vt[NT];
+    lds_tr4x8(vt, vad);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16_t, vt[tt]), pb,
                                                          acc[tt], 0, 0, 0);
-    }
   };
 
   // tile t sits in stage t % 3; tile t + 2 goes to stage (t + 2) % 3, the
-  // one tile t - 1 used
-  static_assert(DMA_PER_WAVE == 5, "the waits count five loads per tile");
+  // one tile t - 1 used.  A producer's loads in flight at step t: tile t's
+  // ten, then (if it exists) tile t + 1's ten.
+  static_assert(DMA_PER_WAVE == 5 && SPW == 2, "the waits count ten loads per tile");
   int st = 0;
   for (int t = 0; t < ntile; ++t) {
     const int sn = (st == 0) ? 2 : st - 1;
-    tile(t, kst[st], vst[st], kst[sn], vst[sn]);
+    if (producer) {
+      if (t + 1 < ntile) __builtin_amdgcn_s_waitcnt(0x0F7A);   // vmcnt(10)
+      else __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
+    }
+    ring_barrier();   // every share of tile t has landed; tile t-1 is consumed
+    if (producer && t + 2 < ntile) issue(t + 2, sn);
+    if (t < my_ntile) tile(t, kst[half][st], vst[half][st]);   // uniform per wavefront
     st = (st == NST - 1) ? 0 : st + 1;
   }
 
+  const int s = SPW * blockIdx.y + half;
   l = sum_across_groups(l);
-  if (g < a.hkv && c < G) {
+  if (my_nk > 0 && g < a.hkv && c < G) {
     const long long idx = ((long long)b * a.hq + g * G + c) * a.nsplit + s;
     float* wo = a.ws + idx * DV + 4 * grp;
 #pragma unroll
@@ -241,8 +297,6 @@ __global__ __launch_bounds__(256, 2) void decode_fp8_split_kernel(AttnArgs a, in
     }
   }
 }
-
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 // Rings of at most 128 slots in one launch (as the bf16 decode's
 // decode_ring_kernel): a workgroup per (sequence, kv head), wavefront w on
@@ -359,16 +413,7 @@ __global__ __launch_bounds__(256, 2) void decode_ring_fp8_kernel(AttnArgs a) {
       wide[2 * j] = __builtin_bit_cast(u32x4_t, widen8(make_uint2(codes[j].x, codes[j].y)));
       wide[2 * j + 1] = __builtin_bit_cast(u32x4_t, widen8(make_uint2(codes[j].z, codes[j].w)));
     }
-    // written in asm too: a plain LDS store would also wait for every copy
-    // in flight (the compiler orders it after all pending LDS writes)
-    asm volatile(
-        "ds_write_b128 %0, %2\n\t"
-        "ds_write_b128 %0, %3 offset:16\n\t"
-        "ds_write_b128 %1, %4\n\t"
-        "ds_write_b128 %1, %5 offset:16"
-        :
-        : "v"(dad[0]), "v"(dad[1]), "v"(wide[0]), "v"(wide[1]), "v"(wide[2]), "v"(wide[3])
-        : "memory");
+    lds_st_wide(dad, wide);
     const int kr = BK * t + c;
     uint32_t kad[KS];
 #pragma unroll
@@ -477,8 +522,8 @@ hipError_t launch_decode_fp8(const AttnArgs& a, int layout, hipStream_t stream) 
                        stream, a);
     return hipGetLastError();
   }
-  dim3 g1((unsigned)(a.hkv / HG), (unsigned)a.nsplit, (unsigned)a.B);
-  hipLaunchKernelGGL(decode_fp8_split_kernel, g1, dim3(256), 0, stream, a, layout);
+  dim3 g1((unsigned)(a.hkv / HG), (unsigned)((a.nsplit + SPW - 1) / SPW), (unsigned)a.B);
+  hipLaunchKernelGGL(decode_fp8_split_kernel, g1, dim3(64 * HG * SPW), 0, stream, a, layout);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_combine(a, layout, stream);
