@@ -83,37 +83,63 @@ __global__ __launch_bounds__(64) void decode_rope_q_kernel(AttnArgs a, int layou
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(AttnArgs a, int layout) {
-  __shared__ __attribute__((aligned(16))) unsigned char kst0[KTILE];
-  __shared__ __attribute__((aligned(16))) unsigned char vst0[VTILE];
-  __shared__ __attribute__((aligned(16))) unsigned char kst1[KTILE];
-  __shared__ __attribute__((aligned(16))) unsigned char vst1[VTILE];
+// A workgroup of 8 wavefronts takes two consecutive splits s = 2 sp and
+// 2 sp + 1 of one (sequence, group of four kv heads): wavefront w computes
+// head w % 4 of split 2 sp + w / 4.  Only wavefronts 0..3 (one per SIMD)
+// issue copies, those of both splits (20 per tile): a wavefront stalls while
+// the vector-memory path accepts its copies, and the other wavefront of its
+// SIMD, which issues none, computes meanwhile.  Two LDS stages per split
+// (the CU's 160 KB): tile t + 1 is requested while tile t is computed.
+constexpr int SPW = 2;   // splits per workgroup
+__global__ __launch_bounds__(64 * HG * SPW, 1) void decode_split_kernel(AttnArgs a, int layout) {
+  __shared__ __attribute__((aligned(16))) unsigned char kst[SPW][2][KTILE];
+  __shared__ __attribute__((aligned(16))) unsigned char vst[SPW][2][VTILE];
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
-  const int gx = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
+  const int wave = wv & (HG - 1);                            // head within the group
+  const int half = wv / HG;                                  // which of the two splits
+  const bool producer = half == 0;
+  const int gx = blockIdx.x, b = blockIdx.z;
   const int g = HG * gx + wave;
   const int lane = tid & 63, c = lane & 15, grp = lane >> 4;
   const int G = a.hq / a.hkv;
 
   long long p, row0, len;
   if (!key_range(a, layout, b, &p, &row0, &len)) return;   // uniform over the workgroup
-  const long long ks0 = (long long)s * a.split_keys;
-  if (ks0 >= len) return;
-  const long long ks1 = (ks0 + a.split_keys < len) ? ks0 + a.split_keys : len;
-  const int nkeys = (int)(ks1 - ks0);
-  const int ntile = (nkeys + BK - 1) / BK;
+  // keys of split 2 sp + h: [ks0[h], ks0[h] + nk[h]); the second may be empty
+  long long ks0[SPW];
+  int nk[SPW];
+#pragma unroll
+  for (int h = 0; h < SPW; ++h) {
+    ks0[h] = (long long)(SPW * blockIdx.y + h) * a.split_keys;
+    const long long e = (ks0[h] + a.split_keys < len) ? ks0[h] + a.split_keys : len;
+    nk[h] = (e > ks0[h]) ? (int)(e - ks0[h]) : 0;
+  }
+  if (nk[0] == 0) return;   // uniform: the second split starts later still
+  const int ntile = (nk[0] + BK - 1) / BK;                 // steps of the loop (the longer split)
+  const int my_nk = nk[half];
+  const int my_ntile = (my_nk + BK - 1) / BK;
 
-  // ---- this lane's 16-byte slots of a tile ------------------------------------
+  // ---- the 16-byte slots of a tile a producer copies ------------------------
   // Load instruction ii = wave + 4u fills LDS bytes [1024 ii', +1024) of the
   // K stage (ii < 24, ii' = ii) or the V stage (ii' = ii - 24).  K slot s is
   // row s / 96, physical chunk pc = s % 96 holding logical chunk pc ^ row%16
   // (XOR on the low four bits, within its aligned 256 B); V slot s is row
   // s / 64, physical 32-byte unit (s % 64) / 2 holding logical unit
-  // unit ^ row%8.  Rows past the split reload its last key (masked later).
-  const unsigned char* kbase = static_cast<const unsigned char*>(a.k) +
-                               (((row0 + ks0) * a.hkv + HG * gx) * (long long)D) * 2;
-  const unsigned char* vbase = static_cast<const unsigned char*>(a.v) +
-                               (((row0 + ks0) * a.hkv + HG * gx) * (long long)DV) * 2;
+  // unit ^ row%8.  Rows past a split reload its last key (masked later); an
+  // empty second split reloads the first one's rows (never read).
+  const unsigned char* kbase[SPW];
+  const unsigned char* vbase[SPW];
+  int lastkey[SPW];
+#pragma unroll
+  for (int h = 0; h < SPW; ++h) {
+    const int hh = (nk[h] > 0) ? h : 0;
+    kbase[h] = static_cast<const unsigned char*>(a.k) +
+               (((row0 + ks0[hh]) * a.hkv + HG * gx) * (long long)D) * 2;
+    vbase[h] = static_cast<const unsigned char*>(a.v) +
+               (((row0 + ks0[hh]) * a.hkv + HG * gx) * (long long)DV) * 2;
+    lastkey[h] = nk[hh] - 1;
+  }
   const int kstride = a.hkv * D * 2, vstride = a.hkv * DV * 2;   // bytes per cache row
   int drow[DMA_PER_WAVE], doff[DMA_PER_WAVE];
 #pragma unroll
@@ -134,23 +160,29 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(AttnArgs a, int la
   // Addresses are a wave-uniform base plus a 32-bit per-lane offset (a
   // split spans at most split_keys * hkv * 384 bytes, and key and row
   // stride both fit 24 bits), the saddr form of the load: one 24-bit
-  // multiply-add per instruction.
-  auto issue = [&](int k0, unsigned char* kd, unsigned char* vd) {
+  // multiply-add per instruction.  The copies of tile t of both splits go
+  // into stage st (producers only).
+  auto issue = [&](int t, int st) {
 #pragma unroll
-    for (int u = 0; u < DMA_PER_WAVE; ++u) {
-      const int ii = wave + HG * u;
-      const int key = min(k0 + drow[u], nkeys - 1);
-      if (u < KINSTR / HG)   // wave-uniform: the first six instructions are K, the rest V
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(kbase + (__umul24(key, kstride) + doff[u])),
-                                         (lds_void_t*)(kd + 1024 * ii), 16, 0, 0);
-      else
-        __builtin_amdgcn_global_load_lds((glb_void_t*)(vbase + (__umul24(key, vstride) + doff[u])),
-                                         (lds_void_t*)(vd + 1024 * (ii - KINSTR)), 16, 0, 0);
+    for (int h = 0; h < SPW; ++h) {
+#pragma unroll
+      for (int u = 0; u < DMA_PER_WAVE; ++u) {
+        const int ii = wave + HG * u;
+        const int key = min(t * BK + drow[u], lastkey[h]);
+        if (u < KINSTR / HG)   // wave-uniform: the first six instructions are K, the rest V
+          __builtin_amdgcn_global_load_lds(
+              (glb_void_t*)(kbase[h] + (__umul24(key, kstride) + doff[u])),
+              (lds_void_t*)(kst[h][st] + 1024 * ii), 16, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds(
+              (glb_void_t*)(vbase[h] + (__umul24(key, vstride) + doff[u])),
+              (lds_void_t*)(vst[h][st] + 1024 * (ii - KINSTR)), 16, 0, 0);
+      }
     }
   };
   static_assert(KINSTR / HG == 6, "the K/V split of a wavefront's loads");
 
-  issue(0, kst0, vst0);
+  if (producer) issue(0, 0);
 
   // q of head g*G + c (rotated to position p by the preparation kernel when
   // RoPE is on); columns c >= G are padding.
@@ -162,7 +194,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(AttnArgs a, int la
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = as_bf16x8(c < G ? ld16(qrow + 32 * ks) : make_uint4(0, 0, 0, 0));
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): q and tile 0 have landed
 
   const float c2 = a.scale * kLog2e;   // raw score -> base-2 units
   float m = kNegInf, l = 0.f;
@@ -177,26 +208,24 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(AttnArgs a, int la
   const int vr = 4 * grp + (c >> 2);
   const int vrow = vr * VROW + 8 * (c & 3);
 
-  auto tile = [&](int t, const unsigned char* kc, const unsigned char* vc, unsigned char* kn,
-                  unsigned char* vn) __attribute__((always_inline)) {
-    // Tile t's loads are this wavefront's only ones in flight.  The wait is
-    // explicit: the compiler does not reliably carry a pending LDS-DMA
-    // write across the loop back-edge into the barrier's fence.
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __syncthreads();   // every wavefront's share of tile t has landed; tile t-1 is consumed
-    if (t + 1 < ntile) issue((t + 1) * BK, kn, vn);
+  // one tile from its stage; the LDS reads are inline asm that wait for
+  // their own data, so the compiler's wait analysis adds no wait for the
+  // copies of the next tile still in flight
+  auto tile = [&](int t, const unsigned char* kc, const unsigned char* vc) __attribute__((always_inline)) {
     const int k0 = t * BK;
+    uint32_t kad[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kad[ks] = lds_off(kc + krow + 16 * ((24 * wave + 4 * ks + grp) ^ c));
+    uint4 kw[KS];
+    lds_b128x6(kw, kad);
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int q = 24 * wave + 4 * ks + grp;
-      sc = mfma16(as_bf16x8(ld16(kc + krow + 16 * (q ^ c))), qf[ks], sc);
-    }
+    for (int ks = 0; ks < KS; ++ks) sc = mfma16(as_bf16x8(kw[ks]), qf[ks], sc);
     // Branch-free on purpose: the first VALU read of an MFMA result needs
     // wait states after it, and with a branch between them the compiler
     // did not insert them on the path that skips the branch body.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = (k0 + 4 * grp + r < nkeys) ? sc[r] : kNegInf;
+    for (int r = 0; r < 4; ++r) sc[r] = (k0 + 4 * grp + r < my_nk) ? sc[r] : kNegInf;
     float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = max_across_groups(mx) * c2;   // base-2 units
     // Lazy rescaling: the reference m moves only when a column's tile max
@@ -222,23 +251,30 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(AttnArgs a, int la
     const v4i16 pb = __builtin_bit_cast(v4i16, pk);
     // -- O^T += V^T . P^T: lane (c, grp) holds keys 4 grp + r, the k-index of
     //    the 16x16x16 form; the transposed read gives V[4 grp + r][16 tt + c]
+    uint32_t vad[NT];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      const uint2 vt = lds_tr4(vc + vrow + 32 * ((8 * wave + tt) ^ (vr & 7)));
-      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, vt), pb,
+    for (int tt = 0; tt < NT; ++tt) vad[tt] = lds_off(vc + vrow + 32 * ((8 * wave + tt) ^ (vr & 7)));
+    uint2 vt[NT];
+    lds_tr4x8(vt, vad);
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, vt[tt]), pb,
                                                          acc[tt], 0, 0, 0);
-    }
   };
+  static_assert(NT == 8 && KS == 6, "the read helpers take six K and eight V pieces");
 
-  int t = 0;
-  for (; t + 2 <= ntile; t += 2) {
-    tile(t, kst0, vst0, kst1, vst1);
-    tile(t + 1, kst1, vst1, kst0, vst0);
+  // A producer's loads in flight at step t are tile t's 20 (and, at t = 0,
+  // its q loads); tile t + 1 goes to the stage tile t - 1 used.
+  for (int t = 0; t < ntile; ++t) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    ring_barrier();   // every share of tile t has landed; tile t-1 is consumed
+    if (producer && t + 1 < ntile) issue(t + 1, (t + 1) & 1);
+    if (t < my_ntile) tile(t, kst[half][t & 1], vst[half][t & 1]);   // uniform per wavefront
   }
-  if (t < ntile) tile(t, kst0, vst0, kst1, vst1);
 
+  const int s = SPW * blockIdx.y + half;
   l = sum_across_groups(l);
-  if (g < a.hkv && c < G) {
+  if (my_nk > 0 && g < a.hkv && c < G) {
     const long long idx = ((long long)b * a.hq + g * G + c) * a.nsplit + s;
     float* wo = a.ws + idx * DV + 4 * grp;
 #pragma unroll
@@ -557,8 +593,8 @@ hipError_t launch_decode_bf16(const AttnArgs& a, int layout, hipStream_t stream)
                        stream, a);
     return hipGetLastError();
   }
-  dim3 g1((unsigned)(a.hkv / HG), (unsigned)a.nsplit, (unsigned)a.B);
-  hipLaunchKernelGGL(decode_split_kernel, g1, dim3(256), 0, stream, a, layout);
+  dim3 g1((unsigned)(a.hkv / HG), (unsigned)((a.nsplit + SPW - 1) / SPW), (unsigned)a.B);
+  hipLaunchKernelGGL(decode_split_kernel, g1, dim3(64 * HG * SPW), 0, stream, a, layout);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_combine(a, layout, stream);
