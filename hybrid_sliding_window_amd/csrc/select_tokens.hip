@@ -423,12 +423,27 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
     const int ntile = (cand_keys + BK - 1) / BK;
     __syncthreads();                       // the previous item's tiles are consumed
     if (ntile > 0) issue(0, cand_keys, kst0);
+    // A tile's importances are stored one tile late, after the next tile's
+    // copies have gone out: the wait for a tile's copies (vmcnt counts the
+    // stores too, and they may complete out of order with the loads) then
+    // finds stores issued a whole tile earlier, not ones just issued.
+    unsigned* const st0 = hi ? scr[1] : scr[0];   // this lane's stored rows: 1 or 0 ...
+    unsigned* const st1 = hi ? scr[3] : scr[2];   // ... and 3 or 2
+    unsigned pend0 = 0u, pend1 = 0u;
+    int jpend = 0;
+    // the candidate count and ranking mode of the rows this lane stores
+    const int ncl[2] = {hi ? ncand[1] : ncand[0], hi ? ncand[3] : ncand[2]};
+    const bool rankl[2] = {(hi ? mode[1] : mode[0]) == 2, (hi ? mode[3] : mode[2]) == 2};
     for (int t = 0; t < ntile; ++t) {
       unsigned char* cur = (t & 1) ? kst1 : kst0;
       unsigned char* nxt = (t & 1) ? kst0 : kst1;
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's copies of tile t
       __syncthreads();                     // everyone's copies landed; tile t - 1 consumed
       if (t + 1 < ntile) issue((t + 1) * BK, cand_keys, nxt);
+      if (t > 0) {   // words past the row's candidates, within its round64(n), are never read
+        st0[jpend] = pend0;
+        st1[jpend] = pend1;
+      }
       const uint32_t base = lds_addr(cur);
       uint32_t ad[4];
 #pragma unroll
@@ -464,12 +479,17 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
         }
         const int rr = 2 * nb + hi;          // the row this lane stores and counts
         const unsigned u = __float_as_uint(hi ? imp2[1] : imp2[0]);
-        const int nc = hi ? ncand[2 * nb + 1] : ncand[2 * nb];
-        const bool rank = hi ? mode[2 * nb + 1] == 2 : mode[2 * nb] == 2;
-        // words past the row's candidates, within its round64(n), are never read
-        (hi ? scr[2 * nb + 1] : scr[2 * nb])[j] = u;
+        const int nc = ncl[nb];
+        const bool rank = rankl[nb];
+        if (nb == 0) pend0 = u;
+        else pend1 = u;
         if (j < nc && rank) lds_inc(lds_addr(&hist[RW * wave + rr][u >> 21]));
       }
+      jpend = j;
+    }
+    if (ntile > 0) {
+      st0[jpend] = pend0;
+      st1[jpend] = pend1;
     }
 
     // ---- level-1 bin of each ranking row, and how many candidates are in it
