@@ -423,10 +423,10 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
     const int ntile = (cand_keys + BK - 1) / BK;
     __syncthreads();                       // the previous item's tiles are consumed
     if (ntile > 0) issue(0, cand_keys, kst0);
-    // A tile's importances are stored one tile late, after the next tile's
-    // copies have gone out: the wait for a tile's copies (vmcnt counts the
-    // stores too, and they may complete out of order with the loads) then
-    // finds stores issued a whole tile earlier, not ones just issued.
+    // A tile's importances are stored one tile late, right after the next
+    // tile's copies have gone out: the vmcnt(0) that waits for a tile's
+    // copies also waits for every store issued before it, and these were
+    // issued a whole tile earlier instead of just before the wait.
     unsigned* const st0 = hi ? scr[1] : scr[0];   // this lane's stored rows: 1 or 0 ...
     unsigned* const st1 = hi ? scr[3] : scr[2];   // ... and 3 or 2
     unsigned pend0 = 0u, pend1 = 0u;
