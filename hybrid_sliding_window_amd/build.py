@@ -27,9 +27,12 @@ SOURCES = ["api.cpp", "rope_prep.hip", "generic.hip", "prefill_bf16.hip", "prefi
 
 # Per-source flags.  The matrix-core prefill kernels keep their accumulators
 # in ordinary VGPRs (the VALU rescales them in place); without this the
-# allocator parks them in AGPRs and copies them every tile.
+# allocator parks them in AGPRs and copies them every tile.  The GA kernel
+# also takes the scheduler strategy that groups memory instructions
+# (measured 21.73 -> 21.49 ms on the GA workload, bit-identical outputs).
 EXTRA_FLAGS = {"prefill_seq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-               "prefill_causal.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+               "prefill_causal.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
+                                      "-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
 
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-fno-honor-nans",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
