@@ -132,6 +132,9 @@ inline size_t select_scratch_bytes(int n) {
 inline size_t select_lse_bytes(int B, int n, int hq) { return (size_t)B * n * hq * 4; }
 bool select_tokens_supported(const AttnArgs& a);
 hipError_t launch_select_tokens(const AttnArgs& a, hipStream_t stream);
+// The first of the two: sel_lse for the rows that rank their candidates,
+// on up to two workgroups per compute unit (cus of them).
+hipError_t launch_select_lse(const AttnArgs& a, int cus, hipStream_t stream);
 
 // dst[row] = src[row] with its first 2 * half dims rotated at position
 // pos0 + (row / heads) % n (cos/sin as launch_rope_k_direct), the rest copied;

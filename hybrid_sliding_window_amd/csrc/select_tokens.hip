@@ -9,22 +9,23 @@
 // importance, equal importances going to the lower position, in ascending
 // order: the lists sparse attention reads.
 //
-// Two kernels.  The first, select_lse_kernel, writes lse_hi (base 2) for
-// every (row, head) of the rows that rank their candidates.  In the second,
-// a workgroup of eight wavefronts owns 16 consecutive query rows of one
-// (sequence, kv head) with G = 16 query heads, two rows per wavefront, so
-// every per-row state (histograms, thresholds, output offsets) belongs to
-// one wavefront and needs no synchronisation.  A wavefront's scores are
-// S = Q . K^T on 32x32x16 MFMAs with its two rows' 16 heads each on M and
-// the 32 keys of a tile on N: lane (key c, half h) holds eight heads of each
-// row for key c, so a key's importance is eight exponentials summed in the
-// lane and one exchange across the halves, and lanes 0..31 own the keys in
-// order.  K tiles of 32 keys stream through LDS with global_load_lds, shared
-// by all 16 rows.  Passes:
-//   1. (first kernel) lse_hi per (row, head), online max / sum in base 2;
+// Two kernels.  The first, select_lse_kernel (select_lse.hip), writes lse_hi
+// (base 2) for every (row, head) of the rows that rank their candidates.  In
+// the second, select_tokens_kernel, a workgroup of eight wavefronts owns 32
+// consecutive query rows of one (sequence, kv head) with G = 16 query heads,
+// four rows per wavefront, so every per-row state (histograms, thresholds,
+// output offsets) belongs to one wavefront and needs no synchronisation.  A
+// wavefront's scores are S = Q . K^T on 32x32x16 MFMAs, two blocks of two
+// rows x 16 heads on M and the 32 keys of a tile on N: lane (key c, half h)
+// holds eight heads of each row for key c, so a key's importance is eight
+// exponentials summed in the lane and one exchange across the halves, and
+// lanes 0..31 own the keys in order.  K tiles of 32 keys stream through LDS
+// with global_load_lds, shared by all 32 rows.  Passes:
+//   1. (first kernel) lse_hi per (row, head), online sum in base 2;
 //   2. importance of every candidate (probabilities summed over the 16
-//      heads), a 2048-bin histogram of its bits 31..21 per row in LDS, then
-//      the bin holding the max_sel-th largest;
+//      heads), stored to the workgroup's scratch slot and counted in a
+//      1024-bin histogram of its bits 30..21 per row in LDS (importances are
+//      >= 0, so bit 31 is 0), then the bin holding the max_sel-th largest;
 //   3. inside that bin, a histogram of bits 20..10: the threshold t of the
 //      22-bit key (importance >> 10, i.e. exponent and 13 mantissa bits) and
 //      how many keys equal to t are taken;
@@ -36,51 +37,19 @@
 
 #include "common.h"
 #include "launch.h"
+#include "select_ops.h"
 
 namespace hswa {
 namespace {
 
-constexpr int D = 192;
-constexpr int KS = D / 16;              // k-steps of the 32x32x16 MFMA
-constexpr int GQ = 16;                   // query heads per kv head (one MFMA column block)
 constexpr int NW = 8;                    // wavefronts per workgroup
 constexpr int RW = 4;                    // rows per wavefront: two blocks of 2 rows x 16 heads
 constexpr int ROWS = NW * RW;            // 32 query rows per workgroup
 static_assert(ROWS == kSelectRows, "select_scratch_bytes sizes slots of kSelectRows rows");
-constexpr int BK = 32;                   // keys per LDS tile
-constexpr int KROW = D * 2;              // 384 B per key row
-constexpr int KTILE = BK * KROW;         // 12 KB
-constexpr int KINSTR = KTILE / 1024;     // 12 copies of 1 KB
 constexpr int NBIN1 = 1024;              // level-1 bins: bits 30..21 (importances are >= 0)
 constexpr int NBIN2 = 2048;              // level-2 bins: bits 20..10
 constexpr int UNR = 8;                   // 16-byte scratch loads in flight per lane
 constexpr int LCAP = kSelectListCap;     // compact-list entries per row
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
-// Max / sum over the 16 lanes of a DPP row, left in every lane: pairs
-// within quads (quad_perm 1,0,3,2 and 2,3,0,1), then quad with quad
-// (row_half_mirror), then half-row with half-row (row_mirror).  Each step
-// pairs every lane with one partner, so all 16 lanes end with the result.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float max16(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));    // quad_perm [1, 0, 3, 2]
-  v = fmaxf(v, dpp<0x4E>(v));    // quad_perm [2, 3, 0, 1]
-  v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
-  v = fmaxf(v, dpp<0x140>(v));   // row_mirror
-  return v;
-}
-__device__ __forceinline__ float sum16(float v) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  v += dpp<0x141>(v);
-  v += dpp<0x140>(v);
-  return v;
-}
 
 // Wave-wide inclusive sum of v over lanes >= this lane (suffix sum).
 __device__ __forceinline__ unsigned suffix_sum(unsigned v, int lane) {
@@ -125,76 +94,6 @@ __device__ __forceinline__ void find_bin(const unsigned* h, unsigned need, int l
   *bin = __shfl(b, src);
   *above = __shfl(ab, src);
 }
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// The partner of v across DPP rows: v_permlane16_swap on two copies of v
-// leaves rows (0, 0, 2, 2) in one and (1, 1, 3, 3) in the other;
-// v_permlane32_swap leaves the lower half twice in one and the upper half
-// twice in the other.  Both are VALU moves (no LDS round trip), and both
-// lanes of a pair see the operands in the same order.
-struct Pair {
-  float a, b;
-};
-__device__ __forceinline__ Pair rows16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
-}
-__device__ __forceinline__ Pair halves32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
-}
-
-// Max / sum over the 32 lanes of a wavefront half (two DPP rows).
-__device__ __forceinline__ float max32(float v) {
-  const Pair p = rows16(max16(v));
-  return fmaxf(p.a, p.b);
-}
-__device__ __forceinline__ float sum32(float v) {
-  const Pair p = rows16(sum16(v));
-  return p.a + p.b;
-}
-
-// The twelve K operands of one key row: k-step 4 u + b sits 128 u bytes on
-// from ad[b].  In asm: for a plain read the compiler would also wait for the
-// next tile's copies in flight; the copies of this tile have been waited for
-// before the barrier.  The block waits for its own reads before it returns.
-__device__ __forceinline__ void lds_k12(bf16x8 (&f)[KS], const uint32_t (&ad)[4]) {
-  uint4 r0, r1, r2, r3, r4, r5, r6, r7, r8, r9, r10, r11;
-  asm volatile(
-      "ds_read_b128 %0, %12\n\t"
-      "ds_read_b128 %1, %13\n\t"
-      "ds_read_b128 %2, %14\n\t"
-      "ds_read_b128 %3, %15\n\t"
-      "ds_read_b128 %4, %12 offset:128\n\t"
-      "ds_read_b128 %5, %13 offset:128\n\t"
-      "ds_read_b128 %6, %14 offset:128\n\t"
-      "ds_read_b128 %7, %15 offset:128\n\t"
-      "ds_read_b128 %8, %12 offset:256\n\t"
-      "ds_read_b128 %9, %13 offset:256\n\t"
-      "ds_read_b128 %10, %14 offset:256\n\t"
-      "ds_read_b128 %11, %15 offset:256\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6),
-        "=&v"(r7), "=&v"(r8), "=&v"(r9), "=&v"(r10), "=&v"(r11)
-      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
-      : "memory");
-  f[0] = as_bf16x8(r0);
-  f[1] = as_bf16x8(r1);
-  f[2] = as_bf16x8(r2);
-  f[3] = as_bf16x8(r3);
-  f[4] = as_bf16x8(r4);
-  f[5] = as_bf16x8(r5);
-  f[6] = as_bf16x8(r6);
-  f[7] = as_bf16x8(r7);
-  f[8] = as_bf16x8(r8);
-  f[9] = as_bf16x8(r9);
-  f[10] = as_bf16x8(r10);
-  f[11] = as_bf16x8(r11);
-}
-static_assert(KS == 12, "twelve k-steps of 16 dims");
 
 // The same operands in two halves of six k-steps (0..5, then 6..11), so that
 // only half of them is live at a time.
@@ -682,164 +581,6 @@ __global__ __launch_bounds__(512, 1) void select_tokens_kernel(AttnArgs a) {
   }  // items
 }
 
-// lse_hi = log2 sum_{j <= i} 2^(c2 s_hij) for every (row, head) of the rows
-// that rank their candidates (i - recent + 1 > max_sel > 0).  A workgroup of
-// four wavefronts owns 16 consecutive rows of one (sequence, kv head), four
-// rows per wavefront: two blocks of 32 (row, head) columns, row 2 nb + c / 16
-// of the wavefront and head c % 16 in column c of block nb.  Each block's
-// product is K . Q^T with the 32 keys of a tile on M, so lane (column c,
-// half h) holds 16 keys of one (row, head): the running max moves once per
-// tile and each score costs one exponential and an add.  The two lane halves
-// hold different keys of the same column and are merged at the end.  Two
-// workgroups share a compute unit, one wavefront of each per SIMD, so that
-// the matrix products of one overlap the exponentials of the other.
-constexpr int LNW = 4;                           // wavefronts per workgroup
-constexpr int LRW = 4;                           // rows per wavefront
-constexpr int LROWS = LNW * LRW;                 // 16 rows per workgroup
-constexpr int LCP = KINSTR / LNW;                // 1 KB tile copies per wavefront
-static_assert(KINSTR % LNW == 0, "copies split evenly over the wavefronts");
-constexpr int LNS = 4;                           // K tile stages: copies run three tiles ahead
-static_assert(LCP == 3, "the waits below count three copies per tile");
-__global__ __launch_bounds__(LNW * 64, 2) void select_lse_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char kst[LNS][KTILE];
-  constexpr int RW = LRW;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, c = lane & 31, hi = lane >> 5;
-  const int n = a.n, hkv = a.hkv, K = a.max_sel, recent = a.recent;
-  const int nblk = (n + LROWS - 1) / LROWS;
-  const int ngrp = a.B * hkv;
-  const int items = ngrp * nblk;
-  const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
-  const float c2 = a.scale * kLog2e;
-  const bf16_t* __restrict__ Qp = static_cast<const bf16_t*>(a.half > 0 ? a.qrot : a.q);
-  const bf16_t* __restrict__ Kp = static_cast<const bf16_t*>(a.half > 0 ? a.krot : a.k);
-  const int kstride = hkv * KROW;
-
-  // K tile copies (layout as in the selection kernel; wavefront w issues
-  // copies w, w + 4, w + 8) and operand addresses
-  int drow[LCP], doff[LCP];
-#pragma unroll
-  for (int u = 0; u < LCP; ++u) {
-    const int sl = 64 * (wave + LNW * u) + lane;
-    const int row = sl / 24, pc = sl - row * 24;
-    drow[u] = row;
-    doff[u] = 16 * (pc ^ ((row >> 1) & 7));
-  }
-  uint32_t koff[4];
-#pragma unroll
-  for (int bb = 0; bb < 4; ++bb) koff[bb] = c * KROW + 16 * ((2 * bb + hi) ^ ((c >> 1) & 7));
-
-  // heaviest items first, alternating direction per round (as the selection kernel)
-  for (int r = 0; r * nwg < items; ++r) {
-    const int item = r * nwg + ((r & 1) ? nwg - 1 - wg : wg);
-    if (item >= items) continue;
-    const int blk = nblk - 1 - item / ngrp;
-    const int bg = item - (item / ngrp) * ngrp;
-    const int b = bg / hkv, g = bg - b * hkv;
-    const int i0 = blk * LROWS;
-    const int ilast = min(n - 1, i0 + LROWS - 1);
-    // the block's last row has the most candidates: nothing to rank if it keeps them all
-    if (K <= 0 || ilast - recent + 1 <= K) continue;
-    const long long tokbase = (long long)b * n;
-    const int r0 = i0 + RW * wave;               // the wavefront's first row
-
-    int myrow[2];
-    bf16x8 qf[2][KS];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      myrow[nb] = r0 + 2 * nb + (c >> 4);
-      const bf16_t* qrow =
-          Qp + ((tokbase + min(myrow[nb], n - 1)) * a.hq + g * GQ + (c & 15)) * D + 8 * hi;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[nb][ks] = as_bf16x8(ld16(qrow + 16 * ks));
-    }
-    const unsigned char* kbase =
-        reinterpret_cast<const unsigned char*>(Kp + (tokbase * hkv + g) * D);
-    auto issue = [&](int k0, int kend, unsigned char* kd) {
-#pragma unroll
-      for (int u = 0; u < LCP; ++u) {
-        const int key = min(k0 + drow[u], kend - 1);
-        __builtin_amdgcn_global_load_lds(
-            (glb_void_t*)(kbase + ((long long)key * kstride + doff[u])),
-            (lds_void_t*)(kd + 1024 * (wave + LNW * u)), 16, 0, 0);
-      }
-    };
-
-    // running (max, sum) of the lane's column in each block over its keys;
-    // the max starts finite, so a masked key (-inf) needs no special case
-    float m[2] = {-__FLT_MAX__, -__FLT_MAX__}, l[2] = {0.f, 0.f};
-    const int nkeys = ilast + 1;
-    const int ntile = (nkeys + BK - 1) / BK;
-    __syncthreads();                             // the previous item's tiles are consumed
-    for (int t = 0; t < LNS - 1 && t < ntile; ++t) issue(t * BK, nkeys, kst[t]);
-    for (int t = 0; t < ntile; ++t) {
-      unsigned char* cur = kst[t % LNS];
-      // this wavefront's copies of tile t have landed once at most those of
-      // the (up to two) tiles issued after it are outstanding
-      const int ahead = min(ntile - 1 - t, LNS - 2);
-      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F76);        // vmcnt(6)
-      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F73);   // vmcnt(3)
-      else __builtin_amdgcn_s_waitcnt(0x0F70);                   // vmcnt(0)
-      __syncthreads();                           // everyone's copies landed; tile t - 1 consumed
-      if (t + LNS - 1 < ntile) issue((t + LNS - 1) * BK, nkeys, kst[(t + LNS - 1) % LNS]);
-      const int k0 = t * BK;
-      if (k0 > r0 + RW - 1) continue;            // keys past all of the wavefront's rows
-      const uint32_t base = lds_addr(cur);
-      uint32_t ad[4];
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) ad[bb] = base + koff[bb];
-      bf16x8 kf[KS];
-      lds_k12(kf, ad);
-      f32x16 sc[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) sc[nb][e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) sc[nb] = mfma32(kf[ks], qf[nb][ks], sc[nb]);
-      // element e is key k0 + 8 (e / 4) + 4 hi + e % 4
-      const bool diag = k0 + BK - 1 > r0;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        f32x16 x = sc[nb];
-        if (diag) {
-          // key k0 + kk (kk = 8 (e / 4) + 4 hi + e % 4) is visible iff kk <= dhi
-          const int dhi = myrow[nb] - (k0 + 4 * hi);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int kk = 8 * (e >> 2) + (e & 3);
-            x[e] = (kk > dhi) ? kNegInf : x[e];
-          }
-        }
-        float mx = fmaxf(x[0], x[1]);
-#pragma unroll
-        for (int e = 2; e < 16; ++e) mx = fmaxf(mx, x[e]);
-        const float mn = fmaxf(m[nb], mx * c2);
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) part[e & 3] += fast_exp2(fmaf(x[e], c2, -mn));
-        l[nb] = fmaf(l[nb], fast_exp2(m[nb] - mn), (part[0] + part[1]) + (part[2] + part[3]));
-        m[nb] = mn;
-      }
-    }
-    // merge the two halves' keys; lane (c, h) writes column c of block h
-    float out[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const Pair pm = halves32(m[nb]), pl = halves32(l[nb]);
-      const float M = fmaxf(pm.a, pm.b);
-      const float L = pl.a * fast_exp2(pm.a - M) + pl.b * fast_exp2(pm.b - M);
-      out[nb] = M + __log2f(L);
-    }
-    const int row = r0 + 2 * hi + (c >> 4);
-    if (row < n) a.sel_lse[(tokbase + row) * a.hq + g * GQ + (c & 15)] = hi ? out[1] : out[0];
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);            // no copy into LDS outlives the workgroup
-}
-
 bool select_tokens_supported(const AttnArgs& a) {
   return a.d_qk == D && a.hq == GQ * a.hkv && 2 * a.half <= D;
 }
@@ -853,10 +594,7 @@ hipError_t launch_select_tokens(const AttnArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const long long lse_items = (long long)a.B * a.hkv * ((a.n + LROWS - 1) / LROWS);
-  const unsigned lse_grid = (unsigned)(lse_items < 2 * cus ? lse_items : 2 * cus);
-  hipLaunchKernelGGL(select_lse_kernel, dim3(lse_grid), dim3(LNW * 64), 0, stream, a);
-  e = hipGetLastError();
+  e = launch_select_lse(a, cus, stream);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(items < kSelectSlots ? items : kSelectSlots);
   hipLaunchKernelGGL(select_tokens_kernel, dim3(grid), dim3(NW * 64), 0, stream, a);

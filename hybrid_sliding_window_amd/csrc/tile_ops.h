@@ -41,6 +41,10 @@ __device__ __forceinline__ void g2lds16_nt(const void* src, void* lds_base) {
 
 
 constexpr float kLazy = 8.f;
+// The two matrix-core prefill kernels sum a tile's P (per lane, 16 keys)
+// against the current reference and move the reference only when that sum
+// passes kLazySum: every P is then at most 2^12, well inside bf16 and fp32.
+constexpr float kLazySum = 4096.f;
 
 // vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt bits
 // 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
