@@ -344,16 +344,27 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
           x[v] = (kk > dhi || kk < dlo) ? kNegInf : x[v];
         }
       }
+      // P against the current reference first; only a tile whose P sum
+      // passes kLazySum (a key more than ~12 above the reference in log2
+      // units) or a row with no reference yet takes the row max and moves
+      // the reference, so the common path has no max over the scores
       const float ms = (m == kNegInf) ? 0.f : m;
-      float xm = kNegInf;
+      float p[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        x[v] = fmaf(x[v], c2, -ms);
-        xm = fmaxf(xm, x[v]);
-      }
-      if (__any(m == kNegInf || xm > kLazy)) {
+      for (int v = 0; v < 16; ++v) p[v] = fast_exp2(fmaf(x[v], c2, -ms));
+      pb0 = pack8(p);
+      pb1 = pack8(p + 8);
+      float t = 0.f;
+      t = add_bf16_pair(pb0.x, t); t = add_bf16_pair(pb0.y, t);
+      t = add_bf16_pair(pb0.z, t); t = add_bf16_pair(pb0.w, t);
+      t = add_bf16_pair(pb1.x, t); t = add_bf16_pair(pb1.y, t);
+      t = add_bf16_pair(pb1.z, t); t = add_bf16_pair(pb1.w, t);
+      if (__any(m == kNegInf || !(t <= kLazySum))) {
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-        const float mx = fmaxf(xm, __shfl_xor(xm, 32)) + ms;
+        float xm = kNegInf;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) xm = fmaxf(xm, x[v]);
+        const float mx = fmaxf(xm, __shfl_xor(xm, 32)) * c2;
         const float mn = fmaxf(m, mx);
         if (mn > m) {
           const float alpha = fast_exp2(m - mn);
@@ -362,20 +373,19 @@ __global__ __launch_bounds__(512, 1) void prefill_seq_kernel(AttnArgs a, int log
           for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
           m = mn;
         }
-        const float shift = ms - ((m == kNegInf) ? 0.f : m);
+        const float mr = (m == kNegInf) ? 0.f : m;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) x[v] += shift;
+        for (int v = 0; v < 16; ++v) p[v] = fast_exp2(fmaf(x[v], c2, -mr));
+        pb0 = pack8(p);
+        pb1 = pack8(p + 8);
+        t = 0.f;
+        t = add_bf16_pair(pb0.x, t); t = add_bf16_pair(pb0.y, t);
+        t = add_bf16_pair(pb0.z, t); t = add_bf16_pair(pb0.w, t);
+        t = add_bf16_pair(pb1.x, t); t = add_bf16_pair(pb1.y, t);
+        t = add_bf16_pair(pb1.z, t); t = add_bf16_pair(pb1.w, t);
         asm volatile("s_nop 4" ::: "memory");
       }
-      float p[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) p[v] = fast_exp2(x[v]);
-      pb0 = pack8(p);
-      pb1 = pack8(p + 8);
-      l = add_bf16_pair(pb0.x, l); l = add_bf16_pair(pb0.y, l);
-      l = add_bf16_pair(pb0.z, l); l = add_bf16_pair(pb0.w, l);
-      l = add_bf16_pair(pb1.x, l); l = add_bf16_pair(pb1.y, l);
-      l = add_bf16_pair(pb1.z, l); l = add_bf16_pair(pb1.w, l);
+      l += t;
     };
 
     for (int x = cur.ta; x <= cur.tb; ++x) {

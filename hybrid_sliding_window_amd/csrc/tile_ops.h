@@ -40,7 +40,6 @@ __device__ __forceinline__ void g2lds16_nt(const void* src, void* lds_base) {
 }
 
 
-constexpr float kLazy = 8.f;
 // The two matrix-core prefill kernels sum a tile's P (per lane, 16 keys)
 // against the current reference and move the reference only when that sum
 // passes kLazySum: every P is then at most 2^12, well inside bf16 and fp32.
