@@ -283,24 +283,34 @@ __global__ __launch_bounds__(256 * CW, (NST == 2 && CW == 1) ? 2 : 1) void decod
     for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) sc[nb][r] = vis[nb][r] ? sc[nb][r] : kNegInf;
-      float mx = fmaxf(fmaxf(sc[nb][0], sc[nb][1]), fmaxf(sc[nb][2], sc[nb][3]));
-      mx = max_across_groups(mx) * c2;
-      // lazy rescaling, as the single-token decode
-      if (__any(mx > m[nb] + kDecLazy)) {
+      // lazy rescaling checked on the P sum: P against the current
+      // reference first; only a lane whose four P sum past kDecLazySum (a key
+      // more than ~10 above the reference in log2 units) or a column with no
+      // reference yet sends the wavefront to take the column max across the
+      // lane groups and move the reference, so the common path has no max
+      float ms = (m[nb] == kNegInf) ? 0.f : m[nb];
+      float pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(fmaf(sc[nb][r], c2, -ms));
+      pk[nb] = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
+      float ts = add_bf16_pair(pk[nb].y, add_bf16_pair(pk[nb].x, 0.f));
+      if (__any(m[nb] == kNegInf || !(ts <= kDecLazySum))) {
+        float mx = fmaxf(fmaxf(sc[nb][0], sc[nb][1]), fmaxf(sc[nb][2], sc[nb][3]));
+        mx = max_across_groups(mx) * c2;
         const float mn = fmaxf(m[nb], mx);
         const float alpha = fast_exp2(m[nb] - ((mn == kNegInf) ? 0.f : mn));
         l[nb] *= alpha;
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) acc[tt][nb] *= alpha;
         m[nb] = mn;
+        ms = (mn == kNegInf) ? 0.f : mn;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(fmaf(sc[nb][r], c2, -ms));
+        pk[nb] = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
+        ts = add_bf16_pair(pk[nb].y, add_bf16_pair(pk[nb].x, 0.f));
         asm volatile("s_nop 4" ::: "memory");   // the PV products read acc below
       }
-      const float ms = (m[nb] == kNegInf) ? 0.f : m[nb];
-      float pv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pv[r] = fast_exp2(fmaf(sc[nb][r], c2, -ms));
-      pk[nb] = make_uint2(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]));
-      l[nb] += add_bf16_pair(pk[nb].y, add_bf16_pair(pk[nb].x, 0.f));
+      l[nb] += ts;
     }
     uint32_t vad[NT];
 #pragma unroll
