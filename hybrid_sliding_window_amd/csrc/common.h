@@ -109,9 +109,6 @@ __device__ __forceinline__ uint2 lds_tr4(const void* p) {
 // a tile's max passes it by more than this, so the probabilities stay
 // below 2^kDecLazy.
 constexpr float kDecLazy = 8.f;
-// The multi-token split kernel checks the sum of a lane's four P of a tile
-// against the current reference instead, so every P stays below 2^10.
-constexpr float kDecLazySum = 1024.f;
 
 // Workgroup barrier without the release fence of __syncthreads(), which
 // would wait for every copy in flight; the caller waits with an explicit

@@ -27,6 +27,11 @@
 namespace hswa {
 namespace {
 
+// The split kernel checks the sum of a lane's four P of a tile against the
+// current reference (rather than the tile max against kDecLazy), so every P
+// stays below 2^10.
+constexpr float kDecLazySum = 1024.f;
+
 constexpr int D = 192;
 constexpr int DV = 128;
 constexpr int KS = D / 32;
